@@ -1,0 +1,330 @@
+"""Reference oracle for the nanochat GPT forward pass with next-token loss.
+
+TEST INFRASTRUCTURE ONLY.  This package is a plain, slow, obviously correct CPU
+implementation of what the forward+loss path computes, written from the pages'
+equations in NumPy, in float64 by default.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import it.  The HIP library never calls it and shares no code with it; both
+sides only consume the seeded inputs of ``gptdata``.
+
+Sources (cited by page title and section):
+  [M]  "The Mathematics of Karpathy's nanochat" -- sections "High-Level Forward
+       Pass", "RMS Normalization", "Rotary Position Embeddings (RoPE)",
+       "Causal Self-Attention", "QK-Norm with Sharpening", "Scaled Dot-Product
+       Attention with Sliding Window", "Feed-Forward Network (MLP)", "Residual
+       Stream with Learnable Scalars", "Logit Softcap", "Cross-Entropy Loss",
+       "Pseudocode: One Training Step".
+  [R]  "Reading nanochat Source: From Configuration to a Training Step" --
+       sections 2 (shifted targets), 5.2-5.4 (attention order, block, LM head).
+  [S]  "nanochat depth sweep" -- section "Architecture" (SSSL windows, last
+       block full context, x0 re-injection, +-15 softcap).
+
+Readings where the pages are silent or disagree (each frozen as a config field
+so the oracle and the GPU path cannot silently diverge):
+  * attention logit = attn_scale * <q_hat, k_hat> with q_hat = RMSNorm(RoPE(q));
+    attn_scale defaults to 1/sqrt(head_dim).  [M] instead multiplies q and k
+    by 1.15 with no 1/sqrt(d) ("QK-Norm with Sharpening"); that reading is
+    attn_scale = 1.15**2 and needs no code change.
+  * RMSNorm(u) = u / sqrt(mean(u^2) + eps) with eps = cfg.norm_eps (1e-6):
+    [M] "RMS Normalization" defines it without eps and remarks that the
+    library call adds 1e-6.  Every norm (embedding, pre-attention, pre-MLP,
+    QK-norm, final) uses the same eps.
+  * window w counts visible keys including the query itself: key j is visible
+    from query i iff j <= i and i - j < w; w >= T is plain causal attention.
+  * SSSL pattern: layer l (0-based) takes pattern[l mod len(pattern)], and the
+    last layer is always long (w = T).  Short window = cfg.short_window.
+  * RoPE positions are 0..T-1 within each packed row; no document masking.
+  * GQA head map: query head h reads KV head floor(h * Hkv / H).
+  * ignored targets (-1) contribute a per-token loss of 0 and are excluded
+    from the mean; with no valid target the mean is NaN.
+
+Every function here is pinned by a ``-m "not gpu"`` test in
+``tests/test_oracle_pins.py`` to something other than itself (worked examples
+printed on the pages, closed forms, invariants, library routines or brute
+force); none is parity unpinned.
+"""
+from __future__ import annotations
+
+import math
+from typing import Any, Dict, List, Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "rms_norm", "rope_angles", "apply_rope", "layer_windows", "visible_mask",
+    "attention", "linear", "relu_squared", "softcap", "token_losses",
+    "mean_loss", "block", "forward_row", "forward",
+]
+
+
+# ----------------------------------------------------------------------------- RMSNorm
+
+def rms_norm(u: np.ndarray, eps: float = 0.0) -> np.ndarray:
+    """RMSNorm over the last axis, no gain and no bias.
+
+    [M] "RMS Normalization", Definition: divide by the root of the mean square
+    of the vector's entries (eps added inside the root, see module readings).
+    """
+    ms = np.mean(u * u, axis=-1, keepdims=True)
+    return u / np.sqrt(ms + eps)
+
+
+# ----------------------------------------------------------------------------- RoPE
+
+def rope_angles(T: int, head_dim: int, base: float, dtype=np.float64):
+    """cos/sin tables of shape [T, head_dim/2].
+
+    [M] "Rotary Position Embeddings (RoPE)", Frequency Construction:
+    omega_j = base^(-2j/d_h) for j < d_h/2 and angle phi_{t,j} = t * omega_j
+    for positions t = 0..T-1.  Computed in float64.
+    """
+    j = np.arange(head_dim // 2, dtype=np.float64)
+    omega = 1.0 / (float(base) ** (2.0 * j / head_dim))
+    t = np.arange(T, dtype=np.float64)
+    phi = np.outer(t, omega)
+    return np.cos(phi).astype(dtype), np.sin(phi).astype(dtype)
+
+
+def apply_rope(u: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
+    """Rotate u[..., T, heads, d] (positions along axis -3) by the half-split rule.
+
+    [M] "Rotary Position Embeddings (RoPE)", Rotation Application: with
+    u = [u1 | u2] split into halves, the result is
+    [u1 cos + u2 sin | -u1 sin + u2 cos] elementwise at the row's position.
+    ``cos``/``sin`` are [T, d/2]; they broadcast over the head axis.
+    """
+    d2 = u.shape[-1] // 2
+    u1, u2 = u[..., :d2], u[..., d2:]
+    c = cos[:, None, :]
+    s = sin[:, None, :]
+    return np.concatenate([u1 * c + u2 * s, -u1 * s + u2 * c], axis=-1)
+
+
+# ----------------------------------------------------------------------------- windows
+
+def layer_windows(pattern: str, short_window: int, seq_len: int, n_layer: int) -> List[int]:
+    """Per-layer window sizes for a tiled short/long pattern.
+
+    [M] "Sliding Window Pattern": the pattern string is tiled across the
+    layers, "L" means full context (w = T), "S" the short window, and the last
+    layer always gets full context.  [S] "Architecture" states the same for
+    the SSSL pattern.  The short window size follows the workload presets
+    (T/2), not the T/3 rounding of [M] (module readings).
+    """
+    out = []
+    for l in range(n_layer):
+        ch = pattern[l % len(pattern)]
+        if ch == "L":
+            out.append(seq_len)
+        elif ch == "S":
+            out.append(short_window)
+        else:
+            raise ValueError(f"unknown window character {ch!r}")
+    out[-1] = seq_len
+    return out
+
+
+def visible_mask(T: int, window: int) -> np.ndarray:
+    """Boolean [T, T]: key j visible from query i iff j <= i and i - j < window.
+
+    [M] "Scaled Dot-Product Attention with Sliding Window": the logit is kept
+    for j <= i and i - j < w, and is -inf otherwise.
+    """
+    i = np.arange(T)[:, None]
+    j = np.arange(T)[None, :]
+    return (j <= i) & (i - j < window)
+
+
+# ----------------------------------------------------------------------------- attention
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, window: int, scale: float) -> np.ndarray:
+    """Windowed causal softmax attention for one row.
+
+    q: [T, H, D]; k, v: [T, Hkv, D] with H a multiple of Hkv.  Returns [T, H, D].
+    [M] "Scaled Dot-Product Attention with Sliding Window": o_{h,i} is the
+    softmax-weighted sum of v_{h,j} over visible keys j.  Computed as an
+    explicit masked T x T matrix per head.  Query head h reads KV head
+    floor(h * Hkv / H) ([M] "Causal Self-Attention" allows Hkv < H without
+    fixing the map; contiguous groups are the reading used here).
+    """
+    T, H, D = q.shape
+    Hkv = k.shape[1]
+    mask = visible_mask(T, window)
+    out = np.empty_like(q)
+    for h in range(H):
+        g = (h * Hkv) // H
+        s = scale * (q[:, h, :] @ k[:, g, :].T)
+        s = np.where(mask, s, -np.inf)
+        m = np.max(s, axis=-1, keepdims=True)
+        e = np.exp(s - m)
+        a = e / np.sum(e, axis=-1, keepdims=True)
+        out[:, h, :] = a @ v[:, g, :]
+    return out
+
+
+# ----------------------------------------------------------------------------- MLP, head
+
+def linear(x: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """x @ w^T for a row-major [out, in] weight with no bias ([M] "Causal
+    Self-Attention", Projections; "Feed-Forward Network (MLP)")."""
+    return x @ w.T
+
+
+def relu_squared(z: np.ndarray) -> np.ndarray:
+    """max(0, z)^2 ([M] "Feed-Forward Network (MLP)")."""
+    r = np.maximum(z, 0.0)
+    return r * r
+
+
+def softcap(z: np.ndarray, cap: float = 15.0) -> np.ndarray:
+    """cap * tanh(z / cap) ([M] "Logit Softcap"; [R] 5.4)."""
+    return cap * np.tanh(z / cap)
+
+
+def token_losses(zhat: np.ndarray, targets: np.ndarray) -> np.ndarray:
+    """Per-token cross-entropy log(sum_v exp(zhat_v)) - zhat_y, 0 where y = -1.
+
+    [M] "Cross-Entropy Loss": negative log-softmax at the target, with targets
+    equal to -1 excluded.  logsumexp uses the row maximum as shift.
+    """
+    zhat = np.asarray(zhat)
+    m = np.max(zhat, axis=-1)
+    lse = m + np.log(np.sum(np.exp(zhat - m[..., None]), axis=-1))
+    valid = targets >= 0
+    idx = np.where(valid, targets, 0)
+    picked = np.take_along_axis(zhat, idx[..., None].astype(np.int64), axis=-1)[..., 0]
+    return np.where(valid, lse - picked, 0.0)
+
+
+def mean_loss(losses: np.ndarray, targets: np.ndarray) -> float:
+    """Mean over tokens with target != -1; NaN when there are none ([M]
+    "Cross-Entropy Loss", the set of kept positions)."""
+    valid = targets >= 0
+    n = int(np.count_nonzero(valid))
+    if n == 0:
+        return float("nan")
+    return float(np.sum(np.where(valid, losses, 0.0)) / n)
+
+
+# ----------------------------------------------------------------------------- forward
+
+def _get(params: Any, name: str, layer: Optional[int] = None):
+    a = params[name]
+    return a if layer is None else a[layer]
+
+
+def block(x: np.ndarray, x0: np.ndarray, l: int, cfg: Any, params: Any, window: int,
+          cos: np.ndarray, sin: np.ndarray, dt, internals: Optional[Dict] = None) -> np.ndarray:
+    """One transformer layer on one row x [T, C].
+
+    [M] "Residual Stream with Learnable Scalars" and "High-Level Forward Pass"
+    step 3: rescale x <- lambda_l x + mu_l x0, then x += Attn(RMSNorm(x)) and
+    x += MLP(RMSNorm(x)).  Inside attention ([M] "Causal Self-Attention",
+    "QK-Norm with Sharpening"; [R] 5.2): project q, k, v with no bias, RoPE on
+    q and k, per-head RMSNorm of q and k, windowed attention, merge heads,
+    output projection.
+    """
+    T, C = x.shape
+    H, Hkv, D = cfg.n_head, cfg.n_kv_head, cfg.head_dim
+    eps = cfg.norm_eps
+    lam = float(np.asarray(_get(params, "resid_lambda"))[l])
+    mu = float(np.asarray(_get(params, "x0_lambda"))[l])
+    x = lam * x + mu * x0
+    xin = x
+    xn = rms_norm(x, eps)
+    q = linear(xn, np.asarray(_get(params, "wq", l), dtype=dt)).reshape(T, H, D)
+    k = linear(xn, np.asarray(_get(params, "wk", l), dtype=dt)).reshape(T, Hkv, D)
+    v = linear(xn, np.asarray(_get(params, "wv", l), dtype=dt)).reshape(T, Hkv, D)
+    q = rms_norm(apply_rope(q, cos, sin), eps)
+    k = rms_norm(apply_rope(k, cos, sin), eps)
+    o = attention(q, k, v, window, cfg.attn_scale)
+    x = x + linear(o.reshape(T, H * D), np.asarray(_get(params, "wo", l), dtype=dt))
+    xa = x
+    xm = rms_norm(x, eps)
+    h = relu_squared(linear(xm, np.asarray(_get(params, "w1", l), dtype=dt)))
+    x = x + linear(h, np.asarray(_get(params, "w2", l), dtype=dt))
+    if internals is not None:
+        internals.update(xin=xin, xn=xn, q=q, k=k, v=v, o=o, x_attn=xa, xm=xm, h=h, x_out=x)
+    return x
+
+
+def forward_row(cfg: Any, params: Any, tokens: np.ndarray, targets: Optional[np.ndarray],
+                dtype=np.float64, want_logits: bool = False, want_internals: bool = False,
+                windows: Optional[Sequence[int]] = None) -> Dict[str, Any]:
+    """Forward pass of one packed row (tokens [T]) and its next-token loss.
+
+    [M] "High-Level Forward Pass" steps 1-6 and "Pseudocode: One Training
+    Step" steps 1-11: embed and RMSNorm, keep x0, L blocks, final RMSNorm,
+    untied lm_head, softcap, cross-entropy.  Rows of a batch never interact,
+    so a batch is this function applied row by row.
+    """
+    dt = np.dtype(dtype)
+    T = tokens.shape[0]
+    eps = cfg.norm_eps
+    if windows is None:
+        windows = layer_windows(cfg.window_pattern, cfg.short_window, cfg.seq_len, cfg.n_layer)
+    cos, sin = rope_angles(T, cfg.head_dim, cfg.rope_base, dtype=dt)
+    wte = np.asarray(_get(params, "wte"))
+    x = rms_norm(np.asarray(wte[tokens], dtype=dt), eps)
+    x0 = x
+    res: Dict[str, Any] = {}
+    layers = []
+    for l in range(cfg.n_layer):
+        internals = {} if want_internals else None
+        x = block(x, x0, l, cfg, params, windows[l], cos, sin, dt, internals)
+        if want_internals:
+            layers.append(internals)
+    xf = rms_norm(x, eps)
+    wu = np.asarray(_get(params, "lm_head"), dtype=dt)
+    if targets is not None:
+        # chunk over positions to bound the [T, V] logits held at once
+        losses = np.zeros(T, dtype=dt)
+        step = max(1, (1 << 24) // max(1, wu.shape[0]))
+        logits_parts = []
+        for a in range(0, T, step):
+            zh = softcap(linear(xf[a:a + step], wu), cfg.softcap)
+            losses[a:a + step] = token_losses(zh, targets[a:a + step])
+            if want_logits:
+                logits_parts.append(zh)
+        res["losses"] = losses
+        if want_logits:
+            res["logits"] = np.concatenate(logits_parts, axis=0)
+    elif want_logits:
+        res["logits"] = softcap(linear(xf, wu), cfg.softcap)
+    if want_internals:
+        res["x0"] = x0
+        res["layers"] = layers
+        res["xf"] = xf
+    return res
+
+
+def forward(cfg: Any, params: Any, tokens: np.ndarray, targets: Optional[np.ndarray] = None,
+            dtype=np.float64, want_logits: bool = False, rows: Optional[Sequence[int]] = None,
+            windows: Optional[Sequence[int]] = None) -> Dict[str, Any]:
+    """Batched forward+loss on tokens [B, T] (optionally only ``rows``).
+
+    Returns ``losses`` [b, T] (when targets are given), ``mean`` over the
+    evaluated rows' valid targets, and ``logits`` [b, T, V] when asked.
+
+    ``params`` maps ``wte``, ``lm_head``, ``resid_lambda``, ``x0_lambda`` to
+    arrays and ``wq``, ``wk``, ``wv``, ``wo``, ``w1``, ``w2`` to per-layer
+    sequences of row-major [out, in] arrays (any float dtype; converted to
+    ``dtype`` one layer at a time).
+    """
+    rows = list(range(tokens.shape[0])) if rows is None else list(rows)
+    out_l, out_z = [], []
+    for b in rows:
+        r = forward_row(cfg, params, tokens[b], None if targets is None else targets[b],
+                        dtype=dtype, want_logits=want_logits, windows=windows)
+        if targets is not None:
+            out_l.append(r["losses"])
+        if want_logits:
+            out_z.append(r["logits"])
+    res: Dict[str, Any] = {}
+    if targets is not None:
+        L = np.stack(out_l)
+        res["losses"] = L
+        res["mean"] = mean_loss(L, targets[rows])
+    if want_logits:
+        res["logits"] = np.stack(out_z)
+    return res

@@ -1,0 +1,442 @@
+"""Pins of the oracle against facts that do not come from the oracle itself.
+
+Each pin is a function that raises AssertionError when the oracle disagrees
+with a worked example printed on the pages (fixtures in tests/golden/), a
+closed form, an invariant the pages state, a library routine, or a brute-force
+computation on tiny inputs.  ``test_oracle_pins.py`` runs them all;
+``test_oracle_mutations.py`` plants plausible mistakes in the oracle and checks
+that some pin catches each one.
+
+Page citations: [M] = "The Mathematics of Karpathy's nanochat" (section named
+per pin), [S] = "nanochat depth sweep", section "Architecture".
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import scipy.special
+
+import gptdata
+import oracle
+from helpers import dense_params, golden, small_preset
+
+EX = golden("worked_examples.json")
+
+
+def _round_eq(got, expected, decimals):
+    got = np.round(np.asarray(got, dtype=np.float64), decimals)
+    assert np.array_equal(got, np.round(np.asarray(expected, dtype=np.float64), decimals)), (got, expected)
+
+
+# ----------------------------------------------------------------------------- RMSNorm
+
+def pin_rmsnorm_worked_example():
+    """[M] "RMS Normalization" worked example, to the printed 3 decimals."""
+    e = EX["rmsnorm"]
+    _round_eq(oracle.rms_norm(np.array(e["x"]), 0.0), e["expected"], e["decimals"])
+
+
+def pin_rmsnorm_unit_rms():
+    """[M] "RMS Normalization": the output has unit RMS (eps = 0), any scale."""
+    rng = np.random.default_rng(1)
+    for d in (1, 3, 128, 1536):
+        u = rng.standard_normal((5, d)) * rng.uniform(0.01, 100, (5, 1))
+        y = oracle.rms_norm(u, 0.0)
+        assert np.allclose(np.mean(y * y, axis=-1), 1.0, rtol=0, atol=1e-12)
+        assert np.allclose(oracle.rms_norm(7.5 * u, 0.0), y, rtol=1e-13, atol=1e-13)
+
+
+def pin_rmsnorm_eps_small_input():
+    """With eps > 0, a tiny vector maps to u/sqrt(eps) scale, not unit RMS."""
+    u = np.full(4, 1e-6)
+    y = oracle.rms_norm(u, 1e-6)
+    assert np.allclose(y, u / math.sqrt(1e-12 + 1e-6), rtol=1e-14)
+
+
+# ----------------------------------------------------------------------------- RoPE
+
+def pin_rope_worked_example():
+    """[M] "Rotary Position Embeddings (RoPE)" worked example, d_h=4, base 1e5, t=5."""
+    e = EX["rope"]
+    T = e["position"] + 1
+    cos, sin = oracle.rope_angles(T, e["head_dim"], e["base"])
+    u = np.zeros((T, 1, e["head_dim"]))
+    u[e["position"], 0] = e["q"]
+    y = oracle.apply_rope(u, cos, sin)[e["position"], 0]
+    _round_eq(y, e["expected"], e["decimals"])
+
+
+def pin_rope_is_complex_rotation():
+    """RoPE on the half-split pairs equals multiplying z_j = u_j + i u_{j+d/2} by
+    exp(-i t omega_j), omega_j = base^(-2j/d) (complex arithmetic in NumPy)."""
+    rng = np.random.default_rng(2)
+    T, H, D, base = 9, 3, 16, 1e5
+    u = rng.standard_normal((T, H, D))
+    cos, sin = oracle.rope_angles(T, D, base)
+    y = oracle.apply_rope(u, cos, sin)
+    j = np.arange(D // 2)
+    omega = base ** (-2.0 * j / D)
+    ph = np.exp(-1j * np.arange(T)[:, None] * omega[None, :])[:, None, :]
+    z = (u[..., :D // 2] + 1j * u[..., D // 2:]) * ph
+    assert np.allclose(y[..., :D // 2], z.real, atol=1e-12)
+    assert np.allclose(y[..., D // 2:], z.imag, atol=1e-12)
+
+
+def pin_rope_relative_position():
+    """[M] RoPE Proposition: <RoPE(q,m), RoPE(k,n)> depends on m - n only, and
+    equals the proposition's sum over pairs with angle phi_{m-n}."""
+    rng = np.random.default_rng(3)
+    D, base = 8, 1e5
+    q, k = rng.standard_normal(D), rng.standard_normal(D)
+    T = 40
+    cos, sin = oracle.rope_angles(T, D, base)
+
+    def rot(v, t):
+        u = np.zeros((T, 1, D))
+        u[t, 0] = v
+        return oracle.apply_rope(u, cos, sin)[t, 0]
+
+    for m, n, s in ((7, 3, 11), (20, 20, 5), (2, 9, 30)):
+        a = rot(q, m) @ rot(k, n)
+        b = rot(q, m + s) @ rot(k, n + s)
+        assert abs(a - b) < 1e-12
+        d2 = D // 2
+        omega = base ** (-2.0 * np.arange(d2) / D)
+        ph = (m - n) * omega
+        q1, q2, k1, k2 = q[:d2], q[d2:], k[:d2], k[d2:]
+        ref = np.sum((q1 * k1 + q2 * k2) * np.cos(ph) + (q2 * k1 - q1 * k2) * np.sin(ph))
+        assert abs(a - ref) < 1e-12
+
+
+def pin_rope_position_zero_and_norm():
+    """Position 0 is the identity; RoPE preserves each head's norm, so it
+    commutes with per-head RMSNorm."""
+    rng = np.random.default_rng(4)
+    T, H, D = 6, 2, 8
+    u = rng.standard_normal((T, H, D))
+    cos, sin = oracle.rope_angles(T, D, 1e5)
+    y = oracle.apply_rope(u, cos, sin)
+    assert np.array_equal(y[0], u[0])
+    assert np.allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(u, axis=-1), atol=1e-12)
+    assert np.allclose(oracle.rms_norm(y, 0.0), oracle.apply_rope(oracle.rms_norm(u, 0.0), cos, sin),
+                       atol=1e-12)
+
+
+def pin_qknorm_worked_example():
+    """[M] "QK-Norm with Sharpening" worked example: RMSNorm of q1."""
+    e = EX["qknorm"]
+    _round_eq(oracle.rms_norm(np.array(e["q"]), 0.0), e["expected"], e["decimals"])
+
+
+# ----------------------------------------------------------------------------- windows
+
+def pin_layer_windows():
+    """[M] "Sliding Window Pattern" and [S] "Architecture": SSSL tiled, last
+    layer full.  d24: 18 short + 6 long; d12: 9 + 3; tiny: [128, 256]."""
+    for name, n_short, n_long in (("d24", 18, 6), ("d12", 9, 3), ("tiny", 1, 1)):
+        p = gptdata.preset(name)
+        w = oracle.layer_windows(p.window_pattern, p.short_window, p.seq_len, p.n_layer)
+        assert len(w) == p.n_layer and w[-1] == p.seq_len
+        assert w.count(p.short_window) == n_short and w.count(p.seq_len) == n_long, (name, w)
+        for l in range(p.n_layer - 1):
+            assert w[l] == (p.seq_len if l % 4 == 3 else p.short_window)
+    assert oracle.layer_windows("SSSL", 128, 256, 2) == [128, 256]
+
+
+def pin_visible_mask_bruteforce():
+    """Window rule by explicit loops: j <= i and i - j < w."""
+    for T, w in ((7, 1), (7, 3), (9, 9), (5, 50)):
+        m = oracle.visible_mask(T, w)
+        for i in range(T):
+            for j in range(T):
+                assert m[i, j] == (j <= i and i - j < w)
+
+
+# ----------------------------------------------------------------------------- attention
+
+def _bruteforce_attention(q, k, v, window, scale):
+    T, H, D = q.shape
+    Hkv = k.shape[1]
+    out = np.zeros_like(q)
+    for h in range(H):
+        g = h * Hkv // H
+        for i in range(T):
+            js = [j for j in range(T) if j <= i and i - j < window]
+            s = [scale * sum(q[i, h, d] * k[j, g, d] for d in range(D)) for j in js]
+            mx = max(s)
+            e = [math.exp(x - mx) for x in s]
+            z = sum(e)
+            for d in range(D):
+                out[i, h, d] = sum(e[n] * v[js[n], g, d] for n in range(len(js))) / z
+    return out
+
+
+def pin_attention_bruteforce():
+    """Masked softmax attention against per-query Python loops (tiny T, GQA)."""
+    rng = np.random.default_rng(5)
+    for T, H, Hkv, D, w, sc in ((6, 2, 2, 4, 3, 0.5), (7, 4, 2, 3, 7, 1.3225), (5, 3, 1, 2, 1, 0.7)):
+        q, k, v = rng.standard_normal((T, H, D)), rng.standard_normal((T, Hkv, D)), rng.standard_normal((T, Hkv, D))
+        assert np.allclose(oracle.attention(q, k, v, w, sc), _bruteforce_attention(q, k, v, w, sc), atol=1e-12)
+
+
+def pin_attention_identical_keys():
+    """Closed form: with every key equal, the softmax is uniform over the
+    visible keys, so o_i is the mean of v_j over j in [max(0, i-w+1), i]."""
+    rng = np.random.default_rng(6)
+    T, D = 20, 4
+    k = np.tile(rng.standard_normal((1, 1, D)), (T, 1, 1))
+    q = rng.standard_normal((T, 1, D))
+    v = rng.standard_normal((T, 1, D))
+    for w in (1, 2, 5, 19, 20, 64):
+        o = oracle.attention(q, k, v, w, 0.9)
+        for i in range(T):
+            lo = max(0, i - w + 1)
+            assert np.allclose(o[i, 0], v[lo:i + 1, 0].mean(axis=0), atol=1e-12), (w, i)
+
+
+def pin_attention_locality():
+    """[M] window definition: perturbing keys/values outside query i's window
+    (j > i or i - j >= w) leaves o_i bitwise unchanged; w = 1 gives o_i = v_i."""
+    rng = np.random.default_rng(7)
+    T, H, D, w = 16, 2, 4, 5
+    q, k, v = (rng.standard_normal((T, H, D)) for _ in range(3))
+    o = oracle.attention(q, k, v, w, 0.5)
+    for i in (0, 4, 9, 15):
+        k2, v2 = k.copy(), v.copy()
+        for j in range(T):
+            if j > i or i - j >= w:
+                k2[j] += rng.standard_normal((H, D))
+                v2[j] += rng.standard_normal((H, D))
+        o2 = oracle.attention(q, k2, v2, w, 0.5)
+        assert np.array_equal(o2[i], o[i])
+    assert np.allclose(oracle.attention(q, k, v, 1, 0.5), v, atol=1e-15)
+    assert np.array_equal(oracle.attention(q, k, v, T, 0.5), oracle.attention(q, k, v, 10 * T, 0.5))
+
+
+def pin_attention_gqa_duplication():
+    """GQA with Hkv heads equals MHA whose KV heads repeat each KV head for its
+    contiguous group of H/Hkv query heads."""
+    rng = np.random.default_rng(8)
+    T, H, Hkv, D = 9, 6, 2, 4
+    q = rng.standard_normal((T, H, D))
+    k, v = rng.standard_normal((T, Hkv, D)), rng.standard_normal((T, Hkv, D))
+    rep = np.repeat(np.arange(Hkv), H // Hkv)
+    assert np.allclose(oracle.attention(q, k, v, 4, 0.6),
+                       oracle.attention(q, k[:, rep], v[:, rep], 4, 0.6), atol=1e-14)
+
+
+# ----------------------------------------------------------------------------- MLP, head
+
+def pin_relu_squared_worked_example():
+    """[M] "Feed-Forward Network (MLP)" worked example."""
+    e = EX["relu_squared"]
+    _round_eq(oracle.relu_squared(np.array(e["h"])), e["expected"], e["decimals"])
+
+
+def pin_softcap_table():
+    """[M] "Logit Softcap" worked example (rows printed correctly) and bounds."""
+    e = EX["softcap"]
+    _round_eq(oracle.softcap(np.array(e["z"]), e["cap"]), e["expected"], e["decimals"])
+    z = np.linspace(-1e4, 1e4, 2001)
+    y = oracle.softcap(z, 15.0)
+    assert np.all(np.abs(y) <= 15.0) and np.all(np.diff(y) >= 0)
+    assert np.allclose(oracle.softcap(-z, 15.0), -y)
+    assert abs(oracle.softcap(np.array(1e-6), 15.0) - 1e-6) < 1e-15
+
+
+def pin_cross_entropy():
+    """Cross-entropy against scipy.special.logsumexp; zero logits give ln V;
+    ignored targets give 0 and drop out of the mean; no valid target -> NaN."""
+    rng = np.random.default_rng(9)
+    z = rng.standard_normal((7, 33)) * 4
+    y = rng.integers(0, 33, 7)
+    y[2] = -1
+    got = oracle.token_losses(z, y)
+    for t in range(7):
+        ref = 0.0 if y[t] < 0 else scipy.special.logsumexp(z[t]) - z[t, y[t]]
+        assert abs(got[t] - ref) < 1e-12
+    assert abs(oracle.mean_loss(got, y) - np.sum(got) / 6) < 1e-12
+    V = EX["initial_loss"]["vocab"]
+    l0 = oracle.token_losses(np.zeros((1, V)), np.array([17]))
+    assert abs(l0[0] - math.log(V)) < 1e-12
+    _round_eq(l0[0], EX["initial_loss"]["expected"], EX["initial_loss"]["decimals"])
+    assert math.isnan(oracle.mean_loss(np.zeros(3), np.array([-1, -1, -1])))
+
+
+# ----------------------------------------------------------------------------- whole model
+
+def _fwd(p, params, tokens, targets=None, **kw):
+    return oracle.forward(p, params, tokens, targets, **kw)
+
+
+def _tokens(p, seed=11):
+    rng = np.random.default_rng(seed)
+    return rng.integers(0, p.vocab, (p.batch, p.seq_len + 1)).astype(np.int32)
+
+
+def pin_identity_blocks_closed_form():
+    """[M] end-to-end trace: with W_O = W_2 = 0 every block is the identity, so
+    x stays a positive multiple of x0 and the logits are
+    softcap(RMSNorm(W_E[t]) W_U^T) (RMSNorm computed here directly)."""
+    p = small_preset(n_layer=3)
+    prm = dense_params(p)
+    prm["wo"] = [np.zeros_like(a) for a in prm["wo"]]
+    prm["w2"] = [np.zeros_like(a) for a in prm["w2"]]
+    prm["lm_head"] = prm["lm_head"] * 9.0   # push logits into the non-linear softcap range
+    rows = _tokens(p)
+    r = _fwd(p, prm, rows[:, :-1], want_logits=True)
+    e = prm["wte"][rows[:, :-1]]
+    xf = e / np.sqrt(np.mean(e * e, axis=-1, keepdims=True))
+    z = xf @ prm["lm_head"].T
+    assert np.allclose(r["logits"], 15.0 * np.tanh(z / 15.0), atol=1e-10)
+
+
+def pin_zero_head_loss_is_ln_v():
+    """W_U = 0 gives uniform logits, so every token's loss is ln V exactly."""
+    p = small_preset(vocab=97)
+    prm = dense_params(p)
+    prm["lm_head"] = np.zeros_like(prm["lm_head"])
+    rows = _tokens(p)
+    r = _fwd(p, prm, rows[:, :-1], rows[:, 1:])
+    assert np.allclose(r["losses"], math.log(97), atol=1e-12)
+    assert abs(r["mean"] - math.log(97)) < 1e-12
+
+
+def pin_logits_bounded():
+    """[M] "Logit Softcap": every logit lies in (-15, 15)."""
+    p = small_preset()
+    prm = dense_params(p)
+    prm["lm_head"] = prm["lm_head"] * 1e3
+    rows = _tokens(p)
+    z = _fwd(p, prm, rows[:, :-1], want_logits=True)["logits"]
+    assert np.all(np.abs(z) <= 15.0) and np.max(np.abs(z)) > 14.0
+
+
+def pin_causality_and_rows():
+    """Outputs at position t do not depend on tokens after t; rows of a batch
+    do not interact."""
+    p = small_preset(n_layer=2, seq_len=10)
+    prm = dense_params(p)
+    rows = _tokens(p)
+    tok = rows[:, :-1]
+    z = _fwd(p, prm, tok, want_logits=True)["logits"]
+    tok2 = tok.copy()
+    tok2[0, 6:] = (tok2[0, 6:] + 5) % p.vocab
+    z2 = _fwd(p, prm, tok2, want_logits=True)["logits"]
+    assert np.array_equal(z2[0, :6], z[0, :6]) and np.array_equal(z2[1], z[1])
+    assert not np.allclose(z2[0, 6:], z[0, 6:])
+
+
+def pin_window_end_to_end():
+    """One layer, MLP off (W_2 = 0): the logits at position i depend on token j
+    iff j == i or j < i <= j + w - 1 (the window, [M] window definition)."""
+    w = 3
+    p = small_preset(n_layer=1, seq_len=10, short_window=w, window_pattern="S")
+    prm = dense_params(p)
+    prm["w2"] = [np.zeros_like(prm["w2"][0])]
+    tok = _tokens(p)[:, :-1]
+    win = [w]
+    z = _fwd(p, prm, tok, want_logits=True, windows=win)["logits"]
+    for j in (0, 4, 8):
+        t2 = tok.copy()
+        t2[0, j] = (t2[0, j] + 1) % p.vocab
+        z2 = _fwd(p, prm, t2, want_logits=True, windows=win)["logits"]
+        for i in range(p.seq_len):
+            changed = not np.array_equal(z2[0, i], z[0, i])
+            assert changed == (j <= i <= j + w - 1), (j, i)
+
+
+def pin_head_permutation():
+    """Permuting heads consistently (rows of W_Q/W_K/W_V by head, the matching
+    input columns of W_O) leaves the model unchanged."""
+    p = small_preset(n_head=3, n_kv_head=3, d_model=24, head_dim=8)
+    prm = dense_params(p)
+    rows = _tokens(p)
+    z = _fwd(p, prm, rows[:, :-1], want_logits=True)["logits"]
+    perm = np.array([2, 0, 1])
+    idx = (perm[:, None] * p.head_dim + np.arange(p.head_dim)[None, :]).reshape(-1)
+    for n in ("wq", "wk", "wv"):
+        prm[n] = [a[idx] for a in prm[n]]
+    prm["wo"] = [a[:, idx] for a in prm["wo"]]
+    z2 = _fwd(p, prm, rows[:, :-1], want_logits=True)["logits"]
+    assert np.allclose(z, z2, atol=1e-11)
+
+
+def pin_relu_squared_homogeneity():
+    """relu(c z)^2 = c^2 relu(z)^2: scaling W_1 by c and W_2 by 1/c^2 leaves the
+    model unchanged (pins the square in the MLP)."""
+    p = small_preset()
+    prm = dense_params(p)
+    rows = _tokens(p)
+    z = _fwd(p, prm, rows[:, :-1], want_logits=True)["logits"]
+    c = 3.0
+    prm["w1"] = [a * c for a in prm["w1"]]
+    prm["w2"] = [a / (c * c) for a in prm["w2"]]
+    z2 = _fwd(p, prm, rows[:, :-1], want_logits=True)["logits"]
+    assert np.allclose(z, z2, atol=1e-11)
+
+
+def pin_qk_scale_invariance():
+    """QK-norm makes the model invariant to positive scaling of W_Q and W_K
+    (eps = 0), and the embedding norm to scaling of W_E."""
+    p = small_preset()
+    prm = dense_params(p)
+    rows = _tokens(p)
+    z = _fwd(p, prm, rows[:, :-1], want_logits=True)["logits"]
+    prm["wq"] = [a * 5.0 for a in prm["wq"]]
+    prm["wk"] = [a * 0.2 for a in prm["wk"]]
+    prm["wte"] = prm["wte"] * 3.0
+    z2 = _fwd(p, prm, rows[:, :-1], want_logits=True)["logits"]
+    assert np.allclose(z, z2, atol=1e-11)
+
+
+def pin_x0_reset():
+    """[M] "Residual Stream with Learnable Scalars": lambda_l = 0, mu_l = 1 resets
+    the stream to x0 at layer l, so the model equals the model made of layers
+    l..L-1 alone; and lambda scales the incoming stream (checked with
+    lambda_l = 0, mu_l = 2 against lambda_l = 0, mu_l = 1 on a no-op stack)."""
+    p = small_preset(n_layer=3)
+    prm = dense_params(p)
+    rows = _tokens(p)
+    tok = rows[:, :-1]
+    prm["resid_lambda"][1] = 0.0
+    prm["x0_lambda"][1] = 1.0
+    full_w = oracle.layer_windows(p.window_pattern, p.short_window, p.seq_len, p.n_layer)
+    z = _fwd(p, prm, tok, want_logits=True, windows=full_w)["logits"]
+    sub = {k: (v[1:] if isinstance(v, list) else v) for k, v in prm.items()}
+    sub["resid_lambda"] = prm["resid_lambda"][1:]
+    sub["x0_lambda"] = prm["x0_lambda"][1:]
+    ps = p.with_(n_layer=2)
+    z2 = _fwd(ps, sub, tok, want_logits=True, windows=full_w[1:])["logits"]
+    assert np.allclose(z, z2, atol=1e-11)
+    # lambda weights the incoming stream: with no-op blocks the final norm hides
+    # any positive scale, so instead compare lambda=1,mu=0 (pure residual) with
+    # lambda=0,mu=1 after one real block: they must differ.
+    prm2 = dense_params(p.with_(n_layer=2))
+    prm2["resid_lambda"][1], prm2["x0_lambda"][1] = 1.0, 0.0
+    za = _fwd(p.with_(n_layer=2), prm2, tok, want_logits=True)["logits"]
+    prm2["resid_lambda"][1], prm2["x0_lambda"][1] = 0.0, 1.0
+    zb = _fwd(p.with_(n_layer=2), prm2, tok, want_logits=True)["logits"]
+    assert not np.allclose(za, zb)
+
+
+def pin_internal_norms():
+    """Every normalised tensor the pages name has unit RMS (eps = 0): the
+    embedding x0, the pre-attention and pre-MLP inputs, per-head q and k after
+    QK-norm, and the final norm."""
+    p = small_preset(n_layer=2)
+    prm = dense_params(p)
+    tok = _tokens(p)[0, :-1]
+    r = oracle.forward_row(p, prm, tok, None, want_internals=True)
+
+    def unit(a):
+        return np.allclose(np.mean(a * a, axis=-1), 1.0, atol=1e-12)
+
+    assert unit(r["x0"]) and unit(r["xf"])
+    for li in r["layers"]:
+        assert unit(li["xn"]) and unit(li["xm"]) and unit(li["q"]) and unit(li["k"])
+        assert not unit(li["v"])
+
+
+PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -1,0 +1,185 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check a pin fails.
+
+Each mutation replaces one oracle function with a wrong variant through
+monkeypatch; the listed pins must then raise.  This shows the pins constrain
+every step of the forward pass, not only that the oracle agrees with itself.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import oracle_pins as P
+
+_orig = {n: getattr(oracle, n) for n in ("apply_rope", "visible_mask", "relu_squared", "softcap",
+                                          "token_losses", "rms_norm", "attention", "block", "linear")}
+
+
+def _rope_sign(u, cos, sin):
+    d2 = u.shape[-1] // 2
+    u1, u2 = u[..., :d2], u[..., d2:]
+    c, s = cos[:, None, :], sin[:, None, :]
+    return np.concatenate([u1 * c - u2 * s, u1 * s + u2 * c], axis=-1)
+
+
+def _rope_interleaved(u, cos, sin):
+    u1, u2 = u[..., 0::2], u[..., 1::2]
+    c, s = cos[:, None, :], sin[:, None, :]
+    y = np.empty_like(u)
+    y[..., 0::2] = u1 * c + u2 * s
+    y[..., 1::2] = -u1 * s + u2 * c
+    return y
+
+
+def _mask_off_by_one(T, w):
+    i, j = np.arange(T)[:, None], np.arange(T)[None, :]
+    return (j <= i) & (i - j <= w)
+
+
+def _mask_not_causal(T, w):
+    i, j = np.arange(T)[:, None], np.arange(T)[None, :]
+    return np.abs(i - j) < w
+
+
+def _relu(z):
+    return np.maximum(z, 0.0)
+
+
+def _no_softcap(z, cap=15.0):
+    return z
+
+
+def _ce_off_index(zhat, targets):
+    return _orig["token_losses"](zhat, np.where(targets >= 0, (targets + 1) % zhat.shape[-1], targets))
+
+
+def _attention_no_scale(q, k, v, window, scale):
+    return _orig["attention"](q, k, v, window, 1.0)
+
+
+def _attention_mod_map(q, k, v, window, scale):
+    H, Hkv = q.shape[1], k.shape[1]
+    rep = np.arange(H) % Hkv
+    return _orig["attention"](q, k[:, rep], v[:, rep], window, scale)
+
+
+def _linear_square_transposed(x, w):
+    return x @ (w if w.shape[0] == w.shape[1] else w.T)
+
+
+def _block_patched(kind):
+    """Wrap block() with a mistake in the residual-scalar or norm handling."""
+    import oracle as o
+
+    def blk(x, x0, l, cfg, params, window, cos, sin, dt, internals=None):
+        if kind == "no_mix":
+            prm = dict(params)
+            prm["resid_lambda"] = np.ones_like(np.asarray(params["resid_lambda"]))
+            prm["x0_lambda"] = np.zeros_like(np.asarray(params["x0_lambda"]))
+            return _orig["block"](x, x0, l, cfg, prm, window, cos, sin, dt, internals)
+        if kind == "swap_mix":
+            prm = dict(params)
+            prm["resid_lambda"], prm["x0_lambda"] = params["x0_lambda"], params["resid_lambda"]
+            return _orig["block"](x, x0, l, cfg, prm, window, cos, sin, dt, internals)
+        raise AssertionError(kind)
+    return blk
+
+
+def _forward_row_no_final_norm(monkeypatch):
+    calls = {"n": 0}
+    real = _orig["rms_norm"]
+
+    # The final norm is the last rms_norm call of forward_row on the full [T, C]
+    # stream; drop it by making rms_norm the identity right after the last block.
+    real_block = _orig["block"]
+
+    def blk(*a, **k):
+        out = real_block(*a, **k)
+        calls["n"] += 1
+        return out
+
+    def norm(u, eps=0.0):
+        if calls.get("armed"):
+            calls["armed"] = False
+            return u
+        return real(u, eps)
+
+    def blk_arm(x, x0, l, cfg, *rest, **kw):
+        out = blk(x, x0, l, cfg, *rest, **kw)
+        if l == cfg.n_layer - 1:
+            calls["armed"] = True
+        return out
+
+    monkeypatch.setattr(oracle, "block", blk_arm)
+    monkeypatch.setattr(oracle, "rms_norm", norm)
+
+
+def _qk_no_norm(monkeypatch):
+    real = _orig["rms_norm"]
+
+    def norm(u, eps=0.0):
+        if u.ndim == 3:           # per-head [T, H, D] tensors are only q and k
+            return u
+        return real(u, eps)
+    monkeypatch.setattr(oracle, "rms_norm", norm)
+
+
+def _no_pre_norm(monkeypatch):
+    real = _orig["rms_norm"]
+    real_block = _orig["block"]
+    state = {"in_block": False, "count": 0}
+
+    def norm(u, eps=0.0):
+        if state["in_block"] and u.ndim == 2:
+            state["count"] += 1
+            if state["count"] == 1:    # the pre-attention norm of each block
+                return u
+        return real(u, eps)
+
+    def blk(*a, **k):
+        state["in_block"], state["count"] = True, 0
+        try:
+            return real_block(*a, **k)
+        finally:
+            state["in_block"] = False
+    monkeypatch.setattr(oracle, "rms_norm", norm)
+    monkeypatch.setattr(oracle, "block", blk)
+
+
+MUTATIONS = {
+    "rope_sign": (lambda mp: mp.setattr(oracle, "apply_rope", _rope_sign), [P.pin_rope_worked_example]),
+    "rope_interleaved": (lambda mp: mp.setattr(oracle, "apply_rope", _rope_interleaved),
+                         [P.pin_rope_is_complex_rotation]),
+    "window_off_by_one": (lambda mp: mp.setattr(oracle, "visible_mask", _mask_off_by_one),
+                          [P.pin_attention_identical_keys, P.pin_visible_mask_bruteforce]),
+    "not_causal": (lambda mp: mp.setattr(oracle, "visible_mask", _mask_not_causal),
+                   [P.pin_attention_locality, P.pin_causality_and_rows]),
+    "relu_not_squared": (lambda mp: mp.setattr(oracle, "relu_squared", _relu),
+                         [P.pin_relu_squared_worked_example, P.pin_relu_squared_homogeneity]),
+    "no_softcap": (lambda mp: mp.setattr(oracle, "softcap", _no_softcap),
+                   [P.pin_softcap_table, P.pin_logits_bounded]),
+    "ce_wrong_target": (lambda mp: mp.setattr(oracle, "token_losses", _ce_off_index), [P.pin_cross_entropy]),
+    "attention_no_scale": (lambda mp: mp.setattr(oracle, "attention", _attention_no_scale),
+                           [P.pin_attention_bruteforce]),
+    "gqa_modulo_map": (lambda mp: mp.setattr(oracle, "attention", _attention_mod_map),
+                       [P.pin_attention_gqa_duplication]),
+    "square_weight_transposed": (lambda mp: mp.setattr(oracle, "linear", _linear_square_transposed),
+                                 [P.pin_head_permutation]),
+    "no_x0_mix": (lambda mp: mp.setattr(oracle, "block", _block_patched("no_mix")), [P.pin_x0_reset]),
+    "swapped_mix": (lambda mp: mp.setattr(oracle, "block", _block_patched("swap_mix")), [P.pin_x0_reset]),
+    "no_final_norm": (_forward_row_no_final_norm, [P.pin_identity_blocks_closed_form]),
+    "no_qk_norm": (_qk_no_norm, [P.pin_qk_scale_invariance, P.pin_internal_norms]),
+    "no_pre_attn_norm": (_no_pre_norm, [P.pin_internal_norms]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_caught(name, monkeypatch):
+    apply, catchers = MUTATIONS[name]
+    apply(monkeypatch)
+    failed = []
+    for pin in catchers:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            failed.append(pin.__name__)
+    assert failed, f"mutation {name} was not caught by {[p.__name__ for p in catchers]}"
