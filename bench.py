@@ -1,0 +1,174 @@
+#!/usr/bin/env python3
+"""Forward+loss throughput of nanochat d24 (T=2048, B=8, bf16) on one MI355X.
+
+One step = one gpt_fwd_loss call over a batch of B*T synthetic tokens resident in HBM:
+embedding, 24 layers, lm_head, softcapped cross-entropy and the mean loss.  The timed region
+holds exactly K steps between device synchronisations; the JSON line reports whole-job
+tokens/s, the dominant kernel's roofline position (HIP events around that kernel's own
+launches of the same shape) and the CPU oracle on a bounded sample of the same workload.
+
+Inputs are synthetic (seeded uniform token ids, N(0, 1/fan_in) weights) with the shapes of the
+pages' workload: 2,048-token packed rows and a 32,768-entry vocabulary.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA peak (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E bandwidth (published)
+
+
+def flops_per_token(p, windows):
+    """Algorithmic forward FLOPs per token: every linear (2 per multiply-add) plus attention's
+    QK^T and PV over the visible keys only (average over positions of min(t+1, w))."""
+    C, H, Hkv, D, F, V, T = p.d_model, p.n_head, p.n_kv_head, p.head_dim, p.mlp_dim, p.vocab, p.seq_len
+    lin = 2 * (C * (H + 2 * Hkv) * D + H * D * C + 2 * C * F)
+    att = 0.0
+    for w in windows:
+        w = min(w, T)
+        avg = (w * (w + 1) / 2 + (T - w) * w) / T
+        att += 4 * H * D * avg
+    return p.n_layer * lin + 2 * C * V + att
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="d24")
+    ap.add_argument("--cpu-tokens", type=int, default=384,
+                    help="tokens of row 0 the CPU oracle evaluates (a causal prefix)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=10)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}): the forward+loss "
+              "path has no cross-GPU step; rows shard over GPUs with no communication.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import decoder_only_transformer_layer_amd as gf
+    import gptdata
+
+    p = gptdata.preset(args.config)
+    t0 = time.time()
+    w, tok, tgt = gptdata.make_inputs(p)
+    print(f"[bench] inputs {args.config} generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    windows = gf.layer_windows(p.window_pattern, p.short_window, p.seq_len, p.n_layer)
+    model = gf.DeviceModel(p, w)
+    dev = torch.device("cuda:0")
+    t_tok = torch.from_numpy(tok).to(dev)
+    t_tgt = torch.from_numpy(tgt).to(dev)
+    B, T = p.batch, p.seq_len
+    loss = torch.empty((B, T), dtype=torch.float32, device=dev)
+    mean = torch.empty(1, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        st = model.forward(t_tok, t_tgt, loss, mean, None, stream)
+        if st != gf.GPT_OK:
+            raise RuntimeError(gf.gpt_status_string(st))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done, mean loss {mean.item():.4f}", file=sys.stderr, flush=True)
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    tok_s = B * T / (ms / 1e3)
+    fpt = flops_per_token(p, windows)
+    assert gf.gpt_device_status(model.ws_ptr) == gf.GPT_OK
+    print(f"[bench] {args.steps} steps: {ms:.3f} ms/step (wall {wall / args.steps * 1e3:.3f}), "
+          f"{tok_s:,.0f} tok/s, {fpt * tok_s / 1e12:.1f} TFLOP/s", file=sys.stderr, flush=True)
+
+    # Dominant kernel: the MLP up-projection GEMM (largest FLOP share), timed alone with HIP
+    # events on the stream it is launched on, at the forward pass's shape and launch config.
+    M, C, F = B * T, p.d_model, p.mlp_dim
+    xa = torch.randn((M, C), device=dev).to(torch.bfloat16)
+    hb = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
+    w1 = model.t["w1"][0]
+    for _ in range(2):
+        gf.gpt_op_linear(gf.GPT_BF16, 1, xa, w1, M, F, C, hb, stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.kernel_reps):
+        gf.gpt_op_linear(gf.GPT_BF16, 1, xa, w1, M, F, C, hb, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    k_ms = e0.elapsed_time(e1) / args.kernel_reps
+    k_flops = 2.0 * M * F * C
+    k_tflops = k_flops / (k_ms / 1e3) / 1e12
+    print(f"[bench] MLP-up GEMM {M}x{F}x{C}: {k_ms * 1e3:.1f} us, {k_tflops:.1f} TFLOP/s",
+          file=sys.stderr, flush=True)
+    del xa, hb
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:
+            cores = os.cpu_count()
+        n = min(args.cpu_tokens, T)
+        params = {
+            "wte": w.value(w.wte), "lm_head": w.value(w.lm_head),
+            "resid_lambda": w.resid_lambda, "x0_lambda": w.x0_lambda,
+            **{k: [w.value(a) for a in getattr(w, k)] for k in ("wq", "wk", "wv", "wo", "w1", "w2")},
+        }
+        c0 = time.perf_counter()
+        oracle.forward(p, params, tok[:1, :n], tgt[:1, :n], windows=windows)
+        cdt = time.perf_counter() - c0
+        cpu = {"value": round(n / cdt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+               "sample": f"row 0, first {n} of {T} tokens (causal prefix), fp64 NumPy oracle, {cdt:.1f}s"}
+        print(f"[bench] cpu oracle: {n} tokens in {cdt:.1f}s", file=sys.stderr, flush=True)
+
+    out = {
+        "metric": "forward+loss tokens/sec at d24 T=2048 bf16; % of MFMA bf16 peak",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded uniform token ids, N(0,1/fan_in) weights",
+        "pct_mfma_peak": round(100.0 * fpt * tok_s / (PEAK_BF16_TFLOPS * 1e12), 2),
+        "config": {"workload": f"nanochat {args.config} forward+loss", "batch": B, "seq_len": T,
+                   "n_layer": p.n_layer, "d_model": p.d_model, "n_head": p.n_head, "vocab": p.vocab,
+                   "flops_per_token": round(fpt), "windows": "SSSL short 1024, last layer full"},
+        "roofline": {"bound": "mfma", "kernel": "gemm_bf16 MLP up-projection (relu^2 epilogue)",
+                     "achieved": round(k_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(k_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "avg_launch_us": round(k_ms * 1e3, 2), "flops_per_launch": k_flops},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

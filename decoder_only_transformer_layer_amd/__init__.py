@@ -1,0 +1,280 @@
+"""Python binding of libgptfwd (nanochat GPT forward + next-token loss on MI355X / gfx950).
+
+Argument marshalling only: every step of the forward pass runs in the HIP kernels of
+``libgptfwd.so`` behind the C ABI of ``include/gptfwd.h`` and ``include/gptfwd_ops.h``.  The
+functions below carry the C names and take either integers (device addresses) or torch
+tensors, whose ``data_ptr()`` is passed through.  PyTorch supplies device memory and the
+stream (``torch.cuda.current_stream()`` unless one is given); nothing is computed in Python.
+
+If the shared library is missing, every entry point raises ``RuntimeError``: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Any, Dict, List, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgptfwd.so")
+
+GPT_OK, GPT_E_INVALID_ARG, GPT_E_UNSUPPORTED, GPT_E_WORKSPACE, GPT_E_HIP, GPT_E_DEVICE_INPUT = 0, -1, -2, -3, -4, -5
+GPT_F32, GPT_BF16 = 0, 1
+
+EXPORTED = [
+    "gpt_validate", "gpt_workspace_bytes", "gpt_fwd_loss", "gpt_device_status", "gpt_status_string",
+    "gpt_op_embed_norm", "gpt_op_mix_norm", "gpt_op_rope_table", "gpt_op_qk_rope_norm",
+    "gpt_op_linear", "gpt_op_qkv", "gpt_op_attention", "gpt_op_lm_head_ce_workspace",
+    "gpt_op_lm_head_ce",
+]
+
+
+class gpt_cfg(ctypes.Structure):
+    _fields_ = [
+        ("n_layer", ctypes.c_int32), ("d_model", ctypes.c_int32), ("n_head", ctypes.c_int32),
+        ("n_kv_head", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("mlp_dim", ctypes.c_int32),
+        ("vocab", ctypes.c_int32), ("seq_len", ctypes.c_int32), ("batch", ctypes.c_int32),
+        ("window", ctypes.POINTER(ctypes.c_int32)),
+        ("softcap", ctypes.c_float), ("rope_base", ctypes.c_float), ("attn_scale", ctypes.c_float),
+        ("norm_eps", ctypes.c_float), ("dtype", ctypes.c_int32),
+    ]
+
+
+class gpt_weights(ctypes.Structure):
+    _fields_ = [
+        ("wte", ctypes.c_void_p), ("lm_head", ctypes.c_void_p),
+        ("resid_lambda", ctypes.c_void_p), ("x0_lambda", ctypes.c_void_p),
+        ("wq", ctypes.POINTER(ctypes.c_void_p)), ("wk", ctypes.POINTER(ctypes.c_void_p)),
+        ("wv", ctypes.POINTER(ctypes.c_void_p)), ("wo", ctypes.POINTER(ctypes.c_void_p)),
+        ("w1", ctypes.POINTER(ctypes.c_void_p)), ("w2", ctypes.POINTER(ctypes.c_void_p)),
+    ]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def _load() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libgptfwd.so not built ({LIB_PATH}); run __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F, S = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    sig = {
+        "gpt_validate": (I, [ctypes.POINTER(gpt_cfg)]),
+        "gpt_workspace_bytes": (S, [ctypes.POINTER(gpt_cfg)]),
+        "gpt_fwd_loss": (I, [ctypes.POINTER(gpt_cfg), ctypes.POINTER(gpt_weights), P, P, P, P, P, P, S, P]),
+        "gpt_device_status": (I, [P, P]),
+        "gpt_status_string": (ctypes.c_char_p, [I]),
+        "gpt_op_embed_norm": (I, [I, P, P, P, P, P, P, P, I, I, I, F, P, P]),
+        "gpt_op_mix_norm": (I, [I, P, P, P, P, I, I, P, I, I, F, P]),
+        "gpt_op_rope_table": (I, [P, I, I, F, P]),
+        "gpt_op_qk_rope_norm": (I, [I, P, I, P, I, I, I, I, F, P]),
+        "gpt_op_linear": (I, [I, I, P, P, I, I, I, P, P]),
+        "gpt_op_qkv": (I, [P, P, P, P, I, I, I, I, I, I, P, P, P]),
+        "gpt_op_attention": (I, [I, P, P, P, I, I, I, I, I, I, F, P]),
+        "gpt_op_lm_head_ce_workspace": (S, [I, I, I]),
+        "gpt_op_lm_head_ce": (I, [I, P, P, P, P, I, I, I, F, P, P, P, P, S, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _ptr(x: Any) -> Optional[int]:
+    """Device address of a torch tensor, or an int / None passed through."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream: Any) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+class GptError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {gpt_status_string(status)} ({status})")
+
+
+def _check(status: int, where: str) -> int:
+    if status != GPT_OK:
+        raise GptError(status, where)
+    return status
+
+
+# ----------------------------------------------------------------------------- configuration
+
+def layer_windows(pattern: str, short_window: int, seq_len: int, n_layer: int) -> List[int]:
+    """Per-layer window sizes: the short/long pattern tiled over the layers ("S" = short
+    window, "L" = seq_len), the last layer forced long ("The Mathematics of Karpathy's
+    nanochat", section "Sliding Window Pattern")."""
+    sizes = {"S": short_window, "L": seq_len}
+    w = [sizes[pattern[l % len(pattern)]] for l in range(n_layer)]
+    w[-1] = seq_len
+    return w
+
+
+def make_cfg(p: Any, batch: Optional[int] = None, windows: Optional[Sequence[int]] = None) -> gpt_cfg:
+    """gpt_cfg from any object with the preset attribute names (n_layer, d_model, ...).
+
+    The window array is kept alive on the returned structure (attribute ``_win``)."""
+    if windows is None:
+        windows = layer_windows(p.window_pattern, p.short_window, p.seq_len, p.n_layer)
+    win = (ctypes.c_int32 * p.n_layer)(*[int(w) for w in windows])
+    c = gpt_cfg(p.n_layer, p.d_model, p.n_head, p.n_kv_head, p.head_dim, p.mlp_dim, p.vocab,
+                p.seq_len, p.batch if batch is None else batch,
+                ctypes.cast(win, ctypes.POINTER(ctypes.c_int32)),
+                p.softcap, p.rope_base, p.attn_scale, p.norm_eps,
+                GPT_BF16 if p.dtype == "bf16" else GPT_F32)
+    c._win = win
+    return c
+
+
+# ----------------------------------------------------------------------------- C entry points
+
+def gpt_status_string(status: int) -> str:
+    return _load().gpt_status_string(status).decode()
+
+
+def gpt_validate(cfg: gpt_cfg) -> int:
+    return _load().gpt_validate(ctypes.byref(cfg))
+
+
+def gpt_workspace_bytes(cfg: gpt_cfg) -> int:
+    return _load().gpt_workspace_bytes(ctypes.byref(cfg))
+
+
+def gpt_fwd_loss(cfg: gpt_cfg, weights: gpt_weights, tokens, targets, loss, mean_loss, logits,
+                 workspace, workspace_bytes: int, stream=None) -> int:
+    return _load().gpt_fwd_loss(ctypes.byref(cfg), ctypes.byref(weights), _ptr(tokens), _ptr(targets),
+                                _ptr(loss), _ptr(mean_loss), _ptr(logits), _ptr(workspace),
+                                workspace_bytes, _stream(stream))
+
+
+def gpt_device_status(workspace, stream=None) -> int:
+    return _load().gpt_device_status(_ptr(workspace), _stream(stream))
+
+
+def gpt_op_embed_norm(dtype, tokens, wte, lam, mu, x0, x, xn, M, C, V, eps, flags, stream=None) -> int:
+    return _load().gpt_op_embed_norm(dtype, _ptr(tokens), _ptr(wte), _ptr(lam), _ptr(mu), _ptr(x0),
+                                     _ptr(x), _ptr(xn), M, C, V, eps, _ptr(flags), _stream(stream))
+
+
+def gpt_op_mix_norm(dtype, x, x0, lam, mu, layer, mix, xn, M, C, eps, stream=None) -> int:
+    return _load().gpt_op_mix_norm(dtype, _ptr(x), _ptr(x0), _ptr(lam), _ptr(mu), layer, int(mix),
+                                   _ptr(xn), M, C, eps, _stream(stream))
+
+
+def gpt_op_rope_table(cs, T, D, base, stream=None) -> int:
+    return _load().gpt_op_rope_table(_ptr(cs), T, D, base, _stream(stream))
+
+
+def gpt_op_qk_rope_norm(dtype, qk, ld, cs, M, T, nheads, D, eps, stream=None) -> int:
+    return _load().gpt_op_qk_rope_norm(dtype, _ptr(qk), ld, _ptr(cs), M, T, nheads, D, eps, _stream(stream))
+
+
+def gpt_op_linear(dtype, epi, a, w, M, N, K, out, stream=None) -> int:
+    return _load().gpt_op_linear(dtype, epi, _ptr(a), _ptr(w), M, N, K, _ptr(out), _stream(stream))
+
+
+def gpt_op_qkv(xn, wq, wk, wv, B, T, C, H, Hkv, D, qk, vt, stream=None) -> int:
+    return _load().gpt_op_qkv(_ptr(xn), _ptr(wq), _ptr(wk), _ptr(wv), B, T, C, H, Hkv, D, _ptr(qk),
+                              _ptr(vt), _stream(stream))
+
+
+def gpt_op_attention(dtype, qk, vt, o, B, T, H, Hkv, D, window, scale, stream=None) -> int:
+    return _load().gpt_op_attention(dtype, _ptr(qk), _ptr(vt), _ptr(o), B, T, H, Hkv, D, window, scale,
+                                    _stream(stream))
+
+
+def gpt_op_lm_head_ce_workspace(dtype, M, V) -> int:
+    return _load().gpt_op_lm_head_ce_workspace(dtype, M, V)
+
+
+def gpt_op_lm_head_ce(dtype, xf, wu, targets, tokens, M, C, V, cap, loss, mean, logits, workspace,
+                      workspace_bytes, stream=None) -> int:
+    return _load().gpt_op_lm_head_ce(dtype, _ptr(xf), _ptr(wu), _ptr(targets), _ptr(tokens), M, C, V, cap,
+                                     _ptr(loss), _ptr(mean), _ptr(logits), _ptr(workspace),
+                                     workspace_bytes, _stream(stream))
+
+
+# ----------------------------------------------------------------------------- device model
+
+def to_device(a: np.ndarray, dtype: str, device: str = "cuda"):
+    """Upload a host array: bf16 given as uint16 bit patterns, or float32."""
+    import torch
+    if dtype == "bf16":
+        a = np.ascontiguousarray(a, dtype=np.uint16)
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+
+class DeviceModel:
+    """Device-resident weights of one configuration plus the structures gpt_fwd_loss needs.
+
+    ``weights`` is any object with attributes wte, lm_head, resid_lambda, x0_lambda and
+    per-layer lists wq, wk, wv, wo, w1, w2 (numpy arrays: uint16 bf16 bits or float32).
+    """
+
+    def __init__(self, p: Any, weights: Any, batch: Optional[int] = None, device: str = "cuda",
+                 windows: Optional[Sequence[int]] = None):
+        import torch
+        self.p = p
+        self.batch = p.batch if batch is None else batch
+        self.cfg = make_cfg(p, self.batch, windows)
+        st = gpt_validate(self.cfg)
+        _check(st, "gpt_validate")
+        dt = p.dtype
+        self.t: Dict[str, Any] = {
+            "wte": to_device(weights.wte, dt, device),
+            "lm_head": to_device(weights.lm_head, dt, device),
+            "resid_lambda": torch.from_numpy(np.asarray(weights.resid_lambda, np.float32)).to(device),
+            "x0_lambda": torch.from_numpy(np.asarray(weights.x0_lambda, np.float32)).to(device),
+        }
+        arrs = {}
+        for n in ("wq", "wk", "wv", "wo", "w1", "w2"):
+            self.t[n] = [to_device(m, dt, device) for m in getattr(weights, n)]
+            arrs[n] = (ctypes.c_void_p * p.n_layer)(*[m.data_ptr() for m in self.t[n]])
+        self._arrs = arrs
+        self.w = gpt_weights(self.t["wte"].data_ptr(), self.t["lm_head"].data_ptr(),
+                             self.t["resid_lambda"].data_ptr(), self.t["x0_lambda"].data_ptr(),
+                             *[ctypes.cast(arrs[n], ctypes.POINTER(ctypes.c_void_p))
+                               for n in ("wq", "wk", "wv", "wo", "w1", "w2")])
+        self.ws_bytes = gpt_workspace_bytes(self.cfg)
+        self.ws = torch.empty(self.ws_bytes + 256, dtype=torch.uint8, device=device)
+        off = (-self.ws.data_ptr()) % 256
+        self.ws_ptr = self.ws.data_ptr() + off
+
+    def forward(self, tokens, targets=None, loss=None, mean=None, logits=None, stream=None) -> int:
+        """Enqueue gpt_fwd_loss on device tensors (outputs preallocated by the caller)."""
+        return gpt_fwd_loss(self.cfg, self.w, tokens, targets, loss, mean, logits, self.ws_ptr,
+                            self.ws_bytes, stream)
+
+    def __call__(self, tokens, targets=None, want_logits: bool = False):
+        """Allocate outputs, run, and return (loss [B,T], mean [1], logits or None)."""
+        import torch
+        B, T, V = self.batch, self.p.seq_len, self.p.vocab
+        dev = tokens.device
+        loss = torch.empty((B, T), dtype=torch.float32, device=dev) if targets is not None else None
+        mean = torch.empty(1, dtype=torch.float32, device=dev) if targets is not None else None
+        logits = torch.empty((B, T, V), dtype=torch.float32, device=dev) if want_logits else None
+        _check(self.forward(tokens, targets, loss, mean, logits), "gpt_fwd_loss")
+        return loss, mean, logits
+
+    def device_status(self) -> int:
+        return gpt_device_status(self.ws_ptr)

@@ -1,0 +1,339 @@
+// libgptfwd host engine: argument validation, workspace planning and the launch sequence of
+// the forward pass, behind the C ABI of include/gptfwd.h and include/gptfwd_ops.h.
+//
+// Layer order follows "The Mathematics of Karpathy's nanochat", sections "High-Level Forward
+// Pass" and "Pseudocode: One Training Step"; see the header for the full statement.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "gptfwd.h"
+#include "gptfwd_ops.h"
+#include "kernels.h"
+
+namespace {
+
+using namespace gptk;
+
+constexpr size_t ALIGN = 256;
+inline size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct Layout {
+  size_t flags, x, x0, xn, qk, vt, o, h, cs, partial, tgt, total;
+  int nnb;
+};
+
+gpt_status validate(const gpt_cfg* c) {
+  if (!c) return GPT_E_INVALID_ARG;
+  if (c->n_layer < 1 || c->d_model < 1 || c->n_head < 1 || c->n_kv_head < 1 || c->head_dim < 1 ||
+      c->mlp_dim < 1 || c->vocab < 2 || c->seq_len < 1 || c->batch < 1)
+    return GPT_E_INVALID_ARG;
+  if (c->n_head % c->n_kv_head) return GPT_E_INVALID_ARG;
+  if (c->dtype != GPT_F32 && c->dtype != GPT_BF16) return GPT_E_INVALID_ARG;
+  if (!c->window) return GPT_E_INVALID_ARG;
+  for (int l = 0; l < c->n_layer; ++l)
+    if (c->window[l] < 1) return GPT_E_INVALID_ARG;
+  if (!(c->softcap > 0.f) || !isfinite(c->softcap)) return GPT_E_INVALID_ARG;
+  if (!(c->rope_base > 0.f) || !isfinite(c->rope_base)) return GPT_E_INVALID_ARG;
+  if (!(c->attn_scale > 0.f) || !isfinite(c->attn_scale)) return GPT_E_INVALID_ARG;
+  if (!(c->norm_eps >= 0.f) || !isfinite(c->norm_eps)) return GPT_E_INVALID_ARG;
+  // Limits of what the kernels implement.
+  const long M = (long)c->batch * c->seq_len;
+  if (M > (1L << 30) || (long)c->vocab * c->d_model > (1L << 31)) return GPT_E_UNSUPPORTED;
+  if (c->head_dim != 64 && c->head_dim != 128) return GPT_E_UNSUPPORTED;
+  if (c->d_model % 64 || c->mlp_dim % 64 || (c->n_head * c->head_dim) % 64) return GPT_E_UNSUPPORTED;
+  if (c->d_model > 8192) return GPT_E_UNSUPPORTED;
+  if (c->dtype == GPT_BF16) {
+    if (c->seq_len % 64) return GPT_E_UNSUPPORTED;
+    if ((c->n_head * c->head_dim) % 128 || (c->n_kv_head * c->head_dim) % 128) return GPT_E_UNSUPPORTED;
+  }
+  return GPT_OK;
+}
+
+Layout plan(const gpt_cfg* c) {
+  Layout L{};
+  const size_t M = (size_t)c->batch * c->seq_len;
+  const size_t C = c->d_model, H = c->n_head, Hkv = c->n_kv_head, D = c->head_dim, F = c->mlp_dim;
+  const bool bf = c->dtype == GPT_BF16;
+  const size_t es = bf ? 2 : 4;
+  L.nnb = bf ? gemm_bf16_ce_blocks(c->vocab) : gemm_f32_ce_blocks(c->vocab);
+  size_t off = 0;
+  L.flags = off; off += up(64);
+  L.x = off; off += up(M * C * 4);
+  L.x0 = off; off += up(M * C * 4);
+  L.xn = off; off += up(M * C * es);
+  if (bf) {
+    L.qk = off; off += up(M * (H + Hkv) * D * 2);
+    L.vt = off; off += up(M * Hkv * D * 2);
+  } else {
+    L.qk = off; off += up(M * (H + 2 * Hkv) * D * 4);
+    L.vt = off;
+  }
+  L.o = off; off += up(M * H * D * es);
+  L.h = off; off += up(M * F * es);
+  L.cs = off; off += up((size_t)c->seq_len * (D / 2) * 8);
+  L.partial = off; off += up(M * (size_t)L.nnb * 4);
+  L.tgt = off; off += up(M * 4);
+  L.total = off;
+  return L;
+}
+
+#define CK(expr)                                 \
+  do {                                           \
+    if ((expr) != hipSuccess) return GPT_E_HIP;  \
+  } while (0)
+
+GemmArgs gemm_args(const void* A, int lda, const void* B, int N, int K, int M, void* out, int ldo) {
+  GemmArgs g{};
+  g.A = A; g.lda = lda;
+  g.B0 = B; g.B1 = B; g.B2 = B; g.nseg0 = N; g.nseg1 = 0; g.ldb = K;
+  g.M = M; g.N = N; g.K = K;
+  g.out = out; g.ldo = ldo;
+  return g;
+}
+
+hipError_t gemm(bool bf, Epi e, const GemmArgs& g, hipStream_t s) {
+  return bf ? launch_gemm_bf16(e, g, s) : launch_gemm_f32(e, g, s);
+}
+
+// lm_head + softcap + CE over M rows into loss/mean (targets may be NULL: logits only).
+gpt_status lm_head_ce(bool bf, const void* xf, const void* wu, const int32_t* targets,
+                      const int32_t* tokens, int M, int C, int V, float cap, float* loss,
+                      float* mean, float* logits, float* partial, float* tgt, int nnb,
+                      unsigned* flags, hipStream_t s) {
+  GemmArgs g = gemm_args(xf, C, wu, V, C, M, nullptr, 0);
+  g.targets = targets; g.partial = partial; g.tgt_logit = tgt; g.logits = logits;
+  g.nnb = nnb; g.cap = cap;
+  CK(gemm(bf, EPI_CE, g, s));
+  if (logits) CK(launch_softcap(logits, (size_t)M * V, cap, s));
+  if (targets) {
+    CK(launch_ce_finalize(partial, nnb, tgt, targets, tokens, M, V, cap, loss, flags, s));
+    CK(launch_ce_mean(loss, targets, M, mean, s));
+  }
+  return GPT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gpt_status gpt_validate(const gpt_cfg* cfg) { return validate(cfg); }
+
+size_t gpt_workspace_bytes(const gpt_cfg* cfg) {
+  if (validate(cfg) != GPT_OK) return 0;
+  return plan(cfg).total;
+}
+
+gpt_status gpt_fwd_loss(const gpt_cfg* c, const gpt_weights* w, const int32_t* tokens,
+                        const int32_t* targets, float* loss, float* mean_loss, float* logits,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  gpt_status st = validate(c);
+  if (st != GPT_OK) return st;
+  if (!w || !tokens) return GPT_E_INVALID_ARG;
+  if (!w->wte || !w->lm_head || !w->resid_lambda || !w->x0_lambda || !w->wq || !w->wk || !w->wv ||
+      !w->wo || !w->w1 || !w->w2)
+    return GPT_E_INVALID_ARG;
+  for (int l = 0; l < c->n_layer; ++l)
+    if (!w->wq[l] || !w->wk[l] || !w->wv[l] || !w->wo[l] || !w->w1[l] || !w->w2[l])
+      return GPT_E_INVALID_ARG;
+  if (targets && (!loss || !mean_loss)) return GPT_E_INVALID_ARG;
+  if (!targets && !logits) return GPT_E_INVALID_ARG;
+  const void* ptrs16[] = {w->wte, w->lm_head};
+  for (const void* p : ptrs16)
+    if (!aligned(p, 16)) return GPT_E_INVALID_ARG;
+  for (int l = 0; l < c->n_layer; ++l)
+    if (!aligned(w->wq[l], 16) || !aligned(w->wk[l], 16) || !aligned(w->wv[l], 16) ||
+        !aligned(w->wo[l], 16) || !aligned(w->w1[l], 16) || !aligned(w->w2[l], 16))
+      return GPT_E_INVALID_ARG;
+  if (!aligned(tokens, 4) || (targets && !aligned(targets, 4)) || (loss && !aligned(loss, 4)) ||
+      (logits && !aligned(logits, 4)))
+    return GPT_E_INVALID_ARG;
+  const Layout L = plan(c);
+  if (!workspace || workspace_bytes < L.total || !aligned(workspace, ALIGN)) return GPT_E_WORKSPACE;
+
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf = c->dtype == GPT_BF16;
+  const int B = c->batch, T = c->seq_len, M = B * T, C = c->d_model, H = c->n_head;
+  const int Hkv = c->n_kv_head, D = c->head_dim, F = c->mlp_dim, V = c->vocab;
+  const float eps = c->norm_eps;
+  char* ws = (char*)workspace;
+  unsigned* flags = (unsigned*)(ws + L.flags);
+  float* x = (float*)(ws + L.x);
+  float* x0 = (float*)(ws + L.x0);
+  void* xn = ws + L.xn;
+  void* qk = ws + L.qk;
+  void* vt = ws + L.vt;
+  void* o = ws + L.o;
+  void* hbuf = ws + L.h;
+  float2* cs = (float2*)(ws + L.cs);
+  float* partial = (float*)(ws + L.partial);
+  float* tgt = (float*)(ws + L.tgt);
+
+  CK(launch_clear_u32(flags, 16, s));
+  CK(launch_rope_table(cs, T, D, c->rope_base, s));
+  CK(launch_embed_norm(tokens, w->wte, bf, w->resid_lambda, w->x0_lambda, x0, x, xn, M, C, V, eps,
+                       flags, s));
+  const int nqk = (H + Hkv) * D;
+  const int nqkv = (H + 2 * Hkv) * D;
+  for (int l = 0; l < c->n_layer; ++l) {
+    // q, k, v projections (one GEMM over the three weight segments)
+    GemmArgs g = gemm_args(xn, C, w->wq[l], nqkv, C, M, qk, bf ? nqk : nqkv);
+    g.B1 = w->wk[l]; g.B2 = w->wv[l]; g.nseg0 = H * D; g.nseg1 = Hkv * D;
+    g.vt = vt; g.T = T; g.D = D; g.Hkv = Hkv; g.nqk = nqk;
+    CK(gemm(bf, bf ? EPI_QKV : EPI_STORE, g, s));
+    // RoPE + QK-norm on the q and k heads
+    CK(launch_qk_rope_norm(qk, bf, bf ? nqk : nqkv, cs, M, T, H + Hkv, D, eps, s));
+    // windowed causal attention
+    const int win = c->window[l] < T ? c->window[l] : T;
+    if (bf) CK(launch_attn_bf16(qk, vt, o, B, T, H, Hkv, D, win, c->attn_scale, s));
+    else CK(launch_attn_f32((const float*)qk, (float*)o, B, T, H, Hkv, D, win, c->attn_scale, s));
+    // x += o W_O^T
+    CK(gemm(bf, EPI_RESID, gemm_args(o, H * D, w->wo[l], C, H * D, M, x, C), s));
+    // MLP: x += relu(RMSNorm(x) W_1^T)^2 W_2^T
+    CK(launch_mix_norm(x, x0, w->resid_lambda, w->x0_lambda, l, false, xn, bf, M, C, eps, s));
+    CK(gemm(bf, EPI_RELU2, gemm_args(xn, C, w->w1[l], F, C, M, hbuf, F), s));
+    CK(gemm(bf, EPI_RESID, gemm_args(hbuf, F, w->w2[l], C, F, M, x, C), s));
+    // next layer's x0 mix and pre-attention norm, or the final norm
+    const bool more = l + 1 < c->n_layer;
+    CK(launch_mix_norm(x, x0, w->resid_lambda, w->x0_lambda, l + 1, more, xn, bf, M, C, eps, s));
+  }
+  return lm_head_ce(bf, xn, w->lm_head, targets, tokens, M, C, V, c->softcap, loss, mean_loss,
+                    logits, partial, tgt, L.nnb, flags, s);
+}
+
+gpt_status gpt_device_status(void* workspace, void* stream) {
+  if (!workspace) return GPT_E_INVALID_ARG;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return GPT_E_HIP;
+  unsigned f = 0;
+  if (hipMemcpy(&f, workspace, sizeof(f), hipMemcpyDeviceToHost) != hipSuccess) return GPT_E_HIP;
+  return f ? GPT_E_DEVICE_INPUT : GPT_OK;
+}
+
+const char* gpt_status_string(gpt_status s) {
+  switch (s) {
+    case GPT_OK: return "ok";
+    case GPT_E_INVALID_ARG: return "invalid argument";
+    case GPT_E_UNSUPPORTED: return "configuration not supported by the kernels";
+    case GPT_E_WORKSPACE: return "workspace missing, too small or misaligned";
+    case GPT_E_HIP: return "HIP launch or runtime error";
+    case GPT_E_DEVICE_INPUT: return "token or target id out of range";
+  }
+  return "unknown status";
+}
+
+// ---------------------------------------------------------------------------- component ops
+
+static bool dtype_ok(int32_t d) { return d == GPT_F32 || d == GPT_BF16; }
+
+gpt_status gpt_op_embed_norm(int32_t dtype, const int32_t* tokens, const void* wte, const float* lam,
+                             const float* mu, float* x0, float* x, void* xn, int32_t M, int32_t C,
+                             int32_t V, float eps, uint32_t* flags, void* stream) {
+  if (!dtype_ok(dtype) || !tokens || !wte || !lam || !mu || !x0 || !x || !xn || !flags)
+    return GPT_E_INVALID_ARG;
+  if (M < 1 || C < 4 || V < 1 || C % 4 || C > 8192 || !(eps >= 0.f)) return GPT_E_INVALID_ARG;
+  CK(launch_embed_norm(tokens, wte, dtype == GPT_BF16, lam, mu, x0, x, xn, M, C, V, eps, flags,
+                       (hipStream_t)stream));
+  return GPT_OK;
+}
+
+gpt_status gpt_op_mix_norm(int32_t dtype, float* x, const float* x0, const float* lam,
+                           const float* mu, int32_t layer, int32_t mix, void* xn, int32_t M,
+                           int32_t C, float eps, void* stream) {
+  if (!dtype_ok(dtype) || !x || !xn || (mix && (!x0 || !lam || !mu))) return GPT_E_INVALID_ARG;
+  if (M < 1 || C < 4 || C % 4 || C > 8192 || layer < 0 || !(eps >= 0.f)) return GPT_E_INVALID_ARG;
+  CK(launch_mix_norm(x, x0, lam, mu, layer, mix != 0, xn, dtype == GPT_BF16, M, C, eps,
+                     (hipStream_t)stream));
+  return GPT_OK;
+}
+
+gpt_status gpt_op_rope_table(float* cs, int32_t T, int32_t D, float base, void* stream) {
+  if (!cs || T < 1 || D < 2 || (D & 1) || !(base > 0.f)) return GPT_E_INVALID_ARG;
+  CK(launch_rope_table((float2*)cs, T, D, base, (hipStream_t)stream));
+  return GPT_OK;
+}
+
+gpt_status gpt_op_qk_rope_norm(int32_t dtype, void* qk, int32_t ld, const float* cs, int32_t M,
+                               int32_t T, int32_t nheads, int32_t D, float eps, void* stream) {
+  if (!dtype_ok(dtype) || !qk || !cs || M < 1 || T < 1 || nheads < 1 || D < 2 || (D & 1) ||
+      D > 128 || ld < nheads * D || !(eps >= 0.f))
+    return GPT_E_INVALID_ARG;
+  CK(launch_qk_rope_norm(qk, dtype == GPT_BF16, ld, (const float2*)cs, M, T, nheads, D, eps,
+                         (hipStream_t)stream));
+  return GPT_OK;
+}
+
+gpt_status gpt_op_linear(int32_t dtype, int32_t epi, const void* a, const void* w, int32_t M,
+                         int32_t N, int32_t K, void* out, void* stream) {
+  if (!dtype_ok(dtype) || !a || !w || !out || M < 1 || N < 1 || K < 1 || epi < 0 || epi > 2)
+    return GPT_E_INVALID_ARG;
+  const bool bf = dtype == GPT_BF16;
+  if (bf && K % 64) return GPT_E_UNSUPPORTED;
+  const Epi e = epi == 0 ? EPI_STORE : epi == 1 ? EPI_RELU2 : EPI_RESID;
+  CK(gemm(bf, e, gemm_args(a, K, w, N, K, M, out, N), (hipStream_t)stream));
+  return GPT_OK;
+}
+
+gpt_status gpt_op_qkv(const void* xn, const void* wq, const void* wk, const void* wv, int32_t B,
+                      int32_t T, int32_t C, int32_t H, int32_t Hkv, int32_t D, void* qk, void* vt,
+                      void* stream) {
+  if (!xn || !wq || !wk || !wv || !qk || !vt || B < 1 || T < 1 || C < 1 || H < 1 || Hkv < 1 || D < 1)
+    return GPT_E_INVALID_ARG;
+  if (C % 64 || T % 4 || (H * D) % 128 || (Hkv * D) % 128) return GPT_E_UNSUPPORTED;
+  const int M = B * T, nqk = (H + Hkv) * D, nqkv = (H + 2 * Hkv) * D;
+  GemmArgs g = gemm_args(xn, C, wq, nqkv, C, M, qk, nqk);
+  g.B1 = wk; g.B2 = wv; g.nseg0 = H * D; g.nseg1 = Hkv * D;
+  g.vt = vt; g.T = T; g.D = D; g.Hkv = Hkv; g.nqk = nqk;
+  CK(launch_gemm_bf16(EPI_QKV, g, (hipStream_t)stream));
+  return GPT_OK;
+}
+
+gpt_status gpt_op_attention(int32_t dtype, const void* qk, const void* vt, void* o, int32_t B,
+                            int32_t T, int32_t H, int32_t Hkv, int32_t D, int32_t window,
+                            float scale, void* stream) {
+  if (!dtype_ok(dtype) || !qk || !o || B < 1 || T < 1 || H < 1 || Hkv < 1 || H % Hkv ||
+      window < 1 || !(scale > 0.f))
+    return GPT_E_INVALID_ARG;
+  if (D != 64 && D != 128) return GPT_E_UNSUPPORTED;
+  const int win = window < T ? window : T;
+  if (dtype == GPT_BF16) {
+    if (!vt) return GPT_E_INVALID_ARG;
+    if (T % 64) return GPT_E_UNSUPPORTED;
+    CK(launch_attn_bf16(qk, vt, o, B, T, H, Hkv, D, win, scale, (hipStream_t)stream));
+  } else {
+    CK(launch_attn_f32((const float*)qk, (float*)o, B, T, H, Hkv, D, win, scale, (hipStream_t)stream));
+  }
+  return GPT_OK;
+}
+
+size_t gpt_op_lm_head_ce_workspace(int32_t dtype, int32_t M, int32_t V) {
+  if (!dtype_ok(dtype) || M < 1 || V < 2) return 0;
+  const int nnb = dtype == GPT_BF16 ? gemm_bf16_ce_blocks(V) : gemm_f32_ce_blocks(V);
+  return up(64) + up((size_t)M * nnb * 4) + up((size_t)M * 4);
+}
+
+gpt_status gpt_op_lm_head_ce(int32_t dtype, const void* xf, const void* wu, const int32_t* targets,
+                             const int32_t* tokens, int32_t M, int32_t C, int32_t V, float cap,
+                             float* loss, float* mean, float* logits, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype) || !xf || !wu || !tokens || M < 1 || C < 1 || V < 2 || !(cap > 0.f))
+    return GPT_E_INVALID_ARG;
+  if (targets && (!loss || !mean)) return GPT_E_INVALID_ARG;
+  if (!targets && !logits) return GPT_E_INVALID_ARG;
+  const bool bf = dtype == GPT_BF16;
+  if (bf && C % 64) return GPT_E_UNSUPPORTED;
+  const size_t need = gpt_op_lm_head_ce_workspace(dtype, M, V);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, ALIGN)) return GPT_E_WORKSPACE;
+  const int nnb = bf ? gemm_bf16_ce_blocks(V) : gemm_f32_ce_blocks(V);
+  char* ws = (char*)workspace;
+  unsigned* flags = (unsigned*)ws;
+  float* partial = (float*)(ws + up(64));
+  float* tgt = (float*)(ws + up(64) + up((size_t)M * nnb * 4));
+  hipStream_t s = (hipStream_t)stream;
+  CK(launch_clear_u32(flags, 16, s));
+  return lm_head_ce(bf, xf, wu, targets, tokens, M, C, V, cap, loss, mean, logits, partial, tgt, nnb,
+                    flags, s);
+}
+
+}  // extern "C"

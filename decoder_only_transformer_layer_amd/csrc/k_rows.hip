@@ -1,0 +1,233 @@
+// Row-wise HBM-bound kernels: embedding gather + RMSNorm, residual x0-mix + RMSNorm, the RoPE
+// table, and RoPE + per-head RMSNorm (QK-norm).  One 64-lane wavefront owns one row and reduces
+// its sum of squares with cross-lane shuffles; statistics are fp32.
+//
+// Sources: "The Mathematics of Karpathy's nanochat", sections "High-Level Forward Pass" (embed,
+// norm, keep x0), "RMS Normalization", "Residual Stream with Learnable Scalars" (x <- lambda x +
+// mu x0), "Rotary Position Embeddings (RoPE)" and "QK-Norm with Sharpening".
+#include "common.h"
+#include "kernels.h"
+
+namespace gptk {
+namespace {
+
+constexpr int ROWS_PER_BLOCK = 4;  // 4 wavefronts of 64 lanes
+
+__device__ __forceinline__ void load4(const float* p, float v[4]) {
+  float4 t = *(const float4*)p;
+  v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+}
+__device__ __forceinline__ void load4(const bf16* p, float v[4]) {
+  bf16x4 t = *(const bf16x4*)p;
+  v[0] = (float)t[0]; v[1] = (float)t[1]; v[2] = (float)t[2]; v[3] = (float)t[3];
+}
+__device__ __forceinline__ void store4(float* p, const float v[4]) {
+  *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store4(bf16* p, const float v[4]) {
+  bf16x4 t;
+  t[0] = (bf16)v[0]; t[1] = (bf16)v[1]; t[2] = (bf16)v[2]; t[3] = (bf16)v[3];
+  *(bf16x4*)p = t;
+}
+
+// NCH = number of 4-element chunks per lane (C <= 256 * NCH).
+template <typename WT, typename AT, int NCH>
+__global__ __launch_bounds__(256) void embed_norm_kernel(
+    const int32_t* __restrict__ tokens, const WT* __restrict__ wte, const float* __restrict__ lam,
+    const float* __restrict__ mu, float* __restrict__ x0, float* __restrict__ x, AT* __restrict__ xn,
+    int M, int C, int V, float eps, unsigned* __restrict__ flags) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
+  if (row >= M) return;
+  int t = tokens[row];
+  if ((unsigned)t >= (unsigned)V) {  // out-of-range id: flag it, read row 0 so nothing faults
+    if (lane == 0) atomicOr(flags, GPT_FLAG_BAD_TOKEN);
+    t = 0;
+  }
+  const WT* src = wte + (size_t)t * C;
+  float v[NCH][4];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int i = (c * 64 + lane) * 4;
+    if (i < C) {
+      load4(src + i, v[c]);
+      ss += v[c][0] * v[c][0] + v[c][1] * v[c][1] + v[c][2] * v[c][2] + v[c][3] * v[c][3];
+    }
+  }
+  ss = wave_sum(ss);
+  const float r0 = rsqrtf(ss / (float)C + eps);
+  const float a = lam[0], b = mu[0];
+  float ss2 = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int i = (c * 64 + lane) * 4;
+    if (i < C) {
+      float e0[4], e1[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        e0[k] = v[c][k] * r0;
+        e1[k] = a * e0[k] + b * e0[k];
+        ss2 += e1[k] * e1[k];
+        v[c][k] = e1[k];
+      }
+      store4(x0 + (size_t)row * C + i, e0);
+      store4(x + (size_t)row * C + i, e1);
+    }
+  }
+  ss2 = wave_sum(ss2);
+  const float r1 = rsqrtf(ss2 / (float)C + eps);
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int i = (c * 64 + lane) * 4;
+    if (i < C) {
+      float e[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) e[k] = v[c][k] * r1;
+      store4(xn + (size_t)row * C + i, e);
+    }
+  }
+}
+
+template <typename AT, int NCH, bool MIX>
+__global__ __launch_bounds__(256) void mix_norm_kernel(
+    float* __restrict__ x, const float* __restrict__ x0, const float* __restrict__ lam,
+    const float* __restrict__ mu, int layer, AT* __restrict__ xn, int M, int C, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
+  if (row >= M) return;
+  float* xr = x + (size_t)row * C;
+  float a = 1.f, b = 0.f;
+  if (MIX) { a = lam[layer]; b = mu[layer]; }
+  float v[NCH][4];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int i = (c * 64 + lane) * 4;
+    if (i < C) {
+      load4(xr + i, v[c]);
+      if (MIX) {
+        float w[4];
+        load4(x0 + (size_t)row * C + i, w);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[c][k] = a * v[c][k] + b * w[k];
+        store4(xr + i, v[c]);
+      }
+      ss += v[c][0] * v[c][0] + v[c][1] * v[c][1] + v[c][2] * v[c][2] + v[c][3] * v[c][3];
+    }
+  }
+  ss = wave_sum(ss);
+  const float r = rsqrtf(ss / (float)C + eps);
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int i = (c * 64 + lane) * 4;
+    if (i < C) {
+      float e[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) e[k] = v[c][k] * r;
+      store4(xn + (size_t)row * C + i, e);
+    }
+  }
+}
+
+__global__ void rope_table_kernel(float2* __restrict__ cs, int T, int half, double base) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= T * half) return;
+  const int t = idx / half, j = idx % half;
+  const double omega = pow(base, -2.0 * (double)j / (double)(2 * half));
+  const double phi = (double)t * omega;
+  cs[idx] = make_float2((float)cos(phi), (float)sin(phi));
+}
+
+// One wavefront per (row, head); lane p rotates the pair (p, p + D/2).
+template <typename AT>
+__global__ __launch_bounds__(256) void qk_rope_norm_kernel(AT* __restrict__ qk, int ld,
+                                                           const float2* __restrict__ cs, int M,
+                                                           int T, int nheads, int D, float eps) {
+  const int lane = threadIdx.x & 63;
+  const long w = (long)blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
+  const int row = (int)(w / nheads), hh = (int)(w % nheads);
+  if (row >= M) return;
+  const int t = row % T, half = D >> 1;
+  AT* p = qk + (size_t)row * ld + (size_t)hh * D;
+  float y1 = 0.f, y2 = 0.f;
+  if (lane < half) {
+    const float u1 = to_f32(p[lane]), u2 = to_f32(p[lane + half]);
+    const float2 c = cs[t * half + lane];
+    y1 = u1 * c.x + u2 * c.y;
+    y2 = -u1 * c.y + u2 * c.x;
+  }
+  const float ss = wave_sum(y1 * y1 + y2 * y2);
+  const float r = rsqrtf(ss / (float)D + eps);
+  if (lane < half) {
+    p[lane] = from_f32<AT>(y1 * r);
+    p[lane + half] = from_f32<AT>(y2 * r);
+  }
+}
+
+template <typename F>
+hipError_t dispatch_nch(int C, F&& f) {
+  if (C <= 256) return f(std::integral_constant<int, 1>{});
+  if (C <= 512) return f(std::integral_constant<int, 2>{});
+  if (C <= 1024) return f(std::integral_constant<int, 4>{});
+  if (C <= 2048) return f(std::integral_constant<int, 8>{});
+  if (C <= 4096) return f(std::integral_constant<int, 16>{});
+  if (C <= 8192) return f(std::integral_constant<int, 32>{});
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_rope_table(float2* cs, int T, int D, float base, hipStream_t s) {
+  const int n = T * (D / 2);
+  rope_table_kernel<<<(n + 255) / 256, 256, 0, s>>>(cs, T, D / 2, (double)base);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed_norm(const int32_t* tokens, const void* wte, bool wbf16, const float* lam,
+                             const float* mu, float* x0, float* x, void* xn, int M, int C, int V,
+                             float eps, unsigned* flags, hipStream_t s) {
+  if (C % 4) return hipErrorInvalidValue;
+  const int grid = (M + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
+  return dispatch_nch(C, [&](auto nch) {
+    constexpr int N = decltype(nch)::value;
+    if (wbf16)
+      embed_norm_kernel<bf16, bf16, N><<<grid, 256, 0, s>>>(tokens, (const bf16*)wte, lam, mu, x0, x,
+                                                            (bf16*)xn, M, C, V, eps, flags);
+    else
+      embed_norm_kernel<float, float, N><<<grid, 256, 0, s>>>(tokens, (const float*)wte, lam, mu, x0,
+                                                              x, (float*)xn, M, C, V, eps, flags);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_mix_norm(float* x, const float* x0, const float* lam, const float* mu, int layer,
+                           bool mix, void* xn, bool xbf16, int M, int C, float eps, hipStream_t s) {
+  if (C % 4) return hipErrorInvalidValue;
+  const int grid = (M + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
+  return dispatch_nch(C, [&](auto nch) {
+    constexpr int N = decltype(nch)::value;
+    if (xbf16) {
+      if (mix) mix_norm_kernel<bf16, N, true><<<grid, 256, 0, s>>>(x, x0, lam, mu, layer, (bf16*)xn, M, C, eps);
+      else mix_norm_kernel<bf16, N, false><<<grid, 256, 0, s>>>(x, x0, lam, mu, layer, (bf16*)xn, M, C, eps);
+    } else {
+      if (mix) mix_norm_kernel<float, N, true><<<grid, 256, 0, s>>>(x, x0, lam, mu, layer, (float*)xn, M, C, eps);
+      else mix_norm_kernel<float, N, false><<<grid, 256, 0, s>>>(x, x0, lam, mu, layer, (float*)xn, M, C, eps);
+    }
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_qk_rope_norm(void* qk, bool bf16_, int ld, const float2* cs, int M, int T,
+                               int nheads, int D, float eps, hipStream_t s) {
+  if (D > 128 || (D & 1)) return hipErrorInvalidValue;
+  const long waves = (long)M * nheads;
+  const int grid = (int)((waves + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK);
+  if (bf16_)
+    qk_rope_norm_kernel<bf16><<<grid, 256, 0, s>>>((bf16*)qk, ld, cs, M, T, nheads, D, eps);
+  else
+    qk_rope_norm_kernel<float><<<grid, 256, 0, s>>>((float*)qk, ld, cs, M, T, nheads, D, eps);
+  return hipGetLastError();
+}
+
+}  // namespace gptk

@@ -1,0 +1,80 @@
+// Host-side launchers of the gfx950 kernels (C++ linkage, internal to libgptfwd).
+// Every launcher enqueues on `stream` and returns hipGetLastError() of the launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gptk {
+
+// ---- row kernels (k_rows.hip) ------------------------------------------------------------
+// cos/sin table cs[t * (D/2) + j] = (cos phi, sin phi), phi = t * base^(-2j/D), in fp64 then fp32.
+hipError_t launch_rope_table(float2* cs, int T, int D, float base, hipStream_t s);
+
+// x0 = RMSNorm(wte[tokens]); x = lam[0] x0 + mu[0] x0; xn = RMSNorm(x).
+// wbf16 selects bf16 (else fp32) embedding storage and xn type.
+hipError_t launch_embed_norm(const int32_t* tokens, const void* wte, bool wbf16, const float* lam,
+                             const float* mu, float* x0, float* x, void* xn, int M, int C, int V,
+                             float eps, unsigned* flags, hipStream_t s);
+
+// If mix: x = lam[layer] x + mu[layer] x0 (in place).  Then xn = RMSNorm(x).
+hipError_t launch_mix_norm(float* x, const float* x0, const float* lam, const float* mu, int layer,
+                           bool mix, void* xn, bool xbf16, int M, int C, float eps, hipStream_t s);
+
+// In place on qk [M][nheads*D] (the q heads then the k heads of each token): RoPE at
+// position row % T, then per-head RMSNorm.
+hipError_t launch_qk_rope_norm(void* qk, bool bf16, int ld, const float2* cs, int M, int T,
+                               int nheads, int D, float eps, hipStream_t s);
+
+// ---- GEMMs (k_gemm.hip) --------------------------------------------------------------------
+enum Epi { EPI_STORE = 0, EPI_RELU2 = 1, EPI_RESID = 2, EPI_QKV = 3, EPI_CE = 4 };
+
+struct GemmArgs {
+  const void* A; int lda;                 // [M, K] row-major
+  const void* B0; const void* B1; const void* B2;  // row segments of B [N, K] (row-major, K contiguous)
+  int nseg0, nseg1;                       // rows [0,nseg0) in B0, [nseg0,nseg0+nseg1) in B1, rest in B2
+  int ldb;
+  int M, N, K;
+  void* out; int ldo;                     // STORE/RELU2: act [M, ldo]; RESID: float [M, ldo] (+=); QKV: qk
+  void* vt; int T, D, Hkv, nqk;           // QKV (bf16 only): columns >= nqk stored transposed to vt [B][Hkv][D][T]
+  const int32_t* targets;                 // CE: [M] (or NULL)
+  float* partial;                         // CE: [M][nnb] sums of exp(zhat - cap) per column block
+  float* tgt_logit;                       // CE: [M] raw logit z at the target column
+  float* logits;                          // CE: optional [M][N] raw fp32 logits (softcap applied later)
+  int nnb;                                // CE: number of column blocks
+  float cap;                              // CE: softcap
+};
+
+// bf16 inputs, fp32 accumulation on MFMA.  Returns hipErrorInvalidValue for shapes the
+// tiling does not cover (K % 64, segment sizes).
+hipError_t launch_gemm_bf16(Epi epi, const GemmArgs& a, hipStream_t s);
+// Number of column blocks the CE epilogue of launch_gemm_bf16 produces for N columns.
+int gemm_bf16_ce_blocks(int N);
+// fp32 SIMT GEMM (small configurations).
+hipError_t launch_gemm_f32(Epi epi, const GemmArgs& a, hipStream_t s);
+int gemm_f32_ce_blocks(int N);
+
+// ---- attention (k_attn.hip) ----------------------------------------------------------------
+// bf16: q/k from qk [B*T][(H+Hkv)*D] (already RoPE'd and normed), v from vt [B][Hkv][D][T];
+// o [B*T][H*D].  D must be 128 or 64, T % 64 == 0.
+hipError_t launch_attn_bf16(const void* qk, const void* vt, void* o, int B, int T, int H, int Hkv,
+                            int D, int window, float scale, hipStream_t s);
+// fp32: q/k/v from qkv [B*T][(H+2Hkv)*D]; o [B*T][H*D].
+hipError_t launch_attn_f32(const float* qkv, float* o, int B, int T, int H, int Hkv, int D,
+                           int window, float scale, hipStream_t s);
+
+// ---- loss (k_loss.hip) ----------------------------------------------------------------------
+// loss[row] = cap + log(sum_nb partial[row][nb]) - cap tanh(tgt_logit[row] / cap); 0 where
+// target = -1;
+// NaN (and a flag bit) for an out-of-range target or token.
+hipError_t launch_ce_finalize(const float* partial, int nnb, const float* tgt_logit,
+                              const int32_t* targets, const int32_t* tokens, int M, int V, float cap,
+                              float* loss, unsigned* flags, hipStream_t s);
+// z = cap * tanh(z / cap) in place over n floats.
+hipError_t launch_softcap(float* z, size_t n, float cap, hipStream_t s);
+// Zero n 32-bit words with a kernel (no memset node, so the call stays graph-capturable).
+hipError_t launch_clear_u32(unsigned* p, int n, hipStream_t s);
+// mean over rows with target != -1 (NaN if none); fixed-order reduction.
+hipError_t launch_ce_mean(const float* loss, const int32_t* targets, int M, float* mean, hipStream_t s);
+
+}  // namespace gptk

@@ -1,0 +1,130 @@
+/*
+ * gptfwd.h -- C ABI of libgptfwd: the nanochat GPT forward pass with next-token loss on AMD
+ * MI355X (gfx950).
+ *
+ * The operation (sources cited by page title and section):
+ *   "The Mathematics of Karpathy's nanochat", sections "High-Level Forward Pass" and
+ *   "Pseudocode: One Training Step": x = RMSNorm(W_E[t]); x0 = x; for every layer l:
+ *   x = lambda_l x + mu_l x0; x += W_O Attn(RoPE + QK-norm of W_Q/W_K/W_V RMSNorm(x));
+ *   x += W_2 relu(W_1 RMSNorm(x))^2; then zhat = cap tanh(W_U RMSNorm(x) / cap) and the
+ *   cross-entropy of zhat against the next token ("Logit Softcap", "Cross-Entropy Loss").
+ *   Attention is causal with a per-layer window w_l: query i sees key j iff j <= i and
+ *   i - j < w_l ("Scaled Dot-Product Attention with Sliding Window"); the short/long window
+ *   pattern is tiled over the layers with the last layer always long ("nanochat depth sweep",
+ *   section "Architecture").  The logit of a visible pair is attn_scale * <q_hat, k_hat>.
+ *   Input/target shift: "Reading nanochat Source: From Configuration to a Training Step",
+ *   section 2 -- targets[b][t] is the token that follows tokens[b][t].
+ *
+ * Conventions
+ *   - All array pointers are DEVICE pointers unless marked "host".  All matrices are row-major;
+ *     weights are [out_features, in_features].
+ *   - Ownership: the caller owns every buffer (weights, inputs, outputs, workspace).  The
+ *     library allocates no memory and keeps no pointer after the enqueued work completes.  It
+ *     keeps no state: calls with distinct workspaces may run concurrently on different streams.
+ *   - Asynchrony: gpt_fwd_loss only enqueues work on `stream` (a hipStream_t; NULL = the null
+ *     stream) and returns; results are valid once the stream reaches that point.
+ *   - Errors: every argument error detectable on the host is reported before any work is
+ *     enqueued, and no output is touched.  A failed kernel launch returns GPT_E_HIP.  Invalid
+ *     token or target ids are detected on the device: the affected per-token losses are NaN and
+ *     gpt_device_status() reports GPT_E_DEVICE_INPUT.
+ *   - Precision: with GPT_BF16 the weights and the GEMM/attention operands are bf16; products
+ *     accumulate in fp32, and the residual stream, every normalisation statistic, the softmax
+ *     and the logits are fp32.  With GPT_F32 everything is fp32.
+ */
+#ifndef GPTFWD_H
+#define GPTFWD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GPT_OK = 0,
+  GPT_E_INVALID_ARG = -1,  /* NULL pointer, non-positive size, inconsistent shape */
+  GPT_E_UNSUPPORTED = -2,  /* valid model, but outside what the kernels implement (see gpt_cfg) */
+  GPT_E_WORKSPACE = -3,    /* workspace NULL, too small or not 256-byte aligned */
+  GPT_E_HIP = -4,          /* a HIP call or kernel launch failed */
+  GPT_E_DEVICE_INPUT = -5  /* (gpt_device_status) a token or target id was out of range */
+} gpt_status;
+
+typedef enum { GPT_F32 = 0, GPT_BF16 = 1 } gpt_dtype;
+
+/* Model and batch shape.  Supported: head_dim in {64, 128}; n_head % n_kv_head == 0;
+ * d_model, n_head*head_dim and mlp_dim multiples of 64; vocab >= 2; for GPT_BF16 seq_len a
+ * multiple of 64 and n_kv_head*head_dim a multiple of 128.  d_model <= 8192. */
+typedef struct {
+  int32_t n_layer;      /* L */
+  int32_t d_model;      /* C, residual width */
+  int32_t n_head;       /* H, query heads */
+  int32_t n_kv_head;    /* Hkv, key/value heads; query head h reads KV head h*Hkv/H */
+  int32_t head_dim;     /* D */
+  int32_t mlp_dim;      /* F, MLP hidden width (4C in nanochat) */
+  int32_t vocab;        /* V */
+  int32_t seq_len;      /* T, tokens per packed row */
+  int32_t batch;        /* B, rows */
+  const int32_t *window;/* host [n_layer]: keys visible to a query, itself included, >= 1;
+                           a value >= seq_len means full causal attention */
+  float softcap;        /* cap > 0 of zhat = cap * tanh(z / cap); nanochat uses 15 */
+  float rope_base;      /* RoPE theta; nanochat uses 100000 */
+  float attn_scale;     /* logit scale applied to <q_hat, k_hat>, e.g. 1/sqrt(head_dim) */
+  float norm_eps;       /* eps inside every RMSNorm's square root, >= 0 (1e-6) */
+  int32_t dtype;        /* gpt_dtype of weights and activations */
+} gpt_cfg;
+
+/* Weights: borrowed device memory of type cfg->dtype (float or bf16), row-major [out, in].
+ * Per-layer matrices are given as HOST arrays of n_layer device pointers.  Every device
+ * pointer must be 16-byte aligned. */
+typedef struct {
+  const void *wte;            /* [vocab, d_model] token embedding W_E */
+  const void *lm_head;        /* [vocab, d_model] unembedding W_U (untied) */
+  const float *resid_lambda;  /* device fp32 [n_layer]: lambda_l */
+  const float *x0_lambda;     /* device fp32 [n_layer]: mu_l */
+  const void *const *wq;      /* host [n_layer] -> [n_head*head_dim, d_model] */
+  const void *const *wk;      /* host [n_layer] -> [n_kv_head*head_dim, d_model] */
+  const void *const *wv;      /* host [n_layer] -> [n_kv_head*head_dim, d_model] */
+  const void *const *wo;      /* host [n_layer] -> [d_model, n_head*head_dim] */
+  const void *const *w1;      /* host [n_layer] -> [mlp_dim, d_model] */
+  const void *const *w2;      /* host [n_layer] -> [d_model, mlp_dim] */
+} gpt_weights;
+
+/* Validate a configuration without touching any device.  Returns GPT_OK, GPT_E_INVALID_ARG or
+ * GPT_E_UNSUPPORTED. */
+gpt_status gpt_validate(const gpt_cfg *cfg);
+
+/* Bytes of device workspace gpt_fwd_loss needs for this configuration (0 if the configuration
+ * does not validate). */
+size_t gpt_workspace_bytes(const gpt_cfg *cfg);
+
+/* Forward pass plus next-token loss over tokens [batch, seq_len].
+ *   tokens     device int32 [B, T], ids in [0, vocab)
+ *   targets    device int32 [B, T], ids in [0, vocab) or -1 (ignored position); may be NULL, in
+ *              which case no loss is computed and `logits` must be non-NULL
+ *   loss       device fp32 [B, T] out: per-token loss, 0 at ignored positions; required iff
+ *              targets is non-NULL
+ *   mean_loss  device fp32 [1] out: mean over positions with target != -1 (NaN if none);
+ *              required iff targets is non-NULL
+ *   logits     device fp32 [B, T, vocab] out: softcapped logits zhat, or NULL (the default
+ *              path never materialises the logits)
+ *   workspace  device scratch of at least gpt_workspace_bytes(cfg), 256-byte aligned; its
+ *              contents on entry do not matter
+ * Returns GPT_OK once everything is enqueued on `stream` (hipStream_t). */
+gpt_status gpt_fwd_loss(const gpt_cfg *cfg, const gpt_weights *w, const int32_t *tokens,
+                        const int32_t *targets, float *loss, float *mean_loss, float *logits,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* Synchronise `stream`, then report whether any gpt_fwd_loss call that used this workspace saw
+ * an out-of-range token or target id since the workspace's last call began (GPT_OK or
+ * GPT_E_DEVICE_INPUT; GPT_E_HIP if synchronising failed). */
+gpt_status gpt_device_status(void *workspace, void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *gpt_status_string(gpt_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTFWD_H */

@@ -1,0 +1,149 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared symbol, and
+rejects bad arguments before touching any device (these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import decoder_only_transformer_layer_amd as gf
+import gptdata
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    for h in ("gptfwd.h", "gptfwd_ops.h"):
+        src = open(os.path.join(ROOT, "include", h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names |= set(re.findall(r"\b(gpt_\w+)\s*\(", src))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gf.LIB_PATH):
+        pytest.skip("libgptfwd.so not built")
+    return gf._load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(gf.EXPORTED) == names
+
+
+def test_status_strings(lib):
+    for s in (0, -1, -2, -3, -4, -5):
+        assert gf.gpt_status_string(s) not in ("", "unknown status")
+    assert gf.gpt_status_string(7) == "unknown status"
+
+
+def _cfg(**kw):
+    p = gptdata.preset("d24")
+    c = gf.make_cfg(p)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_validate_presets(lib):
+    for name in ("tiny", "d12", "d24"):
+        c = gf.make_cfg(gptdata.preset(name))
+        assert gf.gpt_validate(c) == gf.GPT_OK, name
+        assert gf.gpt_workspace_bytes(c) > 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("n_layer", 0, gf.GPT_E_INVALID_ARG),
+    ("vocab", 1, gf.GPT_E_INVALID_ARG),
+    ("n_kv_head", 5, gf.GPT_E_INVALID_ARG),        # 12 % 5 != 0
+    ("softcap", 0.0, gf.GPT_E_INVALID_ARG),
+    ("attn_scale", -1.0, gf.GPT_E_INVALID_ARG),
+    ("norm_eps", -1e-6, gf.GPT_E_INVALID_ARG),
+    ("dtype", 7, gf.GPT_E_INVALID_ARG),
+    ("head_dim", 96, gf.GPT_E_UNSUPPORTED),
+    ("d_model", 1000, gf.GPT_E_UNSUPPORTED),
+    ("mlp_dim", 6100, gf.GPT_E_UNSUPPORTED),
+    ("seq_len", 2000, gf.GPT_E_UNSUPPORTED),        # bf16 needs T % 64 == 0
+])
+def test_validate_rejects(lib, field, value, status):
+    c = _cfg(**{field: value})
+    assert gf.gpt_validate(c) == status
+    assert gf.gpt_workspace_bytes(c) == 0
+
+
+def test_validate_rejects_bad_window(lib):
+    c = _cfg()
+    c._win[3] = 0
+    assert gf.gpt_validate(c) == gf.GPT_E_INVALID_ARG
+    c.window = None
+    assert gf.gpt_validate(c) == gf.GPT_E_INVALID_ARG
+    assert lib.gpt_validate(None) == gf.GPT_E_INVALID_ARG
+
+
+def _weights(L, fake=0x100000):
+    arr = (ctypes.c_void_p * L)(*[fake + 256 * i for i in range(L)])
+    ptr = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+    w = gf.gpt_weights(fake, fake, fake, fake, ptr, ptr, ptr, ptr, ptr, ptr)
+    w._keep = arr
+    return w
+
+
+def test_fwd_loss_argument_errors_return_before_launch(lib):
+    """Every host-detectable error returns before any HIP call: fake device addresses are
+    never dereferenced."""
+    c = _cfg()
+    L = c.n_layer
+    w = _weights(L)
+    need = gf.gpt_workspace_bytes(c)
+    F = 0x200000
+    call = lambda **kw: lib.gpt_fwd_loss(
+        ctypes.byref(kw.get("cfg", c)), ctypes.byref(kw.get("w", w)) if kw.get("w", w) is not None else None,
+        kw.get("tokens", F), kw.get("targets", F), kw.get("loss", F), kw.get("mean", F),
+        kw.get("logits", None), kw.get("ws", 0x10000000), kw.get("wsb", need), None)
+    assert call(tokens=None) == gf.GPT_E_INVALID_ARG
+    assert call(w=None) == gf.GPT_E_INVALID_ARG
+    assert call(loss=None) == gf.GPT_E_INVALID_ARG          # targets given, loss missing
+    assert call(targets=None, logits=None) == gf.GPT_E_INVALID_ARG  # nothing to compute
+    assert call(ws=None) == gf.GPT_E_WORKSPACE
+    assert call(wsb=need - 1) == gf.GPT_E_WORKSPACE
+    assert call(ws=0x10000000 + 8) == gf.GPT_E_WORKSPACE   # not 256-aligned
+    w2 = _weights(L)
+    w2._keep[5] = None
+    assert call(w=w2) == gf.GPT_E_INVALID_ARG
+    w3 = _weights(L)
+    w3._keep[2] = 0x100008                                  # not 16-byte aligned
+    assert call(w=w3) == gf.GPT_E_INVALID_ARG
+    bad = _cfg(head_dim=96)
+    assert call(cfg=bad) == gf.GPT_E_UNSUPPORTED
+
+
+def test_op_argument_errors(lib):
+    F = 0x200000
+    assert lib.gpt_op_linear(1, 0, None, F, 10, 10, 64, F, None) == gf.GPT_E_INVALID_ARG
+    assert lib.gpt_op_linear(1, 3, F, F, 10, 10, 64, F, None) == gf.GPT_E_INVALID_ARG
+    assert lib.gpt_op_linear(1, 0, F, F, 10, 10, 60, F, None) == gf.GPT_E_UNSUPPORTED
+    assert lib.gpt_op_attention(1, F, F, F, 1, 100, 2, 2, 128, 8, 0.1, None) == gf.GPT_E_UNSUPPORTED
+    assert lib.gpt_op_attention(1, F, F, F, 1, 128, 3, 2, 128, 8, 0.1, None) == gf.GPT_E_INVALID_ARG
+    assert lib.gpt_op_attention(1, F, F, F, 1, 128, 2, 2, 80, 8, 0.1, None) == gf.GPT_E_UNSUPPORTED
+    assert lib.gpt_op_embed_norm(1, F, F, F, F, F, F, F, 4, 6, 10, 1e-6, F, None) == gf.GPT_E_INVALID_ARG
+    assert lib.gpt_op_qk_rope_norm(1, F, 100, F, 4, 4, 1, 256, 1e-6, None) == gf.GPT_E_INVALID_ARG
+    assert lib.gpt_op_rope_table(F, 4, 7, 1e5, None) == gf.GPT_E_INVALID_ARG
+    assert lib.gpt_op_lm_head_ce_workspace(1, 16, 1) == 0
+    need = lib.gpt_op_lm_head_ce_workspace(1, 16, 100)
+    assert need > 0
+    assert lib.gpt_op_lm_head_ce(1, F, F, F, F, 16, 64, 100, 15.0, F, F, None, 0x10000000, need - 4,
+                                 None) == gf.GPT_E_WORKSPACE
+    assert lib.gpt_op_lm_head_ce(1, F, F, None, F, 16, 64, 100, 15.0, F, F, None, 0x10000000, need,
+                                 None) == gf.GPT_E_INVALID_ARG
+
+
+def test_layer_windows_matches_pattern():
+    assert gf.layer_windows("SSSL", 1024, 2048, 24) == [1024, 1024, 1024, 2048] * 6
+    assert gf.layer_windows("SSSL", 1024, 2048, 12)[-1] == 2048
+    assert gf.layer_windows("SSSL", 128, 256, 2) == [128, 256]
+    assert gf.layer_windows("SSSL", 1024, 2048, 5) == [1024, 1024, 1024, 2048, 2048]
