@@ -37,8 +37,8 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, extra, build_dir: str = BUILD) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
     cmd = [_hipcc(), *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -46,20 +46,20 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    """Compile and link; returns the path of libgptfwd.so."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, extra=(), out: str = LIB, build_dir: str = BUILD) -> str:
+    """Compile and link; returns the path of the shared library (libgptfwd.so by default)."""
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra)), SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+        objs = list(ex.map(lambda s: _compile(s, list(extra), build_dir), SOURCES))
+    tmp = out + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

@@ -19,13 +19,32 @@
 // 16-byte fragment reads of 8 (or 16) consecutive rows hit distinct banks.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace gptk {
 namespace {
 
+#ifndef GEMM_MIX
+#define GEMM_MIX 0
+#endif
+#ifndef GEMM_N1536
+#define GEMM_N1536 2
+#endif
+#ifndef GEMM_DIRECT_LDS
+#define GEMM_DIRECT_LDS 2
+#endif
+
 constexpr int BK = 64;
+
+// s_waitcnt immediate waiting until at most n vector-memory operations are outstanding
+// (gfx9 encoding: vmcnt[3:0] at bits 3:0 and vmcnt[5:4] at bits 15:14; expcnt and lgkmcnt
+// left at their maxima so they are not waited on).
+constexpr int vmcnt_le(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
+// s_waitcnt immediate waiting for all LDS/scalar-memory operations only.
+constexpr int lgkmcnt_0 = 0xC07F;
 
 __device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
@@ -36,8 +55,26 @@ __device__ __forceinline__ float ce_term(float z, float two_over_cap_log2e, floa
   return exp2_fast(m2cap_log2e * rcp_fast(1.0f + e));
 }
 
+// Block -> output tile.  Workgroups are dispatched round-robin over the 8 XCDs (each with its
+// own L2), so block ids are first regrouped so that XCD x owns a contiguous 1/8 of the tile
+// sequence; within it, tiles run down GM row-blocks before moving one column-block right, so
+// the ~32 tiles resident on one XCD share a few A and B panels.
+template <int GM>
+__device__ __forceinline__ void tile_of(int pid, int nbm, int nbn, int& bm, int& bn) {
+  const int nt = nbm * nbn;
+  int t = pid;
+  if ((nt & 7) == 0) t = (pid & 7) * (nt >> 3) + (pid >> 3);
+  const int group = t / (GM * nbn);
+  const int first = group * GM;
+  const int gsz = min(nbm - first, GM);
+  const int in = t - group * GM * nbn;
+  bm = first + in % gsz;
+  bn = in / gsz;
+}
+
 template <int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the body uses device-only types (buffer resources)
   constexpr int NT = WM * WN * 64;
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
   constexpr int AC = BM * 8 / NT, BC = BN * 8 / NT;  // 16-byte chunks per thread per K step
@@ -52,23 +89,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
   const int wm = wid / WN, wn = wid % WN;
   const int M = g.M, N = g.N, K = g.K;
 
-  // Tile order: groups of 8 row-blocks sweep the column blocks, so concurrently resident
-  // blocks share A panels and B panels in L2.
   const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
   int bm, bn;
-  {
-    const int pid = blockIdx.x;
-    constexpr int GM = 8;
-    const int group = pid / (GM * nbn);
-    const int first = group * GM;
-    const int gsz = min(nbm - first, GM);
-    const int in = pid - group * GM * nbn;
-    bm = first + in % gsz;
-    bn = in / gsz;
-  }
+  tile_of<8>(blockIdx.x, nbm, nbn, bm, bn);
   const int m0 = bm * BM, n0 = bn * BN;
 
-  // B row segment holding this column block (segments are multiples of BN except the last).
+  // B row segment holding this column block (segment boundaries are multiples of BN).
   const bf16* Bseg;
   int nb0, nrows;
   if (n0 < g.nseg0) { Bseg = (const bf16*)g.B0; nb0 = n0; nrows = g.nseg0; }
@@ -77,7 +103,181 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
 
   const bf16* const A = (const bf16*)g.A;
   const int lda = g.lda, ldb = g.ldb;
+  const int nk = K / BK;
 
+  // Fragment read offsets (elements) for k-substep 0; substep kk adds chunk 2*kk.
+  int oa[FM], ob[FN];
+  const int hl = lane >> 5, rl = lane & 31;
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) oa[fm] = (wm * TM + fm * 32 + rl) * BK;
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) ob[fn] = (wn * TN + fn * 32 + rl) * BK;
+  const int sa = swz8(rl);  // rows differ from rl by multiples of 32: same swizzle
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.f;
+
+#define GEMM_SUBSTEP(Ab, Bb, kk)                                                              \
+  do {                                                                                       \
+    const int co = ((2 * (kk) + hl) ^ sa) << 3;                                              \
+    bf16x8 af[FM], bfr[FN];                                                                  \
+    _Pragma("unroll") for (int fm = 0; fm < FM; ++fm) af[fm] = *(const bf16x8*)((Ab) + oa[fm] + co); \
+    _Pragma("unroll") for (int fn = 0; fn < FN; ++fn) bfr[fn] = *(const bf16x8*)((Bb) + ob[fn] + co); \
+    _Pragma("unroll") for (int fm = 0; fm < FM; ++fm)                                        \
+    _Pragma("unroll") for (int fn = 0; fn < FN; ++fn)                                        \
+      acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0); \
+  } while (0)
+
+#if GEMM_DIRECT_LDS
+  // Direct global -> LDS loads (buffer_load_dwordx4 ... lds): one instruction per wave writes
+  // 1 KB (8 rows of 64 bf16) of LDS at consecutive 16-byte slots, lane L filling slot L, so
+  // each lane fetches the global chunk that the swizzled layout places at its slot.  The buffer
+  // resource starts at the tile's first row and ends at the matrix's last row: rows past the
+  // end read as zero, and the K offset travels in the scalar soffset.
+  constexpr int NW = NT / 64;
+  constexpr int AI = BM / 8 / NW, BI = BN / 8 / NW;  // 1 KB instructions per wave per operand
+  static_assert(AI * NW * 8 == BM && BI * NW * 8 == BN, "direct-LDS tiling mismatch");
+  const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(A + (size_t)m0 * lda), (short)0, (int)min((size_t)(M - m0) * lda * 2, (size_t)0x7fffffff), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(Bseg + (size_t)nb0 * ldb), (short)0, (int)min((size_t)(nrows - nb0) * ldb * 2, (size_t)0x7fffffff), 0x00020000);
+  int va[AI], vb[BI];
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int r = (wid * AI + i) * 8 + (lane >> 3), c = (lane & 7) ^ swz8(r);
+    va[i] = (r * lda + c * 8) * 2;
+  }
+#pragma unroll
+  for (int i = 0; i < BI; ++i) {
+    const int r = (wid * BI + i) * 8 + (lane >> 3), c = (lane & 7) ^ swz8(r);
+    vb[i] = (r * ldb + c * 8) * 2;
+  }
+  typedef __attribute__((address_space(3))) void* lds_ptr_t;
+#define GEMM_ISSUE(buf, k0)                                                                   \
+  do {                                                                                       \
+    _Pragma("unroll") for (int i = 0; i < AI; ++i)                                           \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa,                                          \
+        (lds_ptr_t)(As + (buf) * BM * BK + (wid * AI + i) * 512), 16, va[i], (k0) * 2, 0, 0); \
+    _Pragma("unroll") for (int i = 0; i < BI; ++i)                                           \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb,                                          \
+        (lds_ptr_t)(Bs + (buf) * BN * BK + (wid * BI + i) * 512), 16, vb[i], (k0) * 2, 0, 0); \
+  } while (0)
+
+#if GEMM_DIRECT_LDS >= 2
+  // Software pipeline over 16-wide k-substeps with two fragment register sets: the reads for
+  // substep s+1 are issued before the MFMAs of substep s.  The barrier that retires a K step's
+  // buffer sits before that step's last 16 MFMAs, whose operands are already in registers, so
+  // the barrier wait, the next tile's global->LDS issue and the first reads of the next K step
+  // all overlap MFMA work.
+  bf16x8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+  auto rd = [&](const bf16* Ab, const bf16* Bb, int kk, bf16x8 (&fa)[FM], bf16x8 (&fb)[FN]) {
+    const int co = ((2 * kk + hl) ^ sa) << 3;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) fa[fm] = *(const bf16x8*)(Ab + oa[fm] + co);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) fb[fn] = *(const bf16x8*)(Bb + ob[fn] + co);
+  };
+  auto mm = [&](const bf16x8 (&fa)[FM], const bf16x8 (&fb)[FN]) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fm], fb[fn], acc[fm][fn], 0, 0, 0);
+  };
+  GEMM_ISSUE(0, 0);
+  if (nk > 1) {
+    GEMM_ISSUE(1, BK);
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(AI + BI));
+  } else {
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
+  }
+  __syncthreads();
+  // Each region holds the MFMAs of one substep and the reads of the next; sched_group_barrier
+  // interleaves them (2 MFMAs, 1 LDS read) so the LDS command queue never backs up into the
+  // in-order issue stream.  The post-barrier region also interleaves the 16 direct-to-LDS loads.
+#define PIN __builtin_amdgcn_sched_barrier(0)
+#if GEMM_MIX
+#define MIX_PIN
+#define MIX_MM_DS()                                                      \
+  do {                                                                   \
+    _Pragma("unroll") for (int q = 0; q < FM + FN; ++q) {                \
+      __builtin_amdgcn_sched_group_barrier(0x008, (FM * FN) / (FM + FN), 0); \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                 \
+    }                                                                    \
+  } while (0)
+#else
+#define MIX_PIN PIN
+#define MIX_MM_DS()
+#endif
+  rd(As, Bs, 0, fa0, fb0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    const bf16* Ab = As + buf * BM * BK;
+    const bf16* Bb = Bs + buf * BN * BK;
+    PIN; rd(Ab, Bb, 1, fa1, fb1); MIX_PIN; mm(fa0, fb0); MIX_MM_DS();
+    PIN; rd(Ab, Bb, 2, fa0, fb0); MIX_PIN; mm(fa1, fb1); MIX_MM_DS();
+    PIN; rd(Ab, Bb, 3, fa1, fb1); MIX_PIN; mm(fa0, fb0); MIX_MM_DS();
+    PIN;
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(0));  // own loads of tile kt+1 have landed
+    __syncthreads();                          // everyone's too; buffer `buf` fully read
+    PIN;
+#if GEMM_MIX
+    if (kt + 1 < nk) {
+      if (kt + 2 < nk) GEMM_ISSUE(buf, (kt + 2) * BK);
+      rd(As + (buf ^ 1) * BM * BK, Bs + (buf ^ 1) * BN * BK, 0, fa0, fb0);
+      mm(fa1, fb1);
+      if (kt + 2 < nk) {
+        _Pragma("unroll") for (int q = 0; q < AI + BI; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          if (q < FM + FN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      } else {
+        MIX_MM_DS();
+      }
+    } else {
+      mm(fa1, fb1);
+    }
+#else
+    if (kt + 2 < nk) GEMM_ISSUE(buf, (kt + 2) * BK);
+    if (kt + 1 < nk) rd(As + (buf ^ 1) * BM * BK, Bs + (buf ^ 1) * BN * BK, 0, fa0, fb0);
+    PIN; mm(fa1, fb1);
+#endif
+    PIN;
+    // The next substep-0 fragments were issued among those MFMAs; settling the LDS counter
+    // here keeps the waitcnt pass from waiting on fresh reads at the loop top.
+    __builtin_amdgcn_s_waitcnt(lgkmcnt_0);
+  }
+#undef MIX_MM_DS
+#undef MIX_PIN
+#undef PIN
+#else
+  GEMM_ISSUE(0, 0);
+  if (nk > 1) {
+    GEMM_ISSUE(1, BK);
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(AI + BI));  // tile 0 landed, tile 1 in flight
+  } else {
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
+  }
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    const bf16* Ab = As + buf * BM * BK;
+    const bf16* Bb = Bs + buf * BN * BK;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) GEMM_SUBSTEP(Ab, Bb, kk);
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(0));  // own loads of tile kt+1 have landed
+    __syncthreads();                     // ... and everyone's; buffer `buf` is free
+    if (kt + 2 < nk) GEMM_ISSUE(buf, (kt + 2) * BK);
+  }
+#endif
+#undef GEMM_ISSUE
+#else
   u32x4 ra[AC], rb[BC];
   const bf16* pa[AC];
   const bf16* pb[BC];
@@ -105,24 +305,6 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
     _Pragma("unroll") for (int i = 0; i < BC; ++i) *(u32x4*)(Bs + (buf) * BN * BK + lb[i]) = rb[i]; \
   } while (0)
 
-  // Fragment read offsets (elements) for k-substep 0; substep kk adds chunk 2*kk.
-  int oa[FM], ob[FN];
-  const int hl = lane >> 5, rl = lane & 31;
-#pragma unroll
-  for (int fm = 0; fm < FM; ++fm) oa[fm] = (wm * TM + fm * 32 + rl) * BK;
-#pragma unroll
-  for (int fn = 0; fn < FN; ++fn) ob[fn] = (wn * TN + fn * 32 + rl) * BK;
-  const int sa = swz8(rl);  // rows differ from rl by multiples of 32: same swizzle
-
-  f32x16 acc[FM][FN];
-#pragma unroll
-  for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.f;
-
-  const int nk = K / BK;
   GEMM_GLOAD(0);
   GEMM_SSTORE(0);
   if (nk > 1) GEMM_GLOAD(BK);
@@ -132,65 +314,70 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
     const int buf = kt & 1;
     const bf16* Ab = As + buf * BM * BK;
     const bf16* Bb = Bs + buf * BN * BK;
+    // First half of the K step, then stage tile kt+1 into the other buffer (free since the
+    // last barrier) and fetch tile kt+2, then the second half: the LDS writes and the global
+    // load issue overlap the MFMAs.
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int co = ((2 * kk + hl) ^ sa) << 3;
-      bf16x8 af[FM], bfr[FN];
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm) af[fm] = *(const bf16x8*)(Ab + oa[fm] + co);
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) bfr[fn] = *(const bf16x8*)(Bb + ob[fn] + co);
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
-    }
+    for (int kk = 0; kk < BK / 32; ++kk) GEMM_SUBSTEP(Ab, Bb, kk);
     if (kt + 1 < nk) GEMM_SSTORE(buf ^ 1);
     if (kt + 2 < nk) GEMM_GLOAD((kt + 2) * BK);
+#pragma unroll
+    for (int kk = BK / 32; kk < BK / 16; ++kk) GEMM_SUBSTEP(Ab, Bb, kk);
     __syncthreads();
   }
-
 #undef GEMM_GLOAD
 #undef GEMM_SSTORE
+#endif
+#undef GEMM_SUBSTEP
 
   // ---------------------------------------------------------------- epilogues
   // acc[fm][fn][r] is C[row][col] with row = m0 + wm*TM + fm*32 + 8*(r/4) + 4*hl + r%4 and
-  // col = n0 + wn*TN + fn*32 + rl.
+  // col = n0 + wn*TN + fn*32 + rl.  Interior tiles take a branch-free path so that all global
+  // accesses of a lane can be in flight together.
   const int rbase = m0 + wm * TM + 4 * hl;
   const int cbase = n0 + wn * TN + rl;
+  const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
 
   if constexpr (EPI == EPI_STORE || EPI == EPI_RELU2) {
     bf16* out = (bf16*)g.out;
+    auto store = [&](auto checked) {
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
+      for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const int col = cbase + fn * 32;
+        for (int fn = 0; fn < FN; ++fn) {
+          const int col = cbase + fn * 32;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = rbase + fm * 32 + 8 * (r >> 2) + (r & 3);
-          float v = acc[fm][fn][r];
-          if (EPI == EPI_RELU2) { v = fmaxf(v, 0.f); v = v * v; }
-          if (row < M && col < N) out[(size_t)row * g.ldo + col] = (bf16)v;
-        }
-      }
-  } else if constexpr (EPI == EPI_RESID) {
-    float* out = (float*)g.out;
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const int col = cbase + fn * 32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = rbase + fm * 32 + 8 * (r >> 2) + (r & 3);
-          if (row < M && col < N) {
-            float* p = out + (size_t)row * g.ldo + col;
-            *p = *p + acc[fm][fn][r];
+          for (int r = 0; r < 16; ++r) {
+            const int row = rbase + fm * 32 + 8 * (r >> 2) + (r & 3);
+            float v = acc[fm][fn][r];
+            if (EPI == EPI_RELU2) { v = fmaxf(v, 0.f); v = v * v; }
+            if (!decltype(checked)::value || (row < M && col < N)) out[(size_t)row * g.ldo + col] = (bf16)v;
           }
         }
-      }
+    };
+    if (interior) store(std::false_type{}); else store(std::true_type{});
+  } else if constexpr (EPI == EPI_RESID) {
+    float* out = (float*)g.out;
+    auto resid = [&](auto checked) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          const int col = cbase + fn * 32;
+          float prev[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = rbase + fm * 32 + 8 * (r >> 2) + (r & 3);
+            prev[r] = (!decltype(checked)::value || (row < M && col < N)) ? out[(size_t)row * g.ldo + col] : 0.f;
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = rbase + fm * 32 + 8 * (r >> 2) + (r & 3);
+            if (!decltype(checked)::value || (row < M && col < N)) out[(size_t)row * g.ldo + col] = prev[r] + acc[fm][fn][r];
+          }
+        }
+    };
+    if (interior) resid(std::false_type{}); else resid(std::true_type{});
   } else if constexpr (EPI == EPI_QKV) {
     bf16* qk = (bf16*)g.out;
     bf16* vt = (bf16*)g.vt;
@@ -262,6 +449,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
       }
     }
   }
+#endif
 }
 
 template <int BM, int BN, int WM, int WN>
@@ -273,7 +461,10 @@ hipError_t run_bf16(Epi epi, const GemmArgs& a, hipStream_t s) {
     case EPI_RELU2: gemm_bf16_kernel<BM, BN, WM, WN, EPI_RELU2><<<grid, NT, 0, s>>>(a); break;
     case EPI_RESID: gemm_bf16_kernel<BM, BN, WM, WN, EPI_RESID><<<grid, NT, 0, s>>>(a); break;
     case EPI_QKV: gemm_bf16_kernel<BM, BN, WM, WN, EPI_QKV><<<grid, NT, 0, s>>>(a); break;
-    case EPI_CE: gemm_bf16_kernel<BM, BN, WM, WN, EPI_CE><<<grid, NT, 0, s>>>(a); break;
+    case EPI_CE:
+      if constexpr (WN <= 2) gemm_bf16_kernel<BM, BN, WM, WN, EPI_CE><<<grid, NT, 0, s>>>(a);
+      else return hipErrorInvalidValue;  // the CE reduction buffer is sized for WN <= 2
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -383,7 +574,14 @@ hipError_t launch_gemm_bf16(Epi epi, const GemmArgs& a, hipStream_t s) {
   };
   const bool n256 = seg_ok(256), n128 = seg_ok(128);
   const long tiles256 = (long)((a.M + 255) / 256) * ((a.N + 255) / 256);
-  if (n256 && tiles256 >= 1024) return run_bf16<256, 256, 2, 2>(epi, a, s);
+  // Large GEMMs: 256x256 tiles, 8 wavefronts (2 per SIMD, 128x64 each) so one wavefront's
+  // LDS waits overlap the other's MFMAs.
+  if (n256 && tiles256 >= 1024) return run_bf16<256, 256, 2, 4>(epi, a, s);
+#if GEMM_N1536 == 1
+  if (n128) return run_bf16<256, 128, 4, 2>(epi, a, s);
+#elif GEMM_N1536 == 2
+  if (n256) return run_bf16<256, 256, 2, 4>(epi, a, s);
+#endif
   if (n128) return run_bf16<256, 128, 2, 2>(epi, a, s);
   return hipErrorInvalidValue;
 }
