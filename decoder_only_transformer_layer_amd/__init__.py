@@ -74,7 +74,7 @@ def _load() -> ctypes.CDLL:
         "gpt_op_rope_table": (I, [P, I, I, F, P]),
         "gpt_op_qk_rope_norm": (I, [I, P, I, P, I, I, I, I, F, P]),
         "gpt_op_linear": (I, [I, I, P, P, I, I, I, P, P]),
-        "gpt_op_qkv": (I, [P, P, P, P, I, I, I, I, I, I, P, P, P]),
+        "gpt_op_qkv": (I, [P, P, P, P, I, I, I, I, I, I, P, F, P, P, P]),
         "gpt_op_attention": (I, [I, P, P, P, I, I, I, I, I, I, F, P]),
         "gpt_op_lm_head_ce_workspace": (S, [I, I, I]),
         "gpt_op_lm_head_ce": (I, [I, P, P, P, P, I, I, I, F, P, P, P, P, S, P]),
@@ -192,9 +192,9 @@ def gpt_op_linear(dtype, epi, a, w, M, N, K, out, stream=None) -> int:
     return _load().gpt_op_linear(dtype, epi, _ptr(a), _ptr(w), M, N, K, _ptr(out), _stream(stream))
 
 
-def gpt_op_qkv(xn, wq, wk, wv, B, T, C, H, Hkv, D, qk, vt, stream=None) -> int:
-    return _load().gpt_op_qkv(_ptr(xn), _ptr(wq), _ptr(wk), _ptr(wv), B, T, C, H, Hkv, D, _ptr(qk),
-                              _ptr(vt), _stream(stream))
+def gpt_op_qkv(xn, wq, wk, wv, B, T, C, H, Hkv, D, cs, eps, qk, vt, stream=None) -> int:
+    return _load().gpt_op_qkv(_ptr(xn), _ptr(wq), _ptr(wk), _ptr(wv), B, T, C, H, Hkv, D, _ptr(cs), eps,
+                              _ptr(qk), _ptr(vt), _stream(stream))
 
 
 def gpt_op_attention(dtype, qk, vt, o, B, T, H, Hkv, D, window, scale, stream=None) -> int:

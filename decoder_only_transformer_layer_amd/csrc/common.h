@@ -38,6 +38,20 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Sum over each aligned group of 32 lanes, broadcast to the group: DPP butterflies within
+// 16-lane rows (xor 1, xor 2, half-row mirror, row mirror) then a swizzle across the two rows.
+template <int CTRL> __device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float sum32(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);  // row_half_mirror
+  v += dpp<0x140>(v);  // row_mirror
+  v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));  // lane ^ 16
+  return v;
+}
+
 // Fast 2^x and 1/x on the hardware transcendental unit.
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }

@@ -182,9 +182,12 @@ gpt_status gpt_fwd_loss(const gpt_cfg* c, const gpt_weights* w, const int32_t* t
     GemmArgs g = gemm_args(xn, C, w->wq[l], nqkv, C, M, qk, bf ? nqk : nqkv);
     g.B1 = w->wk[l]; g.B2 = w->wv[l]; g.nseg0 = H * D; g.nseg1 = Hkv * D;
     g.vt = vt; g.T = T; g.D = D; g.Hkv = Hkv; g.nqk = nqk;
+    // RoPE + QK-norm on the q and k heads: fused into the projection's epilogue for bf16 with
+    // head_dim 128, else a separate pass
+    const bool fused = bf && D == 128;
+    if (fused) { g.cs = cs; g.eps = eps; }
     CK(gemm(bf, bf ? EPI_QKV : EPI_STORE, g, s));
-    // RoPE + QK-norm on the q and k heads
-    CK(launch_qk_rope_norm(qk, bf, bf ? nqk : nqkv, cs, M, T, H + Hkv, D, eps, s));
+    if (!fused) CK(launch_qk_rope_norm(qk, bf, bf ? nqk : nqkv, cs, M, T, H + Hkv, D, eps, s));
     // windowed causal attention
     const int win = c->window[l] < T ? c->window[l] : T;
     if (bf) CK(launch_attn_bf16(qk, vt, o, B, T, H, Hkv, D, win, c->attn_scale, s));
@@ -276,15 +279,18 @@ gpt_status gpt_op_linear(int32_t dtype, int32_t epi, const void* a, const void* 
 }
 
 gpt_status gpt_op_qkv(const void* xn, const void* wq, const void* wk, const void* wv, int32_t B,
-                      int32_t T, int32_t C, int32_t H, int32_t Hkv, int32_t D, void* qk, void* vt,
-                      void* stream) {
-  if (!xn || !wq || !wk || !wv || !qk || !vt || B < 1 || T < 1 || C < 1 || H < 1 || Hkv < 1 || D < 1)
+                      int32_t T, int32_t C, int32_t H, int32_t Hkv, int32_t D, const float* cs,
+                      float eps, void* qk, void* vt, void* stream) {
+  if (!xn || !wq || !wk || !wv || !qk || !vt || B < 1 || T < 1 || C < 1 || H < 1 || Hkv < 1 || D < 1 ||
+      !(eps >= 0.f))
     return GPT_E_INVALID_ARG;
   if (C % 64 || T % 4 || (H * D) % 128 || (Hkv * D) % 128) return GPT_E_UNSUPPORTED;
+  if (cs && D != 128) return GPT_E_UNSUPPORTED;
   const int M = B * T, nqk = (H + Hkv) * D, nqkv = (H + 2 * Hkv) * D;
   GemmArgs g = gemm_args(xn, C, wq, nqkv, C, M, qk, nqk);
   g.B1 = wk; g.B2 = wv; g.nseg0 = H * D; g.nseg1 = Hkv * D;
   g.vt = vt; g.T = T; g.D = D; g.Hkv = Hkv; g.nqk = nqk;
+  g.cs = (const float2*)cs; g.eps = eps;
   CK(launch_gemm_bf16(EPI_QKV, g, (hipStream_t)stream));
   return GPT_OK;
 }

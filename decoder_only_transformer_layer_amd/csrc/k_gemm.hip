@@ -381,6 +381,54 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
   } else if constexpr (EPI == EPI_QKV) {
     bf16* qk = (bf16*)g.out;
     bf16* vt = (bf16*)g.vt;
+    const int wcol0 = n0 + wn * TN;  // q, k and v segments are multiples of TN columns
+    if constexpr (TN == 128) {
+      if (g.cs != nullptr && wcol0 < g.nqk && wcol0 < N) {
+        // This wavefront owns one whole 128-wide q or k head for its TM rows.  RoPE pairs
+        // (j, j+64) are tiles fn and fn+2 of the same lane; the head's sum of squares is the
+        // lane's two pairs plus a 32-lane butterfly (the 32 lanes of a half share a row).
+        // Rows go in chunks of 8 so the 16 table loads of a chunk are in flight together.
+        auto rope_norm = [&](auto checked) {
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+            for (int hc = 0; hc < 2; ++hc) {
+              float2 c[2][8];
+#pragma unroll
+              for (int q = 0; q < 8; ++q) {
+                const int r = 8 * hc + q;
+                const int row = rbase + fm * 32 + 8 * (r >> 2) + (r & 3);
+                const int t = row % g.T;
+#pragma unroll
+                for (int p = 0; p < 2; ++p) c[p][q] = g.cs[t * 64 + p * 32 + rl];
+              }
+#pragma unroll
+              for (int q = 0; q < 8; ++q) {
+                const int r = 8 * hc + q;
+                const int row = rbase + fm * 32 + 8 * (r >> 2) + (r & 3);
+                float ss = 0.f;
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                  const float u1 = acc[fm][p][r], u2 = acc[fm][p + 2][r];
+                  const float y1 = u1 * c[p][q].x + u2 * c[p][q].y, y2 = -u1 * c[p][q].y + u2 * c[p][q].x;
+                  acc[fm][p][r] = y1;
+                  acc[fm][p + 2][r] = y2;
+                  ss += y1 * y1 + y2 * y2;
+                }
+                const float sc = rsqrtf(sum32(ss) * (1.0f / 128.0f) + g.eps);
+                if (!decltype(checked)::value || row < M) {
+#pragma unroll
+                  for (int fn = 0; fn < 4; ++fn)
+                    qk[(size_t)row * g.ldo + wcol0 + fn * 32 + rl] = (bf16)(acc[fm][fn][r] * sc);
+                }
+              }
+            }
+          }
+        };
+        if (m0 + BM <= M) rope_norm(std::false_type{}); else rope_norm(std::true_type{});
+        return;
+      }
+    }
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
       const int col = cbase + fn * 32;
@@ -411,40 +459,55 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
       }
     }
   } else if constexpr (EPI == EPI_CE) {
-    // Per-row partial sums over this block's columns, reduced through LDS (free after the
-    // main loop's final barrier).
-    constexpr int RW = WN * 32 + 1;  // padded row stride of the reduction buffer
-    static_assert(BM * RW * 4 <= 2 * (BM + BN) * BK * 2, "reduction buffer exceeds LDS");
-    float* red = (float*)lds;
+    // Per row: sum over this block's columns of exp(zhat - cap).  Each lane sums its FN
+    // columns, a 32-lane butterfly sums a wavefront's TN columns, and the WN wavefronts that
+    // share a row combine through LDS (free after the main loop's final barrier).  Targets of
+    // the block's rows are staged in LDS so that the target-logit pick-up is a predicated store.
+    float* red = (float*)lds;                    // [BM][WN]
+    int* tgt = (int*)(lds) + BM * WN;            // [BM]
     const float cap = g.cap;
     const float k1 = 2.0f / cap * GPT_LOG2E, k2 = -2.0f * cap * GPT_LOG2E;
+    for (int i = tid; i < BM; i += NT) tgt[i] = (g.targets != nullptr && m0 + i < M) ? g.targets[m0 + i] : -1;
+    __syncthreads();
+    auto ce = [&](auto checked) {
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
+      for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rloc = wm * TM + fm * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-        const int row = m0 + rloc;
-        const int y = (g.targets != nullptr && row < M) ? g.targets[row] : -1;
-        float s = 0.f;
+        for (int r = 0; r < 16; ++r) {
+          const int rloc = wm * TM + fm * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          const int ycol = tgt[rloc] - cbase;    // target column relative to this lane's first
+          float s = 0.f;
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-          const int col = cbase + fn * 32;
-          const float z = acc[fm][fn][r];
-          if (col < N) {
-            s += ce_term(z, k1, k2);
-            // raw logits: the loss kernel and the logits pass apply the softcap
-            if (col == y) g.tgt_logit[row] = z;
-            if (g.logits != nullptr && row < M) g.logits[(size_t)row * N + col] = z;
+          for (int fn = 0; fn < FN; ++fn) {
+            const float z = acc[fm][fn][r];
+            const float e = ce_term(z, k1, k2);
+            s += (!decltype(checked)::value || cbase + fn * 32 < N) ? e : 0.f;
+            // raw logit; the loss kernel applies the softcap to it
+            if (ycol == fn * 32) g.tgt_logit[m0 + rloc] = z;
           }
+          s = sum32(s);
+          if (rl == 0) red[rloc * WN + wn] = s;
         }
-        red[rloc * RW + wn * 32 + rl] = s;
-      }
+    };
+    if (interior) ce(std::false_type{}); else ce(std::true_type{});
+    if (g.logits != nullptr) {  // raw logits (softcapped afterwards by the logits pass)
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = rbase + fm * 32 + 8 * (r >> 2) + (r & 3), col = cbase + fn * 32;
+            if (row < M && col < N) g.logits[(size_t)row * N + col] = acc[fm][fn][r];
+          }
+    }
     __syncthreads();
     for (int rloc = tid; rloc < BM; rloc += NT) {
       const int row = m0 + rloc;
       if (row < M) {
         float s = 0.f;
-        for (int j = 0; j < WN * 32; ++j) s += red[rloc * RW + j];
+#pragma unroll
+        for (int j = 0; j < WN; ++j) s += red[rloc * WN + j];
         g.partial[(size_t)row * g.nnb + bn] = s;
       }
     }
@@ -461,10 +524,7 @@ hipError_t run_bf16(Epi epi, const GemmArgs& a, hipStream_t s) {
     case EPI_RELU2: gemm_bf16_kernel<BM, BN, WM, WN, EPI_RELU2><<<grid, NT, 0, s>>>(a); break;
     case EPI_RESID: gemm_bf16_kernel<BM, BN, WM, WN, EPI_RESID><<<grid, NT, 0, s>>>(a); break;
     case EPI_QKV: gemm_bf16_kernel<BM, BN, WM, WN, EPI_QKV><<<grid, NT, 0, s>>>(a); break;
-    case EPI_CE:
-      if constexpr (WN <= 2) gemm_bf16_kernel<BM, BN, WM, WN, EPI_CE><<<grid, NT, 0, s>>>(a);
-      else return hipErrorInvalidValue;  // the CE reduction buffer is sized for WN <= 2
-      break;
+    case EPI_CE: gemm_bf16_kernel<BM, BN, WM, WN, EPI_CE><<<grid, NT, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -561,12 +621,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 
 }  // namespace
 
-int gemm_bf16_ce_blocks(int N) { return (N + 127) / 128; }
+int gemm_bf16_ce_blocks(int N) { return (N + 255) / 256; }
 int gemm_f32_ce_blocks(int N) { return (N + FT - 1) / FT; }
 
 hipError_t launch_gemm_bf16(Epi epi, const GemmArgs& a, hipStream_t s) {
   if (a.K % BK || a.M <= 0 || a.N <= 0) return hipErrorInvalidValue;
-  if (epi == EPI_CE) return run_bf16<256, 128, 2, 2>(epi, a, s);  // must match gemm_bf16_ce_blocks
+  if (epi == EPI_CE) return run_bf16<256, 256, 2, 4>(epi, a, s);  // must match gemm_bf16_ce_blocks
   // Interior column-segment boundaries must fall on block-column boundaries.
   auto seg_ok = [&](int bn) {
     const int e0 = a.nseg0, e1 = a.nseg0 + a.nseg1;
@@ -574,6 +634,13 @@ hipError_t launch_gemm_bf16(Epi epi, const GemmArgs& a, hipStream_t s) {
   };
   const bool n256 = seg_ok(256), n128 = seg_ok(128);
   const long tiles256 = (long)((a.M + 255) / 256) * ((a.N + 255) / 256);
+  if (epi == EPI_QKV && a.cs != nullptr) {
+    // fused RoPE + QK-norm: each wavefront must own whole 128-wide heads (4x2 / 4x1 layouts)
+    if (a.D != 128) return hipErrorInvalidValue;
+    if (n256) return run_bf16<256, 256, 4, 2>(epi, a, s);
+    if (n128) return run_bf16<256, 128, 4, 1>(epi, a, s);
+    return hipErrorInvalidValue;
+  }
   // Large GEMMs: 256x256 tiles, 8 wavefronts (2 per SIMD, 128x64 each) so one wavefront's
   // LDS waits overlap the other's MFMAs.
   if (n256 && tiles256 >= 1024) return run_bf16<256, 256, 2, 4>(epi, a, s);

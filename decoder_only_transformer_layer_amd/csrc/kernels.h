@@ -37,6 +37,8 @@ struct GemmArgs {
   int M, N, K;
   void* out; int ldo;                     // STORE/RELU2: act [M, ldo]; RESID: float [M, ldo] (+=); QKV: qk
   void* vt; int T, D, Hkv, nqk;           // QKV (bf16 only): columns >= nqk stored transposed to vt [B][Hkv][D][T]
+  const float2* cs;                       // QKV: if set (head_dim 128), RoPE table [T][D/2] -> the q/k
+  float eps;                              //      heads get RoPE + RMSNorm in the epilogue
   const int32_t* targets;                 // CE: [M] (or NULL)
   float* partial;                         // CE: [M][nnb] sums of exp(zhat - cap) per column block
   float* tgt_logit;                       // CE: [M] raw logit z at the target column

@@ -53,10 +53,13 @@ gpt_status gpt_op_linear(int32_t dtype, int32_t epi, const void *a, const void *
                          int32_t N, int32_t K, void *out, void *stream);
 
 /* QKV projection as the forward pass runs it (GPT_BF16 only): [q|k|v] = xn [wq;wk;wv]^T with
- * xn [B*T, C]; q and k go to qk [B*T, (H+Hkv)*D] row-major, v to vt [B, Hkv, D, T]. */
+ * xn [B*T, C]; q and k go to qk [B*T, (H+Hkv)*D] row-major, v to vt [B, Hkv, D, T].  If cs (a
+ * table from gpt_op_rope_table) is non-NULL, every q and k head is rotated and RMS-normalised
+ * (eps inside the root) in fp32 before rounding, exactly as gpt_op_qk_rope_norm would do to the
+ * unrounded projection; this fused form needs D == 128. */
 gpt_status gpt_op_qkv(const void *xn, const void *wq, const void *wk, const void *wv, int32_t B,
-                      int32_t T, int32_t C, int32_t H, int32_t Hkv, int32_t D, void *qk, void *vt,
-                      void *stream);
+                      int32_t T, int32_t C, int32_t H, int32_t Hkv, int32_t D, const float *cs,
+                      float eps, void *qk, void *vt, void *stream);
 
 /* Windowed causal attention ("Scaled Dot-Product Attention with Sliding Window") on already
  * rotated and normalised q, k.  GPT_BF16: q/k from qk [B*T, (H+Hkv)*D], v from vt

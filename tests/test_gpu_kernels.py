@@ -154,7 +154,7 @@ def test_rope_table():
     assert np.max(np.abs(got[..., 0] - c)) < 1e-7 and np.max(np.abs(got[..., 1] - s)) < 1e-7
 
 
-@pytest.mark.parametrize("H,Hkv,D", [(2, 2, 128), (4, 2, 128), (2, 2, 64)])
+@pytest.mark.parametrize("H,Hkv,D", [(2, 2, 128), (4, 2, 128), (2, 2, 64), (3, 1, 128)])
 def test_qkv_rope_norm_bf16(H, Hkv, D):
     torch = torch_mod()
     rng = np.random.default_rng(H * 10 + Hkv + D)
@@ -166,7 +166,7 @@ def test_qkv_rope_norm_bf16(H, Hkv, D):
     wv, wv64 = bf16_dev(rng.standard_normal((Hkv * D, C), dtype=np.float32) / np.float32(16))
     qk = empty((M, (H + Hkv) * D), "bf16")
     vt = empty((B, Hkv, D, T), "bf16")
-    _ok(gf.gpt_op_qkv(xn, wq, wk, wv, B, T, C, H, Hkv, D, qk, vt), "qkv")
+    _ok(gf.gpt_op_qkv(xn, wq, wk, wv, B, T, C, H, Hkv, D, None, eps, qk, vt), "qkv")
     cs = torch.empty((T, D // 2, 2), dtype=torch.float32).cuda()
     _ok(gf.gpt_op_rope_table(cs, T, D, 1e5), "rope table")
     _sync()
@@ -185,6 +185,18 @@ def test_qkv_rope_norm_bf16(H, Hkv, D):
         ref = oracle.rms_norm(oracle.apply_rope(u, c, s), eps)
         assert np.max(np.abs(got[b] - ref)) < 2e-2
         assert np.mean(np.abs(got[b] - ref)) < 2e-3
+    if D == 128:
+        # fused form: RoPE + norm on the fp32 projection inside the GEMM epilogue
+        qk2 = empty((M, (H + Hkv) * D), "bf16")
+        vt2 = empty((B, Hkv, D, T), "bf16")
+        _ok(gf.gpt_op_qkv(xn, wq, wk, wv, B, T, C, H, Hkv, D, cs, eps, qk2, vt2), "qkv fused")
+        _sync()
+        assert torch.equal(vt2, vt)
+        got2 = to_host(qk2).reshape(B, T, H + Hkv, D)
+        u64 = np.concatenate([oracle.linear(xn64, wq64), oracle.linear(xn64, wk64)], axis=1).reshape(B, T, H + Hkv, D)
+        for b in range(B):
+            ref = oracle.rms_norm(oracle.apply_rope(u64[b], c, s), eps)
+            _bf16_close(got2[b], ref, rel=2 ** -8, atol=2e-5)
 
 
 # ----------------------------------------------------------------------------- attention
