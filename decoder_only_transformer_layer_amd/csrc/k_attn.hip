@@ -23,7 +23,14 @@
 namespace gptk {
 namespace {
 
+#ifndef ATTN_V2
+#define ATTN_V2 1
+#endif
+
 constexpr int BQ = 128, BKV = 64;
+
+// s_waitcnt immediate: at most n vector-memory operations outstanding (gfx9 encoding).
+constexpr int vmcnt_le(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
 
 __device__ __forceinline__ int swap23(int k) {
   return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
@@ -199,6 +206,212 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16* __restric
   }
 }
 
+// Version 2: 256 queries per block, 8 wavefronts (two per SIMD, so one wavefront's softmax
+// VALU work overlaps the other's MFMAs), K and V^T tiles streamed global -> LDS with
+// buffer_load ... lds into a 3-stage ring, the logit scale folded into one FMA before exp2, and
+// lazy rescaling: a row's reference maximum moves only when a new logit exceeds it by more than
+// 2^8 (in log2 units).  Numerator and denominator share the reference, so the result is exact;
+// the bound keeps every probability <= 256.
+constexpr int NW2 = 8, BQ2 = NW2 * 32, STG = 3;
+
+template <int D>
+__global__ __launch_bounds__(NW2 * 64, 1) void attn_bf16_v2_kernel(const bf16* __restrict__ qk,
+                                                                  const bf16* __restrict__ vt,
+                                                                  bf16* __restrict__ o, int T, int H,
+                                                                  int Hkv, int window, float c) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int KCH = D / 8;            // 16-byte chunks per K row
+  constexpr int DT = D / 32;            // 32-row tiles of O^T
+  constexpr int KS = D / 16;            // k-steps of S^T
+  constexpr int KROWS = 64 / KCH;       // K rows per 1 KB DMA instruction
+  constexpr int KI = BKV * KCH / 64 / NW2, VI = D * 8 / 64 / NW2;  // DMA instructions per wave
+  static_assert(KI * NW2 * 64 == BKV * KCH && VI * NW2 * 64 == D * 8, "DMA tiling");
+  __shared__ __attribute__((aligned(16))) bf16 Ks[STG][BKV * D];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[STG][D * BKV];
+
+  const int nqt = (T + BQ2 - 1) / BQ2;
+  const int qt = nqt - 1 - (int)blockIdx.x;  // longest rows first
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int g = (h * Hkv) / H;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int hl = lane >> 5, rl = lane & 31;
+  const int ldqk = (H + Hkv) * D;
+  const int qb = qt * BQ2;
+  const int qw = qb + wid * 32;
+  const int myq = qw + rl;
+
+  bf16x8 qf[KS];
+  {
+    const bf16* qp = qk + (size_t)(b * T + min(myq, T - 1)) * ldqk + h * D + 8 * hl;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = *(const bf16x8*)(qp + 16 * s);
+  }
+
+  const int kmin = max(0, qb - window + 1);
+  const int kmax = min(T - 1, qb + BQ2 - 1);
+  const int t0 = kmin / BKV, t1 = kmax / BKV;
+
+  // DMA sources.  K: buffer over this sequence's rows of the qk matrix, soffset = tile start.
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(qk + (size_t)b * T * ldqk + (H + g) * D), (short)0, (int)min((size_t)T * ldqk * 2, (size_t)0x7fffffff), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(vt + (size_t)(b * Hkv + g) * D * T), (short)0, (int)min((size_t)D * T * 2, (size_t)0x7fffffff), 0x00020000);
+  int ko[KI], vo[VI];
+#pragma unroll
+  for (int i = 0; i < KI; ++i) {
+    const int pr = KROWS * (wid * KI + i) + lane / KCH, slot = lane % KCH;
+    ko[i] = (swap23(pr) * ldqk + ((slot ^ swzk<D>(pr)) << 3)) * 2;
+  }
+#pragma unroll
+  for (int i = 0; i < VI; ++i) {
+    const int d = 8 * (wid * VI + i) + (lane >> 3), slot = lane & 7;
+    vo[i] = (d * T + ((slot ^ swzv(d)) << 3)) * 2;
+  }
+  typedef __attribute__((address_space(3))) void* lds_ptr_t;
+  auto issue = [&](int t) {
+    const int st = (t - t0) % STG, j0 = t * BKV;
+#pragma unroll
+    for (int i = 0; i < KI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(&Ks[st][(wid * KI + i) * 512]), 16, ko[i], j0 * ldqk * 2, 0, 0);
+#pragma unroll
+    for (int i = 0; i < VI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(&Vs[st][(wid * VI + i) * 512]), 16, vo[i], j0 * 2, 0, 0);
+  };
+
+  f32x16 ot[DT];
+#pragma unroll
+  for (int d = 0; d < DT; ++d)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ot[d][r] = 0.f;
+  float m_ref = -1e30f, l_run = 0.f;  // reference max in log2 units (finite: keeps -inf logits at p = 0)
+
+  auto active_tile = [&](int t) {
+    const int j0 = t * BKV;
+    return (j0 <= qw + 31) && (j0 + BKV - 1 >= qw - window + 1) && (qw < T);
+  };
+  // S^T = K Q^T for one tile: sv[rt][r] is the raw logit of key
+  // j0 + rt*32 + 16*(r>>3) + 8*hl + 4*((r>>2)&1) + (r&3) for query myq.
+  auto scores = [&](int t, f32x16 (&sv)[2]) {
+    const int st = (t - t0) % STG;
+    const bf16* kp[2];
+    int sw[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const int kr = rt * 32 + rl;
+      kp[rt] = &Ks[st][kr * D];
+      sw[rt] = swzk<D>(kr);
+    }
+    // k-step outer, row tile inner: consecutive MFMAs never chain on one accumulator; the
+    // first k-step takes a zero accumulator (an inline constant, no register zeroing)
+    const f32x16 zero = {};
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2)
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const bf16x8 a = *(const bf16x8*)(kp[rt] + (((2 * s2 + hl) ^ sw[rt]) << 3));
+        sv[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s2], s2 == 0 ? zero : sv[rt], 0, 0, 0);
+      }
+  };
+
+  // Software pipeline: the logits of tile t+1 are issued to the matrix cores before the softmax
+  // of tile t runs on the VALU, then tile t's P V^T follows.  Ring stages hold tiles t, t+1 and
+  // t+2; the barrier at the top of iteration t publishes tile t+1 and retires tile t-1's stage.
+  f32x16 sA[2], sB[2];
+  issue(t0);
+  if (t0 + 1 <= t1) issue(t0 + 1);
+  if (t0 + 1 <= t1) __builtin_amdgcn_s_waitcnt(vmcnt_le(KI + VI));
+  else __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
+  __syncthreads();
+  bool act_cur = active_tile(t0);
+  if (act_cur) scores(t0, sA);
+  // One pipeline step: tile t's softmax and P V^T with tile t+1's logits issued first.  Called
+  // with the two logit register sets in alternating roles (loop unrolled by two: no copies).
+  auto step = [&](int t, f32x16 (&scur)[2], f32x16 (&snxt)[2]) {
+      const int st = (t - t0) % STG;
+      const int j0 = t * BKV;
+      const bool more = t + 1 <= t1;
+      if (more) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_le(0));  // own loads of tile t+1 landed
+        __syncthreads();                          // everyone's; stage of tile t-1 is free
+        if (t + 2 <= t1) issue(t + 2);
+      }
+      const bool act_nxt = more && active_tile(t + 1);
+      if (act_nxt) scores(t + 1, snxt);
+      if (act_cur) {
+        const bool full = (j0 + BKV - 1 <= qw) && (qw + 31 - j0 < window);
+        if (!full) {
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = j0 + rt * 32 + 16 * (r >> 3) + 8 * hl + 4 * ((r >> 2) & 1) + (r & 3);
+              if (key > myq || myq - key >= window) scur[rt][r] = -INFINITY;
+            }
+        }
+        float mt[16];  // tree reduction: depth 5 instead of a 32-long chain
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt[r] = fmaxf(scur[0][r], scur[1][r]);
+#pragma unroll
+        for (int w = 8; w > 0; w >>= 1)
+#pragma unroll
+          for (int r = 0; r < w; ++r) mt[r] = fmaxf(mt[r], mt[r + w]);
+        float mx = fmaxf(mt[0], __shfl_xor(mt[0], 32, 64)) * c;
+        const bool grow = mx > m_ref + 8.0f;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+          const float corr = grow ? exp2_fast(m_ref - mx) : 1.0f;
+          if (grow) m_ref = mx;
+          l_run *= corr;
+#pragma unroll
+          for (int d = 0; d < DT; ++d)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ot[d][r] *= corr;
+        }
+        const float nm = -m_ref;
+        bf16x8 pf[4];
+        float ps[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums instead of one chain
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = exp2_fast(fmaf(scur[rt][r], c, nm));
+            ps[r & 3] += p;
+            pf[rt * 2 + (r >> 3)][r & 7] = (bf16)p;
+          }
+        l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        // k-step outer, d tile inner: DT independent accumulators between dependent MFMAs
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+          for (int d = 0; d < DT; ++d) {
+            const int vr = d * 32 + rl;
+            const bf16x8 a = *(const bf16x8*)(&Vs[st][vr * BKV] + (((2 * s2 + hl) ^ swzv(vr)) << 3));
+            ot[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[s2], ot[d], 0, 0, 0);
+          }
+      }
+      act_cur = act_nxt;
+  };
+  for (int t = t0; t <= t1; t += 2) {
+    step(t, sA, sB);
+    if (t + 1 <= t1) step(t + 1, sB, sA);
+  }
+
+  const float l = l_run + __shfl_xor(l_run, 32, 64);
+  if (myq < T) {
+    const float inv = 1.0f / l;
+    bf16* op = o + (size_t)(b * T + myq) * (H * D) + h * D;
+#pragma unroll
+    for (int d = 0; d < DT; ++d)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x4 v4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v4[i] = (bf16)(ot[d][4 * j + i] * inv);
+        *(bf16x4*)(op + d * 32 + 8 * j + 4 * hl) = v4;
+      }
+  }
+#endif
+}
+
 // fp32 path: one thread per query, keys read from global memory.
 template <int D>
 __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ qkv, float* __restrict__ o,
@@ -240,14 +453,24 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
 hipError_t launch_attn_bf16(const void* qk, const void* vt, void* o, int B, int T, int H, int Hkv,
                             int D, int window, float scale, hipStream_t s) {
   if (T % BKV) return hipErrorInvalidValue;
-  const dim3 grid((T + BQ - 1) / BQ, H, B);
   const float sl2 = scale * GPT_LOG2E;
+#if ATTN_V2
+  const dim3 grid((T + BQ2 - 1) / BQ2, H, B);
+  if (D == 128)
+    attn_bf16_v2_kernel<128><<<grid, NW2 * 64, 0, s>>>((const bf16*)qk, (const bf16*)vt, (bf16*)o, T, H, Hkv, window, sl2);
+  else if (D == 64)
+    attn_bf16_v2_kernel<64><<<grid, NW2 * 64, 0, s>>>((const bf16*)qk, (const bf16*)vt, (bf16*)o, T, H, Hkv, window, sl2);
+  else
+    return hipErrorInvalidValue;
+#else
+  const dim3 grid((T + BQ - 1) / BQ, H, B);
   if (D == 128)
     attn_bf16_kernel<128><<<grid, 256, 0, s>>>((const bf16*)qk, (const bf16*)vt, (bf16*)o, T, H, Hkv, window, sl2);
   else if (D == 64)
     attn_bf16_kernel<64><<<grid, 256, 0, s>>>((const bf16*)qk, (const bf16*)vt, (bf16*)o, T, H, Hkv, window, sl2);
   else
     return hipErrorInvalidValue;
+#endif
   return hipGetLastError();
 }
 
