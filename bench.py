@@ -39,16 +39,35 @@ def flops_per_token(p, windows):
     return p.n_layer * lin + 2 * C * V + att
 
 
+def measured_traffic(root):
+    """HBM bytes per launch of the MLP up-projection GEMM from the committed rocprofv3 PMC
+    record (profiles/gemm_mlp_up_traffic.json), or None if the GEMM source has changed since
+    the counters were taken (the record stores the source hash)."""
+    import hashlib
+    path = os.path.join(root, "profiles", "gemm_mlp_up_traffic.json")
+    try:
+        rec = json.load(open(path))
+        csrc = os.path.join(root, "decoder_only_transformer_layer_amd", "csrc")
+        h = hashlib.sha256(open(os.path.join(csrc, "k_gemm.hip"), "rb").read()
+                           + open(os.path.join(csrc, "common.h"), "rb").read()).hexdigest()
+        return rec["hbm_bytes_per_dispatch"] if h == rec["kernel_source_sha256"] else None
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="d24")
-    ap.add_argument("--cpu-tokens", type=int, default=384,
+    ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens of row 0 the CPU oracle evaluates (a causal prefix)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=10)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 1 GiB device-to-device copy (a known-size reference "
+                         "for HBM traffic counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -61,6 +80,15 @@ def main():
 
     import decoder_only_transformer_layer_amd as gf
     import gptdata
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)  # reads and writes exactly 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
+        print("[bench] copy calibration: 1 GiB read + 1 GiB written", file=sys.stderr, flush=True)
 
     p = gptdata.preset(args.config)
     t0 = time.time()
@@ -163,7 +191,7 @@ def main():
                    "flops_per_token": round(fpt), "windows": "SSSL short 1024, last layer full"},
         "roofline": {"bound": "mfma", "kernel": "gemm_bf16 MLP up-projection (relu^2 epilogue)",
                      "achieved": round(k_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(k_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(k_tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(ROOT),
                      "avg_launch_us": round(k_ms * 1e3, 2), "flops_per_launch": k_flops},
         "cpu_baseline": cpu,
     }
