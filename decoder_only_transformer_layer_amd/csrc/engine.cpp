@@ -21,7 +21,7 @@ inline size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 struct Layout {
-  size_t flags, x, x0, xn, qk, vt, o, h, cs, partial, tgt, total;
+  size_t flags, x, x0, xn, qk, vt, o, h, cs, ssp, partial, tgt, total;
   int nnb;
 };
 
@@ -74,6 +74,7 @@ Layout plan(const gpt_cfg* c) {
   L.o = off; off += up(M * H * D * es);
   L.h = off; off += up(M * F * es);
   L.cs = off; off += up((size_t)c->seq_len * (D / 2) * 8);
+  L.ssp = off; off += up(M * (size_t)(C / 64) * 4);
   L.partial = off; off += up(M * (size_t)L.nnb * 4);
   L.tgt = off; off += up(M * 4);
   L.total = off;
@@ -98,12 +99,16 @@ hipError_t gemm(bool bf, Epi e, const GemmArgs& g, hipStream_t s) {
   return bf ? launch_gemm_bf16(e, g, s) : launch_gemm_f32(e, g, s);
 }
 
-// lm_head + softcap + CE over M rows into loss/mean (targets may be NULL: logits only).
+// lm_head + softcap + CE over M rows into loss/mean (targets may be NULL: logits only).  If
+// rs_ssp is set, xf is the un-normalised stream and the GEMM applies the final RMSNorm as a row
+// scale from those per-slice sums of squares.
 gpt_status lm_head_ce(bool bf, const void* xf, const void* wu, const int32_t* targets,
                       const int32_t* tokens, int M, int C, int V, float cap, float* loss,
                       float* mean, float* logits, float* partial, float* tgt, int nnb,
-                      unsigned* flags, hipStream_t s) {
+                      unsigned* flags, hipStream_t s, const float* rs_ssp = nullptr,
+                      float eps = 0.f) {
   GemmArgs g = gemm_args(xf, C, wu, V, C, M, nullptr, 0);
+  if (rs_ssp) { g.rs_ssp = rs_ssp; g.rs_n = C / 64; g.rs_c = (float)C; g.eps = eps; }
   g.targets = targets; g.partial = partial; g.tgt_logit = tgt; g.logits = logits;
   g.nnb = nnb; g.cap = cap;
   CK(gemm(bf, EPI_CE, g, s));
@@ -177,30 +182,60 @@ gpt_status gpt_fwd_loss(const gpt_cfg* c, const gpt_weights* w, const int32_t* t
                        flags, s));
   const int nqk = (H + Hkv) * D;
   const int nqkv = (H + 2 * Hkv) * D;
+  float* ssp = (float*)(ws + L.ssp);
+  const int nsl = C / 64;
+  if (bf) {
+    // bf16 path: every RMSNorm after the first is applied as a row scale inside the GEMM that
+    // consumes it (RMSNorm(x) W^T = (x W^T) / rms(x)).  The residual epilogues keep x in fp32,
+    // apply the next layer's x0 mix, and emit bf16(x) plus per-64-column sums of squares.
+    bf16_t* xb = (bf16_t*)xn;
+    for (int l = 0; l < c->n_layer; ++l) {
+      GemmArgs g = gemm_args(xn, C, w->wq[l], nqkv, C, M, qk, nqk);
+      g.B1 = w->wk[l]; g.B2 = w->wv[l]; g.nseg0 = H * D; g.nseg1 = Hkv * D;
+      g.vt = vt; g.T = T; g.D = D; g.Hkv = Hkv; g.nqk = nqk; g.eps = eps;
+      const bool fused = D == 128;
+      if (fused) g.cs = cs;
+      if (l > 0) { g.rs_ssp = ssp; g.rs_n = nsl; g.rs_c = (float)C; }  // layer 0 reads normed xn
+      CK(launch_gemm_bf16(EPI_QKV, g, s));
+      if (!fused) CK(launch_qk_rope_norm(qk, true, nqk, cs, M, T, H + Hkv, D, eps, s));
+      const int win = c->window[l] < T ? c->window[l] : T;
+      CK(launch_attn_bf16(qk, vt, o, B, T, H, Hkv, D, win, c->attn_scale, s));
+      // x += o W_O^T, then bf16(x) and sums of squares for the MLP's norm
+      GemmArgs go = gemm_args(o, H * D, w->wo[l], C, H * D, M, x, C);
+      go.xb = xb; go.ssp = ssp; go.ssp_n = nsl;
+      CK(launch_gemm_bf16(EPI_RESID, go, s));
+      // h = relu(RMSNorm(x) W_1^T)^2
+      GemmArgs gu = gemm_args(xb, C, w->w1[l], F, C, M, hbuf, F);
+      gu.rs_ssp = ssp; gu.rs_n = nsl; gu.rs_c = (float)C; gu.eps = eps;
+      CK(launch_gemm_bf16(EPI_RELU2, gu, s));
+      // x += h W_2^T, then the next layer's x0 mix (if any), bf16(x) and sums of squares
+      GemmArgs gd = gemm_args(hbuf, F, w->w2[l], C, F, M, x, C);
+      gd.xb = xb; gd.ssp = ssp; gd.ssp_n = nsl;
+      if (l + 1 < c->n_layer) { gd.x0 = x0; gd.lam = w->resid_lambda; gd.mu = w->x0_lambda; gd.layer = l + 1; }
+      CK(launch_gemm_bf16(EPI_RESID, gd, s));
+    }
+    return lm_head_ce(bf, xb, w->lm_head, targets, tokens, M, C, V, c->softcap, loss, mean_loss,
+                      logits, partial, tgt, L.nnb, flags, s, ssp, eps);
+  }
   for (int l = 0; l < c->n_layer; ++l) {
     // q, k, v projections (one GEMM over the three weight segments)
-    GemmArgs g = gemm_args(xn, C, w->wq[l], nqkv, C, M, qk, bf ? nqk : nqkv);
+    GemmArgs g = gemm_args(xn, C, w->wq[l], nqkv, C, M, qk, nqkv);
     g.B1 = w->wk[l]; g.B2 = w->wv[l]; g.nseg0 = H * D; g.nseg1 = Hkv * D;
-    g.vt = vt; g.T = T; g.D = D; g.Hkv = Hkv; g.nqk = nqk;
-    // RoPE + QK-norm on the q and k heads: fused into the projection's epilogue for bf16 with
-    // head_dim 128, else a separate pass
-    const bool fused = bf && D == 128;
-    if (fused) { g.cs = cs; g.eps = eps; }
-    CK(gemm(bf, bf ? EPI_QKV : EPI_STORE, g, s));
-    if (!fused) CK(launch_qk_rope_norm(qk, bf, bf ? nqk : nqkv, cs, M, T, H + Hkv, D, eps, s));
+    CK(launch_gemm_f32(EPI_STORE, g, s));
+    // RoPE + QK-norm on the q and k heads
+    CK(launch_qk_rope_norm(qk, false, nqkv, cs, M, T, H + Hkv, D, eps, s));
     // windowed causal attention
     const int win = c->window[l] < T ? c->window[l] : T;
-    if (bf) CK(launch_attn_bf16(qk, vt, o, B, T, H, Hkv, D, win, c->attn_scale, s));
-    else CK(launch_attn_f32((const float*)qk, (float*)o, B, T, H, Hkv, D, win, c->attn_scale, s));
+    CK(launch_attn_f32((const float*)qk, (float*)o, B, T, H, Hkv, D, win, c->attn_scale, s));
     // x += o W_O^T
-    CK(gemm(bf, EPI_RESID, gemm_args(o, H * D, w->wo[l], C, H * D, M, x, C), s));
+    CK(launch_gemm_f32(EPI_RESID, gemm_args(o, H * D, w->wo[l], C, H * D, M, x, C), s));
     // MLP: x += relu(RMSNorm(x) W_1^T)^2 W_2^T
-    CK(launch_mix_norm(x, x0, w->resid_lambda, w->x0_lambda, l, false, xn, bf, M, C, eps, s));
-    CK(gemm(bf, EPI_RELU2, gemm_args(xn, C, w->w1[l], F, C, M, hbuf, F), s));
-    CK(gemm(bf, EPI_RESID, gemm_args(hbuf, F, w->w2[l], C, F, M, x, C), s));
+    CK(launch_mix_norm(x, x0, w->resid_lambda, w->x0_lambda, l, false, xn, false, M, C, eps, s));
+    CK(launch_gemm_f32(EPI_RELU2, gemm_args(xn, C, w->w1[l], F, C, M, hbuf, F), s));
+    CK(launch_gemm_f32(EPI_RESID, gemm_args(hbuf, F, w->w2[l], C, F, M, x, C), s));
     // next layer's x0 mix and pre-attention norm, or the final norm
     const bool more = l + 1 < c->n_layer;
-    CK(launch_mix_norm(x, x0, w->resid_lambda, w->x0_lambda, l + 1, more, xn, bf, M, C, eps, s));
+    CK(launch_mix_norm(x, x0, w->resid_lambda, w->x0_lambda, l + 1, more, xn, false, M, C, eps, s));
   }
   return lm_head_ce(bf, xn, w->lm_head, targets, tokens, M, C, V, c->softcap, loss, mean_loss,
                     logits, partial, tgt, L.nnb, flags, s);

@@ -27,11 +27,11 @@
 namespace gptk {
 namespace {
 
+#ifndef GEMM_SPLIT
+#define GEMM_SPLIT 1
+#endif
 #ifndef GEMM_MIX
 #define GEMM_MIX 0
-#endif
-#ifndef GEMM_N1536
-#define GEMM_N1536 2
 #endif
 #ifndef GEMM_DIRECT_LDS
 #define GEMM_DIRECT_LDS 2
@@ -338,6 +338,38 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
   const int cbase = n0 + wn * TN + rl;
   const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
 
+  if constexpr (EPI != EPI_RESID) {
+    if (g.rs_ssp != nullptr) {
+      // A was not normalised: scale each output row by 1/rms of its A row, from the producer's
+      // per-slice sums of squares (summed here in a fixed order).
+      float* rinv = (float*)lds + BM * (WN + 2);
+      __syncthreads();  // every wavefront is done with the operand tiles
+      // slices are stored slice-major ([slice][M]): consecutive threads read consecutive rows
+      for (int i = tid; i < BM; i += NT) {
+        const int row = m0 + i;
+        float s4[4] = {0.f, 0.f, 0.f, 0.f};
+        if (row < M) {
+          int j = 0;
+          for (; j + 4 <= g.rs_n; j += 4) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) s4[u] += g.rs_ssp[(size_t)(j + u) * M + row];
+          }
+          for (; j < g.rs_n; ++j) s4[0] += g.rs_ssp[(size_t)j * M + row];
+        }
+        rinv[i] = rsqrtf(((s4[0] + s4[1]) + (s4[2] + s4[3])) / g.rs_c + g.eps);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float sc = rinv[wm * TM + fm * 32 + 8 * (r >> 2) + 4 * hl + (r & 3)];
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) acc[fm][fn][r] *= sc;
+        }
+    }
+  }
+
   if constexpr (EPI == EPI_STORE || EPI == EPI_RELU2) {
     bf16* out = (bf16*)g.out;
     auto store = [&](auto checked) {
@@ -358,6 +390,60 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
     if (interior) store(std::false_type{}); else store(std::true_type{});
   } else if constexpr (EPI == EPI_RESID) {
     float* out = (float*)g.out;
+    if constexpr (TN == 64) {  // the producer writes one sum-of-squares slice per 64 columns
+    if (g.xb != nullptr) {
+      // x += acc; optional next-layer mix x = lam x + mu x0; store x and bf16(x); per-row sum of
+      // squares of this wavefront's 64 columns (32-lane butterfly) for the next norm.
+      const bool mix = g.lam != nullptr;
+      const float lam = mix ? g.lam[g.layer] : 1.f, mu = mix ? g.mu[g.layer] : 0.f;
+      const int slice = (g.col_off + n0 + wn * TN) / 64;
+      const bool slice_live = n0 + wn * TN < N;
+      auto produce = [&](auto checked) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+          for (int rh = 0; rh < 2; ++rh) {  // 8 rows at a time keeps the staging registers small
+            float ss[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) ss[q] = 0.f;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+              const int col = cbase + fn * 32;
+              float prev[8], x0v[8];
+#pragma unroll
+              for (int q = 0; q < 8; ++q) {
+                const int r = 8 * rh + q;
+                const int row = rbase + fm * 32 + 8 * (r >> 2) + (r & 3);
+                const bool ok = !decltype(checked)::value || (row < M && col < N);
+                prev[q] = ok ? out[(size_t)row * g.ldo + col] : 0.f;
+                x0v[q] = (ok && mix) ? g.x0[(size_t)row * g.ldo + col] : 0.f;
+              }
+#pragma unroll
+              for (int q = 0; q < 8; ++q) {
+                const int r = 8 * rh + q;
+                const int row = rbase + fm * 32 + 8 * (r >> 2) + (r & 3);
+                float v = prev[q] + acc[fm][fn][r];
+                if (mix) v = lam * v + mu * x0v[q];
+                if (!decltype(checked)::value || (row < M && col < N)) {
+                  out[(size_t)row * g.ldo + col] = v;
+                  g.xb[(size_t)row * g.ldo + col] = (bf16)v;
+                  ss[q] += v * v;
+                }
+              }
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              const int r = 8 * rh + q;
+              const float t = sum32(ss[q]);
+              const int row = rbase + fm * 32 + 8 * (r >> 2) + (r & 3);
+              if (rl == 0 && slice_live && row < M) g.ssp[(size_t)slice * M + row] = t;
+            }
+          }
+      };
+      if (interior) produce(std::false_type{}); else produce(std::true_type{});
+      return;
+    }
+    }
     auto resid = [&](auto checked) {
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
@@ -624,33 +710,101 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 int gemm_bf16_ce_blocks(int N) { return (N + 255) / 256; }
 int gemm_f32_ce_blocks(int N) { return (N + FT - 1) / FT; }
 
+namespace {
+
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cached[dev] = v;
+  }
+  return cached[dev];
+}
+
+int gcd(int x, int y) { while (y) { const int t = x % y; x = y; y = t; } return x; }
+
+// Columns [c0, N) of a GEMM as a GEMM of its own: the B row segments, the output pointer and
+// the QKV column bookkeeping all shift by c0 (a multiple of 256).
+GemmArgs shift_cols(const GemmArgs& a, Epi epi, int c0) {
+  GemmArgs b = a;
+  const void* seg[3] = {a.B0, a.B1, a.B2};
+  const int start[3] = {0, a.nseg0, a.nseg0 + a.nseg1};
+  const int len[3] = {a.nseg0, a.nseg1, a.N - a.nseg0 - a.nseg1};
+  const void* nb[3] = {nullptr, nullptr, nullptr};
+  int nl[3] = {0, 0, 0}, k = 0;
+  for (int i = 0; i < 3; ++i) {
+    const int s0 = start[i], s1 = start[i] + len[i];
+    if (len[i] <= 0 || s1 <= c0) continue;
+    const int off = c0 > s0 ? c0 - s0 : 0;
+    nb[k] = (const bf16*)seg[i] + (size_t)off * a.ldb;
+    nl[k] = s1 - (c0 > s0 ? c0 : s0);
+    ++k;
+  }
+  b.N = a.N - c0;
+  b.B0 = nb[0];
+  b.B1 = k > 1 ? nb[1] : nb[0];
+  b.B2 = k > 2 ? nb[2] : b.B1;
+  b.nseg0 = nl[0];
+  b.nseg1 = k > 1 ? nl[1] : 0;
+  if (epi == EPI_RESID) {
+    b.out = (float*)a.out + c0;
+    if (a.xb) b.xb = a.xb + c0;
+    if (a.x0) b.x0 = a.x0 + c0;
+    b.col_off = a.col_off + c0;
+  } else {
+    b.out = (bf16*)a.out + c0;
+  }
+  if (epi == EPI_QKV) b.nqk = a.nqk - c0;
+  return b;
+}
+
+hipError_t run_main(Epi epi, const GemmArgs& a, hipStream_t s) {
+  if (epi == EPI_QKV && a.cs != nullptr) return run_bf16<256, 256, 4, 2>(epi, a, s);
+  return run_bf16<256, 256, 2, 4>(epi, a, s);
+}
+
+hipError_t run_narrow(Epi epi, const GemmArgs& a, hipStream_t s) {
+  if (epi == EPI_QKV && a.cs != nullptr) return run_bf16<256, 128, 4, 1>(epi, a, s);
+  return run_bf16<256, 128, 2, 2>(epi, a, s);
+}
+
+}  // namespace
+
 hipError_t launch_gemm_bf16(Epi epi, const GemmArgs& a, hipStream_t s) {
   if (a.K % BK || a.M <= 0 || a.N <= 0) return hipErrorInvalidValue;
   if (epi == EPI_CE) return run_bf16<256, 256, 2, 4>(epi, a, s);  // must match gemm_bf16_ce_blocks
+  if (epi == EPI_QKV && a.cs != nullptr && a.D != 128) return hipErrorInvalidValue;
   // Interior column-segment boundaries must fall on block-column boundaries.
   auto seg_ok = [&](int bn) {
     const int e0 = a.nseg0, e1 = a.nseg0 + a.nseg1;
     return (e0 >= a.N || e0 % bn == 0) && (e1 >= a.N || e1 % bn == 0);
   };
   const bool n256 = seg_ok(256), n128 = seg_ok(128);
-  const long tiles256 = (long)((a.M + 255) / 256) * ((a.N + 255) / 256);
-  if (epi == EPI_QKV && a.cs != nullptr) {
-    // fused RoPE + QK-norm: each wavefront must own whole 128-wide heads (4x2 / 4x1 layouts)
-    if (a.D != 128) return hipErrorInvalidValue;
-    if (n256) return run_bf16<256, 256, 4, 2>(epi, a, s);
-    if (n128) return run_bf16<256, 128, 4, 1>(epi, a, s);
-    return hipErrorInvalidValue;
+  if (!n256) return n128 ? run_narrow(epi, a, s) : hipErrorInvalidValue;
+  // 256x256 tiles, 8 wavefronts (2 per SIMD) so one wavefront's LDS waits overlap the other's
+  // MFMAs.  When the tile count leaves a partial last round on the CUs (e.g. 64 x 6 tiles on
+  // 256 CUs), the columns are split: a leading part whose 256x256 tiles fill whole rounds, and
+  // a tail launched with 256x128 tiles, so the partial round costs half a tile per CU.
+  const int ncu = cu_count();
+  const int nbm = (a.M + 255) / 256, nbn = (a.N + 255) / 256;
+  const long tiles = (long)nbm * nbn;
+  if (GEMM_SPLIT && tiles > ncu && tiles % ncu != 0 && a.N % 256 == 0) {
+    const int per = ncu / gcd(nbm, ncu);  // column blocks per whole number of rounds
+    const int c1 = (nbn / per) * per;
+    if (c1 > 0 && c1 < nbn) {
+      GemmArgs head = a;
+      head.N = c1 * 256;
+      if (head.nseg0 > head.N) head.nseg0 = head.N;
+      if (head.nseg0 + head.nseg1 > head.N) head.nseg1 = head.N - head.nseg0;
+      hipError_t e = run_main(epi, head, s);
+      if (e != hipSuccess) return e;
+      return run_narrow(epi, shift_cols(a, epi, c1 * 256), s);
+    }
   }
-  // Large GEMMs: 256x256 tiles, 8 wavefronts (2 per SIMD, 128x64 each) so one wavefront's
-  // LDS waits overlap the other's MFMAs.
-  if (n256 && tiles256 >= 1024) return run_bf16<256, 256, 2, 4>(epi, a, s);
-#if GEMM_N1536 == 1
-  if (n128) return run_bf16<256, 128, 4, 2>(epi, a, s);
-#elif GEMM_N1536 == 2
-  if (n256) return run_bf16<256, 256, 2, 4>(epi, a, s);
-#endif
-  if (n128) return run_bf16<256, 128, 2, 2>(epi, a, s);
-  return hipErrorInvalidValue;
+  return run_main(epi, a, s);
 }
 
 hipError_t launch_gemm_f32(Epi epi, const GemmArgs& a, hipStream_t s) {

@@ -7,6 +7,8 @@
 
 namespace gptk {
 
+typedef __bf16 bf16_t;
+
 // ---- row kernels (k_rows.hip) ------------------------------------------------------------
 // cos/sin table cs[t * (D/2) + j] = (cos phi, sin phi), phi = t * base^(-2j/D), in fp64 then fp32.
 hipError_t launch_rope_table(float2* cs, int T, int D, float base, hipStream_t s);
@@ -39,6 +41,16 @@ struct GemmArgs {
   void* vt; int T, D, Hkv, nqk;           // QKV (bf16 only): columns >= nqk stored transposed to vt [B][Hkv][D][T]
   const float2* cs;                       // QKV: if set (head_dim 128), RoPE table [T][D/2] -> the q/k
   float eps;                              //      heads get RoPE + RMSNorm in the epilogue
+  // Row scale (consumers of an un-normalised A, bf16 path): if rs_ssp is set, every output row
+  // is multiplied by rsqrt(sum_j rs_ssp[j][row] / rs_c + eps) before the epilogue's own work,
+  // i.e. the GEMM computes RMSNorm(A) W^T from A and its row sums of squares.
+  const float* rs_ssp; int rs_n; float rs_c;
+  // Residual producer (EPI_RESID, bf16 path): if xb is set, after x += acc the epilogue
+  // optionally mixes x = lam[layer] x + mu[layer] x0 (when lam != NULL), stores x, a bf16 copy
+  // of x to xb [M, ldo], and per-row sums of squares over each 64-column slice to
+  // ssp[(col_off + col) / 64][row] (slice-major, M rows per slice).
+  bf16_t* xb; const float* x0; const float* lam; const float* mu; int layer;
+  float* ssp; int ssp_n; int col_off;
   const int32_t* targets;                 // CE: [M] (or NULL)
   float* partial;                         // CE: [M][nnb] sums of exp(zhat - cap) per column block
   float* tgt_logit;                       // CE: [M] raw logit z at the target column

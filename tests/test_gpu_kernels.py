@@ -36,7 +36,8 @@ def _bf16_close(got, ref, rel=2 ** -8, atol=1e-5):
 
 # ----------------------------------------------------------------------------- GEMM
 
-@pytest.mark.parametrize("M,N,K", [(300, 384, 192), (512, 1000, 128), (8192, 8192, 64), (64, 128, 6144)])
+@pytest.mark.parametrize("M,N,K", [(300, 384, 192), (512, 1000, 128), (8192, 8192, 64), (64, 128, 6144),
+                                   (16384, 1536, 64)])  # last: 1.5 rounds of 256x256 tiles -> column split
 @pytest.mark.parametrize("epi", [0, 1, 2])
 def test_linear_bf16(M, N, K, epi):
     rng = np.random.default_rng(100 + M + N + K + epi)
@@ -154,11 +155,14 @@ def test_rope_table():
     assert np.max(np.abs(got[..., 0] - c)) < 1e-7 and np.max(np.abs(got[..., 1] - s)) < 1e-7
 
 
-@pytest.mark.parametrize("H,Hkv,D", [(2, 2, 128), (4, 2, 128), (2, 2, 64), (3, 1, 128)])
-def test_qkv_rope_norm_bf16(H, Hkv, D):
+@pytest.mark.parametrize("H,Hkv,D,B,T", [(2, 2, 128, 2, 192), (4, 2, 128, 2, 192), (2, 2, 64, 2, 192),
+                                         (3, 1, 128, 2, 192), (12, 12, 128, 8, 2048)])
+def test_qkv_rope_norm_bf16(H, Hkv, D, B, T):
+    """Last case: the d24 projection shape (N = 4608 columns over 64 row blocks = 4.5 rounds of
+    256x256 tiles), which splits into a 256x256 part and a 256x128 tail."""
     torch = torch_mod()
     rng = np.random.default_rng(H * 10 + Hkv + D)
-    B, T, C, eps = 2, 192, 256, 1e-6
+    C, eps = 256, 1e-6
     M = B * T
     xn, xn64 = bf16_dev(oracle.rms_norm(rng.standard_normal((M, C)), 0).astype(np.float32))
     wq, wq64 = bf16_dev(rng.standard_normal((H * D, C), dtype=np.float32) / np.float32(16))
