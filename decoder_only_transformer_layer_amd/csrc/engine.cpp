@@ -74,7 +74,7 @@ Layout plan(const gpt_cfg* c) {
   L.o = off; off += up(M * H * D * es);
   L.h = off; off += up(M * F * es);
   L.cs = off; off += up((size_t)c->seq_len * (D / 2) * 8);
-  L.ssp = off; off += up(M * (size_t)(C / 64) * 4);
+  L.ssp = off; off += up(M * (size_t)(C / 64) * 4);  // slices are >= 64 columns wide
   L.partial = off; off += up(M * (size_t)L.nnb * 4);
   L.tgt = off; off += up(M * 4);
   L.total = off;
@@ -108,7 +108,7 @@ gpt_status lm_head_ce(bool bf, const void* xf, const void* wu, const int32_t* ta
                       unsigned* flags, hipStream_t s, const float* rs_ssp = nullptr,
                       float eps = 0.f) {
   GemmArgs g = gemm_args(xf, C, wu, V, C, M, nullptr, 0);
-  if (rs_ssp) { g.rs_ssp = rs_ssp; g.rs_n = C / 64; g.rs_c = (float)C; g.eps = eps; }
+  if (rs_ssp) { g.rs_ssp = rs_ssp; g.rs_n = C / gemm_resid_slice_cols(C); g.rs_c = (float)C; g.eps = eps; }
   g.targets = targets; g.partial = partial; g.tgt_logit = tgt; g.logits = logits;
   g.nnb = nnb; g.cap = cap;
   CK(gemm(bf, EPI_CE, g, s));
@@ -183,7 +183,7 @@ gpt_status gpt_fwd_loss(const gpt_cfg* c, const gpt_weights* w, const int32_t* t
   const int nqk = (H + Hkv) * D;
   const int nqkv = (H + 2 * Hkv) * D;
   float* ssp = (float*)(ws + L.ssp);
-  const int nsl = C / 64;
+  const int nsl = C / gemm_resid_slice_cols(C);  // slices the residual GEMMs write
   if (bf) {
     // bf16 path: every RMSNorm after the first is applied as a row scale inside the GEMM that
     // consumes it (RMSNorm(x) W^T = (x W^T) / rms(x)).  The residual epilogues keep x in fp32,

@@ -13,10 +13,11 @@
 // "Logit Softcap" and "Cross-Entropy Loss".
 //
 // bf16 kernel (gfx950): v_mfma_f32_32x32x16_bf16 on 32x32 output tiles, fp32 accumulators.
-// Block tile BM x BN x 64, WM x WN wavefronts each owning (BM/WM) x (BN/WN).  Operand tiles
-// are staged global -> registers -> LDS, double-buffered, one barrier per 64-wide K step.  LDS
-// rows are 64 bf16 = eight 16-byte chunks; chunk c of row r lives at c ^ swz(r) so that the
-// 16-byte fragment reads of 8 (or 16) consecutive rows hit distinct banks.
+// Block tile BM x BN x 64, WM x WN wavefronts each owning (BM/WM) x (BN/WN).  Operand tiles go
+// global -> LDS directly (buffer loads with the LDS flag), double-buffered, one barrier per
+// 64-wide K step.  LDS rows are 64 bf16 = eight 16-byte chunks; chunk c of row r lives at
+// c ^ swz(r) so that the 16-byte fragment reads of 8 (or 16) consecutive rows hit distinct
+// banks.
 #include <math.h>
 
 #include <type_traits>
@@ -27,17 +28,10 @@
 namespace gptk {
 namespace {
 
-#ifndef GEMM_SPLIT
-#define GEMM_SPLIT 1
-#endif
-#ifndef GEMM_MIX
-#define GEMM_MIX 0
-#endif
-#ifndef GEMM_DIRECT_LDS
-#define GEMM_DIRECT_LDS 2
-#endif
-
 constexpr int BK = 64;
+// Kernel-internal residual variants: + bf16 copy and row sums of squares; + next-layer mix.
+constexpr int EPI_RESID_PROD = 5, EPI_RESID_MIX = 6;
+template <int E> constexpr bool is_resid = E == EPI_RESID || E == EPI_RESID_PROD || E == EPI_RESID_MIX;
 
 // s_waitcnt immediate waiting until at most n vector-memory operations are outstanding
 // (gfx9 encoding: vmcnt[3:0] at bits 3:0 and vmcnt[5:4] at bits 15:14; expcnt and lgkmcnt
@@ -77,8 +71,6 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses device-only types (buffer resources)
   constexpr int NT = WM * WN * 64;
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
-  constexpr int AC = BM * 8 / NT, BC = BN * 8 / NT;  // 16-byte chunks per thread per K step
-  static_assert(AC * NT == BM * 8 && BC * NT == BN * 8, "tile/thread mismatch");
   static_assert(FM * 32 == TM && FN * 32 == TN, "wave tile must be a multiple of 32");
 
   __shared__ __attribute__((aligned(16))) bf16 lds[2 * (BM + BN) * BK];
@@ -122,18 +114,6 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.f;
 
-#define GEMM_SUBSTEP(Ab, Bb, kk)                                                              \
-  do {                                                                                       \
-    const int co = ((2 * (kk) + hl) ^ sa) << 3;                                              \
-    bf16x8 af[FM], bfr[FN];                                                                  \
-    _Pragma("unroll") for (int fm = 0; fm < FM; ++fm) af[fm] = *(const bf16x8*)((Ab) + oa[fm] + co); \
-    _Pragma("unroll") for (int fn = 0; fn < FN; ++fn) bfr[fn] = *(const bf16x8*)((Bb) + ob[fn] + co); \
-    _Pragma("unroll") for (int fm = 0; fm < FM; ++fm)                                        \
-    _Pragma("unroll") for (int fn = 0; fn < FN; ++fn)                                        \
-      acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0); \
-  } while (0)
-
-#if GEMM_DIRECT_LDS
   // Direct global -> LDS loads (buffer_load_dwordx4 ... lds): one instruction per wave writes
   // 1 KB (8 rows of 64 bf16) of LDS at consecutive 16-byte slots, lane L filling slot L, so
   // each lane fetches the global chunk that the swizzled layout places at its slot.  The buffer
@@ -146,39 +126,45 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
       (void*)(A + (size_t)m0 * lda), (short)0, (int)min((size_t)(M - m0) * lda * 2, (size_t)0x7fffffff), 0x00020000);
   const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(Bseg + (size_t)nb0 * ldb), (short)0, (int)min((size_t)(nrows - nb0) * ldb * 2, (size_t)0x7fffffff), 0x00020000);
-  int va[AI], vb[BI];
+  // Row block rb (8 rows) of an operand tile sits at row 8*rb: its lanes' chunk swizzle is
+  // (lane & 7) ^ (lane >> 3) ^ (rb & 1), so two per-lane offsets serve every row block, and
+  // the row block's start and the K offset travel in the scalar soffset.
+  static_assert(AI % 2 == 0 && BI % 2 == 0, "row blocks per wave must be even");
+  const int wids = __builtin_amdgcn_readfirstlane(wid);
+  // A and B share their row pitch (lda == ldb, checked by the launcher).
+  int va[2];
 #pragma unroll
-  for (int i = 0; i < AI; ++i) {
-    const int r = (wid * AI + i) * 8 + (lane >> 3), c = (lane & 7) ^ swz8(r);
-    va[i] = (r * lda + c * 8) * 2;
-  }
-#pragma unroll
-  for (int i = 0; i < BI; ++i) {
-    const int r = (wid * BI + i) * 8 + (lane >> 3), c = (lane & 7) ^ swz8(r);
-    vb[i] = (r * ldb + c * 8) * 2;
-  }
+  for (int p = 0; p < 2; ++p) va[p] = ((lane >> 3) * lda + (((lane & 7) ^ (lane >> 3) ^ p) << 3)) * 2;
   typedef __attribute__((address_space(3))) void* lds_ptr_t;
 #define GEMM_ISSUE(buf, k0)                                                                   \
   do {                                                                                       \
     _Pragma("unroll") for (int i = 0; i < AI; ++i)                                           \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa,                                          \
-        (lds_ptr_t)(As + (buf) * BM * BK + (wid * AI + i) * 512), 16, va[i], (k0) * 2, 0, 0); \
+        (lds_ptr_t)(As + (buf) * BM * BK + (wids * AI + i) * 512), 16, va[i & 1],           \
+        (k0) * 2 + (wids * AI + i) * 16 * lda, 0, 0);                                        \
     _Pragma("unroll") for (int i = 0; i < BI; ++i)                                           \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb,                                          \
-        (lds_ptr_t)(Bs + (buf) * BN * BK + (wid * BI + i) * 512), 16, vb[i], (k0) * 2, 0, 0); \
+        (lds_ptr_t)(Bs + (buf) * BN * BK + (wids * BI + i) * 512), 16, va[i & 1],           \
+        (k0) * 2 + (wids * BI + i) * 16 * ldb, 0, 0);                                        \
   } while (0)
 
-#if GEMM_DIRECT_LDS >= 2
   // Software pipeline over 16-wide k-substeps with two fragment register sets: the reads for
   // substep s+1 are issued before the MFMAs of substep s.  The barrier that retires a K step's
   // buffer sits before that step's last 16 MFMAs, whose operands are already in registers, so
   // the barrier wait, the next tile's global->LDS issue and the first reads of the next K step
   // all overlap MFMA work.
-  bf16x8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
-  auto rd = [&](const bf16* Ab, const bf16* Bb, int kk, bf16x8 (&fa)[FM], bf16x8 (&fb)[FN]) {
-    const int co = ((2 * kk + hl) ^ sa) << 3;
+  // ROLL (wide wave tiles, where two full fragment sets do not fit beside the accumulators):
+  // A fragments keep two sets, B fragments one; a substep's MFMAs run B-fragment-major and each
+  // B fragment is reloaded for the next substep right after its last MFMA, pinned in place.
+  constexpr bool ROLL = FM * FN * 16 + 4 * 2 * (FM + FN) > 232;
+  auto co_of = [&](int kk) { return ((2 * kk + hl) ^ sa) << 3; };
+  auto rda = [&](const bf16* Ab, int kk, bf16x8 (&fa)[FM]) {
+    const int co = co_of(kk);
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) fa[fm] = *(const bf16x8*)(Ab + oa[fm] + co);
+  };
+  auto rdb = [&](const bf16* Bb, int kk, bf16x8 (&fb)[FN]) {
+    const int co = co_of(kk);
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) fb[fn] = *(const bf16x8*)(Bb + ob[fn] + co);
   };
@@ -197,138 +183,63 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
     __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
   }
   __syncthreads();
-  // Each region holds the MFMAs of one substep and the reads of the next; sched_group_barrier
-  // interleaves them (2 MFMAs, 1 LDS read) so the LDS command queue never backs up into the
-  // in-order issue stream.  The post-barrier region also interleaves the 16 direct-to-LDS loads.
 #define PIN __builtin_amdgcn_sched_barrier(0)
-#if GEMM_MIX
-#define MIX_PIN
-#define MIX_MM_DS()                                                      \
-  do {                                                                   \
-    _Pragma("unroll") for (int q = 0; q < FM + FN; ++q) {                \
-      __builtin_amdgcn_sched_group_barrier(0x008, (FM * FN) / (FM + FN), 0); \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                 \
-    }                                                                    \
-  } while (0)
-#else
-#define MIX_PIN PIN
-#define MIX_MM_DS()
-#endif
-  rd(As, Bs, 0, fa0, fb0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    const bf16* Ab = As + buf * BM * BK;
-    const bf16* Bb = Bs + buf * BN * BK;
-    PIN; rd(Ab, Bb, 1, fa1, fb1); MIX_PIN; mm(fa0, fb0); MIX_MM_DS();
-    PIN; rd(Ab, Bb, 2, fa0, fb0); MIX_PIN; mm(fa1, fb1); MIX_MM_DS();
-    PIN; rd(Ab, Bb, 3, fa1, fb1); MIX_PIN; mm(fa0, fb0); MIX_MM_DS();
-    PIN;
-    __builtin_amdgcn_s_waitcnt(vmcnt_le(0));  // own loads of tile kt+1 have landed
-    __syncthreads();                          // everyone's too; buffer `buf` fully read
-    PIN;
-#if GEMM_MIX
-    if (kt + 1 < nk) {
+  if constexpr (!ROLL) {
+    bf16x8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+    rda(As, 0, fa0); rdb(Bs, 0, fb0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      const bf16* Ab = As + buf * BM * BK;
+      const bf16* Bb = Bs + buf * BN * BK;
+      PIN; rda(Ab, 1, fa1); rdb(Bb, 1, fb1); PIN; mm(fa0, fb0);
+      PIN; rda(Ab, 2, fa0); rdb(Bb, 2, fb0); PIN; mm(fa1, fb1);
+      PIN; rda(Ab, 3, fa1); rdb(Bb, 3, fb1); PIN; mm(fa0, fb0);
+      PIN;
+      __builtin_amdgcn_s_waitcnt(vmcnt_le(0));  // own loads of tile kt+1 have landed
+      __syncthreads();                          // everyone's too; buffer `buf` fully read
+      PIN;
       if (kt + 2 < nk) GEMM_ISSUE(buf, (kt + 2) * BK);
-      rd(As + (buf ^ 1) * BM * BK, Bs + (buf ^ 1) * BN * BK, 0, fa0, fb0);
-      mm(fa1, fb1);
-      if (kt + 2 < nk) {
-        _Pragma("unroll") for (int q = 0; q < AI + BI; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-          if (q < FM + FN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-      } else {
-        MIX_MM_DS();
-      }
-    } else {
-      mm(fa1, fb1);
+      if (kt + 1 < nk) { rda(As + (buf ^ 1) * BM * BK, 0, fa0); rdb(Bs + (buf ^ 1) * BN * BK, 0, fb0); }
+      PIN; mm(fa1, fb1);
+      PIN;
+      // The next substep-0 fragments were issued among those MFMAs; settling the LDS counter
+      // here keeps the waitcnt pass from waiting on fresh reads at the loop top.
+      __builtin_amdgcn_s_waitcnt(lgkmcnt_0);
     }
-#else
-    if (kt + 2 < nk) GEMM_ISSUE(buf, (kt + 2) * BK);
-    if (kt + 1 < nk) rd(As + (buf ^ 1) * BM * BK, Bs + (buf ^ 1) * BN * BK, 0, fa0, fb0);
-    PIN; mm(fa1, fb1);
-#endif
-    PIN;
-    // The next substep-0 fragments were issued among those MFMAs; settling the LDS counter
-    // here keeps the waitcnt pass from waiting on fresh reads at the loop top.
-    __builtin_amdgcn_s_waitcnt(lgkmcnt_0);
-  }
-#undef MIX_MM_DS
-#undef MIX_PIN
-#undef PIN
-#else
-  GEMM_ISSUE(0, 0);
-  if (nk > 1) {
-    GEMM_ISSUE(1, BK);
-    __builtin_amdgcn_s_waitcnt(vmcnt_le(AI + BI));  // tile 0 landed, tile 1 in flight
   } else {
-    __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
-  }
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    const bf16* Ab = As + buf * BM * BK;
-    const bf16* Bb = Bs + buf * BN * BK;
+    bf16x8 fa0[FM], fa1[FM], fb[FN];
+    // MFMAs of one substep with fragments fa and fb; B fragment fn is then refilled from
+    // (Bn, kn).  After the last K step these refills read a stale buffer: harmless, unused.
+    auto mmroll = [&](const bf16x8 (&fa)[FM], const bf16* Bn, int kn) {
+      const int co = co_of(kn);
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) GEMM_SUBSTEP(Ab, Bb, kk);
-    __builtin_amdgcn_s_waitcnt(vmcnt_le(0));  // own loads of tile kt+1 have landed
-    __syncthreads();                     // ... and everyone's; buffer `buf` is free
-    if (kt + 2 < nk) GEMM_ISSUE(buf, (kt + 2) * BK);
+      for (int fn = 0; fn < FN; ++fn) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fm], fb[fn], acc[fm][fn], 0, 0, 0);
+        fb[fn] = *(const bf16x8*)(Bn + ob[fn] + co);
+        PIN;
+      }
+    };
+    rda(As, 0, fa0); rdb(Bs, 0, fb);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      const bf16* Ab = As + buf * BM * BK;
+      const bf16* Bb = Bs + buf * BN * BK;
+      PIN; rda(Ab, 1, fa1); PIN; mmroll(fa0, Bb, 1);
+      rda(Ab, 2, fa0); PIN; mmroll(fa1, Bb, 2);
+      rda(Ab, 3, fa1); PIN; mmroll(fa0, Bb, 3);
+      __builtin_amdgcn_s_waitcnt(vmcnt_le(0));  // own loads of tile kt+1 have landed
+      __syncthreads();                          // everyone's too; buffer `buf` fully read
+      PIN;
+      if (kt + 2 < nk) GEMM_ISSUE(buf, (kt + 2) * BK);
+      rda(As + (buf ^ 1) * BM * BK, 0, fa0);
+      PIN; mmroll(fa1, Bs + (buf ^ 1) * BN * BK, 0);
+      __builtin_amdgcn_s_waitcnt(lgkmcnt_0);
+    }
   }
-#endif
+#undef PIN
 #undef GEMM_ISSUE
-#else
-  u32x4 ra[AC], rb[BC];
-  const bf16* pa[AC];
-  const bf16* pb[BC];
-  int la[AC], lb[BC];
-#pragma unroll
-  for (int i = 0; i < AC; ++i) {
-    const int c = tid + i * NT, r = c >> 3, kc = c & 7;
-    pa[i] = A + (size_t)min(m0 + r, M - 1) * lda + kc * 8;
-    la[i] = r * BK + ((kc ^ swz8(r)) << 3);
-  }
-#pragma unroll
-  for (int i = 0; i < BC; ++i) {
-    const int c = tid + i * NT, r = c >> 3, kc = c & 7;
-    pb[i] = Bseg + (size_t)min(nb0 + r, nrows - 1) * ldb + kc * 8;
-    lb[i] = r * BK + ((kc ^ swz8(r)) << 3);
-  }
-#define GEMM_GLOAD(k0)                                                      \
-  do {                                                                      \
-    _Pragma("unroll") for (int i = 0; i < AC; ++i) ra[i] = *(const u32x4*)(pa[i] + (k0)); \
-    _Pragma("unroll") for (int i = 0; i < BC; ++i) rb[i] = *(const u32x4*)(pb[i] + (k0)); \
-  } while (0)
-#define GEMM_SSTORE(buf)                                                                        \
-  do {                                                                                          \
-    _Pragma("unroll") for (int i = 0; i < AC; ++i) *(u32x4*)(As + (buf) * BM * BK + la[i]) = ra[i]; \
-    _Pragma("unroll") for (int i = 0; i < BC; ++i) *(u32x4*)(Bs + (buf) * BN * BK + lb[i]) = rb[i]; \
-  } while (0)
-
-  GEMM_GLOAD(0);
-  GEMM_SSTORE(0);
-  if (nk > 1) GEMM_GLOAD(BK);
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    const bf16* Ab = As + buf * BM * BK;
-    const bf16* Bb = Bs + buf * BN * BK;
-    // First half of the K step, then stage tile kt+1 into the other buffer (free since the
-    // last barrier) and fetch tile kt+2, then the second half: the LDS writes and the global
-    // load issue overlap the MFMAs.
-#pragma unroll
-    for (int kk = 0; kk < BK / 32; ++kk) GEMM_SUBSTEP(Ab, Bb, kk);
-    if (kt + 1 < nk) GEMM_SSTORE(buf ^ 1);
-    if (kt + 2 < nk) GEMM_GLOAD((kt + 2) * BK);
-#pragma unroll
-    for (int kk = BK / 32; kk < BK / 16; ++kk) GEMM_SUBSTEP(Ab, Bb, kk);
-    __syncthreads();
-  }
-#undef GEMM_GLOAD
-#undef GEMM_SSTORE
-#endif
-#undef GEMM_SUBSTEP
 
   // ---------------------------------------------------------------- epilogues
   // acc[fm][fn][r] is C[row][col] with row = m0 + wm*TM + fm*32 + 8*(r/4) + 4*hl + r%4 and
@@ -338,7 +249,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
   const int cbase = n0 + wn * TN + rl;
   const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
 
-  if constexpr (EPI != EPI_RESID) {
+  if constexpr (!is_resid<EPI>) {
     if (g.rs_ssp != nullptr) {
       // A was not normalised: scale each output row by 1/rms of its A row, from the producer's
       // per-slice sums of squares (summed here in a fixed order).
@@ -388,82 +299,75 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
         }
     };
     if (interior) store(std::false_type{}); else store(std::true_type{});
-  } else if constexpr (EPI == EPI_RESID) {
-    float* out = (float*)g.out;
-    if constexpr (TN == 64) {  // the producer writes one sum-of-squares slice per 64 columns
-    if (g.xb != nullptr) {
-      // x += acc; optional next-layer mix x = lam x + mu x0; store x and bf16(x); per-row sum of
-      // squares of this wavefront's 64 columns (32-lane butterfly) for the next norm.
-      const bool mix = g.lam != nullptr;
-      const float lam = mix ? g.lam[g.layer] : 1.f, mu = mix ? g.mu[g.layer] : 0.f;
-      const int slice = (g.col_off + n0 + wn * TN) / 64;
-      const bool slice_live = n0 + wn * TN < N;
-      auto produce = [&](auto checked) {
+  } else if constexpr (is_resid<EPI>) {
+    // x += acc.  With a bf16 copy (the producer of the next RMSNorm) also: the optional
+    // next-layer mix x = lam x + mu x0, the bf16 copy xb, and each row's sum of squares over
+    // this wavefront's TN columns (one slice of width TN), written slice-major for the
+    // consumer's row scale.  Each 32-row group of the wavefront's tile is staged through LDS
+    // (wavefront-private) and read back row-contiguous, so that the global read-modify-write
+    // moves 16 bytes per lane over whole 128-byte lines.
+    constexpr bool prod = EPI != EPI_RESID, mix = EPI == EPI_RESID_MIX;
+    constexpr int LDP = TN + 4;  // staging row pitch (floats)
+    static_assert(WM * WN * 32 * LDP * 4 <= (int)sizeof(lds), "staging exceeds LDS");
+    float* const out = (float*)g.out;
+    float* const stg = (float*)lds + wid * 32 * LDP;
+    const float lam = mix ? g.lam[g.layer] : 1.f, mu = mix ? g.mu[g.layer] : 0.f;
+    const int slice = (g.col_off + n0 + wn * TN) / TN;
+    const bool slice_live = prod && n0 + wn * TN < N;
+    const bool vec = (g.ldo & 3) == 0;
+    const int lr = lane >> 3, lc = (lane & 7) * 4;  // read-back: rows lr + 8j, columns lc + 32c
+    __syncthreads();  // every wavefront is done with the operand tiles
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
+    for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
-          for (int rh = 0; rh < 2; ++rh) {  // 8 rows at a time keeps the staging registers small
-            float ss[8];
+      for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-            for (int q = 0; q < 8; ++q) ss[q] = 0.f;
+        for (int r = 0; r < 16; ++r)
+          stg[(8 * (r >> 2) + 4 * hl + (r & 3)) * LDP + fn * 32 + rl] = acc[fm][fn][r];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-              const int col = cbase + fn * 32;
-              float prev[8], x0v[8];
+      for (int j = 0; j < 4; ++j) {
+        const int row = m0 + wm * TM + fm * 32 + lr + 8 * j;
+        float ss = 0.f;
 #pragma unroll
-              for (int q = 0; q < 8; ++q) {
-                const int r = 8 * rh + q;
-                const int row = rbase + fm * 32 + 8 * (r >> 2) + (r & 3);
-                const bool ok = !decltype(checked)::value || (row < M && col < N);
-                prev[q] = ok ? out[(size_t)row * g.ldo + col] : 0.f;
-                x0v[q] = (ok && mix) ? g.x0[(size_t)row * g.ldo + col] : 0.f;
-              }
+        for (int c = 0; c < FN; ++c) {
+          const int col = n0 + wn * TN + 32 * c + lc;
+          const f32x4 a = *(const f32x4*)(stg + (lr + 8 * j) * LDP + 32 * c + lc);
+          const size_t o = (size_t)row * g.ldo + col;
+          if ((interior || (row < M && col + 4 <= N)) && vec) {
+            f32x4 v = *(const f32x4*)(out + o) + a;
+            if (mix) v = lam * v + mu * *(const f32x4*)(g.x0 + o);
+            *(f32x4*)(out + o) = v;
+            if (prod) {
+              bf16x4 h;
 #pragma unroll
-              for (int q = 0; q < 8; ++q) {
-                const int r = 8 * rh + q;
-                const int row = rbase + fm * 32 + 8 * (r >> 2) + (r & 3);
-                float v = prev[q] + acc[fm][fn][r];
-                if (mix) v = lam * v + mu * x0v[q];
-                if (!decltype(checked)::value || (row < M && col < N)) {
-                  out[(size_t)row * g.ldo + col] = v;
-                  g.xb[(size_t)row * g.ldo + col] = (bf16)v;
-                  ss[q] += v * v;
-                }
+              for (int e = 0; e < 4; ++e) h[e] = (bf16)v[e];
+              *(bf16x4*)(g.xb + o) = h;
+              ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+            }
+          } else if (row < M) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (col + e < N) {
+                float v = out[o + e] + a[e];
+                if (mix) v = lam * v + mu * g.x0[o + e];
+                out[o + e] = v;
+                if (prod) { g.xb[o + e] = (bf16)v; ss += v * v; }
               }
             }
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-              const int r = 8 * rh + q;
-              const float t = sum32(ss[q]);
-              const int row = rbase + fm * 32 + 8 * (r >> 2) + (r & 3);
-              if (rl == 0 && slice_live && row < M) g.ssp[(size_t)slice * M + row] = t;
-            }
-          }
-      };
-      if (interior) produce(std::false_type{}); else produce(std::true_type{});
-      return;
-    }
-    }
-    auto resid = [&](auto checked) {
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-          const int col = cbase + fn * 32;
-          float prev[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = rbase + fm * 32 + 8 * (r >> 2) + (r & 3);
-            prev[r] = (!decltype(checked)::value || (row < M && col < N)) ? out[(size_t)row * g.ldo + col] : 0.f;
-          }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = rbase + fm * 32 + 8 * (r >> 2) + (r & 3);
-            if (!decltype(checked)::value || (row < M && col < N)) out[(size_t)row * g.ldo + col] = prev[r] + acc[fm][fn][r];
           }
         }
-    };
-    if (interior) resid(std::false_type{}); else resid(std::true_type{});
+        if (prod) {
+          ss += __shfl_xor(ss, 1);
+          ss += __shfl_xor(ss, 2);
+          ss += __shfl_xor(ss, 4);
+          if ((lane & 7) == 0 && slice_live && row < M) g.ssp[(size_t)slice * M + row] = ss;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();  // reads of this group precede the next group's writes
+    }
   } else if constexpr (EPI == EPI_QKV) {
     bf16* qk = (bf16*)g.out;
     bf16* vt = (bf16*)g.vt;
@@ -608,7 +512,12 @@ hipError_t run_bf16(Epi epi, const GemmArgs& a, hipStream_t s) {
   switch (epi) {
     case EPI_STORE: gemm_bf16_kernel<BM, BN, WM, WN, EPI_STORE><<<grid, NT, 0, s>>>(a); break;
     case EPI_RELU2: gemm_bf16_kernel<BM, BN, WM, WN, EPI_RELU2><<<grid, NT, 0, s>>>(a); break;
-    case EPI_RESID: gemm_bf16_kernel<BM, BN, WM, WN, EPI_RESID><<<grid, NT, 0, s>>>(a); break;
+    case EPI_RESID:
+      if constexpr (WM * WN * 32 * (BN / WN + 4) * 4 > 2 * (BM + BN) * BK * 2) return hipErrorInvalidValue;  // staging would not fit
+      else if (a.xb == nullptr) gemm_bf16_kernel<BM, BN, WM, WN, EPI_RESID><<<grid, NT, 0, s>>>(a);
+      else if (a.lam == nullptr) gemm_bf16_kernel<BM, BN, WM, WN, EPI_RESID_PROD><<<grid, NT, 0, s>>>(a);
+      else gemm_bf16_kernel<BM, BN, WM, WN, EPI_RESID_MIX><<<grid, NT, 0, s>>>(a);
+      break;
     case EPI_QKV: gemm_bf16_kernel<BM, BN, WM, WN, EPI_QKV><<<grid, NT, 0, s>>>(a); break;
     case EPI_CE: gemm_bf16_kernel<BM, BN, WM, WN, EPI_CE><<<grid, NT, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
@@ -707,7 +616,6 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 
 }  // namespace
 
-int gemm_bf16_ce_blocks(int N) { return (N + 255) / 256; }
 int gemm_f32_ce_blocks(int N) { return (N + FT - 1) / FT; }
 
 namespace {
@@ -771,27 +679,40 @@ hipError_t run_narrow(Epi epi, const GemmArgs& a, hipStream_t s) {
   return run_bf16<256, 128, 2, 2>(epi, a, s);
 }
 
+// Interior column-segment boundaries must fall on block-column boundaries.
+bool seg_ok(const GemmArgs& a, int bn) {
+  const int e0 = a.nseg0, e1 = a.nseg0 + a.nseg1;
+  return (e0 >= a.N || e0 % bn == 0) && (e1 >= a.N || e1 % bn == 0);
+}
+
+// 256x384 tiles (8 wavefronts of 128x96) for the residual and MLP-up GEMMs when the columns
+// allow: on the model's widths they fill whole rounds of the CUs (64 x 4 tiles for a
+// 16384 x 1536 output) where 256x256 tiles would leave half a round.
+bool use_wide(Epi epi, const GemmArgs& a) {
+  return (epi == EPI_RESID || epi == EPI_RELU2 || epi == EPI_STORE) && a.N % 384 == 0 && seg_ok(a, 384);
+}
+
 }  // namespace
 
+int gemm_bf16_ce_blocks(int N) { return (N + 255) / 256; }
+
+int gemm_resid_slice_cols(int N) { return N % 384 == 0 ? 96 : 64; }
+
 hipError_t launch_gemm_bf16(Epi epi, const GemmArgs& a, hipStream_t s) {
-  if (a.K % BK || a.M <= 0 || a.N <= 0) return hipErrorInvalidValue;
+  if (a.K % BK || a.M <= 0 || a.N <= 0 || a.lda != a.ldb) return hipErrorInvalidValue;
   if (epi == EPI_CE) return run_bf16<256, 256, 2, 4>(epi, a, s);  // must match gemm_bf16_ce_blocks
   if (epi == EPI_QKV && a.cs != nullptr && a.D != 128) return hipErrorInvalidValue;
-  // Interior column-segment boundaries must fall on block-column boundaries.
-  auto seg_ok = [&](int bn) {
-    const int e0 = a.nseg0, e1 = a.nseg0 + a.nseg1;
-    return (e0 >= a.N || e0 % bn == 0) && (e1 >= a.N || e1 % bn == 0);
-  };
-  const bool n256 = seg_ok(256), n128 = seg_ok(128);
-  if (!n256) return n128 ? run_narrow(epi, a, s) : hipErrorInvalidValue;
+  if (use_wide(epi, a)) return run_bf16<256, 384, 2, 4>(epi, a, s);  // slices of 96 columns
+  if (!seg_ok(a, 256)) return seg_ok(a, 128) ? run_narrow(epi, a, s) : hipErrorInvalidValue;
   // 256x256 tiles, 8 wavefronts (2 per SIMD) so one wavefront's LDS waits overlap the other's
-  // MFMAs.  When the tile count leaves a partial last round on the CUs (e.g. 64 x 6 tiles on
+  // MFMAs.  When the tile count leaves a partial last round on the CUs (e.g. 64 x 18 tiles on
   // 256 CUs), the columns are split: a leading part whose 256x256 tiles fill whole rounds, and
-  // a tail launched with 256x128 tiles, so the partial round costs half a tile per CU.
+  // a tail launched with 256x128 tiles, so the partial round costs half a tile per CU.  Both
+  // parts keep 64-column wavefront slices.
   const int ncu = cu_count();
   const int nbm = (a.M + 255) / 256, nbn = (a.N + 255) / 256;
   const long tiles = (long)nbm * nbn;
-  if (GEMM_SPLIT && tiles > ncu && tiles % ncu != 0 && a.N % 256 == 0) {
+  if (tiles > ncu && tiles % ncu != 0 && a.N % 256 == 0) {
     const int per = ncu / gcd(nbm, ncu);  // column blocks per whole number of rounds
     const int c1 = (nbn / per) * per;
     if (c1 > 0 && c1 < nbn) {

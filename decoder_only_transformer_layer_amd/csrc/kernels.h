@@ -47,8 +47,8 @@ struct GemmArgs {
   const float* rs_ssp; int rs_n; float rs_c;
   // Residual producer (EPI_RESID, bf16 path): if xb is set, after x += acc the epilogue
   // optionally mixes x = lam[layer] x + mu[layer] x0 (when lam != NULL), stores x, a bf16 copy
-  // of x to xb [M, ldo], and per-row sums of squares over each 64-column slice to
-  // ssp[(col_off + col) / 64][row] (slice-major, M rows per slice).
+  // of x to xb [M, ldo], and per-row sums of squares over each column slice of width
+  // w = gemm_resid_slice_cols(N) to ssp[(col_off + col) / w][row] (slice-major, M per slice).
   bf16_t* xb; const float* x0; const float* lam; const float* mu; int layer;
   float* ssp; int ssp_n; int col_off;
   const int32_t* targets;                 // CE: [M] (or NULL)
@@ -60,10 +60,13 @@ struct GemmArgs {
 };
 
 // bf16 inputs, fp32 accumulation on MFMA.  Returns hipErrorInvalidValue for shapes the
-// tiling does not cover (K % 64, segment sizes).
+// tiling does not cover (K % 64, segment sizes, lda != ldb).
 hipError_t launch_gemm_bf16(Epi epi, const GemmArgs& a, hipStream_t s);
 // Number of column blocks the CE epilogue of launch_gemm_bf16 produces for N columns.
 int gemm_bf16_ce_blocks(int N);
+// Width of the column slices whose per-row sums of squares a RESID GEMM with xb set writes
+// (ssp [N / width][M]); divides N whenever N % 64 == 0.
+int gemm_resid_slice_cols(int N);
 // fp32 SIMT GEMM (small configurations).
 hipError_t launch_gemm_f32(Epi epi, const GemmArgs& a, hipStream_t s);
 int gemm_f32_ce_blocks(int N);
