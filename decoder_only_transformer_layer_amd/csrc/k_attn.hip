@@ -217,8 +217,8 @@ constexpr int NW2 = 8, BQ2 = NW2 * 32, STG = 3;
 template <int D>
 __global__ __launch_bounds__(NW2 * 64, 1) void attn_bf16_v2_kernel(const bf16* __restrict__ qk,
                                                                   const bf16* __restrict__ vt,
-                                                                  bf16* __restrict__ o, int T, int H,
-                                                                  int Hkv, int window, float c) {
+                                                                  bf16* __restrict__ o, int B, int T,
+                                                                  int H, int Hkv, int window, float c) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int KCH = D / 8;            // 16-byte chunks per K row
   constexpr int DT = D / 32;            // 32-row tiles of O^T
@@ -229,9 +229,13 @@ __global__ __launch_bounds__(NW2 * 64, 1) void attn_bf16_v2_kernel(const bf16* _
   __shared__ __attribute__((aligned(16))) bf16 Ks[STG][BKV * D];
   __shared__ __attribute__((aligned(16))) bf16 Vs[STG][D * BKV];
 
+  // Blocks are dispatched in launch order, so the linear block index runs over query tiles
+  // from the last (the most key tiles) to the first, every (head, batch) pair within a tile
+  // row: the longest blocks start first and the short ones fill in at the end.
   const int nqt = (T + BQ2 - 1) / BQ2;
-  const int qt = nqt - 1 - (int)blockIdx.x;  // longest rows first
-  const int h = blockIdx.y, b = blockIdx.z;
+  const int hb = (int)blockIdx.x % (H * B), qrank = (int)blockIdx.x / (H * B);
+  const int qt = nqt - 1 - qrank;
+  const int h = hb % H, b = hb / H;
   const int g = (h * Hkv) / H;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int hl = lane >> 5, rl = lane & 31;
@@ -455,11 +459,11 @@ hipError_t launch_attn_bf16(const void* qk, const void* vt, void* o, int B, int 
   if (T % BKV) return hipErrorInvalidValue;
   const float sl2 = scale * GPT_LOG2E;
 #if ATTN_V2
-  const dim3 grid((T + BQ2 - 1) / BQ2, H, B);
+  const dim3 grid(((T + BQ2 - 1) / BQ2) * H * B);
   if (D == 128)
-    attn_bf16_v2_kernel<128><<<grid, NW2 * 64, 0, s>>>((const bf16*)qk, (const bf16*)vt, (bf16*)o, T, H, Hkv, window, sl2);
+    attn_bf16_v2_kernel<128><<<grid, NW2 * 64, 0, s>>>((const bf16*)qk, (const bf16*)vt, (bf16*)o, B, T, H, Hkv, window, sl2);
   else if (D == 64)
-    attn_bf16_v2_kernel<64><<<grid, NW2 * 64, 0, s>>>((const bf16*)qk, (const bf16*)vt, (bf16*)o, T, H, Hkv, window, sl2);
+    attn_bf16_v2_kernel<64><<<grid, NW2 * 64, 0, s>>>((const bf16*)qk, (const bf16*)vt, (bf16*)o, B, T, H, Hkv, window, sl2);
   else
     return hipErrorInvalidValue;
 #else
