@@ -253,7 +253,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
     if (g.rs_ssp != nullptr) {
       // A was not normalised: scale each output row by 1/rms of its A row, from the producer's
       // per-slice sums of squares (summed here in a fixed order).
-      float* rinv = (float*)lds + BM * (WN + 2);
+      float* rinv = (float*)lds + (sizeof(lds) / 4 - BM);  // past any epilogue staging
       __syncthreads();  // every wavefront is done with the operand tiles
       // slices are stored slice-major ([slice][M]): consecutive threads read consecutive rows
       for (int i = tid; i < BM; i += NT) {
@@ -282,23 +282,66 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
   }
 
   if constexpr (EPI == EPI_STORE || EPI == EPI_RELU2) {
-    bf16* out = (bf16*)g.out;
-    auto store = [&](auto checked) {
+    bf16* const out = (bf16*)g.out;
+    constexpr int LDP = TN + 4;  // staging row pitch (floats)
+    if constexpr (WM * WN * 32 * LDP * 4 + BM * 4 <= (int)sizeof(lds)) {
+      // Each 32-row group of the wavefront's tile is staged through LDS (wavefront-private,
+      // fp32) and read back row-contiguous: every lane then stores 8 bf16 (16 bytes).
+      constexpr int CPR = TN / 8, PER = CPR / 2;  // 16-byte chunks per row; per lane
+      float* const stg = (float*)lds + wid * 32 * LDP;
+      const bool vec = (g.ldo & 7) == 0;
+      __syncthreads();  // every wavefront is done with the operand tiles
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
+      for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-          const int col = cbase + fn * 32;
+        for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int row = rbase + fm * 32 + 8 * (r >> 2) + (r & 3);
             float v = acc[fm][fn][r];
             if (EPI == EPI_RELU2) { v = fmaxf(v, 0.f); v = v * v; }
-            if (!decltype(checked)::value || (row < M && col < N)) out[(size_t)row * g.ldo + col] = (bf16)v;
+            stg[(8 * (r >> 2) + 4 * hl + (r & 3)) * LDP + fn * 32 + rl] = v;
+          }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+          const int idx = lane + 64 * k, lr = idx / CPR, ch = idx % CPR;
+          const f32x4 a0 = *(const f32x4*)(stg + lr * LDP + ch * 8);
+          const f32x4 a1 = *(const f32x4*)(stg + lr * LDP + ch * 8 + 4);
+          bf16x8 hv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { hv[e] = (bf16)a0[e]; hv[e + 4] = (bf16)a1[e]; }
+          const int row = m0 + wm * TM + fm * 32 + lr, col = n0 + wn * TN + ch * 8;
+          bf16* const op = out + (size_t)row * g.ldo + col;
+          if ((interior || (row < M && col + 8 <= N)) && vec) {
+            *(bf16x8*)op = hv;
+          } else if (row < M) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (col + e < N) op[e] = hv[e];
           }
         }
-    };
-    if (interior) store(std::false_type{}); else store(std::true_type{});
+        __builtin_amdgcn_wave_barrier();  // reads of this group precede the next group's writes
+      }
+    } else {
+      auto store = [&](auto checked) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) {
+            const int col = cbase + fn * 32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int row = rbase + fm * 32 + 8 * (r >> 2) + (r & 3);
+              float v = acc[fm][fn][r];
+              if (EPI == EPI_RELU2) { v = fmaxf(v, 0.f); v = v * v; }
+              if (!decltype(checked)::value || (row < M && col < N)) out[(size_t)row * g.ldo + col] = (bf16)v;
+            }
+          }
+      };
+      if (interior) store(std::false_type{}); else store(std::true_type{});
+    }
   } else if constexpr (is_resid<EPI>) {
     // x += acc.  With a bf16 copy (the producer of the next RMSNorm) also: the optional
     // next-layer mix x = lam x + mu x0, the bf16 copy xb, and each row's sum of squares over
