@@ -320,7 +320,7 @@ gpt_status gpt_op_qkv(const void* xn, const void* wq, const void* wk, const void
       !(eps >= 0.f))
     return GPT_E_INVALID_ARG;
   if (C % 64 || T % 4 || (H * D) % 128 || (Hkv * D) % 128) return GPT_E_UNSUPPORTED;
-  if (cs && D != 128) return GPT_E_UNSUPPORTED;
+  if (cs && (D != 128 || T % 32)) return GPT_E_UNSUPPORTED;  // fused epilogue: whole heads, 32-row groups
   const int M = B * T, nqk = (H + Hkv) * D, nqkv = (H + 2 * Hkv) * D;
   GemmArgs g = gemm_args(xn, C, wq, nqkv, C, M, qk, nqk);
   g.B1 = wk; g.B2 = wv; g.nseg0 = H * D; g.nseg1 = Hkv * D;

@@ -416,29 +416,36 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
     bf16* vt = (bf16*)g.vt;
     const int wcol0 = n0 + wn * TN;  // q, k and v segments are multiples of TN columns
     if constexpr (TN == 128) {
-      if (g.cs != nullptr && wcol0 < g.nqk && wcol0 < N) {
-        // This wavefront owns one whole 128-wide q or k head for its TM rows.  RoPE pairs
-        // (j, j+64) are tiles fn and fn+2 of the same lane; the head's sum of squares is the
-        // lane's two pairs plus a 32-lane butterfly (the 32 lanes of a half share a row).
-        // Rows go in chunks of 8 so the 16 table loads of a chunk are in flight together.
-        auto rope_norm = [&](auto checked) {
+      if (g.cs != nullptr) {
+        // This wavefront owns one whole 128-wide head (q, k or v) for its TM rows.  Each
+        // 32-row group is finished in registers, staged through wavefront-private LDS as
+        // bf16 and written back with 16-byte stores: q/k rows row-major, v transposed.
+        // RoPE pairs (j, j+64) of a q/k head are tiles fn and fn+2 of the same lane; the
+        // head's sum of squares is the lane's two pairs plus a 32-lane butterfly (the 32
+        // lanes of a half share a row).  Rows go in chunks of 8 so that the 16 table loads of
+        // a chunk are in flight together.
+        constexpr int LQ = TN + 8, LV = 32 + 8;  // staging pitches (bf16): [row][col], [d][t]
+        constexpr int WREG = 32 * LQ > TN * LV ? 32 * LQ : TN * LV;
+        static_assert(WM * WN * WREG * 2 + BM * 4 <= (int)sizeof(lds), "QKV staging exceeds LDS");
+        bf16* const stg = lds + wid * WREG;
+        const bool live = wcol0 < N, is_qk = wcol0 < g.nqk;
+        __syncthreads();  // every wavefront is done with the operand tiles
 #pragma unroll
-          for (int fm = 0; fm < FM; ++fm) {
+        for (int fm = 0; fm < FM; ++fm) {
+          if (is_qk) {
 #pragma unroll
             for (int hc = 0; hc < 2; ++hc) {
               float2 c[2][8];
 #pragma unroll
               for (int q = 0; q < 8; ++q) {
                 const int r = 8 * hc + q;
-                const int row = rbase + fm * 32 + 8 * (r >> 2) + (r & 3);
-                const int t = row % g.T;
+                const int t = (rbase + fm * 32 + 8 * (r >> 2) + (r & 3)) % g.T;
 #pragma unroll
                 for (int p = 0; p < 2; ++p) c[p][q] = g.cs[t * 64 + p * 32 + rl];
               }
 #pragma unroll
               for (int q = 0; q < 8; ++q) {
                 const int r = 8 * hc + q;
-                const int row = rbase + fm * 32 + 8 * (r >> 2) + (r & 3);
                 float ss = 0.f;
 #pragma unroll
                 for (int p = 0; p < 2; ++p) {
@@ -449,16 +456,46 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
                   ss += y1 * y1 + y2 * y2;
                 }
                 const float sc = rsqrtf(sum32(ss) * (1.0f / 128.0f) + g.eps);
-                if (!decltype(checked)::value || row < M) {
+                bf16* const sr = stg + (8 * (r >> 2) + 4 * hl + (r & 3)) * LQ + rl;
 #pragma unroll
-                  for (int fn = 0; fn < 4; ++fn)
-                    qk[(size_t)row * g.ldo + wcol0 + fn * 32 + rl] = (bf16)(acc[fm][fn][r] * sc);
-                }
+                for (int fn = 0; fn < 4; ++fn) sr[fn * 32] = (bf16)(acc[fm][fn][r] * sc);
               }
             }
+          } else {
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {  // rows 8j + 4hl + (0..3): four consecutive t
+                bf16x4 v4;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v4[i] = (bf16)acc[fm][fn][4 * j + i];
+                *(bf16x4*)(stg + (fn * 32 + rl) * LV + 8 * j + 4 * hl) = v4;
+              }
           }
-        };
-        if (m0 + BM <= M) rope_norm(std::false_type{}); else rope_norm(std::true_type{});
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          const int row0 = m0 + wm * TM + fm * 32;
+          if (live && is_qk) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {  // 32 rows x 16 chunks
+              const int idx = lane + 64 * k, lr = idx >> 4, ch = idx & 15;
+              if (row0 + lr < M)
+                *(bf16x8*)(qk + (size_t)(row0 + lr) * g.ldo + wcol0 + ch * 8) = *(const bf16x8*)(stg + lr * LQ + ch * 8);
+            }
+          } else if (live) {
+            // 32 consecutive rows are 32 consecutive positions of one sequence (T % 32 == 0)
+            const int bb = row0 / g.T, t0 = row0 - bb * g.T, gg = (wcol0 - g.nqk) / g.D;
+            bf16* const vb = vt + ((size_t)(bb * g.Hkv + gg) * g.D) * g.T + t0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {  // 128 d rows x 4 chunks of 8 positions
+              const int idx = lane + 64 * k, d = idx >> 2, ch = idx & 3;
+              if (row0 + ch * 8 < M)
+                *(bf16x8*)(vb + (size_t)d * g.T + ch * 8) = *(const bf16x8*)(stg + d * LV + ch * 8);
+            }
+          }
+          __builtin_amdgcn_wave_barrier();  // reads of this group precede the next group's writes
+        }
         return;
       }
     }
