@@ -4,8 +4,10 @@
 One step = one gpt_fwd_loss call over a batch of B*T synthetic tokens resident in HBM:
 embedding, 24 layers, lm_head, softcapped cross-entropy and the mean loss.  The timed region
 holds exactly K steps between device synchronisations; the JSON line reports whole-job
-tokens/s, the dominant kernel's roofline position (HIP events around that kernel's own
-launches of the same shape) and the CPU oracle on a bounded sample of the same workload.
+tokens/s, the dominant kernel's roofline position and the CPU oracle on a bounded sample of the
+same workload.  Per-kernel times come from HIP events that gpt_fwd_loss_timed has the
+dispatches themselves stamp (start of a launch's first kernel, end of its last) for every launch
+of one kind in the forward pass, over separate measurement steps outside the throughput region.
 
 Inputs are synthetic (seeded uniform token ids, N(0, 1/fan_in) weights) with the shapes of the
 pages' workload: 2,048-token packed rows and a 32,768-entry vocabulary.
@@ -39,18 +41,37 @@ def flops_per_token(p, windows):
     return p.n_layer * lin + 2 * C * V + att
 
 
-def measured_traffic(root):
-    """HBM bytes per launch of the MLP up-projection GEMM from the committed rocprofv3 PMC
-    record (profiles/gemm_mlp_up_traffic.json), or None if the GEMM source has changed since
-    the counters were taken (the record stores the source hash)."""
+KINDS = {  # gpt_kernel_kind -> name
+    1: "qkv", 2: "attention", 3: "attn_out", 4: "mlp_up", 5: "mlp_down", 6: "lm_head",
+}
+
+
+def flops_per_launch(p, windows):
+    """Algorithmic FLOPs of one launch of each kind (attention: the mean over the layers)."""
+    M, C, H, Hkv, D, F, V, T = (p.batch * p.seq_len, p.d_model, p.n_head, p.n_kv_head, p.head_dim,
+                                p.mlp_dim, p.vocab, p.seq_len)
+    att = []
+    for w in windows:
+        w = min(w, T)
+        att.append(4.0 * p.batch * H * D * (w * (w + 1) / 2 + (T - w) * w))
+    return {1: 2.0 * M * C * (H + 2 * Hkv) * D, 2: sum(att) / len(att), 3: 2.0 * M * H * D * C,
+            4: 2.0 * M * C * F, 5: 2.0 * M * F * C, 6: 2.0 * M * C * V}
+
+
+def measured_traffic(root, kind):
+    """HBM bytes per launch of kernel kind `kind` from the committed rocprofv3 PMC record
+    (profiles/gemm_traffic.json), or None if the record lacks that kind or the GEMM source has
+    changed since the counters were taken (the record stores the source hash)."""
     import hashlib
-    path = os.path.join(root, "profiles", "gemm_mlp_up_traffic.json")
+    path = os.path.join(root, "profiles", "gemm_traffic.json")
     try:
         rec = json.load(open(path))
         csrc = os.path.join(root, "decoder_only_transformer_layer_amd", "csrc")
         h = hashlib.sha256(open(os.path.join(csrc, "k_gemm.hip"), "rb").read()
                            + open(os.path.join(csrc, "common.h"), "rb").read()).hexdigest()
-        return rec["hbm_bytes_per_dispatch"] if h == rec["kernel_source_sha256"] else None
+        if h != rec["kernel_source_sha256"]:
+            return None
+        return rec["kinds"][KINDS[kind]]["hbm_bytes_per_dispatch"]
     except (OSError, KeyError, ValueError):
         return None
 
@@ -64,7 +85,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens of row 0 the CPU oracle evaluates (a causal prefix)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--kernel-reps", type=int, default=10)
+    ap.add_argument("--kernel-steps", type=int, default=3,
+                    help="measurement steps per kernel kind for the per-kernel event timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy (a known-size reference "
                          "for HBM traffic counters)")
@@ -130,26 +152,37 @@ def main():
     print(f"[bench] {args.steps} steps: {ms:.3f} ms/step (wall {wall / args.steps * 1e3:.3f}), "
           f"{tok_s:,.0f} tok/s, {fpt * tok_s / 1e12:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
-    # Dominant kernel: the MLP up-projection GEMM (largest FLOP share), timed alone with HIP
-    # events on the stream it is launched on, at the forward pass's shape and launch config.
-    M, C, F = B * T, p.d_model, p.mlp_dim
-    xa = torch.randn((M, C), device=dev).to(torch.bfloat16)
-    hb = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
-    w1 = model.t["w1"][0]
-    for _ in range(2):
-        gf.gpt_op_linear(gf.GPT_BF16, 1, xa, w1, M, F, C, hb, stream)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.kernel_reps):
-        gf.gpt_op_linear(gf.GPT_BF16, 1, xa, w1, M, F, C, hb, stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    k_ms = e0.elapsed_time(e1) / args.kernel_reps
-    k_flops = 2.0 * M * F * C
-    k_tflops = k_flops / (k_ms / 1e3) / 1e12
-    print(f"[bench] MLP-up GEMM {M}x{F}x{C}: {k_ms * 1e3:.1f} us, {k_tflops:.1f} TFLOP/s",
-          file=sys.stderr, flush=True)
-    del xa, hb
+    # Per-kernel time inside the forward pass: kernel start/end stamps on HIP events, for every
+    # launch of one kind, over separate measurement steps on the forward's own stream.
+    per_step = {1: p.n_layer, 2: p.n_layer, 3: p.n_layer, 4: p.n_layer, 5: p.n_layer, 6: 1}
+    fpl = flops_per_launch(p, windows)
+    kern = {}
+    for kind in KINDS:
+        n = per_step[kind] * args.kernel_steps
+        evb = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        eve = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in evb + eve:
+            e.record(stream)  # creates the underlying hipEvent_t
+        torch.cuda.synchronize()
+        for i in range(args.kernel_steps):  # one slice of event pairs per step
+            sl = slice(i * per_step[kind], (i + 1) * per_step[kind])
+            t = gf.launch_timing(kind, evb[sl], eve[sl])
+            st = model.forward(t_tok, t_tgt, loss, mean, None, stream, timing=t)
+            if st != gf.GPT_OK:
+                raise RuntimeError(gf.gpt_status_string(st))
+            assert t.recorded == per_step[kind]
+        torch.cuda.synchronize()
+        us = [b.elapsed_time(e) * 1e3 for b, e in zip(evb, eve)]
+        avg = sum(us) / len(us)
+        kern[KINDS[kind]] = {"kind": kind, "avg_us": round(avg, 2), "launches_per_step": per_step[kind],
+                             "us_per_step": round(avg * per_step[kind], 1),
+                             "tflops": round(fpl[kind] / (avg * 1e-6) / 1e12, 1)}
+    dom = max(kern.values(), key=lambda k: k["us_per_step"])
+    dk = dom["kind"]
+    k_tflops = fpl[dk] / (dom["avg_us"] * 1e-6) / 1e12
+    print("[bench] per-kernel (in the forward, HIP events): " + ", ".join(
+        f"{n} {k['avg_us']:.1f} us x{k['launches_per_step']} ({k['tflops']:.0f} TF/s)" for n, k in kern.items()),
+        file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -189,10 +222,11 @@ def main():
         "config": {"workload": f"nanochat {args.config} forward+loss", "batch": B, "seq_len": T,
                    "n_layer": p.n_layer, "d_model": p.d_model, "n_head": p.n_head, "vocab": p.vocab,
                    "flops_per_token": round(fpt), "windows": "SSSL short 1024, last layer full"},
-        "roofline": {"bound": "mfma", "kernel": "gemm_bf16 MLP up-projection (relu^2 epilogue)",
+        "roofline": {"bound": "mfma", "kernel": KINDS[dk],
                      "achieved": round(k_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(k_tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(ROOT),
-                     "avg_launch_us": round(k_ms * 1e3, 2), "flops_per_launch": k_flops},
+                     "frac": round(k_tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(ROOT, dk),
+                     "avg_launch_us": dom["avg_us"], "flops_per_launch": fpl[dk]},
+        "kernels": kern,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -22,9 +22,12 @@ LIB_PATH = os.path.join(_HERE, "libgptfwd.so")
 
 GPT_OK, GPT_E_INVALID_ARG, GPT_E_UNSUPPORTED, GPT_E_WORKSPACE, GPT_E_HIP, GPT_E_DEVICE_INPUT = 0, -1, -2, -3, -4, -5
 GPT_F32, GPT_BF16 = 0, 1
+(GPT_KERNEL_QKV, GPT_KERNEL_ATTENTION, GPT_KERNEL_ATTN_OUT, GPT_KERNEL_MLP_UP, GPT_KERNEL_MLP_DOWN,
+ GPT_KERNEL_LM_HEAD) = 1, 2, 3, 4, 5, 6
 
 EXPORTED = [
-    "gpt_validate", "gpt_workspace_bytes", "gpt_fwd_loss", "gpt_device_status", "gpt_status_string",
+    "gpt_validate", "gpt_workspace_bytes", "gpt_fwd_loss", "gpt_fwd_loss_timed", "gpt_device_status",
+    "gpt_status_string",
     "gpt_op_embed_norm", "gpt_op_mix_norm", "gpt_op_rope_table", "gpt_op_qk_rope_norm",
     "gpt_op_linear", "gpt_op_qkv", "gpt_op_attention", "gpt_op_lm_head_ce_workspace",
     "gpt_op_lm_head_ce",
@@ -52,6 +55,14 @@ class gpt_weights(ctypes.Structure):
     ]
 
 
+class gpt_launch_timing(ctypes.Structure):
+    _fields_ = [
+        ("kind", ctypes.c_int32), ("capacity", ctypes.c_int32),
+        ("begin", ctypes.POINTER(ctypes.c_void_p)), ("end", ctypes.POINTER(ctypes.c_void_p)),
+        ("recorded", ctypes.c_int32),
+    ]
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 
@@ -67,6 +78,8 @@ def _load() -> ctypes.CDLL:
         "gpt_validate": (I, [ctypes.POINTER(gpt_cfg)]),
         "gpt_workspace_bytes": (S, [ctypes.POINTER(gpt_cfg)]),
         "gpt_fwd_loss": (I, [ctypes.POINTER(gpt_cfg), ctypes.POINTER(gpt_weights), P, P, P, P, P, P, S, P]),
+        "gpt_fwd_loss_timed": (I, [ctypes.POINTER(gpt_cfg), ctypes.POINTER(gpt_weights), P, P, P, P, P, P, S, P,
+                                   ctypes.POINTER(gpt_launch_timing)]),
         "gpt_device_status": (I, [P, P]),
         "gpt_status_string": (ctypes.c_char_p, [I]),
         "gpt_op_embed_norm": (I, [I, P, P, P, P, P, P, P, I, I, I, F, P, P]),
@@ -166,6 +179,26 @@ def gpt_fwd_loss(cfg: gpt_cfg, weights: gpt_weights, tokens, targets, loss, mean
                                 workspace_bytes, _stream(stream))
 
 
+def gpt_fwd_loss_timed(cfg: gpt_cfg, weights: gpt_weights, tokens, targets, loss, mean_loss, logits,
+                       workspace, workspace_bytes: int, stream, timing: Optional[gpt_launch_timing]) -> int:
+    return _load().gpt_fwd_loss_timed(ctypes.byref(cfg), ctypes.byref(weights), _ptr(tokens), _ptr(targets),
+                                      _ptr(loss), _ptr(mean_loss), _ptr(logits), _ptr(workspace),
+                                      workspace_bytes, _stream(stream),
+                                      None if timing is None else ctypes.byref(timing))
+
+
+def launch_timing(kind: int, begin_events, end_events) -> gpt_launch_timing:
+    """A gpt_launch_timing over torch.cuda.Event pairs (each recorded once beforehand, so that the
+    underlying hipEvent_t exists)."""
+    n = len(begin_events)
+    b = (ctypes.c_void_p * n)(*[e.cuda_event for e in begin_events])
+    e = (ctypes.c_void_p * n)(*[e.cuda_event for e in end_events])
+    t = gpt_launch_timing(kind, n, ctypes.cast(b, ctypes.POINTER(ctypes.c_void_p)),
+                          ctypes.cast(e, ctypes.POINTER(ctypes.c_void_p)), 0)
+    t._keep = (b, e)  # the arrays must outlive the call
+    return t
+
+
 def gpt_device_status(workspace, stream=None) -> int:
     return _load().gpt_device_status(_ptr(workspace), _stream(stream))
 
@@ -260,8 +293,13 @@ class DeviceModel:
         off = (-self.ws.data_ptr()) % 256
         self.ws_ptr = self.ws.data_ptr() + off
 
-    def forward(self, tokens, targets=None, loss=None, mean=None, logits=None, stream=None) -> int:
-        """Enqueue gpt_fwd_loss on device tensors (outputs preallocated by the caller)."""
+    def forward(self, tokens, targets=None, loss=None, mean=None, logits=None, stream=None,
+                timing: Optional[gpt_launch_timing] = None) -> int:
+        """Enqueue gpt_fwd_loss (gpt_fwd_loss_timed if `timing` is given) on device tensors
+        (outputs preallocated by the caller)."""
+        if timing is not None:
+            return gpt_fwd_loss_timed(self.cfg, self.w, tokens, targets, loss, mean, logits,
+                                      self.ws_ptr, self.ws_bytes, stream, timing)
         return gpt_fwd_loss(self.cfg, self.w, tokens, targets, loss, mean, logits, self.ws_ptr,
                             self.ws_bytes, stream)
 

@@ -99,19 +99,42 @@ hipError_t gemm(bool bf, Epi e, const GemmArgs& g, hipStream_t s) {
   return bf ? launch_gemm_bf16(e, g, s) : launch_gemm_f32(e, g, s);
 }
 
+// Launch timing (gpt_fwd_loss_timed): pair `recorded` of the caller's events takes the start
+// of the first and the end of the last kernel enqueued at one launch site of the requested kind
+// (hipExtLaunchKernelGGL stamps them from the dispatch itself), while pairs remain.
+struct Timer {
+  gpt_launch_timing* t;
+  bool on(int kind) const { return t && t->kind == kind && t->recorded < t->capacity; }
+  void begin(int kind) const {
+    if (on(kind)) launch_events = {(hipEvent_t)t->begin[t->recorded], (hipEvent_t)t->end[t->recorded]};
+  }
+  void end(int kind) const {
+    if (on(kind)) { launch_events = {}; ++t->recorded; }
+  }
+};
+// Enqueue `call` (a hipError_t expression) inside the timer's window; the window is closed
+// before an error returns.
+#define TIMED(tm, kind, call)                        \
+  do {                                               \
+    (tm).begin(kind);                                \
+    const hipError_t timed_err_ = (call);            \
+    (tm).end(kind);                                  \
+    if (timed_err_ != hipSuccess) return GPT_E_HIP;  \
+  } while (0)
+
 // lm_head + softcap + CE over M rows into loss/mean (targets may be NULL: logits only).  If
 // rs_ssp is set, xf is the un-normalised stream and the GEMM applies the final RMSNorm as a row
 // scale from those per-slice sums of squares.
 gpt_status lm_head_ce(bool bf, const void* xf, const void* wu, const int32_t* targets,
                       const int32_t* tokens, int M, int C, int V, float cap, float* loss,
                       float* mean, float* logits, float* partial, float* tgt, int nnb,
-                      unsigned* flags, hipStream_t s, const float* rs_ssp = nullptr,
+                      unsigned* flags, hipStream_t s, const Timer& tm, const float* rs_ssp = nullptr,
                       float eps = 0.f) {
   GemmArgs g = gemm_args(xf, C, wu, V, C, M, nullptr, 0);
   if (rs_ssp) { g.rs_ssp = rs_ssp; g.rs_n = C / gemm_resid_slice_cols(C); g.rs_c = (float)C; g.eps = eps; }
   g.targets = targets; g.partial = partial; g.tgt_logit = tgt; g.logits = logits;
   g.nnb = nnb; g.cap = cap;
-  CK(gemm(bf, EPI_CE, g, s));
+  TIMED(tm, GPT_KERNEL_LM_HEAD, gemm(bf, EPI_CE, g, s));
   if (logits) CK(launch_softcap(logits, (size_t)M * V, cap, s));
   if (targets) {
     CK(launch_ce_finalize(partial, nnb, tgt, targets, tokens, M, V, cap, loss, flags, s));
@@ -134,6 +157,20 @@ size_t gpt_workspace_bytes(const gpt_cfg* cfg) {
 gpt_status gpt_fwd_loss(const gpt_cfg* c, const gpt_weights* w, const int32_t* tokens,
                         const int32_t* targets, float* loss, float* mean_loss, float* logits,
                         void* workspace, size_t workspace_bytes, void* stream) {
+  return gpt_fwd_loss_timed(c, w, tokens, targets, loss, mean_loss, logits, workspace,
+                            workspace_bytes, stream, nullptr);
+}
+
+gpt_status gpt_fwd_loss_timed(const gpt_cfg* c, const gpt_weights* w, const int32_t* tokens,
+                              const int32_t* targets, float* loss, float* mean_loss,
+                              float* logits, void* workspace, size_t workspace_bytes,
+                              void* stream, gpt_launch_timing* timing) {
+  if (timing) {
+    if (timing->kind < GPT_KERNEL_QKV || timing->kind > GPT_KERNEL_LM_HEAD || timing->capacity < 0 ||
+        (timing->capacity > 0 && (!timing->begin || !timing->end)))
+      return GPT_E_INVALID_ARG;
+    timing->recorded = 0;
+  }
   gpt_status st = validate(c);
   if (st != GPT_OK) return st;
   if (!w || !tokens) return GPT_E_INVALID_ARG;
@@ -159,6 +196,7 @@ gpt_status gpt_fwd_loss(const gpt_cfg* c, const gpt_weights* w, const int32_t* t
   if (!workspace || workspace_bytes < L.total || !aligned(workspace, ALIGN)) return GPT_E_WORKSPACE;
 
   hipStream_t s = (hipStream_t)stream;
+  const Timer tm{timing};
   const bool bf = c->dtype == GPT_BF16;
   const int B = c->batch, T = c->seq_len, M = B * T, C = c->d_model, H = c->n_head;
   const int Hkv = c->n_kv_head, D = c->head_dim, F = c->mlp_dim, V = c->vocab;
@@ -187,7 +225,7 @@ gpt_status gpt_fwd_loss(const gpt_cfg* c, const gpt_weights* w, const int32_t* t
   if (bf) {
     // bf16 path: every RMSNorm after the first is applied as a row scale inside the GEMM that
     // consumes it (RMSNorm(x) W^T = (x W^T) / rms(x)).  The residual epilogues keep x in fp32,
-    // apply the next layer's x0 mix, and emit bf16(x) plus per-64-column sums of squares.
+    // apply the next layer's x0 mix, and emit bf16(x) plus per-slice sums of squares.
     bf16_t* xb = (bf16_t*)xn;
     for (int l = 0; l < c->n_layer; ++l) {
       GemmArgs g = gemm_args(xn, C, w->wq[l], nqkv, C, M, qk, nqk);
@@ -196,26 +234,26 @@ gpt_status gpt_fwd_loss(const gpt_cfg* c, const gpt_weights* w, const int32_t* t
       const bool fused = D == 128;
       if (fused) g.cs = cs;
       if (l > 0) { g.rs_ssp = ssp; g.rs_n = nsl; g.rs_c = (float)C; }  // layer 0 reads normed xn
-      CK(launch_gemm_bf16(EPI_QKV, g, s));
+      TIMED(tm, GPT_KERNEL_QKV, launch_gemm_bf16(EPI_QKV, g, s));
       if (!fused) CK(launch_qk_rope_norm(qk, true, nqk, cs, M, T, H + Hkv, D, eps, s));
       const int win = c->window[l] < T ? c->window[l] : T;
-      CK(launch_attn_bf16(qk, vt, o, B, T, H, Hkv, D, win, c->attn_scale, s));
+      TIMED(tm, GPT_KERNEL_ATTENTION, launch_attn_bf16(qk, vt, o, B, T, H, Hkv, D, win, c->attn_scale, s));
       // x += o W_O^T, then bf16(x) and sums of squares for the MLP's norm
       GemmArgs go = gemm_args(o, H * D, w->wo[l], C, H * D, M, x, C);
       go.xb = xb; go.ssp = ssp; go.ssp_n = nsl;
-      CK(launch_gemm_bf16(EPI_RESID, go, s));
+      TIMED(tm, GPT_KERNEL_ATTN_OUT, launch_gemm_bf16(EPI_RESID, go, s));
       // h = relu(RMSNorm(x) W_1^T)^2
       GemmArgs gu = gemm_args(xb, C, w->w1[l], F, C, M, hbuf, F);
       gu.rs_ssp = ssp; gu.rs_n = nsl; gu.rs_c = (float)C; gu.eps = eps;
-      CK(launch_gemm_bf16(EPI_RELU2, gu, s));
+      TIMED(tm, GPT_KERNEL_MLP_UP, launch_gemm_bf16(EPI_RELU2, gu, s));
       // x += h W_2^T, then the next layer's x0 mix (if any), bf16(x) and sums of squares
       GemmArgs gd = gemm_args(hbuf, F, w->w2[l], C, F, M, x, C);
       gd.xb = xb; gd.ssp = ssp; gd.ssp_n = nsl;
       if (l + 1 < c->n_layer) { gd.x0 = x0; gd.lam = w->resid_lambda; gd.mu = w->x0_lambda; gd.layer = l + 1; }
-      CK(launch_gemm_bf16(EPI_RESID, gd, s));
+      TIMED(tm, GPT_KERNEL_MLP_DOWN, launch_gemm_bf16(EPI_RESID, gd, s));
     }
     return lm_head_ce(bf, xb, w->lm_head, targets, tokens, M, C, V, c->softcap, loss, mean_loss,
-                      logits, partial, tgt, L.nnb, flags, s, ssp, eps);
+                      logits, partial, tgt, L.nnb, flags, s, tm, ssp, eps);
   }
   for (int l = 0; l < c->n_layer; ++l) {
     // q, k, v projections (one GEMM over the three weight segments)
@@ -238,7 +276,7 @@ gpt_status gpt_fwd_loss(const gpt_cfg* c, const gpt_weights* w, const int32_t* t
     CK(launch_mix_norm(x, x0, w->resid_lambda, w->x0_lambda, l + 1, more, xn, false, M, C, eps, s));
   }
   return lm_head_ce(bf, xn, w->lm_head, targets, tokens, M, C, V, c->softcap, loss, mean_loss,
-                    logits, partial, tgt, L.nnb, flags, s);
+                    logits, partial, tgt, L.nnb, flags, s, tm);
 }
 
 gpt_status gpt_device_status(void* workspace, void* stream) {
@@ -374,7 +412,7 @@ gpt_status gpt_op_lm_head_ce(int32_t dtype, const void* xf, const void* wu, cons
   hipStream_t s = (hipStream_t)stream;
   CK(launch_clear_u32(flags, 16, s));
   return lm_head_ce(bf, xf, wu, targets, tokens, M, C, V, cap, loss, mean, logits, partial, tgt, nnb,
-                    flags, s);
+                    flags, s, Timer{nullptr});
 }
 
 }  // extern "C"

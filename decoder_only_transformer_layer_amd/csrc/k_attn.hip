@@ -5,16 +5,15 @@
 // output = weighted sum of values.  q and k arrive already rotated (RoPE) and normalised
 // (QK-norm); the logit is scale * <q, k>.
 //
-// bf16 kernel (gfx950, head_dim 128 or 64).  A block owns 128 queries of one (batch, head)
-// and four wavefronts, 32 queries each.  Key/value tiles of 64 keys are staged in LDS
-// (double-buffered) and only tiles that intersect the block's window band are visited.
-// Each wavefront computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 so that every lane holds
-// one query's logits (query = lane % 32): the softmax max needs one exchange with lane ^ 32
-// and the running sum none.  K rows are stored in LDS with bits 2 and 3 of the key index
-// swapped, which makes each lane's S^T accumulators hold 8 consecutive keys per 16-key step;
-// packed to bf16 they are directly the B operand of O^T += V^T P^T, whose A operand is read
-// from the transposed value tile [D][64 keys].  Values arrive transposed ([B][Hkv][D][T]) from
-// the QKV projection's epilogue.
+// bf16 kernel (gfx950, head_dim 128 or 64).  A block owns 256 queries of one (batch, head)
+// and eight wavefronts (two per SIMD), 32 queries each; only key tiles (64 keys) that
+// intersect the block's window band are visited.  Each wavefront computes S^T = K Q^T with
+// v_mfma_f32_32x32x16_bf16 so that every lane holds one query's logits (query = lane % 32):
+// the softmax max needs one exchange with lane ^ 32 and the running sum none.  K rows are
+// stored in LDS with bits 2 and 3 of the key index swapped, which makes each lane's S^T
+// accumulators hold 8 consecutive keys per 16-key step; packed to bf16 they are directly the
+// B operand of O^T += V^T P^T, whose A operand is read from the transposed value tile
+// [D][64 keys].  Values arrive transposed ([B][Hkv][D][T]) from the QKV projection's epilogue.
 #include <math.h>
 
 #include "common.h"
@@ -23,11 +22,7 @@
 namespace gptk {
 namespace {
 
-#ifndef ATTN_V2
-#define ATTN_V2 1
-#endif
-
-constexpr int BQ = 128, BKV = 64;
+constexpr int BKV = 64;
 
 // s_waitcnt immediate: at most n vector-memory operations outstanding (gfx9 encoding).
 constexpr int vmcnt_le(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
@@ -39,175 +34,8 @@ __device__ __forceinline__ int swap23(int k) {
 template <int D> __device__ __forceinline__ int swzk(int r) { return (D == 128) ? (r & 15) : (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int swzv(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16* __restrict__ qk,
-                                                           const bf16* __restrict__ vt,
-                                                           bf16* __restrict__ o, int T, int H,
-                                                           int Hkv, int window, float scale_log2) {
-  constexpr int KCH = D / 8;          // 16-byte chunks per K row
-  constexpr int DT = D / 32;          // 32-row tiles of O^T
-  constexpr int KS = D / 16;          // k-steps of S^T
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][BKV * D];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][D * BKV];
-
-  const int nqt = (T + BQ - 1) / BQ;
-  const int qt = nqt - 1 - (int)blockIdx.x;  // longest rows first
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int g = (h * Hkv) / H;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int hl = lane >> 5, rl = lane & 31;
-  const int ldqk = (H + Hkv) * D;
-  const int qb = qt * BQ;
-  const int qw = qb + wid * 32;
-  const int myq = qw + rl;
-
-  // Q fragments: B operand of S^T (column = query, k = head dims).
-  bf16x8 qf[KS];
-  {
-    const bf16* qp = qk + (size_t)(b * T + min(myq, T - 1)) * ldqk + h * D + 8 * hl;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = *(const bf16x8*)(qp + 16 * s);
-  }
-
-  const int kmin = max(0, qb - window + 1);
-  const int kmax = min(T - 1, qb + BQ - 1);
-  const int t0 = kmin / BKV, t1 = kmax / BKV;
-
-  // Global -> register staging for one K tile and one V^T tile.
-  constexpr int KC_PER = BKV * KCH / 256;  // K chunks per thread
-  constexpr int VC_PER = D * 8 / 256;      // V^T chunks per thread
-  u32x4 rk[KC_PER], rv[VC_PER];
-  const bf16* kbase = qk + (size_t)(b * T) * ldqk + (H + g) * D;
-  const bf16* vbase = vt + (size_t)(b * Hkv + g) * D * T;
-  auto gload = [&](int j0) {
-#pragma unroll
-    for (int i = 0; i < KC_PER; ++i) {
-      const int c = tid + i * 256, r = c / KCH, kc = c % KCH;
-      rk[i] = *(const u32x4*)(kbase + (size_t)min(j0 + r, T - 1) * ldqk + kc * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < VC_PER; ++i) {
-      const int c = tid + i * 256, r = c >> 3, kc = c & 7;
-      rv[i] = *(const u32x4*)(vbase + (size_t)r * T + j0 + kc * 8);  // T % 64 == 0
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KC_PER; ++i) {
-      const int c = tid + i * 256, r = c / KCH, kc = c % KCH;
-      const int pr = swap23(r);
-      *(u32x4*)(&Ks[buf][pr * D + ((kc ^ swzk<D>(pr)) << 3)]) = rk[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VC_PER; ++i) {
-      const int c = tid + i * 256, r = c >> 3, kc = c & 7;
-      *(u32x4*)(&Vs[buf][r * BKV + ((kc ^ swzv(r)) << 3)]) = rv[i];
-    }
-  };
-
-  f32x16 ot[DT];
-#pragma unroll
-  for (int d = 0; d < DT; ++d)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) ot[d][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-
-  gload(t0 * BKV);
-  sstore(0);
-  if (t0 + 1 <= t1) gload((t0 + 1) * BKV);
-  __syncthreads();
-
-  for (int t = t0; t <= t1; ++t) {
-    const int buf = (t - t0) & 1;
-    const int j0 = t * BKV;
-    // Does this tile intersect the wave's band [qw - w + 1, qw + 31]?
-    const bool active = (j0 <= qw + 31) && (j0 + BKV - 1 >= qw - window + 1) && (qw < T);
-    if (active) {
-      f32x16 st[2];
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st[rt][r] = 0.f;
-        const int kr = rt * 32 + rl;
-        const bf16* kp = &Ks[buf][kr * D];
-        const int sw = swzk<D>(kr);
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const bf16x8 a = *(const bf16x8*)(kp + (((2 * s + hl) ^ sw) << 3));
-          st[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], st[rt], 0, 0, 0);
-        }
-      }
-      // st[rt][r] is the logit of key j0 + rt*32 + 8*hl + 4*((r>>2)&1) + 16*(r>>3) + (r&3)
-      // (row 8*(r/4) + 4*hl + r%4 of the MFMA, mapped through swap23) for query myq.
-      const bool full = (j0 + BKV - 1 <= qw) && (qw + 31 - j0 < window);
-      float mx = -INFINITY;
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float sv = st[rt][r] * scale_log2;
-          if (!full) {
-            const int key = j0 + rt * 32 + 16 * (r >> 3) + 8 * hl + 4 * ((r >> 2) & 1) + (r & 3);
-            if (key > myq || myq - key >= window) sv = -INFINITY;
-          }
-          st[rt][r] = sv;
-          mx = fmaxf(mx, sv);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float corr = exp2_fast(m_run - m_use);
-      m_run = m_new;
-      l_run *= corr;
-#pragma unroll
-      for (int d = 0; d < DT; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) ot[d][r] *= corr;
-      bf16x8 pf[4];
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = exp2_fast(st[rt][r] - m_use);
-          l_run += p;
-          pf[rt * 2 + (r >> 3)][r & 7] = (bf16)p;
-        }
-      // O^T[d][q] += sum_key V^T[d][key] P^T[key][q]; k-step s covers keys 16s..16s+15.
-#pragma unroll
-      for (int d = 0; d < DT; ++d) {
-        const int vr = d * 32 + rl;
-        const bf16* vp = &Vs[buf][vr * BKV];
-        const int sw = swzv(vr);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8 a = *(const bf16x8*)(vp + (((2 * s + hl) ^ sw) << 3));
-          ot[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[s], ot[d], 0, 0, 0);
-        }
-      }
-    }
-    if (t + 1 <= t1) sstore(buf ^ 1);
-    if (t + 2 <= t1) gload((t + 2) * BKV);
-    __syncthreads();
-  }
-
-  const float l = l_run + __shfl_xor(l_run, 32, 64);
-  if (myq < T) {
-    const float inv = 1.0f / l;
-    bf16* op = o + (size_t)(b * T + myq) * (H * D) + h * D;
-#pragma unroll
-    for (int d = 0; d < DT; ++d)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bf16x4 v4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v4[i] = (bf16)(ot[d][4 * j + i] * inv);
-        *(bf16x4*)(op + d * 32 + 8 * j + 4 * hl) = v4;
-      }
-  }
-}
-
-// Version 2: 256 queries per block, 8 wavefronts (two per SIMD, so one wavefront's softmax
-// VALU work overlaps the other's MFMAs), K and V^T tiles streamed global -> LDS with
+// 256 queries per block, 8 wavefronts (two per SIMD, so one wavefront's softmax VALU work
+// overlaps the other's MFMAs), K and V^T tiles streamed global -> LDS with
 // buffer_load ... lds into a 3-stage ring, the logit scale folded into one FMA before exp2, and
 // lazy rescaling: a row's reference maximum moves only when a new logit exceeds it by more than
 // 2^8 (in log2 units).  Numerator and denominator share the reference, so the result is exact;
@@ -215,7 +43,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16* __restric
 constexpr int NW2 = 8, BQ2 = NW2 * 32, STG = 3;
 
 template <int D>
-__global__ __launch_bounds__(NW2 * 64, 1) void attn_bf16_v2_kernel(const bf16* __restrict__ qk,
+__global__ __launch_bounds__(NW2 * 64, 1) void attn_bf16_kernel(const bf16* __restrict__ qk,
                                                                   const bf16* __restrict__ vt,
                                                                   bf16* __restrict__ o, int B, int T,
                                                                   int H, int Hkv, int window, float c) {
@@ -458,31 +286,21 @@ hipError_t launch_attn_bf16(const void* qk, const void* vt, void* o, int B, int 
                             int D, int window, float scale, hipStream_t s) {
   if (T % BKV) return hipErrorInvalidValue;
   const float sl2 = scale * GPT_LOG2E;
-#if ATTN_V2
   const dim3 grid(((T + BQ2 - 1) / BQ2) * H * B);
   if (D == 128)
-    attn_bf16_v2_kernel<128><<<grid, NW2 * 64, 0, s>>>((const bf16*)qk, (const bf16*)vt, (bf16*)o, B, T, H, Hkv, window, sl2);
+    GPTK_LAUNCH(attn_bf16_kernel<128>, grid, NW2 * 64, s, (const bf16*)qk, (const bf16*)vt, (bf16*)o, B, T, H, Hkv, window, sl2);
   else if (D == 64)
-    attn_bf16_v2_kernel<64><<<grid, NW2 * 64, 0, s>>>((const bf16*)qk, (const bf16*)vt, (bf16*)o, B, T, H, Hkv, window, sl2);
+    GPTK_LAUNCH(attn_bf16_kernel<64>, grid, NW2 * 64, s, (const bf16*)qk, (const bf16*)vt, (bf16*)o, B, T, H, Hkv, window, sl2);
   else
     return hipErrorInvalidValue;
-#else
-  const dim3 grid((T + BQ - 1) / BQ, H, B);
-  if (D == 128)
-    attn_bf16_kernel<128><<<grid, 256, 0, s>>>((const bf16*)qk, (const bf16*)vt, (bf16*)o, T, H, Hkv, window, sl2);
-  else if (D == 64)
-    attn_bf16_kernel<64><<<grid, 256, 0, s>>>((const bf16*)qk, (const bf16*)vt, (bf16*)o, T, H, Hkv, window, sl2);
-  else
-    return hipErrorInvalidValue;
-#endif
   return hipGetLastError();
 }
 
 hipError_t launch_attn_f32(const float* qkv, float* o, int B, int T, int H, int Hkv, int D,
                            int window, float scale, hipStream_t s) {
   const dim3 grid((T + 63) / 64, H, B);
-  if (D == 128) attn_f32_kernel<128><<<grid, 64, 0, s>>>(qkv, o, T, H, Hkv, window, scale);
-  else if (D == 64) attn_f32_kernel<64><<<grid, 64, 0, s>>>(qkv, o, T, H, Hkv, window, scale);
+  if (D == 128) GPTK_LAUNCH(attn_f32_kernel<128>, grid, 64, s, qkv, o, T, H, Hkv, window, scale);
+  else if (D == 64) GPTK_LAUNCH(attn_f32_kernel<64>, grid, 64, s, qkv, o, T, H, Hkv, window, scale);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

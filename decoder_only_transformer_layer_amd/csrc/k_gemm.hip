@@ -590,16 +590,16 @@ hipError_t run_bf16(Epi epi, const GemmArgs& a, hipStream_t s) {
   const int grid = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   constexpr int NT = WM * WN * 64;
   switch (epi) {
-    case EPI_STORE: gemm_bf16_kernel<BM, BN, WM, WN, EPI_STORE><<<grid, NT, 0, s>>>(a); break;
-    case EPI_RELU2: gemm_bf16_kernel<BM, BN, WM, WN, EPI_RELU2><<<grid, NT, 0, s>>>(a); break;
+    case EPI_STORE: GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_STORE>), grid, NT, s, a); break;
+    case EPI_RELU2: GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_RELU2>), grid, NT, s, a); break;
     case EPI_RESID:
       if constexpr (WM * WN * 32 * (BN / WN + 4) * 4 > 2 * (BM + BN) * BK * 2) return hipErrorInvalidValue;  // staging would not fit
-      else if (a.xb == nullptr) gemm_bf16_kernel<BM, BN, WM, WN, EPI_RESID><<<grid, NT, 0, s>>>(a);
-      else if (a.lam == nullptr) gemm_bf16_kernel<BM, BN, WM, WN, EPI_RESID_PROD><<<grid, NT, 0, s>>>(a);
-      else gemm_bf16_kernel<BM, BN, WM, WN, EPI_RESID_MIX><<<grid, NT, 0, s>>>(a);
+      else if (a.xb == nullptr) GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_RESID>), grid, NT, s, a);
+      else if (a.lam == nullptr) GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_RESID_PROD>), grid, NT, s, a);
+      else GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_RESID_MIX>), grid, NT, s, a);
       break;
-    case EPI_QKV: gemm_bf16_kernel<BM, BN, WM, WN, EPI_QKV><<<grid, NT, 0, s>>>(a); break;
-    case EPI_CE: gemm_bf16_kernel<BM, BN, WM, WN, EPI_CE><<<grid, NT, 0, s>>>(a); break;
+    case EPI_QKV: GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_QKV>), grid, NT, s, a); break;
+    case EPI_CE: GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_CE>), grid, NT, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -774,6 +774,8 @@ bool use_wide(Epi epi, const GemmArgs& a) {
 
 }  // namespace
 
+thread_local LaunchEvents launch_events;
+
 int gemm_bf16_ce_blocks(int N) { return (N + 255) / 256; }
 
 int gemm_resid_slice_cols(int N) { return N % 384 == 0 ? 96 : 64; }
@@ -812,10 +814,10 @@ hipError_t launch_gemm_f32(Epi epi, const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0 || a.K <= 0) return hipErrorInvalidValue;
   const int grid = ((a.M + FT - 1) / FT) * ((a.N + FT - 1) / FT);
   switch (epi) {
-    case EPI_STORE: case EPI_QKV: gemm_f32_kernel<EPI_STORE><<<grid, 256, 0, s>>>(a); break;
-    case EPI_RELU2: gemm_f32_kernel<EPI_RELU2><<<grid, 256, 0, s>>>(a); break;
-    case EPI_RESID: gemm_f32_kernel<EPI_RESID><<<grid, 256, 0, s>>>(a); break;
-    case EPI_CE: gemm_f32_kernel<EPI_CE><<<grid, 256, 0, s>>>(a); break;
+    case EPI_STORE: case EPI_QKV: GPTK_LAUNCH((gemm_f32_kernel<EPI_STORE>), grid, 256, s, a); break;
+    case EPI_RELU2: GPTK_LAUNCH((gemm_f32_kernel<EPI_RELU2>), grid, 256, s, a); break;
+    case EPI_RESID: GPTK_LAUNCH((gemm_f32_kernel<EPI_RESID>), grid, 256, s, a); break;
+    case EPI_CE: GPTK_LAUNCH((gemm_f32_kernel<EPI_CE>), grid, 256, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -1,6 +1,7 @@
 // Host-side launchers of the gfx950 kernels (C++ linkage, internal to libgptfwd).
 // Every launcher enqueues on `stream` and returns hipGetLastError() of the launch.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -8,6 +9,26 @@
 namespace gptk {
 
 typedef __bf16 bf16_t;
+
+// Measurement hook: while `stop` is set, every kernel the GEMM and attention launchers enqueue
+// goes through hipExtLaunchKernelGGL, which stamps `start` with the start of the first such
+// kernel (then `start` is cleared) and `stop` with the end of each, i.e. of the last.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+extern thread_local LaunchEvents launch_events;
+
+#define GPTK_LAUNCH(kernel, grid, block, stream, ...)                                        \
+  do {                                                                                     \
+    if (::gptk::launch_events.stop) {                                                      \
+      hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(block), 0, stream,                    \
+                            ::gptk::launch_events.start, ::gptk::launch_events.stop, 0,      \
+                            __VA_ARGS__);                                                  \
+      ::gptk::launch_events.start = nullptr;                                               \
+    } else {                                                                               \
+      hipLaunchKernelGGL(kernel, dim3(grid), dim3(block), 0, stream, __VA_ARGS__);         \
+    }                                                                                      \
+  } while (0)
 
 // ---- row kernels (k_rows.hip) ------------------------------------------------------------
 // cos/sin table cs[t * (D/2) + j] = (cos phi, sin phi), phi = t * base^(-2j/D), in fp64 then fp32.

@@ -115,6 +115,46 @@ gpt_status gpt_fwd_loss(const gpt_cfg *cfg, const gpt_weights *w, const int32_t 
                         const int32_t *targets, float *loss, float *mean_loss, float *logits,
                         void *workspace, size_t workspace_bytes, void *stream);
 
+/* Measurement hook.  Kinds of launch in the forward pass, one per layer unless noted:
+ * GPT_KERNEL_QKV          q/k/v projection with its RoPE + QK-norm epilogue (bf16: one or two
+ *                         GEMM kernels)
+ * GPT_KERNEL_ATTENTION    windowed causal attention
+ * GPT_KERNEL_ATTN_OUT     attention output projection + residual add
+ * GPT_KERNEL_MLP_UP       MLP up-projection with the ReLU^2 epilogue
+ * GPT_KERNEL_MLP_DOWN     MLP down-projection + residual add (+ the next layer's x0 mix)
+ * GPT_KERNEL_LM_HEAD      lm_head GEMM with the softcapped cross-entropy epilogue (once)
+ * The fp32 path times only GPT_KERNEL_LM_HEAD. */
+typedef enum {
+  GPT_KERNEL_QKV = 1,
+  GPT_KERNEL_ATTENTION = 2,
+  GPT_KERNEL_ATTN_OUT = 3,
+  GPT_KERNEL_MLP_UP = 4,
+  GPT_KERNEL_MLP_DOWN = 5,
+  GPT_KERNEL_LM_HEAD = 6
+} gpt_kernel_kind;
+
+/* Caller-owned timing record: begin[i] and end[i] are HIP events (hipEvent_t, created by the
+ * caller with timing enabled) that take the start time of the first kernel and the end time of
+ * the last kernel of the i-th launch of `kind` (in launch order, while i < capacity), stamped
+ * by the dispatches themselves (hipExtLaunchKernelGGL).  `recorded` (out) counts the pairs
+ * used by the call.  The library keeps no pointer to the record after returning. */
+typedef struct {
+  int32_t kind;          /* gpt_kernel_kind */
+  int32_t capacity;      /* pairs available in begin/end (>= 0) */
+  void *const *begin;    /* host [capacity] hipEvent_t */
+  void *const *end;      /* host [capacity] hipEvent_t */
+  int32_t recorded;      /* out */
+} gpt_launch_timing;
+
+/* gpt_fwd_loss, plus kernel timestamps for the launches that `timing` selects (NULL: exactly
+ * gpt_fwd_loss).  Meant for measurement runs: the timed launches take a different (slower to
+ * enqueue) host path.  GPT_E_INVALID_ARG for an unknown kind, a negative capacity or NULL event
+ * arrays with capacity > 0. */
+gpt_status gpt_fwd_loss_timed(const gpt_cfg *cfg, const gpt_weights *w, const int32_t *tokens,
+                              const int32_t *targets, float *loss, float *mean_loss,
+                              float *logits, void *workspace, size_t workspace_bytes,
+                              void *stream, gpt_launch_timing *timing);
+
 /* Synchronise `stream`, then report whether any gpt_fwd_loss call that used this workspace saw
  * an out-of-range token or target id since the workspace's last call began (GPT_OK or
  * GPT_E_DEVICE_INPUT; GPT_E_HIP if synchronising failed). */

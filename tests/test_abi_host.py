@@ -122,6 +122,27 @@ def test_fwd_loss_argument_errors_return_before_launch(lib):
     assert call(cfg=bad) == gf.GPT_E_UNSUPPORTED
 
 
+def test_fwd_loss_timed_argument_errors(lib):
+    """The timing record is checked before anything else; a bad one never reaches a launch."""
+    c = _cfg()
+    w = _weights(c.n_layer)
+    need = gf.gpt_workspace_bytes(c)
+    F = 0x200000
+    ev = (ctypes.c_void_p * 2)(F, F)
+    evp = ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p))
+
+    def call(t, ws=0x10000000):
+        return lib.gpt_fwd_loss_timed(ctypes.byref(c), ctypes.byref(w), F, F, F, F, None, ws, need,
+                                      None, ctypes.byref(t))
+    assert call(gf.gpt_launch_timing(0, 2, evp, evp, 0)) == gf.GPT_E_INVALID_ARG      # no such kind
+    assert call(gf.gpt_launch_timing(7, 2, evp, evp, 0)) == gf.GPT_E_INVALID_ARG
+    assert call(gf.gpt_launch_timing(gf.GPT_KERNEL_MLP_UP, -1, evp, evp, 0)) == gf.GPT_E_INVALID_ARG
+    assert call(gf.gpt_launch_timing(gf.GPT_KERNEL_MLP_UP, 2, None, evp, 0)) == gf.GPT_E_INVALID_ARG
+    t = gf.gpt_launch_timing(gf.GPT_KERNEL_MLP_UP, 2, evp, evp, 5)
+    assert call(t, ws=None) == gf.GPT_E_WORKSPACE                  # then the usual checks
+    assert t.recorded == 0
+
+
 def test_op_argument_errors(lib):
     F = 0x200000
     assert lib.gpt_op_linear(1, 0, None, F, 10, 10, 64, F, None) == gf.GPT_E_INVALID_ARG

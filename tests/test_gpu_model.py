@@ -172,3 +172,31 @@ def test_d24_bf16_bench_config(d24):
     err = np.abs(got["losses"][7, :512] - ref7["losses"][0])
     print(f"  row 7 prefix: max |err| {err.max():.3e}")
     assert err.max() <= 2e-2
+
+
+def test_launch_timing_hook_bf16():
+    """gpt_fwd_loss_timed stamps one event pair per launch of the chosen kind and leaves the
+    results bit-identical to gpt_fwd_loss."""
+    torch = torch_mod()
+    p = _ragged_preset(seed=17)
+    w, tok, tgt = gptdata.make_inputs(p)
+    m = gf.DeviceModel(p, w)
+    t_tok, t_tgt = torch.from_numpy(tok).cuda(), torch.from_numpy(tgt).cuda()
+    ref, ref_mean, _ = m(t_tok, t_tgt)
+    per_step = {gf.GPT_KERNEL_QKV: p.n_layer, gf.GPT_KERNEL_ATTENTION: p.n_layer,
+                gf.GPT_KERNEL_ATTN_OUT: p.n_layer, gf.GPT_KERNEL_MLP_UP: p.n_layer,
+                gf.GPT_KERNEL_MLP_DOWN: p.n_layer, gf.GPT_KERNEL_LM_HEAD: 1}
+    for kind, n in per_step.items():
+        evb = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        eve = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        for e in evb + eve:
+            e.record()
+        t = gf.launch_timing(kind, evb, eve)
+        loss = torch.empty_like(ref)
+        mean = torch.empty_like(ref_mean)
+        assert m.forward(t_tok, t_tgt, loss, mean, None, None, timing=t) == gf.GPT_OK
+        torch.cuda.synchronize()
+        assert t.recorded == n
+        us = [b.elapsed_time(e) * 1e3 for b, e in zip(evb[:n], eve[:n])]
+        assert all(0.0 < u < 1e6 for u in us), us
+        assert torch.equal(loss, ref) and torch.equal(mean, ref_mean)
