@@ -17,7 +17,10 @@ Draw order for one preset (seeded ``numpy.random.default_rng(seed)``):
   2. per layer: W_Q, W_K, W_V, W_O, W_1, W_2
   3. lm_head W_U [V, C]
   4. per-layer residual scalars lambda[L] then x0 scalars mu[L]
-  5. token rows [B, T+1]
+  5. (value-embedding presets only) per layer: value-embedding table [V, Hkv*D] ~ N(0, 1)
+     and gate weights [Hkv, 12] ~ N(0, 1/12), drawn for every layer (the model uses the
+     layers its selection rule picks)
+  6. token rows [B, T+1]
 """
 from __future__ import annotations
 
@@ -56,6 +59,8 @@ class Preset:
     mu_range: tuple = (0.1, 0.1)       # x0 scalar mu: constant if lo == hi, else U[lo, hi]
     seed: int = 0
     qk_scale: Optional[float] = None   # attention logit scale; None means 1/sqrt(head_dim)
+    value_embeds: bool = False         # per-layer value-embedding tables and gates are drawn
+    ve_gate_channels: int = 12         # input channels the value-embedding gate reads
 
     @property
     def attn_scale(self) -> float:
@@ -77,6 +82,9 @@ PRESETS: Dict[str, Preset] = {
     # nanochat d24: width 1536, 12 heads of 128, V=32768, T=2048, B=8, bf16, seeded lambda/mu
     "d24": Preset("d24", 24, 1536, 12, 12, 128, 6144, 32768, 2048, 8, "bf16", short_window=1024,
                   lambda_range=(0.9, 1.1), mu_range=(0.0, 0.2)),
+    # d24 with grouped-query attention (4 KV heads) and value embeddings
+    "d24gve": Preset("d24gve", 24, 1536, 12, 4, 128, 6144, 32768, 2048, 8, "bf16", short_window=1024,
+                     lambda_range=(0.9, 1.1), mu_range=(0.0, 0.2), value_embeds=True),
 }
 
 
@@ -130,6 +138,8 @@ class Weights:
     lm_head: np.ndarray             # [V, C]
     resid_lambda: np.ndarray        # [L] float32
     x0_lambda: np.ndarray           # [L] float32
+    ve: Optional[List[np.ndarray]] = None       # L x [V, Hkv*D] value-embedding tables
+    ve_gate: Optional[List[np.ndarray]] = None  # L x [Hkv, ve_gate_channels] gate weights
 
     def value(self, a: np.ndarray) -> np.ndarray:
         return bf16_bits_to_f32(a) if self.dtype == "bf16" else a
@@ -176,7 +186,13 @@ def make_weights(p: Preset, rng: Optional[np.random.Generator] = None) -> Weight
     lm_head = _gauss(rng, (V, C), C, p.dtype)
     lam = _scalars(rng, p.lambda_range, L)
     mu = _scalars(rng, p.mu_range, L)
-    return Weights(p.dtype, wte, wq, wk, wv, wo, w1, w2, lm_head, lam, mu)
+    ve = ve_gate = None
+    if p.value_embeds:
+        ve, ve_gate = [], []
+        for _ in range(L):
+            ve.append(_gauss(rng, (V, Hkv * D), 1, p.dtype))
+            ve_gate.append(_gauss(rng, (Hkv, p.ve_gate_channels), p.ve_gate_channels, p.dtype))
+    return Weights(p.dtype, wte, wq, wk, wv, wo, w1, w2, lm_head, lam, mu, ve, ve_gate)
 
 
 def make_tokens(p: Preset, rng: np.random.Generator, batch: Optional[int] = None,

@@ -12,8 +12,8 @@ Sources (cited by page title and section):
        Pass", "RMS Normalization", "Rotary Position Embeddings (RoPE)",
        "Causal Self-Attention", "QK-Norm with Sharpening", "Scaled Dot-Product
        Attention with Sliding Window", "Feed-Forward Network (MLP)", "Residual
-       Stream with Learnable Scalars", "Logit Softcap", "Cross-Entropy Loss",
-       "Pseudocode: One Training Step".
+       Stream with Learnable Scalars", "Value Embeddings (ResFormer)", "Logit
+       Softcap", "Cross-Entropy Loss", "Pseudocode: One Training Step".
   [R]  "Reading nanochat Source: From Configuration to a Training Step" --
        sections 2 (shifted targets), 5.2-5.4 (attention order, block, LM head).
   [S]  "nanochat depth sweep" -- section "Architecture" (SSSL windows, last
@@ -37,6 +37,10 @@ so the oracle and the GPU path cannot silently diverge):
   * GQA head map: query head h reads KV head floor(h * Hkv / H).
   * ignored targets (-1) contribute a per-token loss of 0 and are excluded
     from the mean; with no valid target the mean is NaN.
+  * value embeddings (when cfg.value_embeds): the gate reads the first 12
+    channels of the attention block's normalised input x_tilde (the input of
+    the Q/K/V projections), and the mixed value v + g * e is what attention
+    averages; layers follow the pages' selection rule (has_ve).
 
 Every function here is pinned by a ``-m "not gpu"`` test in
 ``tests/test_oracle_pins.py`` to something other than itself (worked examples
@@ -53,7 +57,7 @@ import numpy as np
 __all__ = [
     "rms_norm", "rope_angles", "apply_rope", "layer_windows", "visible_mask",
     "attention", "linear", "relu_squared", "softcap", "token_losses",
-    "mean_loss", "block", "forward_row", "forward",
+    "mean_loss", "has_ve", "value_embed_mix", "block", "forward_row", "forward",
 ]
 
 
@@ -206,6 +210,27 @@ def mean_loss(losses: np.ndarray, targets: np.ndarray) -> float:
     return float(np.sum(np.where(valid, losses, 0.0)) / n)
 
 
+# ----------------------------------------------------------------------------- value embeddings
+
+def has_ve(l: int, n_layer: int) -> bool:
+    """[M] "Value Embeddings (ResFormer)", layer selection: layer l (0-based) takes a value
+    embedding iff l mod 2 equals (L - 1) mod 2 -- every other layer, the last one always."""
+    return l % 2 == (n_layer - 1) % 2
+
+
+def value_embed_mix(v: np.ndarray, e: np.ndarray, x_gate: np.ndarray, w_gate: np.ndarray) -> np.ndarray:
+    """Gated value-embedding mix for one row.
+
+    [M] "Value Embeddings (ResFormer)": the gate is 3 * sigmoid of a linear map of the input's
+    first channels, one scalar per KV head and position, broadcast over the head dimension,
+    and v_h <- v_h + g_h * e_h.  v, e: [T, Hkv, D]; x_gate: [T, n] (the first n channels);
+    w_gate: [Hkv, n].
+    """
+    logit = x_gate @ w_gate.T
+    g = 3.0 / (1.0 + np.exp(-logit))
+    return v + g[:, :, None] * e
+
+
 # ----------------------------------------------------------------------------- forward
 
 def _get(params: Any, name: str, layer: Optional[int] = None):
@@ -214,7 +239,8 @@ def _get(params: Any, name: str, layer: Optional[int] = None):
 
 
 def block(x: np.ndarray, x0: np.ndarray, l: int, cfg: Any, params: Any, window: int,
-          cos: np.ndarray, sin: np.ndarray, dt, internals: Optional[Dict] = None) -> np.ndarray:
+          cos: np.ndarray, sin: np.ndarray, dt, internals: Optional[Dict] = None,
+          tokens: Optional[np.ndarray] = None) -> np.ndarray:
     """One transformer layer on one row x [T, C].
 
     [M] "Residual Stream with Learnable Scalars" and "High-Level Forward Pass"
@@ -222,7 +248,8 @@ def block(x: np.ndarray, x0: np.ndarray, l: int, cfg: Any, params: Any, window: 
     x += MLP(RMSNorm(x)).  Inside attention ([M] "Causal Self-Attention",
     "QK-Norm with Sharpening"; [R] 5.2): project q, k, v with no bias, RoPE on
     q and k, per-head RMSNorm of q and k, windowed attention, merge heads,
-    output projection.
+    output projection.  With value embeddings on a selected layer ([M] "Value Embeddings
+    (ResFormer)"), v is mixed with the gated table rows of ``tokens`` before attention.
     """
     T, C = x.shape
     H, Hkv, D = cfg.n_head, cfg.n_kv_head, cfg.head_dim
@@ -235,6 +262,10 @@ def block(x: np.ndarray, x0: np.ndarray, l: int, cfg: Any, params: Any, window: 
     q = linear(xn, np.asarray(_get(params, "wq", l), dtype=dt)).reshape(T, H, D)
     k = linear(xn, np.asarray(_get(params, "wk", l), dtype=dt)).reshape(T, Hkv, D)
     v = linear(xn, np.asarray(_get(params, "wv", l), dtype=dt)).reshape(T, Hkv, D)
+    if getattr(cfg, "value_embeds", False) and has_ve(l, cfg.n_layer):
+        e = np.asarray(_get(params, "ve", l)[tokens], dtype=dt).reshape(T, Hkv, D)
+        wg = np.asarray(_get(params, "ve_gate", l), dtype=dt)
+        v = value_embed_mix(v, e, xn[:, :wg.shape[1]], wg)
     q = rms_norm(apply_rope(q, cos, sin), eps)
     k = rms_norm(apply_rope(k, cos, sin), eps)
     o = attention(q, k, v, window, cfg.attn_scale)
@@ -271,7 +302,7 @@ def forward_row(cfg: Any, params: Any, tokens: np.ndarray, targets: Optional[np.
     layers = []
     for l in range(cfg.n_layer):
         internals = {} if want_internals else None
-        x = block(x, x0, l, cfg, params, windows[l], cos, sin, dt, internals)
+        x = block(x, x0, l, cfg, params, windows[l], cos, sin, dt, internals, tokens=tokens)
         if want_internals:
             layers.append(internals)
     xf = rms_norm(x, eps)
@@ -309,7 +340,8 @@ def forward(cfg: Any, params: Any, tokens: np.ndarray, targets: Optional[np.ndar
     ``params`` maps ``wte``, ``lm_head``, ``resid_lambda``, ``x0_lambda`` to
     arrays and ``wq``, ``wk``, ``wv``, ``wo``, ``w1``, ``w2`` to per-layer
     sequences of row-major [out, in] arrays (any float dtype; converted to
-    ``dtype`` one layer at a time).
+    ``dtype`` one layer at a time); with ``cfg.value_embeds`` also ``ve``
+    (per layer [V, Hkv*D]) and ``ve_gate`` (per layer [Hkv, 12]).
     """
     rows = list(range(tokens.shape[0])) if rows is None else list(rows)
     out_l, out_z = [], []

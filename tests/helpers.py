@@ -39,6 +39,7 @@ def oracle_params(w: gptdata.Weights) -> dict:
         "x0_lambda": w.x0_lambda,
         "wq": _LazyLayers(w, w.wq), "wk": _LazyLayers(w, w.wk), "wv": _LazyLayers(w, w.wv),
         "wo": _LazyLayers(w, w.wo), "w1": _LazyLayers(w, w.w1), "w2": _LazyLayers(w, w.w2),
+        **({"ve": _LazyLayers(w, w.ve), "ve_gate": _LazyLayers(w, w.ve_gate)} if w.ve is not None else {}),
     }
 
 
@@ -52,6 +53,9 @@ def dense_params(p: gptdata.Preset, seed: int = 0) -> dict:
     }
     for n in ("wq", "wk", "wv", "wo", "w1", "w2"):
         d[n] = [m.astype(np.float64) for m in getattr(w, n)]
+    if w.ve is not None:
+        d["ve"] = [m.astype(np.float64) for m in w.ve]
+        d["ve_gate"] = [m.astype(np.float64) for m in w.ve_gate]
     return d
 
 

@@ -439,4 +439,82 @@ def pin_internal_norms():
         assert not unit(li["v"])
 
 
+# ----------------------------------------------------------------------------- value embeddings
+
+def pin_value_embedding_worked_example():
+    """[M] "Value Embeddings (ResFormer)" worked example: one KV head, d_h = 3, gate logit 1.2
+    (a one-channel gate input of 1 and weight 1.2 give that logit).  The page rounds
+    sigmoid(1.2) to 3 decimals before scaling, so the gate is checked through the sigmoid to
+    the printed decimals and the gate and mixed value within what that rounding implies
+    (3 * 0.0005 on the gate, that times |e| plus the printed half-unit on the value)."""
+    e = EX["value_embedding"]
+    v = np.array(e["v"]).reshape(1, 1, 3)
+    ev = np.array(e["e"]).reshape(1, 1, 3)
+    out = oracle.value_embed_mix(v, ev, np.ones((1, 1)), np.array([[e["gate_logit"]]]))
+    g = (out[0, 0, 0] - e["v"][0]) / e["e"][0]
+    _round_eq(g / 3.0, e["expected_sigmoid"], e["sigmoid_decimals"])
+    tol_g = 3 * 0.5 * 10.0 ** -e["sigmoid_decimals"]
+    assert abs(g - e["expected_gate"]) <= tol_g + 1e-12
+    tol_v = tol_g * np.abs(np.array(e["e"])) + 0.5 * 10.0 ** -e["decimals"]
+    assert np.all(np.abs(out.reshape(3) - np.array(e["expected"])) <= tol_v + 1e-12), out
+
+
+def pin_value_embedding_zero_gate():
+    """A zero gate weight gives g = 3 * sigmoid(0) = 1.5 exactly, whatever the input."""
+    rng = np.random.default_rng(3)
+    v, e = rng.standard_normal((5, 2, 4)), rng.standard_normal((5, 2, 4))
+    out = oracle.value_embed_mix(v, e, rng.standard_normal((5, 12)), np.zeros((2, 12)))
+    assert np.allclose(out, v + 1.5 * e, rtol=0, atol=1e-15)
+
+
+def pin_ve_layer_rule():
+    """[M] "Value Embeddings (ResFormer)": alternating layers with the last one always
+    included -- L = 24 selects the odd layers, L = 5 the even ones."""
+    assert [l for l in range(24) if oracle.has_ve(l, 24)] == list(range(1, 24, 2))
+    assert [l for l in range(5) if oracle.has_ve(l, 5)] == [0, 2, 4]
+    for L in range(1, 9):
+        assert oracle.has_ve(L - 1, L)
+        assert all(oracle.has_ve(l, L) != oracle.has_ve(l + 1, L) for l in range(L - 1))
+
+
+def _ve_preset(**kw):
+    base = dict(n_layer=3, n_head=4, n_kv_head=2, head_dim=4, d_model=16, value_embeds=True)
+    base.update(kw)
+    return small_preset(**base)
+
+
+def pin_value_embedding_zero_tables():
+    """All-zero value-embedding tables leave the forward pass exactly as without them."""
+    p = _ve_preset()
+    prm = dense_params(p)
+    prm["ve"] = [np.zeros_like(a) for a in prm["ve"]]
+    rows = _tokens(p)
+    a = _fwd(p, prm, rows[:, :-1], rows[:, 1:], want_logits=True)
+    b = _fwd(p.with_(value_embeds=False), prm, rows[:, :-1], rows[:, 1:], want_logits=True)
+    assert np.array_equal(a["logits"], b["logits"]) and np.array_equal(a["losses"], b["losses"])
+    c = _fwd(p, dense_params(p), rows[:, :-1], rows[:, 1:])   # non-zero tables do change it
+    assert not np.allclose(c["losses"], a["losses"])
+
+
+def pin_value_embedding_gate_scale_invariance():
+    """The gate reads the block's normalised input, so scaling the residual stream entering
+    a block (x and x0 together) leaves the mixed values unchanged; the last layer (which
+    always has a value embedding) is checked."""
+    p = _ve_preset(n_layer=2)
+    prm = dense_params(p)
+    rng = np.random.default_rng(5)
+    T, C = p.seq_len, p.d_model
+    x, x0 = rng.standard_normal((T, C)), rng.standard_normal((T, C))
+    tok = rng.integers(0, p.vocab, T)
+    cos, sin = oracle.rope_angles(T, p.head_dim, p.rope_base)
+    l = p.n_layer - 1
+    ia, ib = {}, {}
+    oracle.block(x, x0, l, p, prm, T, cos, sin, np.float64, ia, tokens=tok)
+    oracle.block(37.0 * x, 37.0 * x0, l, p, prm, T, cos, sin, np.float64, ib, tokens=tok)
+    assert np.allclose(ia["v"], ib["v"], rtol=1e-12, atol=1e-12)
+    base = {}
+    oracle.block(x, x0, l, p.with_(value_embeds=False), prm, T, cos, sin, np.float64, base, tokens=tok)
+    assert not np.allclose(ia["v"], base["v"])
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

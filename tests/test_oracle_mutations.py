@@ -11,7 +11,8 @@ import oracle
 import oracle_pins as P
 
 _orig = {n: getattr(oracle, n) for n in ("apply_rope", "visible_mask", "relu_squared", "softcap",
-                                          "token_losses", "rms_norm", "attention", "block", "linear")}
+                                          "token_losses", "rms_norm", "attention", "block", "linear",
+                                          "has_ve", "value_embed_mix")}
 
 
 def _rope_sign(u, cos, sin):
@@ -70,16 +71,16 @@ def _block_patched(kind):
     """Wrap block() with a mistake in the residual-scalar or norm handling."""
     import oracle as o
 
-    def blk(x, x0, l, cfg, params, window, cos, sin, dt, internals=None):
+    def blk(x, x0, l, cfg, params, window, cos, sin, dt, internals=None, **kw):
         if kind == "no_mix":
             prm = dict(params)
             prm["resid_lambda"] = np.ones_like(np.asarray(params["resid_lambda"]))
             prm["x0_lambda"] = np.zeros_like(np.asarray(params["x0_lambda"]))
-            return _orig["block"](x, x0, l, cfg, prm, window, cos, sin, dt, internals)
+            return _orig["block"](x, x0, l, cfg, prm, window, cos, sin, dt, internals, **kw)
         if kind == "swap_mix":
             prm = dict(params)
             prm["resid_lambda"], prm["x0_lambda"] = params["x0_lambda"], params["resid_lambda"]
-            return _orig["block"](x, x0, l, cfg, prm, window, cos, sin, dt, internals)
+            return _orig["block"](x, x0, l, cfg, prm, window, cos, sin, dt, internals, **kw)
         raise AssertionError(kind)
     return blk
 
@@ -145,6 +146,33 @@ def _no_pre_norm(monkeypatch):
     monkeypatch.setattr(oracle, "block", blk)
 
 
+def _ve_no_factor3(v, e, x_gate, w_gate):
+    g = 1.0 / (1.0 + np.exp(-(x_gate @ w_gate.T)))
+    return v + g[:, :, None] * e
+
+
+def _ve_even_layers(l, n_layer):
+    return l % 2 == 0
+
+
+def _ve_gate_unnormed(monkeypatch):
+    """Gate fed from the un-normalised residual stream instead of the block's normed input."""
+    real_block = _orig["block"]
+    real_mix = _orig["value_embed_mix"]
+    state = {}
+
+    def blk(x, x0, l, cfg, params, *a, **k):
+        lam = float(np.asarray(params["resid_lambda"])[l])
+        mu = float(np.asarray(params["x0_lambda"])[l])
+        state["x"] = lam * x + mu * x0
+        return real_block(x, x0, l, cfg, params, *a, **k)
+
+    def mix(v, e, x_gate, w_gate):
+        return real_mix(v, e, state["x"][:, :x_gate.shape[1]], w_gate)
+    monkeypatch.setattr(oracle, "block", blk)
+    monkeypatch.setattr(oracle, "value_embed_mix", mix)
+
+
 MUTATIONS = {
     "rope_sign": (lambda mp: mp.setattr(oracle, "apply_rope", _rope_sign), [P.pin_rope_worked_example]),
     "rope_interleaved": (lambda mp: mp.setattr(oracle, "apply_rope", _rope_interleaved),
@@ -169,6 +197,10 @@ MUTATIONS = {
     "no_final_norm": (_forward_row_no_final_norm, [P.pin_identity_blocks_closed_form]),
     "no_qk_norm": (_qk_no_norm, [P.pin_qk_scale_invariance, P.pin_internal_norms]),
     "no_pre_attn_norm": (_no_pre_norm, [P.pin_internal_norms]),
+    "ve_gate_without_factor_3": (lambda mp: mp.setattr(oracle, "value_embed_mix", _ve_no_factor3),
+                                 [P.pin_value_embedding_worked_example, P.pin_value_embedding_zero_gate]),
+    "ve_on_even_layers": (lambda mp: mp.setattr(oracle, "has_ve", _ve_even_layers), [P.pin_ve_layer_rule]),
+    "ve_gate_from_unnormed_stream": (_ve_gate_unnormed, [P.pin_value_embedding_gate_scale_invariance]),
 }
 
 
