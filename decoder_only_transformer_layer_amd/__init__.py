@@ -42,6 +42,7 @@ class gpt_cfg(ctypes.Structure):
         ("window", ctypes.POINTER(ctypes.c_int32)),
         ("softcap", ctypes.c_float), ("rope_base", ctypes.c_float), ("attn_scale", ctypes.c_float),
         ("norm_eps", ctypes.c_float), ("dtype", ctypes.c_int32),
+        ("has_ve", ctypes.POINTER(ctypes.c_uint8)),
     ]
 
 
@@ -52,6 +53,7 @@ class gpt_weights(ctypes.Structure):
         ("wq", ctypes.POINTER(ctypes.c_void_p)), ("wk", ctypes.POINTER(ctypes.c_void_p)),
         ("wv", ctypes.POINTER(ctypes.c_void_p)), ("wo", ctypes.POINTER(ctypes.c_void_p)),
         ("w1", ctypes.POINTER(ctypes.c_void_p)), ("w2", ctypes.POINTER(ctypes.c_void_p)),
+        ("ve", ctypes.POINTER(ctypes.c_void_p)), ("ve_gate", ctypes.POINTER(ctypes.c_void_p)),
     ]
 
 
@@ -142,19 +144,28 @@ def layer_windows(pattern: str, short_window: int, seq_len: int, n_layer: int) -
     return w
 
 
-def make_cfg(p: Any, batch: Optional[int] = None, windows: Optional[Sequence[int]] = None) -> gpt_cfg:
-    """gpt_cfg from any object with the preset attribute names (n_layer, d_model, ...).
+def ve_layers(n_layer: int) -> List[int]:
+    """Layers that mix a value embedding into v: every other layer, the last one always
+    ("The Mathematics of Karpathy's nanochat", section "Value Embeddings (ResFormer)")."""
+    return [1 if l % 2 == (n_layer - 1) % 2 else 0 for l in range(n_layer)]
 
-    The window array is kept alive on the returned structure (attribute ``_win``)."""
+
+def make_cfg(p: Any, batch: Optional[int] = None, windows: Optional[Sequence[int]] = None) -> gpt_cfg:
+    """gpt_cfg from any object with the preset attribute names (n_layer, d_model, ...); a
+    true ``value_embeds`` attribute selects value embeddings on the ve_layers() layers.
+
+    The window and has_ve arrays are kept alive on the returned structure."""
     if windows is None:
         windows = layer_windows(p.window_pattern, p.short_window, p.seq_len, p.n_layer)
     win = (ctypes.c_int32 * p.n_layer)(*[int(w) for w in windows])
+    ve = (ctypes.c_uint8 * p.n_layer)(*ve_layers(p.n_layer)) if getattr(p, "value_embeds", False) else None
     c = gpt_cfg(p.n_layer, p.d_model, p.n_head, p.n_kv_head, p.head_dim, p.mlp_dim, p.vocab,
                 p.seq_len, p.batch if batch is None else batch,
                 ctypes.cast(win, ctypes.POINTER(ctypes.c_int32)),
                 p.softcap, p.rope_base, p.attn_scale, p.norm_eps,
-                GPT_BF16 if p.dtype == "bf16" else GPT_F32)
-    c._win = win
+                GPT_BF16 if p.dtype == "bf16" else GPT_F32,
+                None if ve is None else ctypes.cast(ve, ctypes.POINTER(ctypes.c_uint8)))
+    c._win, c._ve = win, ve
     return c
 
 
@@ -261,7 +272,8 @@ class DeviceModel:
     """Device-resident weights of one configuration plus the structures gpt_fwd_loss needs.
 
     ``weights`` is any object with attributes wte, lm_head, resid_lambda, x0_lambda and
-    per-layer lists wq, wk, wv, wo, w1, w2 (numpy arrays: uint16 bf16 bits or float32).
+    per-layer lists wq, wk, wv, wo, w1, w2 (numpy arrays: uint16 bf16 bits or float32), plus
+    per-layer ve and ve_gate lists when the configuration has value embeddings.
     """
 
     def __init__(self, p: Any, weights: Any, batch: Optional[int] = None, device: str = "cuda",
@@ -283,11 +295,21 @@ class DeviceModel:
         for n in ("wq", "wk", "wv", "wo", "w1", "w2"):
             self.t[n] = [to_device(m, dt, device) for m in getattr(weights, n)]
             arrs[n] = (ctypes.c_void_p * p.n_layer)(*[m.data_ptr() for m in self.t[n]])
+        ve_ptr = gate_ptr = None
+        if getattr(p, "value_embeds", False):
+            sel = ve_layers(p.n_layer)   # upload only the tables the selected layers read
+            self.t["ve"] = [to_device(m, dt, device) if s else None for m, s in zip(weights.ve, sel)]
+            self.t["ve_gate"] = [to_device(m, dt, device) if s else None for m, s in zip(weights.ve_gate, sel)]
+            for n in ("ve", "ve_gate"):
+                arrs[n] = (ctypes.c_void_p * p.n_layer)(*[m.data_ptr() if m is not None else None
+                                                         for m in self.t[n]])
+            ve_ptr = ctypes.cast(arrs["ve"], ctypes.POINTER(ctypes.c_void_p))
+            gate_ptr = ctypes.cast(arrs["ve_gate"], ctypes.POINTER(ctypes.c_void_p))
         self._arrs = arrs
         self.w = gpt_weights(self.t["wte"].data_ptr(), self.t["lm_head"].data_ptr(),
                              self.t["resid_lambda"].data_ptr(), self.t["x0_lambda"].data_ptr(),
                              *[ctypes.cast(arrs[n], ctypes.POINTER(ctypes.c_void_p))
-                               for n in ("wq", "wk", "wv", "wo", "w1", "w2")])
+                               for n in ("wq", "wk", "wv", "wo", "w1", "w2")], ve_ptr, gate_ptr)
         self.ws_bytes = gpt_workspace_bytes(self.cfg)
         self.ws = torch.empty(self.ws_bytes + 256, dtype=torch.uint8, device=device)
         off = (-self.ws.data_ptr()) % 256

@@ -25,6 +25,15 @@ struct Layout {
   int nnb;
 };
 
+constexpr int VE_GATE_CH = 12;  // input channels of the value-embedding gate
+
+bool any_ve(const gpt_cfg* c) {
+  if (!c->has_ve) return false;
+  for (int l = 0; l < c->n_layer; ++l)
+    if (c->has_ve[l]) return true;
+  return false;
+}
+
 gpt_status validate(const gpt_cfg* c) {
   if (!c) return GPT_E_INVALID_ARG;
   if (c->n_layer < 1 || c->d_model < 1 || c->n_head < 1 || c->n_kv_head < 1 || c->head_dim < 1 ||
@@ -48,6 +57,10 @@ gpt_status validate(const gpt_cfg* c) {
   if (c->dtype == GPT_BF16) {
     if (c->seq_len % 64) return GPT_E_UNSUPPORTED;
     if ((c->n_head * c->head_dim) % 128 || (c->n_kv_head * c->head_dim) % 128) return GPT_E_UNSUPPORTED;
+  }
+  if (any_ve(c)) {
+    if (c->d_model < VE_GATE_CH) return GPT_E_UNSUPPORTED;
+    if (c->dtype == GPT_BF16 && c->head_dim != 128) return GPT_E_UNSUPPORTED;  // fused epilogue only
   }
   return GPT_OK;
 }
@@ -180,6 +193,13 @@ gpt_status gpt_fwd_loss_timed(const gpt_cfg* c, const gpt_weights* w, const int3
   for (int l = 0; l < c->n_layer; ++l)
     if (!w->wq[l] || !w->wk[l] || !w->wv[l] || !w->wo[l] || !w->w1[l] || !w->w2[l])
       return GPT_E_INVALID_ARG;
+  if (any_ve(c)) {
+    if (!w->ve || !w->ve_gate) return GPT_E_INVALID_ARG;
+    for (int l = 0; l < c->n_layer; ++l)
+      if (c->has_ve[l] && (!w->ve[l] || !w->ve_gate[l] || !aligned(w->ve[l], 16) ||
+                           !aligned(w->ve_gate[l], 4)))
+        return GPT_E_INVALID_ARG;
+  }
   if (targets && (!loss || !mean_loss)) return GPT_E_INVALID_ARG;
   if (!targets && !logits) return GPT_E_INVALID_ARG;
   const void* ptrs16[] = {w->wte, w->lm_head};
@@ -234,6 +254,10 @@ gpt_status gpt_fwd_loss_timed(const gpt_cfg* c, const gpt_weights* w, const int3
       const bool fused = D == 128;
       if (fused) g.cs = cs;
       if (l > 0) { g.rs_ssp = ssp; g.rs_n = nsl; g.rs_c = (float)C; }  // layer 0 reads normed xn
+      if (c->has_ve && c->has_ve[l]) {  // validated: D == 128, so the fused epilogue adds it
+        g.ve = (const bf16_t*)w->ve[l]; g.ve_gate = (const bf16_t*)w->ve_gate[l];
+        g.tokens = tokens; g.vocab = V;
+      }
       TIMED(tm, GPT_KERNEL_QKV, launch_gemm_bf16(EPI_QKV, g, s));
       if (!fused) CK(launch_qk_rope_norm(qk, true, nqk, cs, M, T, H + Hkv, D, eps, s));
       const int win = c->window[l] < T ? c->window[l] : T;
@@ -260,6 +284,9 @@ gpt_status gpt_fwd_loss_timed(const gpt_cfg* c, const gpt_weights* w, const int3
     GemmArgs g = gemm_args(xn, C, w->wq[l], nqkv, C, M, qk, nqkv);
     g.B1 = w->wk[l]; g.B2 = w->wv[l]; g.nseg0 = H * D; g.nseg1 = Hkv * D;
     CK(launch_gemm_f32(EPI_STORE, g, s));
+    if (c->has_ve && c->has_ve[l])
+      CK(launch_ve_mix_f32((float*)qk, nqkv, nqk, (const float*)xn, C, tokens, V,
+                           (const float*)w->ve[l], (const float*)w->ve_gate[l], M, Hkv, D, s));
     // RoPE + QK-norm on the q and k heads
     CK(launch_qk_rope_norm(qk, false, nqkv, cs, M, T, H + Hkv, D, eps, s));
     // windowed causal attention

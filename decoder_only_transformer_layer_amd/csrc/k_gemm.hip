@@ -462,6 +462,34 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
               }
             }
           } else {
+            if (g.ve != nullptr) {
+              // Value embedding: lane L's gate is row L % 32 of this group's; each lane then
+              // adds g * ve[token] for its 16 rows and 4 columns.
+              const int gg = (wcol0 - g.nqk) / g.D, ldve = g.Hkv * g.D;
+              const int grp0 = m0 + wm * TM + fm * 32;
+              const int lrow = lane & 31;
+              float logit = 0.f;
+              if (grp0 + lrow < M) {
+                const bf16* xa = (const bf16*)g.A + (size_t)(grp0 + lrow) * g.lda;
+                const bf16* wg = g.ve_gate + gg * 12;
+#pragma unroll
+                for (int c = 0; c < 12; ++c) logit += (float)xa[c] * (float)wg[c];
+                if (g.rs_ssp != nullptr) logit *= ((const float*)lds)[sizeof(lds) / 4 - BM + wm * TM + fm * 32 + lrow];
+              }
+              const float gate = 3.f / (1.f + __expf(-logit));
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int lr = 8 * (r >> 2) + 4 * hl + (r & 3);
+                const float gr = __shfl(gate, lr, 64);
+                if (grp0 + lr < M) {
+                  int tk = g.tokens[grp0 + lr];
+                  tk = (tk >= 0 && tk < g.vocab) ? tk : 0;
+                  const bf16* er = g.ve + (size_t)tk * ldve + gg * g.D + rl;
+#pragma unroll
+                  for (int fn = 0; fn < FN; ++fn) acc[fm][fn][r] += gr * (float)er[fn * 32];
+                }
+              }
+            }
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
 #pragma unroll

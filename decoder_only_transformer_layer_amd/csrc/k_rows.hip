@@ -176,6 +176,30 @@ hipError_t dispatch_nch(int C, F&& f) {
   return hipErrorInvalidValue;
 }
 
+// Value embedding of the fp32 path ("The Mathematics of Karpathy's nanochat", section "Value
+// Embeddings (ResFormer)"): one wavefront per token; each KV head's gate is 3 sigmoid of the
+// first 12 normalised input channels against that head's gate row, then v += gate * ve[token].
+__global__ __launch_bounds__(256) void ve_mix_f32_kernel(float* __restrict__ qkv, int ld, int voff,
+                                                         const float* __restrict__ xn, int ldx,
+                                                         const int32_t* __restrict__ tokens, int vocab,
+                                                         const float* __restrict__ ve,
+                                                         const float* __restrict__ gate, int M,
+                                                         int Hkv, int D) {
+  const int row = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= M) return;
+  int tk = tokens[row];
+  tk = (tk >= 0 && tk < vocab) ? tk : 0;
+  const float* xr = xn + (size_t)row * ldx;
+  float* vr = qkv + (size_t)row * ld + voff;
+  const float* er = ve + (size_t)tk * Hkv * D;
+  for (int h = 0; h < Hkv; ++h) {
+    float z = 0.f;
+    for (int c = 0; c < 12; ++c) z = fmaf(xr[c], gate[h * 12 + c], z);
+    const float gv = 3.f / (1.f + expf(-z));
+    for (int d = lane; d < D; d += 64) vr[h * D + d] += gv * er[h * D + d];
+  }
+}
+
 }  // namespace
 
 hipError_t launch_rope_table(float2* cs, int T, int D, float base, hipStream_t s) {
@@ -216,6 +240,14 @@ hipError_t launch_mix_norm(float* x, const float* x0, const float* lam, const fl
     }
     return hipGetLastError();
   });
+}
+
+hipError_t launch_ve_mix_f32(float* qkv, int ld, int voff, const float* xn, int ldx,
+                             const int32_t* tokens, int vocab, const float* ve, const float* gate,
+                             int M, int Hkv, int D, hipStream_t s) {
+  const int grid = (M + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
+  ve_mix_f32_kernel<<<grid, 256, 0, s>>>(qkv, ld, voff, xn, ldx, tokens, vocab, ve, gate, M, Hkv, D);
+  return hipGetLastError();
 }
 
 hipError_t launch_qk_rope_norm(void* qk, bool bf16_, int ld, const float2* cs, int M, int T,

@@ -44,6 +44,12 @@ hipError_t launch_embed_norm(const int32_t* tokens, const void* wte, bool wbf16,
 hipError_t launch_mix_norm(float* x, const float* x0, const float* lam, const float* mu, int layer,
                            bool mix, void* xn, bool xbf16, int M, int C, float eps, hipStream_t s);
 
+// fp32 path value embedding, in place on the v columns of qkv [M][ld] (v head h at column
+// voff + h*D): v += 3 sigmoid(xn[m][0:12] . gate[h]) * ve[tokens[m]][h*D : (h+1)*D].
+hipError_t launch_ve_mix_f32(float* qkv, int ld, int voff, const float* xn, int ldx,
+                             const int32_t* tokens, int vocab, const float* ve, const float* gate,
+                             int M, int Hkv, int D, hipStream_t s);
+
 // In place on qk [M][nheads*D] (the q heads then the k heads of each token): RoPE at
 // position row % T, then per-head RMSNorm.
 hipError_t launch_qk_rope_norm(void* qk, bool bf16, int ld, const float2* cs, int M, int T,
@@ -62,6 +68,11 @@ struct GemmArgs {
   void* vt; int T, D, Hkv, nqk;           // QKV (bf16 only): columns >= nqk stored transposed to vt [B][Hkv][D][T]
   const float2* cs;                       // QKV: if set (head_dim 128), RoPE table [T][D/2] -> the q/k
   float eps;                              //      heads get RoPE + RMSNorm in the epilogue
+  // QKV with cs set: if ve is set, every v head h of row m gets
+  // + 3 sigmoid(rownorm(A[m][0:12]) . ve_gate[h]) * ve[tokens[m]][h*D : (h+1)*D], where rownorm is
+  // the row scale below when rs_ssp is set (else A is already normalised).  Token ids outside
+  // [0, vocab) read table row 0 (the embedding pass flags them).
+  const bf16_t* ve; const bf16_t* ve_gate; const int32_t* tokens; int vocab;
   // Row scale (consumers of an un-normalised A, bf16 path): if rs_ssp is set, every output row
   // is multiplied by rsqrt(sum_j rs_ssp[j][row] / rs_c + eps) before the epilogue's own work,
   // i.e. the GEMM computes RMSNorm(A) W^T from A and its row sums of squares.

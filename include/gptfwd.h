@@ -72,6 +72,10 @@ typedef struct {
   float attn_scale;     /* logit scale applied to <q_hat, k_hat>, e.g. 1/sqrt(head_dim) */
   float norm_eps;       /* eps inside every RMSNorm's square root, >= 0 (1e-6) */
   int32_t dtype;        /* gpt_dtype of weights and activations */
+  const uint8_t *has_ve;/* host [n_layer] or NULL: nonzero where the layer mixes a value
+                           embedding into v ("Value Embeddings (ResFormer)": the pages select
+                           l % 2 == (n_layer - 1) % 2); needs d_model >= 12, and head_dim 128
+                           for GPT_BF16 */
 } gpt_cfg;
 
 /* Weights: borrowed device memory of type cfg->dtype (float or bf16), row-major [out, in].
@@ -88,6 +92,13 @@ typedef struct {
   const void *const *wo;      /* host [n_layer] -> [d_model, n_head*head_dim] */
   const void *const *w1;      /* host [n_layer] -> [mlp_dim, d_model] */
   const void *const *w2;      /* host [n_layer] -> [d_model, mlp_dim] */
+  /* Value embeddings, read only on layers with cfg->has_ve[l] (the arrays may be NULL when
+   * cfg->has_ve is NULL; entries of other layers are ignored):
+   *   ve[l]      [vocab, n_kv_head*head_dim] table; row t is added to token t's v heads
+   *   ve_gate[l] [n_kv_head, 12] gate weights: g = 3 sigmoid(x_tilde[:12] . ve_gate[l][h])
+   *              per KV head h, x_tilde the normalised input of the layer's projections */
+  const void *const *ve;      /* host [n_layer] */
+  const void *const *ve_gate; /* host [n_layer] */
 } gpt_weights;
 
 /* Validate a configuration without touching any device.  Returns GPT_OK, GPT_E_INVALID_ARG or

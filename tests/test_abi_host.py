@@ -51,7 +51,7 @@ def _cfg(**kw):
 
 
 def test_validate_presets(lib):
-    for name in ("tiny", "d12", "d24"):
+    for name in ("tiny", "d12", "d24", "d24gve"):
         c = gf.make_cfg(gptdata.preset(name))
         assert gf.gpt_validate(c) == gf.GPT_OK, name
         assert gf.gpt_workspace_bytes(c) > 0
@@ -120,6 +120,30 @@ def test_fwd_loss_argument_errors_return_before_launch(lib):
     assert call(w=w3) == gf.GPT_E_INVALID_ARG
     bad = _cfg(head_dim=96)
     assert call(cfg=bad) == gf.GPT_E_UNSUPPORTED
+
+
+def test_value_embedding_validation(lib):
+    """has_ve needs head_dim 128 on the bf16 path (fp32 takes any) and the tables/gates of
+    every selected layer; the selection follows the alternating rule, last layer included."""
+    assert gf.ve_layers(24) == [l % 2 for l in range(24)]
+    assert gf.ve_layers(5) == [1, 0, 1, 0, 1]
+    p = gptdata.preset("d24gve")
+    c = gf.make_cfg(p.with_(head_dim=64, n_head=24, n_kv_head=8))
+    assert gf.gpt_validate(c) == gf.GPT_E_UNSUPPORTED
+    c32 = gf.make_cfg(p.with_(head_dim=64, n_head=24, n_kv_head=8, dtype="f32"))
+    assert gf.gpt_validate(c32) == gf.GPT_OK
+    c = gf.make_cfg(p)
+    assert gf.gpt_validate(c) == gf.GPT_OK
+    L, F = c.n_layer, 0x200000
+    need = gf.gpt_workspace_bytes(c)
+    w = _weights(L)                       # no ve / ve_gate arrays
+    call = lambda w: lib.gpt_fwd_loss(ctypes.byref(c), ctypes.byref(w), F, F, F, F, None,
+                                      0x10000000, need, None)
+    assert call(w) == gf.GPT_E_INVALID_ARG
+    arr = (ctypes.c_void_p * L)(*[0x300000 + 256 * i for i in range(L)])
+    w.ve = w.ve_gate = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+    arr[1] = None                         # layer 1 is selected (L = 24: odd layers)
+    assert call(w) == gf.GPT_E_INVALID_ARG
 
 
 def test_fwd_loss_timed_argument_errors(lib):

@@ -200,3 +200,59 @@ def test_launch_timing_hook_bf16():
         us = [b.elapsed_time(e) * 1e3 for b, e in zip(evb[:n], eve[:n])]
         assert all(0.0 < u < 1e6 for u in us), us
         assert torch.equal(loss, ref) and torch.equal(mean, ref_mean)
+
+
+# ----------------------------------------------------------------------------- value embeddings
+
+def test_gqa_value_embeddings_fp32():
+    """fp32 path with GQA 4:2 and value embeddings on alternating layers (last included)."""
+    p = gptdata.Preset(name="ve32", n_layer=3, d_model=128, n_head=4, n_kv_head=2, head_dim=64,
+                       mlp_dim=512, vocab=1000, seq_len=128, batch=2, dtype="f32", short_window=64,
+                       value_embeds=True, seed=21)
+    w, tok, tgt = gptdata.make_inputs(p)
+    _, got = _run(p, w, tok, tgt, want_logits=True)
+    ref = oracle.forward(p, params_of(w), tok, tgt, want_logits=True)
+    rel = abs(got["mean"] - ref["mean"]) / abs(ref["mean"])
+    zerr = np.max(np.abs(got["logits"] - ref["logits"])) / np.max(np.abs(ref["logits"]))
+    print(f"  ve fp32: mean rel err {rel:.2e}, logits err/max {zerr:.2e}")
+    assert rel <= 1e-4 and zerr <= 1e-3
+    # the value embeddings change the result (the tables are not silently skipped)
+    ref0 = oracle.forward(p.with_(value_embeds=False), params_of(w), tok, tgt)
+    assert abs(ref0["mean"] - got["mean"]) > 1e-3
+
+
+def test_gqa_value_embeddings_bf16_ragged():
+    """bf16 fused QKV epilogue with value embeddings: GQA 4:2, B*T = 640 rows (ragged tile
+    tail), V = 1000, 10% ignored targets, windows 100 / 64 / full."""
+    p = _ragged_preset(value_embeds=True, seed=23)
+    w, tok, tgt = gptdata.make_inputs(p, ignore_frac=0.1)
+    windows = [100, 64, 320]
+    _, got = _run(p, w, tok, tgt, want_logits=True, windows=windows)
+    ref = oracle.forward(p, params_of(w), tok, tgt, want_logits=True, windows=windows)
+    _check_bf16(got, ref)
+    ref0 = oracle.forward(p.with_(value_embeds=False), params_of(w), tok, tgt, windows=windows)
+    assert np.max(np.abs(ref0["losses"] - ref["losses"])) > 0.1
+
+
+@pytest.fixture(scope="module")
+def d24gve():
+    p = gptdata.preset("d24gve")
+    w, tok, tgt = gptdata.make_inputs(p)
+    return p, w, tok, tgt
+
+
+def test_d24_gqa_value_embeddings_bf16(d24gve):
+    """d24 with 4 KV heads and value embeddings at the benchmarked size (B=8, T=2048): oracle
+    on row 0 and on the first 512 tokens of row 5."""
+    p, w, tok, tgt = d24gve
+    _, got = _run(p, w, tok, tgt)
+    assert got["status"] == gf.GPT_OK
+    assert math.isfinite(got["mean"])
+    prm = params_of(w)
+    _check_bf16(got, oracle.forward(p, prm, tok, tgt, rows=[0]), rows=[0])
+    pre = p.with_(seq_len=512)
+    ref5 = oracle.forward(pre, prm, tok[5:6, :512], tgt[5:6, :512],
+                          windows=oracle.layer_windows(p.window_pattern, p.short_window, p.seq_len, p.n_layer))
+    err = np.abs(got["losses"][5, :512] - ref5["losses"][0])
+    print(f"  row 5 prefix: max |err| {err.max():.3e}")
+    assert err.max() <= 2e-2
