@@ -20,7 +20,9 @@ Draw order for one preset (seeded ``numpy.random.default_rng(seed)``):
   5. (value-embedding presets only) per layer: value-embedding table [V, Hkv*D] ~ N(0, 1)
      and gate weights [Hkv, 12] ~ N(0, 1/12), drawn for every layer (the model uses the
      layers its selection rule picks)
-  6. token rows [B, T+1]
+  6. (looped presets only) pass embeddings [2, C] ~ N(0, 1/C), then per-layer routing gate
+     logits [L] = ln(exp(0.05) - 1) + 0.1 N(0, 1) (float32), i.e. gates near 0.05
+  7. token rows [B, T+1]
 """
 from __future__ import annotations
 
@@ -61,6 +63,7 @@ class Preset:
     qk_scale: Optional[float] = None   # attention logit scale; None means 1/sqrt(head_dim)
     value_embeds: bool = False         # per-layer value-embedding tables and gates are drawn
     ve_gate_channels: int = 12         # input channels the value-embedding gate reads
+    looped: bool = False               # two-pass trunk: pass embeddings and routing gate logits
 
     @property
     def attn_scale(self) -> float:
@@ -82,6 +85,9 @@ PRESETS: Dict[str, Preset] = {
     # nanochat d24: width 1536, 12 heads of 128, V=32768, T=2048, B=8, bf16, seeded lambda/mu
     "d24": Preset("d24", 24, 1536, 12, 12, 128, 6144, 32768, 2048, 8, "bf16", short_window=1024,
                   lambda_range=(0.9, 1.1), mu_range=(0.0, 0.2)),
+    # looped two-pass d24 (B=4)
+    "d24loop": Preset("d24loop", 24, 1536, 12, 12, 128, 6144, 32768, 2048, 4, "bf16", short_window=1024,
+                      lambda_range=(0.9, 1.1), mu_range=(0.0, 0.2), looped=True),
     # d24 with grouped-query attention (4 KV heads) and value embeddings
     "d24gve": Preset("d24gve", 24, 1536, 12, 4, 128, 6144, 32768, 2048, 8, "bf16", short_window=1024,
                      lambda_range=(0.9, 1.1), mu_range=(0.0, 0.2), value_embeds=True),
@@ -140,6 +146,8 @@ class Weights:
     x0_lambda: np.ndarray           # [L] float32
     ve: Optional[List[np.ndarray]] = None       # L x [V, Hkv*D] value-embedding tables
     ve_gate: Optional[List[np.ndarray]] = None  # L x [Hkv, ve_gate_channels] gate weights
+    pass_emb: Optional[np.ndarray] = None       # [2, C] per-pass embeddings (looped)
+    gate_logit: Optional[np.ndarray] = None     # [L] float32 routing gate logits (looped)
 
     def value(self, a: np.ndarray) -> np.ndarray:
         return bf16_bits_to_f32(a) if self.dtype == "bf16" else a
@@ -192,7 +200,13 @@ def make_weights(p: Preset, rng: Optional[np.random.Generator] = None) -> Weight
         for _ in range(L):
             ve.append(_gauss(rng, (V, Hkv * D), 1, p.dtype))
             ve_gate.append(_gauss(rng, (Hkv, p.ve_gate_channels), p.ve_gate_channels, p.dtype))
-    return Weights(p.dtype, wte, wq, wk, wv, wo, w1, w2, lm_head, lam, mu, ve, ve_gate)
+    pass_emb = gate_logit = None
+    if p.looped:
+        pass_emb = _gauss(rng, (2, C), C, p.dtype)
+        gate_logit = (np.float32(math.log(math.expm1(0.05)))
+                      + np.float32(0.1) * rng.standard_normal(L, dtype=np.float32)).astype(np.float32)
+    return Weights(p.dtype, wte, wq, wk, wv, wo, w1, w2, lm_head, lam, mu, ve, ve_gate,
+                   pass_emb, gate_logit)
 
 
 def make_tokens(p: Preset, rng: np.random.Generator, batch: Optional[int] = None,

@@ -18,6 +18,9 @@ Sources (cited by page title and section):
        sections 2 (shifted targets), 5.2-5.4 (attention order, block, LM head).
   [S]  "nanochat depth sweep" -- section "Architecture" (SSSL windows, last
        block full context, x0 re-injection, +-15 softcap).
+  [L]  "looped-nanochat-d24" -- section "What is the routing loop?" (two-pass
+       trunk, attention-logit prior from pass 1, softplus gate, pass
+       embeddings).
 
 Readings where the pages are silent or disagree (each frozen as a config field
 so the oracle and the GPU path cannot silently diverge):
@@ -37,6 +40,10 @@ so the oracle and the GPU path cannot silently diverge):
   * GQA head map: query head h reads KV head floor(h * Hkv / H).
   * ignored targets (-1) contribute a per-token loss of 0 and are excluded
     from the mean; with no valid target the mean is NaN.
+  * looped two-pass trunk (when cfg.looped): pass p (0, 1) starts from
+    RMSNorm(W_E[t] + pass_emb[p]); pass-2 layer l takes the prior of pass-1
+    layer l (identity routing), shares that layer's window mask and scale,
+    and the loss comes from pass 2 only.
   * value embeddings (when cfg.value_embeds): the gate reads the first 12
     channels of the attention block's normalised input x_tilde (the input of
     the Q/K/V projections), and the mixed value v + g * e is what attention
@@ -57,7 +64,8 @@ import numpy as np
 __all__ = [
     "rms_norm", "rope_angles", "apply_rope", "layer_windows", "visible_mask",
     "attention", "linear", "relu_squared", "softcap", "token_losses",
-    "mean_loss", "has_ve", "value_embed_mix", "block", "forward_row", "forward",
+    "mean_loss", "has_ve", "value_embed_mix", "softplus", "attention_with_prior", "block",
+    "forward_row", "forward",
 ]
 
 
@@ -144,7 +152,8 @@ def visible_mask(T: int, window: int) -> np.ndarray:
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, window: int, scale: float) -> np.ndarray:
     """Windowed causal softmax attention for one row.
 
-    q: [T, H, D]; k, v: [T, Hkv, D] with H a multiple of Hkv.  Returns [T, H, D].
+    q: [T, H, D]; k: [T, Hkv, D]; v: [T, Hkv, Dv] with H a multiple of Hkv.  Returns
+    [T, H, Dv].
     [M] "Scaled Dot-Product Attention with Sliding Window": o_{h,i} is the
     softmax-weighted sum of v_{h,j} over visible keys j.  Computed as an
     explicit masked T x T matrix per head.  Query head h reads KV head
@@ -154,7 +163,7 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, window: int, scale: f
     T, H, D = q.shape
     Hkv = k.shape[1]
     mask = visible_mask(T, window)
-    out = np.empty_like(q)
+    out = np.empty((T, H, v.shape[-1]), dtype=np.result_type(q, v))
     for h in range(H):
         g = (h * Hkv) // H
         s = scale * (q[:, h, :] @ k[:, g, :].T)
@@ -163,6 +172,36 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, window: int, scale: f
         e = np.exp(s - m)
         a = e / np.sum(e, axis=-1, keepdims=True)
         out[:, h, :] = a @ v[:, g, :]
+    return out
+
+
+def softplus(z):
+    """log(1 + exp(z)), the routing gate of [L] "What is the routing loop?" (g = softplus of
+    the per-layer gate logit); written as max(z, 0) + log1p(exp(-|z|)) to stay finite."""
+    z = np.asarray(z, dtype=np.float64)
+    return np.maximum(z, 0.0) + np.log1p(np.exp(-np.abs(z)))
+
+
+def attention_with_prior(q: np.ndarray, k: np.ndarray, v: np.ndarray, q1: np.ndarray,
+                         k1: np.ndarray, g: float, window: int, scale: float) -> np.ndarray:
+    """Windowed causal attention whose logits carry the pass-1 prior.
+
+    [L] "What is the routing loop?": attn_logits = q2 k2^T / sqrt(D) + g q1 k1^T / sqrt(D)
+    (here with the configured scale in place of 1/sqrt(D)), then the usual masked softmax over
+    the visible keys and the weighted sum of v.  q, q1: [T, H, D]; k, k1, v: [T, Hkv, D].
+    Explicit T x T logits per head, as written on the page.
+    """
+    T, H, D = q.shape
+    Hkv = k.shape[1]
+    mask = visible_mask(T, window)
+    out = np.empty((T, H, v.shape[-1]), dtype=np.result_type(q, v))
+    for h in range(H):
+        gh = (h * Hkv) // H
+        s = scale * (q[:, h, :] @ k[:, gh, :].T) + g * scale * (q1[:, h, :] @ k1[:, gh, :].T)
+        s = np.where(mask, s, -np.inf)
+        m = np.max(s, axis=-1, keepdims=True)
+        e = np.exp(s - m)
+        out[:, h, :] = (e / np.sum(e, axis=-1, keepdims=True)) @ v[:, gh, :]
     return out
 
 
@@ -240,7 +279,7 @@ def _get(params: Any, name: str, layer: Optional[int] = None):
 
 def block(x: np.ndarray, x0: np.ndarray, l: int, cfg: Any, params: Any, window: int,
           cos: np.ndarray, sin: np.ndarray, dt, internals: Optional[Dict] = None,
-          tokens: Optional[np.ndarray] = None) -> np.ndarray:
+          tokens: Optional[np.ndarray] = None, prior: Optional[tuple] = None) -> np.ndarray:
     """One transformer layer on one row x [T, C].
 
     [M] "Residual Stream with Learnable Scalars" and "High-Level Forward Pass"
@@ -250,6 +289,7 @@ def block(x: np.ndarray, x0: np.ndarray, l: int, cfg: Any, params: Any, window: 
     q and k, per-head RMSNorm of q and k, windowed attention, merge heads,
     output projection.  With value embeddings on a selected layer ([M] "Value Embeddings
     (ResFormer)"), v is mixed with the gated table rows of ``tokens`` before attention.
+    ``prior`` = (q1, k1, g) adds the pass-1 logit prior of the looped trunk ([L]).
     """
     T, C = x.shape
     H, Hkv, D = cfg.n_head, cfg.n_kv_head, cfg.head_dim
@@ -268,7 +308,10 @@ def block(x: np.ndarray, x0: np.ndarray, l: int, cfg: Any, params: Any, window: 
         v = value_embed_mix(v, e, xn[:, :wg.shape[1]], wg)
     q = rms_norm(apply_rope(q, cos, sin), eps)
     k = rms_norm(apply_rope(k, cos, sin), eps)
-    o = attention(q, k, v, window, cfg.attn_scale)
+    if prior is None:
+        o = attention(q, k, v, window, cfg.attn_scale)
+    else:
+        o = attention_with_prior(q, k, v, prior[0], prior[1], prior[2], window, cfg.attn_scale)
     x = x + linear(o.reshape(T, H * D), np.asarray(_get(params, "wo", l), dtype=dt))
     xa = x
     xm = rms_norm(x, eps)
@@ -296,13 +339,29 @@ def forward_row(cfg: Any, params: Any, tokens: np.ndarray, targets: Optional[np.
         windows = layer_windows(cfg.window_pattern, cfg.short_window, cfg.seq_len, cfg.n_layer)
     cos, sin = rope_angles(T, cfg.head_dim, cfg.rope_base, dtype=dt)
     wte = np.asarray(_get(params, "wte"))
-    x = rms_norm(np.asarray(wte[tokens], dtype=dt), eps)
-    x0 = x
     res: Dict[str, Any] = {}
     layers = []
+    priors = None
+    if getattr(cfg, "looped", False):
+        # [L] "What is the routing loop?": pass 1 runs the ordinary trunk and keeps every
+        # layer's normalised, rotated q and k; pass 2 starts again from the embeddings.
+        pe = np.asarray(_get(params, "pass_emb"), dtype=dt)
+        gates = softplus(np.asarray(_get(params, "gate_logit"), dtype=np.float64))
+        x = rms_norm(np.asarray(wte[tokens], dtype=dt) + pe[0], eps)
+        x0 = x
+        priors = []
+        for l in range(cfg.n_layer):
+            cap: Dict[str, Any] = {}
+            x = block(x, x0, l, cfg, params, windows[l], cos, sin, dt, cap, tokens=tokens)
+            priors.append((cap["q"], cap["k"], float(gates[l])))
+        x = rms_norm(np.asarray(wte[tokens], dtype=dt) + pe[1], eps)
+    else:
+        x = rms_norm(np.asarray(wte[tokens], dtype=dt), eps)
+    x0 = x
     for l in range(cfg.n_layer):
         internals = {} if want_internals else None
-        x = block(x, x0, l, cfg, params, windows[l], cos, sin, dt, internals, tokens=tokens)
+        x = block(x, x0, l, cfg, params, windows[l], cos, sin, dt, internals, tokens=tokens,
+                  prior=None if priors is None else priors[l])
         if want_internals:
             layers.append(internals)
     xf = rms_norm(x, eps)
@@ -341,7 +400,8 @@ def forward(cfg: Any, params: Any, tokens: np.ndarray, targets: Optional[np.ndar
     arrays and ``wq``, ``wk``, ``wv``, ``wo``, ``w1``, ``w2`` to per-layer
     sequences of row-major [out, in] arrays (any float dtype; converted to
     ``dtype`` one layer at a time); with ``cfg.value_embeds`` also ``ve``
-    (per layer [V, Hkv*D]) and ``ve_gate`` (per layer [Hkv, 12]).
+    (per layer [V, Hkv*D]) and ``ve_gate`` (per layer [Hkv, 12]); with
+    ``cfg.looped`` also ``pass_emb`` ([2, C]) and ``gate_logit`` ([L]).
     """
     rows = list(range(tokens.shape[0])) if rows is None else list(rows)
     out_l, out_z = [], []

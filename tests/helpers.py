@@ -40,6 +40,7 @@ def oracle_params(w: gptdata.Weights) -> dict:
         "wq": _LazyLayers(w, w.wq), "wk": _LazyLayers(w, w.wk), "wv": _LazyLayers(w, w.wv),
         "wo": _LazyLayers(w, w.wo), "w1": _LazyLayers(w, w.w1), "w2": _LazyLayers(w, w.w2),
         **({"ve": _LazyLayers(w, w.ve), "ve_gate": _LazyLayers(w, w.ve_gate)} if w.ve is not None else {}),
+        **({"pass_emb": w.value(w.pass_emb), "gate_logit": w.gate_logit} if w.pass_emb is not None else {}),
     }
 
 
@@ -56,6 +57,9 @@ def dense_params(p: gptdata.Preset, seed: int = 0) -> dict:
     if w.ve is not None:
         d["ve"] = [m.astype(np.float64) for m in w.ve]
         d["ve_gate"] = [m.astype(np.float64) for m in w.ve_gate]
+    if w.pass_emb is not None:
+        d["pass_emb"] = w.pass_emb.astype(np.float64)
+        d["gate_logit"] = w.gate_logit.astype(np.float64).copy()
     return d
 
 

@@ -517,4 +517,89 @@ def pin_value_embedding_gate_scale_invariance():
     assert not np.allclose(ia["v"], base["v"])
 
 
+# ----------------------------------------------------------------------------- looped trunk
+
+def pin_softplus_library():
+    """The routing gate's softplus against numpy's log(exp(0) + exp(z)), from -1000 to 1000."""
+    z = np.concatenate([np.linspace(-60, 60, 241), [-1000.0, -745.0, 0.0, 745.0, 1000.0]])
+    assert np.allclose(oracle.softplus(z), np.logaddexp(0.0, z), rtol=1e-15, atol=0)
+    assert oracle.softplus(0.0) == math.log(2.0)
+
+
+def pin_looped_augmented_width():
+    """[L] "What is the routing loop?": the prior q2 k2^T + g q1 k1^T equals ordinary attention
+    over the augmented-width Q = [q2, sqrt(g) q1], K = [k2, sqrt(g) k1] (GQA 4:2, two windows)."""
+    rng = np.random.default_rng(8)
+    T, H, Hkv, D = 9, 4, 2, 5
+    q, q1 = rng.standard_normal((T, H, D)), rng.standard_normal((T, H, D))
+    k, k1, v = (rng.standard_normal((T, Hkv, D)) for _ in range(3))
+    for g, w in ((0.37, 4), (2.5, 9)):
+        r = math.sqrt(g)
+        aug = oracle.attention(np.concatenate([q, r * q1], -1), np.concatenate([k, r * k1], -1), v, w, 0.6)
+        got = oracle.attention_with_prior(q, k, v, q1, k1, g, w, 0.6)
+        assert np.allclose(got, aug, rtol=1e-12, atol=1e-12)
+
+
+def _loop_preset(**kw):
+    base = dict(n_layer=2, n_head=2, n_kv_head=2, head_dim=8, d_model=16, looped=True)
+    base.update(kw)
+    return small_preset(**base)
+
+
+def pin_looped_zero_gate_is_plain_with_pass_embedding():
+    """Gate logits of -1000 make g = 0, so pass 1 has no effect and the result is the plain
+    model whose embedding rows are W_E[t] + pass_emb[1] (bitwise)."""
+    p = _loop_preset(n_layer=3)
+    prm = dense_params(p)
+    prm["gate_logit"] = np.full(p.n_layer, -1000.0)
+    rows = _tokens(p)
+    a = _fwd(p, prm, rows[:, :-1], rows[:, 1:], want_logits=True)
+    plain = dict(prm)
+    plain["wte"] = prm["wte"] + prm["pass_emb"][1]
+    b = _fwd(p.with_(looped=False), plain, rows[:, :-1], rows[:, 1:], want_logits=True)
+    assert np.array_equal(a["logits"], b["logits"]) and np.array_equal(a["losses"], b["losses"])
+
+
+def pin_looped_equal_passes_closed_form():
+    """With equal pass embeddings, pass 1's layer-0 q and k are pass 2's own, so (gate of
+    layer 1 off) layer 0's logits become (1 + g_0) times the plain ones: the looped model
+    equals plain blocks with attention scale s(1 + softplus(logit_0)) on layer 0."""
+    p = _loop_preset()
+    prm = dense_params(p)
+    prm["pass_emb"] = np.stack([prm["pass_emb"][0], prm["pass_emb"][0]])
+    prm["gate_logit"] = np.array([0.8, -1000.0])
+    rows = _tokens(p)
+    tok, tgt = rows[0, :-1], rows[0, 1:]
+    got = _fwd(p, prm, tok[None], tgt[None], want_logits=True)
+    T = p.seq_len
+    cos, sin = oracle.rope_angles(T, p.head_dim, p.rope_base)
+    win = oracle.layer_windows(p.window_pattern, p.short_window, T, p.n_layer)
+    g0 = math.log1p(math.exp(0.8))
+    x = oracle.rms_norm(prm["wte"][tok] + prm["pass_emb"][0], p.norm_eps)
+    x0 = x
+    base = p.with_(looped=False)
+    x = oracle.block(x, x0, 0, base.with_(qk_scale=p.attn_scale * (1.0 + g0)), prm, win[0], cos, sin, np.float64)
+    x = oracle.block(x, x0, 1, base, prm, win[1], cos, sin, np.float64)
+    z = oracle.softcap(oracle.rms_norm(x, p.norm_eps) @ prm["lm_head"].T, p.softcap)
+    assert np.allclose(got["logits"][0], z, rtol=1e-10, atol=1e-10)
+
+
+def pin_looped_prior_comes_from_pass_one():
+    """Different pass embeddings give pass 1 different q, k than pass 2 has, so the single
+    layer's result departs from the equal-passes closed form (which it meets when they match)."""
+    p = _loop_preset(n_layer=1)
+    prm = dense_params(p)
+    rows = _tokens(p)
+    tok, tgt = rows[:, :-1], rows[:, 1:]
+    g0 = float(oracle.softplus(prm["gate_logit"][0]))
+    plain = dict(prm)
+    plain["wte"] = prm["wte"] + prm["pass_emb"][1]
+    ref = _fwd(p.with_(looped=False, qk_scale=p.attn_scale * (1.0 + g0)), plain, tok, tgt)
+    got = _fwd(p, prm, tok, tgt)
+    assert not np.allclose(got["losses"], ref["losses"], rtol=1e-6, atol=1e-6)
+    same = dict(prm)
+    same["pass_emb"] = np.stack([prm["pass_emb"][1], prm["pass_emb"][1]])
+    assert np.allclose(_fwd(p, same, tok, tgt)["losses"], ref["losses"], rtol=1e-10, atol=1e-10)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

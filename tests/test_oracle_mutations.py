@@ -12,7 +12,8 @@ import oracle_pins as P
 
 _orig = {n: getattr(oracle, n) for n in ("apply_rope", "visible_mask", "relu_squared", "softcap",
                                           "token_losses", "rms_norm", "attention", "block", "linear",
-                                          "has_ve", "value_embed_mix")}
+                                          "has_ve", "value_embed_mix", "softplus",
+                                          "attention_with_prior")}
 
 
 def _rope_sign(u, cos, sin):
@@ -173,6 +174,28 @@ def _ve_gate_unnormed(monkeypatch):
     monkeypatch.setattr(oracle, "value_embed_mix", mix)
 
 
+def _prior_from_pass_two(q, k, v, q1, k1, g, window, scale):
+    return _orig["attention_with_prior"](q, k, v, q, k, g, window, scale)
+
+
+def _routing_reversed(monkeypatch):
+    """Pass-2 layer l takes the prior of pass-1 layer L-1-l."""
+    real_block = _orig["block"]
+    caps = []
+
+    def blk(x, x0, l, cfg, params, window, cos, sin, dt, internals=None, tokens=None, prior=None):
+        if prior is None and getattr(cfg, "looped", False) and internals is not None and "q" not in internals:
+            out = real_block(x, x0, l, cfg, params, window, cos, sin, dt, internals, tokens=tokens)
+            caps.append((internals["q"], internals["k"]))
+            return out
+        if prior is not None:
+            n = cfg.n_layer
+            q1, k1 = caps[-n:][n - 1 - l]
+            prior = (q1, k1, prior[2])
+        return real_block(x, x0, l, cfg, params, window, cos, sin, dt, internals, tokens=tokens, prior=prior)
+    monkeypatch.setattr(oracle, "block", blk)
+
+
 MUTATIONS = {
     "rope_sign": (lambda mp: mp.setattr(oracle, "apply_rope", _rope_sign), [P.pin_rope_worked_example]),
     "rope_interleaved": (lambda mp: mp.setattr(oracle, "apply_rope", _rope_interleaved),
@@ -201,6 +224,11 @@ MUTATIONS = {
                                  [P.pin_value_embedding_worked_example, P.pin_value_embedding_zero_gate]),
     "ve_on_even_layers": (lambda mp: mp.setattr(oracle, "has_ve", _ve_even_layers), [P.pin_ve_layer_rule]),
     "ve_gate_from_unnormed_stream": (_ve_gate_unnormed, [P.pin_value_embedding_gate_scale_invariance]),
+    "gate_without_softplus": (lambda mp: mp.setattr(oracle, "softplus", lambda z: np.asarray(z, dtype=np.float64)),
+                              [P.pin_softplus_library, P.pin_looped_equal_passes_closed_form]),
+    "prior_from_pass_two": (lambda mp: mp.setattr(oracle, "attention_with_prior", _prior_from_pass_two),
+                            [P.pin_looped_prior_comes_from_pass_one, P.pin_looped_augmented_width]),
+    "routing_reversed": (_routing_reversed, [P.pin_looped_equal_passes_closed_form]),
 }
 
 
