@@ -28,17 +28,28 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E bandwidth (published)
 
 
+def _attn_flops(p, w, prior=False):
+    """Attention FLOPs per token of one layer: QK^T and PV over the visible keys (average over
+    positions of min(t+1, w)); the looped prior adds a second QK^T of the same width."""
+    T = p.seq_len
+    w = min(w, T)
+    avg = (w * (w + 1) / 2 + (T - w) * w) / T
+    return (6 if prior else 4) * p.n_head * p.head_dim * avg
+
+
 def flops_per_token(p, windows):
-    """Algorithmic forward FLOPs per token: every linear (2 per multiply-add) plus attention's
-    QK^T and PV over the visible keys only (average over positions of min(t+1, w))."""
-    C, H, Hkv, D, F, V, T = p.d_model, p.n_head, p.n_kv_head, p.head_dim, p.mlp_dim, p.vocab, p.seq_len
-    lin = 2 * (C * (H + 2 * Hkv) * D + H * D * C + 2 * C * F)
-    att = 0.0
-    for w in windows:
-        w = min(w, T)
-        avg = (w * (w + 1) / 2 + (T - w) * w) / T
-        att += 4 * H * D * avg
-    return p.n_layer * lin + 2 * C * V + att
+    """Algorithmic forward FLOPs per token: every linear (2 per multiply-add) plus attention
+    over the visible keys only.  Looped trunk: pass 1 needs L-1 full layers and the last
+    layer's projection (its q, k), pass 2 all L layers with the prior."""
+    C, H, Hkv, D, F, V = p.d_model, p.n_head, p.n_kv_head, p.head_dim, p.mlp_dim, p.vocab
+    qkv = 2 * C * (H + 2 * Hkv) * D
+    lin = qkv + 2 * (H * D * C + 2 * C * F)
+    L = p.n_layer
+    if getattr(p, "looped", False):
+        pass1 = (L - 1) * lin + qkv + sum(_attn_flops(p, w) for w in windows[:-1])
+        pass2 = L * lin + sum(_attn_flops(p, w, prior=True) for w in windows)
+        return pass1 + pass2 + 2 * C * V
+    return L * lin + 2 * C * V + sum(_attn_flops(p, w) for w in windows)
 
 
 KINDS = {  # gpt_kernel_kind -> name
@@ -47,14 +58,14 @@ KINDS = {  # gpt_kernel_kind -> name
 
 
 def flops_per_launch(p, windows):
-    """Algorithmic FLOPs of one launch of each kind (attention: the mean over the layers)."""
-    M, C, H, Hkv, D, F, V, T = (p.batch * p.seq_len, p.d_model, p.n_head, p.n_kv_head, p.head_dim,
-                                p.mlp_dim, p.vocab, p.seq_len)
-    att = []
-    for w in windows:
-        w = min(w, T)
-        att.append(4.0 * p.batch * H * D * (w * (w + 1) / 2 + (T - w) * w))
-    return {1: 2.0 * M * C * (H + 2 * Hkv) * D, 2: sum(att) / len(att), 3: 2.0 * M * H * D * C,
+    """Algorithmic FLOPs of one launch of each kind (attention: the mean over its launches)."""
+    M, C, H, Hkv, D, F, V = (p.batch * p.seq_len, p.d_model, p.n_head, p.n_kv_head, p.head_dim,
+                             p.mlp_dim, p.vocab)
+    if getattr(p, "looped", False):
+        att = [_attn_flops(p, w) for w in windows[:-1]] + [_attn_flops(p, w, True) for w in windows]
+    else:
+        att = [_attn_flops(p, w) for w in windows]
+    return {1: 2.0 * M * C * (H + 2 * Hkv) * D, 2: M * sum(att) / len(att), 3: 2.0 * M * H * D * C,
             4: 2.0 * M * C * F, 5: 2.0 * M * F * C, 6: 2.0 * M * C * V}
 
 
@@ -154,7 +165,11 @@ def main():
 
     # Per-kernel time inside the forward pass: kernel start/end stamps on HIP events, for every
     # launch of one kind, over separate measurement steps on the forward's own stream.
-    per_step = {1: p.n_layer, 2: p.n_layer, 3: p.n_layer, 4: p.n_layer, 5: p.n_layer, 6: 1}
+    L = p.n_layer
+    if getattr(p, "looped", False):  # pass 1 stops after its last layer's projection
+        per_step = {1: 2 * L, 2: 2 * L - 1, 3: 2 * L - 1, 4: 2 * L - 1, 5: 2 * L - 1, 6: 1}
+    else:
+        per_step = {1: L, 2: L, 3: L, 4: L, 5: L, 6: 1}
     fpl = flops_per_launch(p, windows)
     kern = {}
     for kind in KINDS:

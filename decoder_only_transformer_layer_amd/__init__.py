@@ -42,7 +42,7 @@ class gpt_cfg(ctypes.Structure):
         ("window", ctypes.POINTER(ctypes.c_int32)),
         ("softcap", ctypes.c_float), ("rope_base", ctypes.c_float), ("attn_scale", ctypes.c_float),
         ("norm_eps", ctypes.c_float), ("dtype", ctypes.c_int32),
-        ("has_ve", ctypes.POINTER(ctypes.c_uint8)),
+        ("has_ve", ctypes.POINTER(ctypes.c_uint8)), ("looped", ctypes.c_int32),
     ]
 
 
@@ -54,6 +54,7 @@ class gpt_weights(ctypes.Structure):
         ("wv", ctypes.POINTER(ctypes.c_void_p)), ("wo", ctypes.POINTER(ctypes.c_void_p)),
         ("w1", ctypes.POINTER(ctypes.c_void_p)), ("w2", ctypes.POINTER(ctypes.c_void_p)),
         ("ve", ctypes.POINTER(ctypes.c_void_p)), ("ve_gate", ctypes.POINTER(ctypes.c_void_p)),
+        ("pass_emb", ctypes.c_void_p), ("gate_logit", ctypes.c_void_p),
     ]
 
 
@@ -164,7 +165,8 @@ def make_cfg(p: Any, batch: Optional[int] = None, windows: Optional[Sequence[int
                 ctypes.cast(win, ctypes.POINTER(ctypes.c_int32)),
                 p.softcap, p.rope_base, p.attn_scale, p.norm_eps,
                 GPT_BF16 if p.dtype == "bf16" else GPT_F32,
-                None if ve is None else ctypes.cast(ve, ctypes.POINTER(ctypes.c_uint8)))
+                None if ve is None else ctypes.cast(ve, ctypes.POINTER(ctypes.c_uint8)),
+                1 if getattr(p, "looped", False) else 0)
     c._win, c._ve = win, ve
     return c
 
@@ -273,7 +275,8 @@ class DeviceModel:
 
     ``weights`` is any object with attributes wte, lm_head, resid_lambda, x0_lambda and
     per-layer lists wq, wk, wv, wo, w1, w2 (numpy arrays: uint16 bf16 bits or float32), plus
-    per-layer ve and ve_gate lists when the configuration has value embeddings.
+    per-layer ve and ve_gate lists when the configuration has value embeddings, and
+    pass_emb ([2, C]) and gate_logit ([L] float32) for the looped trunk.
     """
 
     def __init__(self, p: Any, weights: Any, batch: Optional[int] = None, device: str = "cuda",
@@ -305,11 +308,17 @@ class DeviceModel:
                                                          for m in self.t[n]])
             ve_ptr = ctypes.cast(arrs["ve"], ctypes.POINTER(ctypes.c_void_p))
             gate_ptr = ctypes.cast(arrs["ve_gate"], ctypes.POINTER(ctypes.c_void_p))
+        pe_ptr = gl_ptr = None
+        if getattr(p, "looped", False):
+            self.t["pass_emb"] = to_device(weights.pass_emb, dt, device)
+            self.t["gate_logit"] = torch.from_numpy(np.asarray(weights.gate_logit, np.float32)).to(device)
+            pe_ptr, gl_ptr = self.t["pass_emb"].data_ptr(), self.t["gate_logit"].data_ptr()
         self._arrs = arrs
         self.w = gpt_weights(self.t["wte"].data_ptr(), self.t["lm_head"].data_ptr(),
                              self.t["resid_lambda"].data_ptr(), self.t["x0_lambda"].data_ptr(),
                              *[ctypes.cast(arrs[n], ctypes.POINTER(ctypes.c_void_p))
-                               for n in ("wq", "wk", "wv", "wo", "w1", "w2")], ve_ptr, gate_ptr)
+                               for n in ("wq", "wk", "wv", "wo", "w1", "w2")], ve_ptr, gate_ptr,
+                             pe_ptr, gl_ptr)
         self.ws_bytes = gpt_workspace_bytes(self.cfg)
         self.ws = torch.empty(self.ws_bytes + 256, dtype=torch.uint8, device=device)
         off = (-self.ws.data_ptr()) % 256

@@ -21,7 +21,7 @@ inline size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 struct Layout {
-  size_t flags, x, x0, xn, qk, vt, o, h, cs, ssp, partial, tgt, total;
+  size_t flags, x, x0, xn, qk, vt, o, h, cs, ssp, partial, tgt, qk1, total;
   int nnb;
 };
 
@@ -62,6 +62,8 @@ gpt_status validate(const gpt_cfg* c) {
     if (c->d_model < VE_GATE_CH) return GPT_E_UNSUPPORTED;
     if (c->dtype == GPT_BF16 && c->head_dim != 128) return GPT_E_UNSUPPORTED;  // fused epilogue only
   }
+  if (c->looped != 0 && c->looped != 1) return GPT_E_INVALID_ARG;
+  if (c->looped && c->dtype == GPT_BF16 && c->head_dim != 128) return GPT_E_UNSUPPORTED;
   return GPT_OK;
 }
 
@@ -90,6 +92,9 @@ Layout plan(const gpt_cfg* c) {
   L.ssp = off; off += up(M * (size_t)(C / 64) * 4);  // slices are >= 64 columns wide
   L.partial = off; off += up(M * (size_t)L.nnb * 4);
   L.tgt = off; off += up(M * 4);
+  // looped trunk: every pass-1 layer's q, k (bf16: the qk layout; fp32: the whole qkv rows)
+  L.qk1 = off;
+  if (c->looped) off += up((size_t)c->n_layer * M * (bf ? (H + Hkv) * D * 2 : (H + 2 * Hkv) * D * 4));
   L.total = off;
   return L;
 }
@@ -144,7 +149,7 @@ gpt_status lm_head_ce(bool bf, const void* xf, const void* wu, const int32_t* ta
                       unsigned* flags, hipStream_t s, const Timer& tm, const float* rs_ssp = nullptr,
                       float eps = 0.f) {
   GemmArgs g = gemm_args(xf, C, wu, V, C, M, nullptr, 0);
-  if (rs_ssp) { g.rs_ssp = rs_ssp; g.rs_n = C / gemm_resid_slice_cols(C); g.rs_c = (float)C; g.eps = eps; }
+  if (rs_ssp) { g.rs_ssp = rs_ssp; g.rs_n = C / gemm_resid_slice_cols(M, C); g.rs_c = (float)C; g.eps = eps; }
   g.targets = targets; g.partial = partial; g.tgt_logit = tgt; g.logits = logits;
   g.nnb = nnb; g.cap = cap;
   TIMED(tm, GPT_KERNEL_LM_HEAD, gemm(bf, EPI_CE, g, s));
@@ -200,6 +205,9 @@ gpt_status gpt_fwd_loss_timed(const gpt_cfg* c, const gpt_weights* w, const int3
                            !aligned(w->ve_gate[l], 4)))
         return GPT_E_INVALID_ARG;
   }
+  if (c->looped && (!w->pass_emb || !w->gate_logit || !aligned(w->pass_emb, 16) ||
+                    !aligned(w->gate_logit, 4)))
+    return GPT_E_INVALID_ARG;
   if (targets && (!loss || !mean_loss)) return GPT_E_INVALID_ARG;
   if (!targets && !logits) return GPT_E_INVALID_ARG;
   const void* ptrs16[] = {w->wte, w->lm_head};
@@ -236,72 +244,87 @@ gpt_status gpt_fwd_loss_timed(const gpt_cfg* c, const gpt_weights* w, const int3
 
   CK(launch_clear_u32(flags, 16, s));
   CK(launch_rope_table(cs, T, D, c->rope_base, s));
-  CK(launch_embed_norm(tokens, w->wte, bf, w->resid_lambda, w->x0_lambda, x0, x, xn, M, C, V, eps,
-                       flags, s));
   const int nqk = (H + Hkv) * D;
   const int nqkv = (H + 2 * Hkv) * D;
   float* ssp = (float*)(ws + L.ssp);
-  const int nsl = C / gemm_resid_slice_cols(C);  // slices the residual GEMMs write
-  if (bf) {
-    // bf16 path: every RMSNorm after the first is applied as a row scale inside the GEMM that
-    // consumes it (RMSNorm(x) W^T = (x W^T) / rms(x)).  The residual epilogues keep x in fp32,
-    // apply the next layer's x0 mix, and emit bf16(x) plus per-slice sums of squares.
-    bf16_t* xb = (bf16_t*)xn;
+  const int nsl = C / gemm_resid_slice_cols(M, C);  // slices the residual GEMMs write
+  // The looped trunk runs two passes: pass 0 keeps every layer's q, k in the qk1 cache (and
+  // stops after the last layer's projection, the only part of it pass 2 reads); pass 1 adds
+  // the layer's cached prior to its attention logits.  Otherwise there is one pass.
+  const size_t es = bf ? 2 : 4;
+  const size_t qk1_layer = (size_t)M * (bf ? nqk : nqkv) * es;
+  for (int pass = c->looped ? 0 : 1; pass < 2; ++pass) {
+    const bool capture = c->looped && pass == 0, prior = c->looped && pass == 1;
+    const void* pe = c->looped ? (const char*)w->pass_emb + (size_t)pass * C * es : nullptr;
+    CK(launch_embed_norm(tokens, w->wte, bf, w->resid_lambda, w->x0_lambda, x0, x, xn, M, C, V,
+                         eps, flags, s, pe));
     for (int l = 0; l < c->n_layer; ++l) {
-      GemmArgs g = gemm_args(xn, C, w->wq[l], nqkv, C, M, qk, nqk);
-      g.B1 = w->wk[l]; g.B2 = w->wv[l]; g.nseg0 = H * D; g.nseg1 = Hkv * D;
-      g.vt = vt; g.T = T; g.D = D; g.Hkv = Hkv; g.nqk = nqk; g.eps = eps;
-      const bool fused = D == 128;
-      if (fused) g.cs = cs;
-      if (l > 0) { g.rs_ssp = ssp; g.rs_n = nsl; g.rs_c = (float)C; }  // layer 0 reads normed xn
-      if (c->has_ve && c->has_ve[l]) {  // validated: D == 128, so the fused epilogue adds it
-        g.ve = (const bf16_t*)w->ve[l]; g.ve_gate = (const bf16_t*)w->ve_gate[l];
-        g.tokens = tokens; g.vocab = V;
-      }
-      TIMED(tm, GPT_KERNEL_QKV, launch_gemm_bf16(EPI_QKV, g, s));
-      if (!fused) CK(launch_qk_rope_norm(qk, true, nqk, cs, M, T, H + Hkv, D, eps, s));
+      void* qk_l = capture ? (void*)(ws + L.qk1 + l * qk1_layer) : qk;
+      const void* qk1_l = prior ? (const void*)(ws + L.qk1 + l * qk1_layer) : nullptr;
+      const float* gl = prior ? w->gate_logit : nullptr;
       const int win = c->window[l] < T ? c->window[l] : T;
-      TIMED(tm, GPT_KERNEL_ATTENTION, launch_attn_bf16(qk, vt, o, B, T, H, Hkv, D, win, c->attn_scale, s));
-      // x += o W_O^T, then bf16(x) and sums of squares for the MLP's norm
-      GemmArgs go = gemm_args(o, H * D, w->wo[l], C, H * D, M, x, C);
-      go.xb = xb; go.ssp = ssp; go.ssp_n = nsl;
-      TIMED(tm, GPT_KERNEL_ATTN_OUT, launch_gemm_bf16(EPI_RESID, go, s));
-      // h = relu(RMSNorm(x) W_1^T)^2
-      GemmArgs gu = gemm_args(xb, C, w->w1[l], F, C, M, hbuf, F);
-      gu.rs_ssp = ssp; gu.rs_n = nsl; gu.rs_c = (float)C; gu.eps = eps;
-      TIMED(tm, GPT_KERNEL_MLP_UP, launch_gemm_bf16(EPI_RELU2, gu, s));
-      // x += h W_2^T, then the next layer's x0 mix (if any), bf16(x) and sums of squares
-      GemmArgs gd = gemm_args(hbuf, F, w->w2[l], C, F, M, x, C);
-      gd.xb = xb; gd.ssp = ssp; gd.ssp_n = nsl;
-      if (l + 1 < c->n_layer) { gd.x0 = x0; gd.lam = w->resid_lambda; gd.mu = w->x0_lambda; gd.layer = l + 1; }
-      TIMED(tm, GPT_KERNEL_MLP_DOWN, launch_gemm_bf16(EPI_RESID, gd, s));
+      if (bf) {
+        // bf16: every RMSNorm after the first is applied as a row scale inside the GEMM that
+        // consumes it (RMSNorm(x) W^T = (x W^T) / rms(x)).  The residual epilogues keep x in
+        // fp32, apply the next layer's x0 mix, and emit bf16(x) plus per-slice sums of squares.
+        bf16_t* xb = (bf16_t*)xn;
+        GemmArgs g = gemm_args(xn, C, w->wq[l], nqkv, C, M, qk_l, nqk);
+        g.B1 = w->wk[l]; g.B2 = w->wv[l]; g.nseg0 = H * D; g.nseg1 = Hkv * D;
+        g.vt = vt; g.T = T; g.D = D; g.Hkv = Hkv; g.nqk = nqk; g.eps = eps;
+        const bool fused = D == 128;
+        if (fused) g.cs = cs;
+        if (l > 0) { g.rs_ssp = ssp; g.rs_n = nsl; g.rs_c = (float)C; }  // layer 0 reads normed xn
+        if (c->has_ve && c->has_ve[l]) {  // validated: D == 128, so the fused epilogue adds it
+          g.ve = (const bf16_t*)w->ve[l]; g.ve_gate = (const bf16_t*)w->ve_gate[l];
+          g.tokens = tokens; g.vocab = V;
+        }
+        TIMED(tm, GPT_KERNEL_QKV, launch_gemm_bf16(EPI_QKV, g, s));
+        if (!fused) CK(launch_qk_rope_norm(qk_l, true, nqk, cs, M, T, H + Hkv, D, eps, s));
+        if (capture && l + 1 == c->n_layer) break;
+        TIMED(tm, GPT_KERNEL_ATTENTION, launch_attn_bf16(qk_l, vt, o, B, T, H, Hkv, D, win,
+                                                         c->attn_scale, s, qk1_l, gl, l));
+        // x += o W_O^T, then bf16(x) and sums of squares for the MLP's norm
+        GemmArgs go = gemm_args(o, H * D, w->wo[l], C, H * D, M, x, C);
+        go.xb = xb; go.ssp = ssp; go.ssp_n = nsl;
+        TIMED(tm, GPT_KERNEL_ATTN_OUT, launch_gemm_bf16(EPI_RESID, go, s));
+        // h = relu(RMSNorm(x) W_1^T)^2
+        GemmArgs gu = gemm_args(xb, C, w->w1[l], F, C, M, hbuf, F);
+        gu.rs_ssp = ssp; gu.rs_n = nsl; gu.rs_c = (float)C; gu.eps = eps;
+        TIMED(tm, GPT_KERNEL_MLP_UP, launch_gemm_bf16(EPI_RELU2, gu, s));
+        // x += h W_2^T, then the next layer's x0 mix (if any), bf16(x) and sums of squares
+        GemmArgs gd = gemm_args(hbuf, F, w->w2[l], C, F, M, x, C);
+        gd.xb = xb; gd.ssp = ssp; gd.ssp_n = nsl;
+        if (l + 1 < c->n_layer) { gd.x0 = x0; gd.lam = w->resid_lambda; gd.mu = w->x0_lambda; gd.layer = l + 1; }
+        TIMED(tm, GPT_KERNEL_MLP_DOWN, launch_gemm_bf16(EPI_RESID, gd, s));
+      } else {
+        // q, k, v projections (one GEMM over the three weight segments)
+        GemmArgs g = gemm_args(xn, C, w->wq[l], nqkv, C, M, qk_l, nqkv);
+        g.B1 = w->wk[l]; g.B2 = w->wv[l]; g.nseg0 = H * D; g.nseg1 = Hkv * D;
+        CK(launch_gemm_f32(EPI_STORE, g, s));
+        if (c->has_ve && c->has_ve[l])
+          CK(launch_ve_mix_f32((float*)qk_l, nqkv, nqk, (const float*)xn, C, tokens, V,
+                               (const float*)w->ve[l], (const float*)w->ve_gate[l], M, Hkv, D, s));
+        // RoPE + QK-norm on the q and k heads
+        CK(launch_qk_rope_norm(qk_l, false, nqkv, cs, M, T, H + Hkv, D, eps, s));
+        if (capture && l + 1 == c->n_layer) break;
+        // windowed causal attention
+        CK(launch_attn_f32((const float*)qk_l, (float*)o, B, T, H, Hkv, D, win, c->attn_scale, s,
+                           (const float*)qk1_l, gl, l));
+        // x += o W_O^T
+        CK(launch_gemm_f32(EPI_RESID, gemm_args(o, H * D, w->wo[l], C, H * D, M, x, C), s));
+        // MLP: x += relu(RMSNorm(x) W_1^T)^2 W_2^T
+        CK(launch_mix_norm(x, x0, w->resid_lambda, w->x0_lambda, l, false, xn, false, M, C, eps, s));
+        CK(launch_gemm_f32(EPI_RELU2, gemm_args(xn, C, w->w1[l], F, C, M, hbuf, F), s));
+        CK(launch_gemm_f32(EPI_RESID, gemm_args(hbuf, F, w->w2[l], C, F, M, x, C), s));
+        // next layer's x0 mix and pre-attention norm, or the final norm
+        const bool more = l + 1 < c->n_layer;
+        CK(launch_mix_norm(x, x0, w->resid_lambda, w->x0_lambda, l + 1, more, xn, false, M, C, eps, s));
+      }
     }
-    return lm_head_ce(bf, xb, w->lm_head, targets, tokens, M, C, V, c->softcap, loss, mean_loss,
+  }
+  if (bf)
+    return lm_head_ce(bf, xn, w->lm_head, targets, tokens, M, C, V, c->softcap, loss, mean_loss,
                       logits, partial, tgt, L.nnb, flags, s, tm, ssp, eps);
-  }
-  for (int l = 0; l < c->n_layer; ++l) {
-    // q, k, v projections (one GEMM over the three weight segments)
-    GemmArgs g = gemm_args(xn, C, w->wq[l], nqkv, C, M, qk, nqkv);
-    g.B1 = w->wk[l]; g.B2 = w->wv[l]; g.nseg0 = H * D; g.nseg1 = Hkv * D;
-    CK(launch_gemm_f32(EPI_STORE, g, s));
-    if (c->has_ve && c->has_ve[l])
-      CK(launch_ve_mix_f32((float*)qk, nqkv, nqk, (const float*)xn, C, tokens, V,
-                           (const float*)w->ve[l], (const float*)w->ve_gate[l], M, Hkv, D, s));
-    // RoPE + QK-norm on the q and k heads
-    CK(launch_qk_rope_norm(qk, false, nqkv, cs, M, T, H + Hkv, D, eps, s));
-    // windowed causal attention
-    const int win = c->window[l] < T ? c->window[l] : T;
-    CK(launch_attn_f32((const float*)qk, (float*)o, B, T, H, Hkv, D, win, c->attn_scale, s));
-    // x += o W_O^T
-    CK(launch_gemm_f32(EPI_RESID, gemm_args(o, H * D, w->wo[l], C, H * D, M, x, C), s));
-    // MLP: x += relu(RMSNorm(x) W_1^T)^2 W_2^T
-    CK(launch_mix_norm(x, x0, w->resid_lambda, w->x0_lambda, l, false, xn, false, M, C, eps, s));
-    CK(launch_gemm_f32(EPI_RELU2, gemm_args(xn, C, w->w1[l], F, C, M, hbuf, F), s));
-    CK(launch_gemm_f32(EPI_RESID, gemm_args(hbuf, F, w->w2[l], C, F, M, x, C), s));
-    // next layer's x0 mix and pre-attention norm, or the final norm
-    const bool more = l + 1 < c->n_layer;
-    CK(launch_mix_norm(x, x0, w->resid_lambda, w->x0_lambda, l + 1, more, xn, false, M, C, eps, s));
-  }
   return lm_head_ce(bf, xn, w->lm_head, targets, tokens, M, C, V, c->softcap, loss, mean_loss,
                     logits, partial, tgt, L.nnb, flags, s, tm);
 }

@@ -40,21 +40,34 @@ __device__ __forceinline__ int swzv(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 // lazy rescaling: a row's reference maximum moves only when a new logit exceeds it by more than
 // 2^8 (in log2 units).  Numerator and denominator share the reference, so the result is exact;
 // the bound keeps every probability <= 256.
-constexpr int NW2 = 8, BQ2 = NW2 * 32, STG = 3;
+//
+// PRIOR (looped trunk, "looped-nanochat-d24", section "What is the routing loop?"): the logits
+// also carry g * <q1, k1> from pass 1's q and k of this layer (qk1, the qk layout), g =
+// softplus(gate_logit[layer]).  This is attention over the augmented width [q, g q1] . [k, k1]:
+// K tiles hold both halves (k from qk, k1 from qk1), the query fragments both (q1 scaled by g
+// before rounding), so S^T takes 2 D/16 k-steps; V and everything after are unchanged.  The
+// doubled query fragments need more registers than two wavefronts per SIMD allow, so this form
+// runs 4 wavefronts (128 queries) per block.
+constexpr int STG = 3;
 
-template <int D>
-__global__ __launch_bounds__(NW2 * 64, 1) void attn_bf16_kernel(const bf16* __restrict__ qk,
-                                                                  const bf16* __restrict__ vt,
-                                                                  bf16* __restrict__ o, int B, int T,
-                                                                  int H, int Hkv, int window, float c) {
+template <int D, int NW, bool PRIOR>
+__global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(const bf16* __restrict__ qk,
+                                                                const bf16* __restrict__ vt,
+                                                                bf16* __restrict__ o, int B, int T,
+                                                                int H, int Hkv, int window, float c,
+                                                                const bf16* __restrict__ qk1,
+                                                                const float* __restrict__ gate_logit,
+                                                                int layer) {
 #if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int BQ2 = NW * 32;          // queries per block
+  constexpr int NK = PRIOR ? 2 : 1;     // K halves (k, k1)
   constexpr int KCH = D / 8;            // 16-byte chunks per K row
   constexpr int DT = D / 32;            // 32-row tiles of O^T
-  constexpr int KS = D / 16;            // k-steps of S^T
+  constexpr int KS = D / 16;            // k-steps of S^T per K half
   constexpr int KROWS = 64 / KCH;       // K rows per 1 KB DMA instruction
-  constexpr int KI = BKV * KCH / 64 / NW2, VI = D * 8 / 64 / NW2;  // DMA instructions per wave
-  static_assert(KI * NW2 * 64 == BKV * KCH && VI * NW2 * 64 == D * 8, "DMA tiling");
-  __shared__ __attribute__((aligned(16))) bf16 Ks[STG][BKV * D];
+  constexpr int KI = BKV * KCH / 64 / NW, VI = D * 8 / 64 / NW;  // DMA instructions per wave
+  static_assert(KI * NW * 64 == BKV * KCH && VI * NW * 64 == D * 8, "DMA tiling");
+  __shared__ __attribute__((aligned(16))) bf16 Ks[STG][NK * BKV * D];
   __shared__ __attribute__((aligned(16))) bf16 Vs[STG][D * BKV];
 
   // Blocks are dispatched in launch order, so the linear block index runs over query tiles
@@ -72,11 +85,21 @@ __global__ __launch_bounds__(NW2 * 64, 1) void attn_bf16_kernel(const bf16* __re
   const int qw = qb + wid * 32;
   const int myq = qw + rl;
 
-  bf16x8 qf[KS];
+  bf16x8 qf[NK * KS];
   {
-    const bf16* qp = qk + (size_t)(b * T + min(myq, T - 1)) * ldqk + h * D + 8 * hl;
+    const size_t qrow = (size_t)(b * T + min(myq, T - 1)) * ldqk + h * D + 8 * hl;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = *(const bf16x8*)(qp + 16 * s);
+    for (int s = 0; s < KS; ++s) qf[s] = *(const bf16x8*)(qk + qrow + 16 * s);
+    if constexpr (PRIOR) {
+      const float z = gate_logit[layer];
+      const float gp = fmaxf(z, 0.f) + log1pf(expf(-fabsf(z)));  // softplus
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8 u = *(const bf16x8*)(qk1 + qrow + 16 * s);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[KS + s][e] = (bf16)((float)u[e] * gp);
+      }
+    }
   }
 
   const int kmin = max(0, qb - window + 1);
@@ -88,6 +111,8 @@ __global__ __launch_bounds__(NW2 * 64, 1) void attn_bf16_kernel(const bf16* __re
       (void*)(qk + (size_t)b * T * ldqk + (H + g) * D), (short)0, (int)min((size_t)T * ldqk * 2, (size_t)0x7fffffff), 0x00020000);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(vt + (size_t)(b * Hkv + g) * D * T), (short)0, (int)min((size_t)D * T * 2, (size_t)0x7fffffff), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rk1 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((PRIOR ? qk1 : qk) + (size_t)b * T * ldqk + (H + g) * D), (short)0, (int)min((size_t)T * ldqk * 2, (size_t)0x7fffffff), 0x00020000);
   int ko[KI], vo[VI];
 #pragma unroll
   for (int i = 0; i < KI; ++i) {
@@ -105,6 +130,11 @@ __global__ __launch_bounds__(NW2 * 64, 1) void attn_bf16_kernel(const bf16* __re
 #pragma unroll
     for (int i = 0; i < KI; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(&Ks[st][(wid * KI + i) * 512]), 16, ko[i], j0 * ldqk * 2, 0, 0);
+    if constexpr (PRIOR) {
+#pragma unroll
+      for (int i = 0; i < KI; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk1, (lds_ptr_t)(&Ks[st][BKV * D + (wid * KI + i) * 512]), 16, ko[i], j0 * ldqk * 2, 0, 0);
+    }
 #pragma unroll
     for (int i = 0; i < VI; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(&Vs[st][(wid * VI + i) * 512]), 16, vo[i], j0 * 2, 0, 0);
@@ -137,10 +167,11 @@ __global__ __launch_bounds__(NW2 * 64, 1) void attn_bf16_kernel(const bf16* __re
     // first k-step takes a zero accumulator (an inline constant, no register zeroing)
     const f32x16 zero = {};
 #pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2)
+    for (int s2 = 0; s2 < NK * KS; ++s2)
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
-        const bf16x8 a = *(const bf16x8*)(kp[rt] + (((2 * s2 + hl) ^ sw[rt]) << 3));
+        const int half = s2 / KS, ss = s2 % KS;  // K half (k or k1) and k-step within it
+        const bf16x8 a = *(const bf16x8*)(kp[rt] + half * BKV * D + (((2 * ss + hl) ^ sw[rt]) << 3));
         sv[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s2], s2 == 0 ? zero : sv[rt], 0, 0, 0);
       }
   };
@@ -151,7 +182,7 @@ __global__ __launch_bounds__(NW2 * 64, 1) void attn_bf16_kernel(const bf16* __re
   f32x16 sA[2], sB[2];
   issue(t0);
   if (t0 + 1 <= t1) issue(t0 + 1);
-  if (t0 + 1 <= t1) __builtin_amdgcn_s_waitcnt(vmcnt_le(KI + VI));
+  if (t0 + 1 <= t1) __builtin_amdgcn_s_waitcnt(vmcnt_le(NK * KI + VI));
   else __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
   __syncthreads();
   bool act_cur = active_tile(t0);
@@ -244,10 +275,13 @@ __global__ __launch_bounds__(NW2 * 64, 1) void attn_bf16_kernel(const bf16* __re
 #endif
 }
 
-// fp32 path: one thread per query, keys read from global memory.
+// fp32 path: one thread per query, keys read from global memory.  With qkv1 (looped pass 2)
+// each logit adds g * <q1_i, k1_j> from pass 1's q and k (same layout as qkv).
 template <int D>
 __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ qkv, float* __restrict__ o,
-                                                      int T, int H, int Hkv, int window, float scale) {
+                                                      int T, int H, int Hkv, int window, float scale,
+                                                      const float* __restrict__ qkv1,
+                                                      const float* __restrict__ gate_logit, int layer) {
   const int i = blockIdx.x * 64 + threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
   if (i >= T) return;
@@ -257,6 +291,11 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
   float qv[D], acc[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) { qv[d] = q[d]; acc[d] = 0.f; }
+  float gp = 0.f;
+  if (qkv1 != nullptr) {
+    const float z = gate_logit[layer];
+    gp = fmaxf(z, 0.f) + log1pf(expf(-fabsf(z)));  // softplus
+  }
   float m = -INFINITY, l = 0.f;
   const int j_lo = max(0, i - window + 1);
   for (int j = j_lo; j <= i; ++j) {
@@ -265,6 +304,13 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
     float s = 0.f;
 #pragma unroll
     for (int d = 0; d < D; ++d) s = fmaf(qv[d], k[d], s);
+    if (qkv1 != nullptr) {
+      const float* q1 = qkv1 + (size_t)(b * T + i) * ld + h * D;
+      const float* k1 = qkv1 + (size_t)(b * T + j) * ld + (H + g) * D;
+      float s1 = 0.f;
+      for (int d = 0; d < D; ++d) s1 = fmaf(q1[d], k1[d], s1);
+      s = fmaf(gp, s1, s);
+    }
     s *= scale;
     const float m_new = fmaxf(m, s);
     const float corr = expf(m - m_new);
@@ -283,24 +329,39 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
 }  // namespace
 
 hipError_t launch_attn_bf16(const void* qk, const void* vt, void* o, int B, int T, int H, int Hkv,
-                            int D, int window, float scale, hipStream_t s) {
+                            int D, int window, float scale, hipStream_t s, const void* qk1,
+                            const float* gate_logit, int layer) {
   if (T % BKV) return hipErrorInvalidValue;
   const float sl2 = scale * GPT_LOG2E;
-  const dim3 grid(((T + BQ2 - 1) / BQ2) * H * B);
+  const bf16* q = (const bf16*)qk;
+  const bf16* v = (const bf16*)vt;
+  bf16* out = (bf16*)o;
+  if (qk1 != nullptr) {  // looped pass 2: prior from pass 1
+    if (D != 128 || gate_logit == nullptr) return hipErrorInvalidValue;
+    const dim3 grid(((T + 127) / 128) * H * B);
+    GPTK_LAUNCH((attn_bf16_kernel<128, 4, true>), grid, 256, s, q, v, out, B, T, H, Hkv, window, sl2,
+                (const bf16*)qk1, gate_logit, layer);
+    return hipGetLastError();
+  }
+  const dim3 grid(((T + 255) / 256) * H * B);
   if (D == 128)
-    GPTK_LAUNCH(attn_bf16_kernel<128>, grid, NW2 * 64, s, (const bf16*)qk, (const bf16*)vt, (bf16*)o, B, T, H, Hkv, window, sl2);
+    GPTK_LAUNCH((attn_bf16_kernel<128, 8, false>), grid, 512, s, q, v, out, B, T, H, Hkv, window, sl2,
+                (const bf16*)nullptr, (const float*)nullptr, 0);
   else if (D == 64)
-    GPTK_LAUNCH(attn_bf16_kernel<64>, grid, NW2 * 64, s, (const bf16*)qk, (const bf16*)vt, (bf16*)o, B, T, H, Hkv, window, sl2);
+    GPTK_LAUNCH((attn_bf16_kernel<64, 8, false>), grid, 512, s, q, v, out, B, T, H, Hkv, window, sl2,
+                (const bf16*)nullptr, (const float*)nullptr, 0);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 hipError_t launch_attn_f32(const float* qkv, float* o, int B, int T, int H, int Hkv, int D,
-                           int window, float scale, hipStream_t s) {
+                           int window, float scale, hipStream_t s, const float* qkv1,
+                           const float* gate_logit, int layer) {
+  if (qkv1 != nullptr && gate_logit == nullptr) return hipErrorInvalidValue;
   const dim3 grid((T + 63) / 64, H, B);
-  if (D == 128) GPTK_LAUNCH(attn_f32_kernel<128>, grid, 64, s, qkv, o, T, H, Hkv, window, scale);
-  else if (D == 64) GPTK_LAUNCH(attn_f32_kernel<64>, grid, 64, s, qkv, o, T, H, Hkv, window, scale);
+  if (D == 128) GPTK_LAUNCH(attn_f32_kernel<128>, grid, 64, s, qkv, o, T, H, Hkv, window, scale, qkv1, gate_logit, layer);
+  else if (D == 64) GPTK_LAUNCH(attn_f32_kernel<64>, grid, 64, s, qkv, o, T, H, Hkv, window, scale, qkv1, gate_logit, layer);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

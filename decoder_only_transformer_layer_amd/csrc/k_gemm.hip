@@ -129,8 +129,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
   // Row block rb (8 rows) of an operand tile sits at row 8*rb: its lanes' chunk swizzle is
   // (lane & 7) ^ (lane >> 3) ^ (rb & 1), so two per-lane offsets serve every row block, and
   // the row block's start and the K offset travel in the scalar soffset.
-  static_assert(AI % 2 == 0 && BI % 2 == 0, "row blocks per wave must be even");
+  static_assert(AI % 2 == 0, "A row blocks per wave must be even");
   const int wids = __builtin_amdgcn_readfirstlane(wid);
+  const int pb = (wids * BI) & 1;  // parity of this wave's first B row block (0 when BI is even)
   // A and B share their row pitch (lda == ldb, checked by the launcher).
   int va[2];
 #pragma unroll
@@ -144,7 +145,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
         (k0) * 2 + (wids * AI + i) * 16 * lda, 0, 0);                                        \
     _Pragma("unroll") for (int i = 0; i < BI; ++i)                                           \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb,                                          \
-        (lds_ptr_t)(Bs + (buf) * BN * BK + (wids * BI + i) * 512), 16, va[i & 1],           \
+        (lds_ptr_t)(Bs + (buf) * BN * BK + (wids * BI + i) * 512), 16,                      \
+        (BI % 2 == 0 ? va[i & 1] : (((pb + i) & 1) ? va[1] : va[0])),                        \
         (k0) * 2 + (wids * BI + i) * 16 * ldb, 0, 0);                                        \
   } while (0)
 
@@ -793,11 +795,50 @@ bool seg_ok(const GemmArgs& a, int bn) {
   return (e0 >= a.N || e0 % bn == 0) && (e1 >= a.N || e1 % bn == 0);
 }
 
-// 256x384 tiles (8 wavefronts of 128x96) for the residual and MLP-up GEMMs when the columns
-// allow: on the model's widths they fill whole rounds of the CUs (64 x 4 tiles for a
-// 16384 x 1536 output) where 256x256 tiles would leave half a round.
-bool use_wide(Epi epi, const GemmArgs& a) {
-  return (epi == EPI_RESID || epi == EPI_RELU2 || epi == EPI_STORE) && a.N % 384 == 0 && seg_ok(a, 384);
+// Tile plan of one GEMM.  Candidates: 256x384 tiles (8 wavefronts of 128x96) and 256x192
+// tiles (8 wavefronts of 64x96) for the residual, ReLU^2 and store epilogues when N allows, and
+// 256x256 tiles (8 wavefronts), the latter with the columns split when the tile count leaves a
+// partial last round on the CUs: a leading part whose 256x256 tiles fill whole rounds and a
+// tail of 256x128 tiles (4 wavefronts), so the partial round costs half a tile per CU.
+// Cost = rounds x tile area / relative efficiency (256x128 and 256x192 tiles run at about 3/4
+// and 9/10 of the larger tiles' rate, their wavefront tiles re-reading LDS more per MFMA); the
+// cheapest plan wins, wider tiles on a tie.  E.g. 16384 x 1536 takes one round of 256 tiles of
+// 256x384 (256x256 would need 1.5 rounds) and 8192 x 1536 one round of 256 tiles of 256x192.
+enum class Tiles { T256, T384, T192 };
+struct Plan {
+  Tiles tiles;
+  int split_cols;  // 256x256 plan: columns of the leading part (0 = no split)
+};
+
+Plan plan_gemm(Epi epi, int M, int N, int nseg0, int nseg1, int ncu) {
+  auto seg_ok_n = [&](int bn) {
+    const int e0 = nseg0, e1 = nseg0 + nseg1;
+    return (e0 >= N || e0 % bn == 0) && (e1 >= N || e1 % bn == 0);
+  };
+  auto rounds = [&](long t) { return (double)((t + ncu - 1) / ncu); };
+  const long nbm = (M + 255) / 256, nbn = (N + 255) / 256;
+  const long tiles = nbm * nbn;
+  Plan p{Tiles::T256, 0};
+  double cost = rounds(tiles);  // in rounds of 256x256 tiles
+  if (tiles > ncu && tiles % ncu != 0 && N % 256 == 0 && epi != EPI_CE) {
+    const long per = ncu / gcd((int)nbm, ncu);  // column blocks per whole number of rounds
+    const long c1 = (nbn / per) * per;
+    if (c1 > 0 && c1 < nbn) {
+      const double c = (double)(nbm * c1 / ncu) + rounds(nbm * (nbn - c1) * 2) * 0.5 / 0.75;
+      if (c < cost) { cost = c; p.split_cols = (int)(c1 * 256); }
+    }
+  }
+  if (epi == EPI_RESID || epi == EPI_RELU2 || epi == EPI_STORE) {
+    if (N % 192 == 0 && seg_ok_n(192)) {
+      const double c = rounds(nbm * (N / 192)) * 0.75 / 0.9;
+      if (c <= cost) { cost = c; p = Plan{Tiles::T192, 0}; }
+    }
+    if (N % 384 == 0 && seg_ok_n(384)) {
+      const double c = rounds(nbm * (N / 384)) * 1.5;
+      if (c <= cost) { cost = c; p = Plan{Tiles::T384, 0}; }
+    }
+  }
+  return p;
 }
 
 }  // namespace
@@ -806,34 +847,26 @@ thread_local LaunchEvents launch_events;
 
 int gemm_bf16_ce_blocks(int N) { return (N + 255) / 256; }
 
-int gemm_resid_slice_cols(int N) { return N % 384 == 0 ? 96 : 64; }
+int gemm_resid_slice_cols(int M, int N) {
+  return plan_gemm(EPI_RESID, M, N, N, 0, cu_count()).tiles == Tiles::T256 ? 64 : 96;
+}
 
 hipError_t launch_gemm_bf16(Epi epi, const GemmArgs& a, hipStream_t s) {
   if (a.K % BK || a.M <= 0 || a.N <= 0 || a.lda != a.ldb) return hipErrorInvalidValue;
   if (epi == EPI_CE) return run_bf16<256, 256, 2, 4>(epi, a, s);  // must match gemm_bf16_ce_blocks
   if (epi == EPI_QKV && a.cs != nullptr && a.D != 128) return hipErrorInvalidValue;
-  if (use_wide(epi, a)) return run_bf16<256, 384, 2, 4>(epi, a, s);  // slices of 96 columns
+  const Plan p = plan_gemm(epi, a.M, a.N, a.nseg0, a.nseg1, cu_count());
+  if (p.tiles == Tiles::T384) return run_bf16<256, 384, 2, 4>(epi, a, s);  // slices of 96 columns
+  if (p.tiles == Tiles::T192) return run_bf16<256, 192, 4, 2>(epi, a, s);  // slices of 96 columns
   if (!seg_ok(a, 256)) return seg_ok(a, 128) ? run_narrow(epi, a, s) : hipErrorInvalidValue;
-  // 256x256 tiles, 8 wavefronts (2 per SIMD) so one wavefront's LDS waits overlap the other's
-  // MFMAs.  When the tile count leaves a partial last round on the CUs (e.g. 64 x 18 tiles on
-  // 256 CUs), the columns are split: a leading part whose 256x256 tiles fill whole rounds, and
-  // a tail launched with 256x128 tiles, so the partial round costs half a tile per CU.  Both
-  // parts keep 64-column wavefront slices.
-  const int ncu = cu_count();
-  const int nbm = (a.M + 255) / 256, nbn = (a.N + 255) / 256;
-  const long tiles = (long)nbm * nbn;
-  if (tiles > ncu && tiles % ncu != 0 && a.N % 256 == 0) {
-    const int per = ncu / gcd(nbm, ncu);  // column blocks per whole number of rounds
-    const int c1 = (nbn / per) * per;
-    if (c1 > 0 && c1 < nbn) {
-      GemmArgs head = a;
-      head.N = c1 * 256;
-      if (head.nseg0 > head.N) head.nseg0 = head.N;
-      if (head.nseg0 + head.nseg1 > head.N) head.nseg1 = head.N - head.nseg0;
-      hipError_t e = run_main(epi, head, s);
-      if (e != hipSuccess) return e;
-      return run_narrow(epi, shift_cols(a, epi, c1 * 256), s);
-    }
+  if (p.split_cols > 0) {  // both parts keep 64-column wavefront slices
+    GemmArgs head = a;
+    head.N = p.split_cols;
+    if (head.nseg0 > head.N) head.nseg0 = head.N;
+    if (head.nseg0 + head.nseg1 > head.N) head.nseg1 = head.N - head.nseg0;
+    hipError_t e = run_main(epi, head, s);
+    if (e != hipSuccess) return e;
+    return run_narrow(epi, shift_cols(a, epi, p.split_cols), s);
   }
   return run_main(epi, a, s);
 }

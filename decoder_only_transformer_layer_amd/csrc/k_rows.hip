@@ -35,7 +35,7 @@ template <typename WT, typename AT, int NCH>
 __global__ __launch_bounds__(256) void embed_norm_kernel(
     const int32_t* __restrict__ tokens, const WT* __restrict__ wte, const float* __restrict__ lam,
     const float* __restrict__ mu, float* __restrict__ x0, float* __restrict__ x, AT* __restrict__ xn,
-    int M, int C, int V, float eps, unsigned* __restrict__ flags) {
+    int M, int C, int V, float eps, unsigned* __restrict__ flags, const WT* __restrict__ pe) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
   if (row >= M) return;
@@ -52,6 +52,12 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(
     const int i = (c * 64 + lane) * 4;
     if (i < C) {
       load4(src + i, v[c]);
+      if (pe != nullptr) {  // per-pass embedding of the looped trunk, added before the norm
+        float pv[4];
+        load4(pe + i, pv);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[c][k] += pv[k];
+      }
       ss += v[c][0] * v[c][0] + v[c][1] * v[c][1] + v[c][2] * v[c][2] + v[c][3] * v[c][3];
     }
   }
@@ -210,17 +216,19 @@ hipError_t launch_rope_table(float2* cs, int T, int D, float base, hipStream_t s
 
 hipError_t launch_embed_norm(const int32_t* tokens, const void* wte, bool wbf16, const float* lam,
                              const float* mu, float* x0, float* x, void* xn, int M, int C, int V,
-                             float eps, unsigned* flags, hipStream_t s) {
+                             float eps, unsigned* flags, hipStream_t s, const void* pe) {
   if (C % 4) return hipErrorInvalidValue;
   const int grid = (M + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
   return dispatch_nch(C, [&](auto nch) {
     constexpr int N = decltype(nch)::value;
     if (wbf16)
       embed_norm_kernel<bf16, bf16, N><<<grid, 256, 0, s>>>(tokens, (const bf16*)wte, lam, mu, x0, x,
-                                                            (bf16*)xn, M, C, V, eps, flags);
+                                                            (bf16*)xn, M, C, V, eps, flags,
+                                                            (const bf16*)pe);
     else
       embed_norm_kernel<float, float, N><<<grid, 256, 0, s>>>(tokens, (const float*)wte, lam, mu, x0,
-                                                              x, (float*)xn, M, C, V, eps, flags);
+                                                              x, (float*)xn, M, C, V, eps, flags,
+                                                              (const float*)pe);
     return hipGetLastError();
   });
 }

@@ -34,11 +34,12 @@ extern thread_local LaunchEvents launch_events;
 // cos/sin table cs[t * (D/2) + j] = (cos phi, sin phi), phi = t * base^(-2j/D), in fp64 then fp32.
 hipError_t launch_rope_table(float2* cs, int T, int D, float base, hipStream_t s);
 
-// x0 = RMSNorm(wte[tokens]); x = lam[0] x0 + mu[0] x0; xn = RMSNorm(x).
-// wbf16 selects bf16 (else fp32) embedding storage and xn type.
+// x0 = RMSNorm(wte[tokens] (+ pe)); x = lam[0] x0 + mu[0] x0; xn = RMSNorm(x).
+// wbf16 selects bf16 (else fp32) embedding storage and xn type; pe (optional, [C], the
+// embedding's type) is added to every embedding row before the norm.
 hipError_t launch_embed_norm(const int32_t* tokens, const void* wte, bool wbf16, const float* lam,
                              const float* mu, float* x0, float* x, void* xn, int M, int C, int V,
-                             float eps, unsigned* flags, hipStream_t s);
+                             float eps, unsigned* flags, hipStream_t s, const void* pe = nullptr);
 
 // If mix: x = lam[layer] x + mu[layer] x0 (in place).  Then xn = RMSNorm(x).
 hipError_t launch_mix_norm(float* x, const float* x0, const float* lam, const float* mu, int layer,
@@ -96,21 +97,24 @@ struct GemmArgs {
 hipError_t launch_gemm_bf16(Epi epi, const GemmArgs& a, hipStream_t s);
 // Number of column blocks the CE epilogue of launch_gemm_bf16 produces for N columns.
 int gemm_bf16_ce_blocks(int N);
-// Width of the column slices whose per-row sums of squares a RESID GEMM with xb set writes
-// (ssp [N / width][M]); divides N whenever N % 64 == 0.
-int gemm_resid_slice_cols(int N);
+// Width of the column slices whose per-row sums of squares an M x N RESID GEMM with xb set
+// writes (ssp [N / width][M]); divides N whenever N % 64 == 0.
+int gemm_resid_slice_cols(int M, int N);
 // fp32 SIMT GEMM (small configurations).
 hipError_t launch_gemm_f32(Epi epi, const GemmArgs& a, hipStream_t s);
 int gemm_f32_ce_blocks(int N);
 
 // ---- attention (k_attn.hip) ----------------------------------------------------------------
 // bf16: q/k from qk [B*T][(H+Hkv)*D] (already RoPE'd and normed), v from vt [B][Hkv][D][T];
-// o [B*T][H*D].  D must be 128 or 64, T % 64 == 0.
+// o [B*T][H*D].  D must be 128 or 64, T % 64 == 0.  If qk1 is set (looped pass 2; D == 128),
+// every logit also gets softplus(gate_logit[layer]) * <q1, k1> from qk1 (same layout as qk).
 hipError_t launch_attn_bf16(const void* qk, const void* vt, void* o, int B, int T, int H, int Hkv,
-                            int D, int window, float scale, hipStream_t s);
-// fp32: q/k/v from qkv [B*T][(H+2Hkv)*D]; o [B*T][H*D].
+                            int D, int window, float scale, hipStream_t s, const void* qk1 = nullptr,
+                            const float* gate_logit = nullptr, int layer = 0);
+// fp32: q/k/v from qkv [B*T][(H+2Hkv)*D]; o [B*T][H*D]; qkv1 as qk1 above (qkv layout).
 hipError_t launch_attn_f32(const float* qkv, float* o, int B, int T, int H, int Hkv, int D,
-                           int window, float scale, hipStream_t s);
+                           int window, float scale, hipStream_t s, const float* qkv1 = nullptr,
+                           const float* gate_logit = nullptr, int layer = 0);
 
 // ---- loss (k_loss.hip) ----------------------------------------------------------------------
 // loss[row] = cap + log(sum_nb partial[row][nb]) - cap tanh(tgt_logit[row] / cap); 0 where

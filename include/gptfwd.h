@@ -76,6 +76,11 @@ typedef struct {
                            embedding into v ("Value Embeddings (ResFormer)": the pages select
                            l % 2 == (n_layer - 1) % 2); needs d_model >= 12, and head_dim 128
                            for GPT_BF16 */
+  int32_t looped;       /* 0, or 1 for the two-pass looped trunk ("looped-nanochat-d24", section
+                           "What is the routing loop?"): pass p in {0, 1} starts from
+                           RMSNorm(W_E[t] + pass_emb[p]); pass-2 layer l adds
+                           softplus(gate_logit[l]) * attn_scale * <q1, k1> of pass-1 layer l to
+                           its logits; the loss comes from pass 2.  GPT_BF16 needs head_dim 128. */
 } gpt_cfg;
 
 /* Weights: borrowed device memory of type cfg->dtype (float or bf16), row-major [out, in].
@@ -99,6 +104,9 @@ typedef struct {
    *              per KV head h, x_tilde the normalised input of the layer's projections */
   const void *const *ve;      /* host [n_layer] */
   const void *const *ve_gate; /* host [n_layer] */
+  /* Looped trunk only (cfg->looped): */
+  const void *pass_emb;       /* [2, d_model] per-pass embeddings */
+  const float *gate_logit;    /* device fp32 [n_layer] routing gate logits */
 } gpt_weights;
 
 /* Validate a configuration without touching any device.  Returns GPT_OK, GPT_E_INVALID_ARG or

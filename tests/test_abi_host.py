@@ -51,7 +51,7 @@ def _cfg(**kw):
 
 
 def test_validate_presets(lib):
-    for name in ("tiny", "d12", "d24", "d24gve"):
+    for name in ("tiny", "d12", "d24", "d24gve", "d24loop"):
         c = gf.make_cfg(gptdata.preset(name))
         assert gf.gpt_validate(c) == gf.GPT_OK, name
         assert gf.gpt_workspace_bytes(c) > 0
@@ -144,6 +144,24 @@ def test_value_embedding_validation(lib):
     w.ve = w.ve_gate = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
     arr[1] = None                         # layer 1 is selected (L = 24: odd layers)
     assert call(w) == gf.GPT_E_INVALID_ARG
+
+
+def test_looped_validation(lib):
+    """The looped trunk needs head_dim 128 on bf16, a 0/1 flag, and its pass embeddings and
+    gate logits."""
+    p = gptdata.preset("d24loop")
+    c = gf.make_cfg(p)
+    assert gf.gpt_validate(c) == gf.GPT_OK
+    assert gf.gpt_workspace_bytes(c) > gf.gpt_workspace_bytes(gf.make_cfg(p.with_(looped=False)))
+    assert gf.gpt_validate(gf.make_cfg(p.with_(head_dim=64, n_head=24, n_kv_head=24))) == gf.GPT_E_UNSUPPORTED
+    bad = gf.make_cfg(p)
+    bad.looped = 2
+    assert gf.gpt_validate(bad) == gf.GPT_E_INVALID_ARG
+    w = _weights(c.n_layer)               # no pass embeddings / gate logits
+    need = gf.gpt_workspace_bytes(c)
+    F = 0x200000
+    assert lib.gpt_fwd_loss(ctypes.byref(c), ctypes.byref(w), F, F, F, F, None, 0x10000000, need,
+                            None) == gf.GPT_E_INVALID_ARG
 
 
 def test_fwd_loss_timed_argument_errors(lib):

@@ -256,3 +256,58 @@ def test_d24_gqa_value_embeddings_bf16(d24gve):
     err = np.abs(got["losses"][5, :512] - ref5["losses"][0])
     print(f"  row 5 prefix: max |err| {err.max():.3e}")
     assert err.max() <= 2e-2
+
+
+# ----------------------------------------------------------------------------- looped trunk
+
+def test_looped_fp32():
+    """fp32 looped two-pass trunk (GQA 2:1, head_dim 64): pass-1 prior on every pass-2 layer."""
+    p = gptdata.Preset(name="loop32", n_layer=3, d_model=128, n_head=2, n_kv_head=1, head_dim=64,
+                       mlp_dim=512, vocab=800, seq_len=128, batch=2, dtype="f32", short_window=64,
+                       looped=True, seed=31)
+    w, tok, tgt = gptdata.make_inputs(p)
+    w.gate_logit[:] = np.array([0.5, -1.0, 1.5], np.float32)   # gates well away from 0
+    _, got = _run(p, w, tok, tgt, want_logits=True)
+    ref = oracle.forward(p, params_of(w), tok, tgt, want_logits=True)
+    rel = abs(got["mean"] - ref["mean"]) / abs(ref["mean"])
+    zerr = np.max(np.abs(got["logits"] - ref["logits"])) / np.max(np.abs(ref["logits"]))
+    print(f"  looped fp32: mean rel err {rel:.2e}, logits err/max {zerr:.2e}")
+    assert rel <= 1e-4 and zerr <= 1e-3
+
+
+def test_looped_bf16_ragged():
+    """bf16 looped trunk: GQA 4:2, B*T = 640 rows (ragged), windows 100 / 64 / full, ignores."""
+    p = _ragged_preset(looped=True, seed=33)
+    w, tok, tgt = gptdata.make_inputs(p, ignore_frac=0.1)
+    w.gate_logit[:] = np.array([1.0, 0.2, 2.0], np.float32)
+    windows = [100, 64, 320]
+    _, got = _run(p, w, tok, tgt, want_logits=True, windows=windows)
+    ref = oracle.forward(p, params_of(w), tok, tgt, want_logits=True, windows=windows)
+    _check_bf16(got, ref)
+    # the prior matters at these gates
+    ref0 = oracle.forward(p.with_(looped=False), params_of(w), tok, tgt, windows=windows)
+    assert np.max(np.abs(ref0["losses"] - ref["losses"])) > 0.05
+
+
+@pytest.fixture(scope="module")
+def d24loop():
+    p = gptdata.preset("d24loop")
+    w, tok, tgt = gptdata.make_inputs(p)
+    return p, w, tok, tgt
+
+
+def test_d24_looped_bf16(d24loop):
+    """Looped two-pass d24 at its configured size (B=4, T=2048): oracle on row 0 and on the
+    first 512 tokens of row 3."""
+    p, w, tok, tgt = d24loop
+    _, got = _run(p, w, tok, tgt)
+    assert got["status"] == gf.GPT_OK
+    assert math.isfinite(got["mean"])
+    prm = params_of(w)
+    _check_bf16(got, oracle.forward(p, prm, tok, tgt, rows=[0]), rows=[0])
+    pre = p.with_(seq_len=512)
+    ref3 = oracle.forward(pre, prm, tok[3:4, :512], tgt[3:4, :512],
+                          windows=oracle.layer_windows(p.window_pattern, p.short_window, p.seq_len, p.n_layer))
+    err = np.abs(got["losses"][3, :512] - ref3["losses"][0])
+    print(f"  row 3 prefix: max |err| {err.max():.3e}")
+    assert err.max() <= 2e-2
