@@ -23,6 +23,11 @@ Draw order for one preset (seeded ``numpy.random.default_rng(seed)``):
   6. (looped presets only) pass embeddings [2, C] ~ N(0, 1/C), then per-layer routing gate
      logits [L] = ln(exp(0.05) - 1) + 0.1 N(0, 1) (float32), i.e. gates near 0.05
   7. token rows [B, T+1]
+
+Nested presets (nested_c1 > 0, two blocks): every per-layer linear is block lower triangular
+and drawn as its two row blocks, in order: row block 1 [out_1, in_1] ~ N(0, 1/in_1), then row
+block 2 [out_2, in_1 + in_2] ~ N(0, 1/(in_1 + in_2)); each dimension splits in the proportion
+nested_c1 : d_model (q/k/v by heads, the MLP hidden proportionally).
 """
 from __future__ import annotations
 
@@ -64,6 +69,7 @@ class Preset:
     value_embeds: bool = False         # per-layer value-embedding tables and gates are drawn
     ve_gate_channels: int = 12         # input channels the value-embedding gate reads
     looped: bool = False               # two-pass trunk: pass embeddings and routing gate logits
+    nested_c1: int = 0                 # > 0: two nested blocks, the inner one nested_c1 wide
 
     @property
     def attn_scale(self) -> float:
@@ -85,6 +91,9 @@ PRESETS: Dict[str, Preset] = {
     # nanochat d24: width 1536, 12 heads of 128, V=32768, T=2048, B=8, bf16, seeded lambda/mu
     "d24": Preset("d24", 24, 1536, 12, 12, 128, 6144, 32768, 2048, 8, "bf16", short_window=1024,
                   lambda_range=(0.9, 1.1), mu_range=(0.0, 0.2)),
+    # StairFormer nested d24: 24 heads of 64 in blocks of 6 + 18 (inner width 384), B=4
+    "d24nest": Preset("d24nest", 24, 1536, 24, 24, 64, 6144, 32768, 2048, 4, "bf16", short_window=1024,
+                      lambda_range=(0.9, 1.1), mu_range=(0.0, 0.2), nested_c1=384),
     # looped two-pass d24 (B=4)
     "d24loop": Preset("d24loop", 24, 1536, 12, 12, 128, 6144, 32768, 2048, 4, "bf16", short_window=1024,
                       lambda_range=(0.9, 1.1), mu_range=(0.0, 0.2), looped=True),
@@ -131,7 +140,8 @@ class Weights:
 
     For bf16 presets every matrix is held as uint16 bf16 bit patterns; for f32
     presets as float32.  ``value(a)`` returns the float32 values either way.
-    Matrices are row-major [out_features, in_features].
+    Matrices are row-major [out_features, in_features].  In nested presets each per-layer
+    linear is a list of its row blocks ([out_1, in_1], [out_2, in_1 + in_2]).
     """
     dtype: str
     wte: np.ndarray                 # [V, C]
@@ -149,7 +159,9 @@ class Weights:
     pass_emb: Optional[np.ndarray] = None       # [2, C] per-pass embeddings (looped)
     gate_logit: Optional[np.ndarray] = None     # [L] float32 routing gate logits (looped)
 
-    def value(self, a: np.ndarray) -> np.ndarray:
+    def value(self, a):
+        if isinstance(a, list):
+            return [self.value(b) for b in a]
         return bf16_bits_to_f32(a) if self.dtype == "bf16" else a
 
     def matrices(self):
@@ -184,7 +196,22 @@ def make_weights(p: Preset, rng: Optional[np.random.Generator] = None) -> Weight
     C, H, Hkv, D, F, V, L = p.d_model, p.n_head, p.n_kv_head, p.head_dim, p.mlp_dim, p.vocab, p.n_layer
     wte = _gauss(rng, (V, C), C, p.dtype)
     wq, wk, wv, wo, w1, w2 = [], [], [], [], [], []
+    if p.nested_c1:
+        c1 = p.nested_c1
+        part = lambda n: n * c1 // C  # inner share of a dimension
+
+        def blocks(out, inp):
+            o1, i1 = part(out), part(inp)
+            return [_gauss(rng, (o1, i1), i1, p.dtype), _gauss(rng, (out - o1, inp), inp, p.dtype)]
     for _ in range(L):
+        if p.nested_c1:
+            wq.append(blocks(H * D, C))
+            wk.append(blocks(Hkv * D, C))
+            wv.append(blocks(Hkv * D, C))
+            wo.append(blocks(C, H * D))
+            w1.append(blocks(F, C))
+            w2.append(blocks(C, F))
+            continue
         wq.append(_gauss(rng, (H * D, C), C, p.dtype))
         wk.append(_gauss(rng, (Hkv * D, C), C, p.dtype))
         wv.append(_gauss(rng, (Hkv * D, C), C, p.dtype))

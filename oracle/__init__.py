@@ -21,6 +21,9 @@ Sources (cited by page title and section):
   [L]  "looped-nanochat-d24" -- section "What is the routing loop?" (two-pass
        trunk, attention-logit prior from pass 1, softplus gate, pass
        embeddings).
+  [F]  "Fully Nested Transformers" -- the StairFormer description: block lower
+       triangular weights, PrefixRMSNorm, per-block heads, kfront submodel
+       forward, prefix cross-entropy.
 
 Readings where the pages are silent or disagree (each frozen as a config field
 so the oracle and the GPU path cannot silently diverge):
@@ -44,6 +47,13 @@ so the oracle and the GPU path cannot silently diverge):
     RMSNorm(W_E[t] + pass_emb[p]); pass-2 layer l takes the prior of pass-1
     layer l (identity routing), shares that layer's window mask and scale,
     and the loss comes from pass 2 only.
+  * nested model (cfg.nested_c1 > 0, two blocks): the residual splits into
+    dims [0, c1) and [c1, C); every other dimension (q/k/v heads, MLP hidden)
+    splits in the same proportion; every per-layer linear is block lower
+    triangular, stored as its row blocks [out_1, in_1] and [out_2, in_1+in_2];
+    every RMSNorm is the PrefixRMSNorm (block-1 coordinates over the RMS of
+    dims [0, c1), block-2 coordinates over the RMS of all dims); the lm_head is
+    shared, kfront=1 reading input columns [0, c1).  No value embeddings.
   * value embeddings (when cfg.value_embeds): the gate reads the first 12
     channels of the attention block's normalised input x_tilde (the input of
     the Q/K/V projections), and the mixed value v + g * e is what attention
@@ -65,7 +75,8 @@ __all__ = [
     "rms_norm", "rope_angles", "apply_rope", "layer_windows", "visible_mask",
     "attention", "linear", "relu_squared", "softcap", "token_losses",
     "mean_loss", "has_ve", "value_embed_mix", "softplus", "attention_with_prior", "block",
-    "forward_row", "forward",
+    "forward_row", "forward", "prefix_rms_norm", "blocktri_linear", "forward_nested_row",
+    "forward_nested",
 ]
 
 
@@ -388,6 +399,109 @@ def forward_row(cfg: Any, params: Any, tokens: np.ndarray, targets: Optional[np.
     return res
 
 
+# ----------------------------------------------------------------------------- nested model
+
+def prefix_rms_norm(u: np.ndarray, c1: int, eps: float = 0.0) -> np.ndarray:
+    """PrefixRMSNorm with two blocks ([F] and the nested configuration): coordinates [0, c1)
+    are divided by the RMS of dims [0, c1), coordinates [c1, C) by the RMS of all dims, so the
+    first block never sees the second.  Block 1 is exactly RMSNorm of the prefix."""
+    first = rms_norm(np.ascontiguousarray(u[..., :c1]), eps)
+    if c1 == u.shape[-1]:
+        return first
+    return np.concatenate([first, rms_norm(u, eps)[..., c1:]], axis=-1)
+
+
+def blocktri_linear(x: np.ndarray, blocks: Sequence[np.ndarray], in1: int) -> np.ndarray:
+    """x W^T for a block lower triangular W given as its row blocks ([F]: the upper block is
+    zero and only the live blocks are stored): rows of block 1 read inputs [0, in1), rows of
+    block 2 read all inputs.  Block 1 is computed on the contiguous input prefix, exactly as a
+    standalone model of that width would."""
+    w1, w2 = blocks
+    y1 = linear(np.ascontiguousarray(x[..., :in1]), w1)
+    if w2.shape[0] == 0:
+        return y1
+    return np.concatenate([y1, linear(x, w2)], axis=-1)
+
+
+def forward_nested_row(cfg: Any, params: Any, tokens: np.ndarray, targets: Optional[np.ndarray],
+                       dtype=np.float64, want_logits: bool = False,
+                       windows: Optional[Sequence[int]] = None) -> Dict[str, Any]:
+    """Nested (two-block StairFormer) forward of one row and both prefix losses.
+
+    [F]: the nanochat forward with every linear block lower triangular and every norm a
+    PrefixRMSNorm, so the first block of the residual stream evolves as a standalone model of
+    width c1 would; one pass gives the kfront=1 logits (input columns [0, c1) of the final
+    normalised stream against the same columns of the shared lm_head) and the full logits.
+    Returns ``losses`` (full model), ``losses_k1`` (kfront=1) and optionally both logits.
+    """
+    dt = np.dtype(dtype)
+    T = tokens.shape[0]
+    eps, c1, C = cfg.norm_eps, cfg.nested_c1, cfg.d_model
+    H, Hkv, D, F = cfg.n_head, cfg.n_kv_head, cfg.head_dim, cfg.mlp_dim
+    h1d, f1 = H * c1 // C * D, F * c1 // C   # inner widths of the head and hidden dims
+    if windows is None:
+        windows = layer_windows(cfg.window_pattern, cfg.short_window, cfg.seq_len, cfg.n_layer)
+    cos, sin = rope_angles(T, D, cfg.rope_base, dtype=dt)
+    blk = lambda n, l: [np.asarray(b, dtype=dt) for b in _get(params, n, l)]
+    wte = np.asarray(_get(params, "wte"))
+    x = prefix_rms_norm(np.asarray(wte[tokens], dtype=dt), c1, eps)
+    x0 = x
+    lam_all = np.asarray(_get(params, "resid_lambda"))
+    mu_all = np.asarray(_get(params, "x0_lambda"))
+    for l in range(cfg.n_layer):
+        x = float(lam_all[l]) * x + float(mu_all[l]) * x0
+        xn = prefix_rms_norm(x, c1, eps)
+        q = blocktri_linear(xn, blk("wq", l), c1).reshape(T, H, D)
+        k = blocktri_linear(xn, blk("wk", l), c1).reshape(T, Hkv, D)
+        v = blocktri_linear(xn, blk("wv", l), c1).reshape(T, Hkv, D)
+        q = rms_norm(apply_rope(q, cos, sin), eps)
+        k = rms_norm(apply_rope(k, cos, sin), eps)
+        o = attention(q, k, v, windows[l], cfg.attn_scale)
+        x = x + blocktri_linear(o.reshape(T, H * D), blk("wo", l), h1d)
+        xm = prefix_rms_norm(x, c1, eps)
+        h = relu_squared(blocktri_linear(xm, blk("w1", l), c1))
+        x = x + blocktri_linear(h, blk("w2", l), f1)
+    xf = prefix_rms_norm(x, c1, eps)
+    wu = np.asarray(_get(params, "lm_head"), dtype=dt)
+    wu1 = np.ascontiguousarray(wu[:, :c1])
+    xf1 = np.ascontiguousarray(xf[:, :c1])
+    res: Dict[str, Any] = {}
+    step = max(1, (1 << 24) // max(1, wu.shape[0]))
+    for key, xs, w in (("", xf, wu), ("_k1", xf1, wu1)):
+        losses = np.zeros(T, dtype=dt)
+        parts = []
+        for a in range(0, T, step):
+            zh = softcap(linear(xs[a:a + step], w), cfg.softcap)
+            if targets is not None:
+                losses[a:a + step] = token_losses(zh, targets[a:a + step])
+            if want_logits:
+                parts.append(zh)
+        if targets is not None:
+            res["losses" + key] = losses
+        if want_logits:
+            res["logits" + key] = np.concatenate(parts, axis=0)
+    return res
+
+
+def forward_nested(cfg: Any, params: Any, tokens: np.ndarray, targets: Optional[np.ndarray] = None,
+                   dtype=np.float64, want_logits: bool = False, rows: Optional[Sequence[int]] = None,
+                   windows: Optional[Sequence[int]] = None) -> Dict[str, Any]:
+    """Batched nested forward: ``losses``/``mean`` (full model) and ``losses_k1``/``mean_k1``
+    (kfront=1), plus ``logits``/``logits_k1`` when asked."""
+    rows = list(range(tokens.shape[0])) if rows is None else list(rows)
+    acc: Dict[str, list] = {}
+    for b in rows:
+        r = forward_nested_row(cfg, params, tokens[b], None if targets is None else targets[b],
+                               dtype=dtype, want_logits=want_logits, windows=windows)
+        for k, v in r.items():
+            acc.setdefault(k, []).append(v)
+    res: Dict[str, Any] = {k: np.stack(v) for k, v in acc.items()}
+    if targets is not None:
+        res["mean"] = mean_loss(res["losses"], targets[rows])
+        res["mean_k1"] = mean_loss(res["losses_k1"], targets[rows])
+    return res
+
+
 def forward(cfg: Any, params: Any, tokens: np.ndarray, targets: Optional[np.ndarray] = None,
             dtype=np.float64, want_logits: bool = False, rows: Optional[Sequence[int]] = None,
             windows: Optional[Sequence[int]] = None) -> Dict[str, Any]:
@@ -403,6 +517,8 @@ def forward(cfg: Any, params: Any, tokens: np.ndarray, targets: Optional[np.ndar
     (per layer [V, Hkv*D]) and ``ve_gate`` (per layer [Hkv, 12]); with
     ``cfg.looped`` also ``pass_emb`` ([2, C]) and ``gate_logit`` ([L]).
     """
+    if getattr(cfg, "nested_c1", 0):
+        return forward_nested(cfg, params, tokens, targets, dtype, want_logits, rows, windows)
     rows = list(range(tokens.shape[0])) if rows is None else list(rows)
     out_l, out_z = [], []
     for b in rows:

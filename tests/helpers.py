@@ -53,7 +53,8 @@ def dense_params(p: gptdata.Preset, seed: int = 0) -> dict:
         "x0_lambda": w.x0_lambda.astype(np.float64).copy(),
     }
     for n in ("wq", "wk", "wv", "wo", "w1", "w2"):
-        d[n] = [m.astype(np.float64) for m in getattr(w, n)]
+        d[n] = [[b.astype(np.float64) for b in m] if isinstance(m, list) else m.astype(np.float64)
+                for m in getattr(w, n)]
     if w.ve is not None:
         d["ve"] = [m.astype(np.float64) for m in w.ve]
         d["ve_gate"] = [m.astype(np.float64) for m in w.ve_gate]

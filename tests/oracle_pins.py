@@ -602,4 +602,102 @@ def pin_looped_prior_comes_from_pass_one():
     assert np.allclose(_fwd(p, same, tok, tgt)["losses"], ref["losses"], rtol=1e-10, atol=1e-10)
 
 
+# ----------------------------------------------------------------------------- nested model
+
+def _nest_preset(**kw):
+    base = dict(n_layer=2, n_head=4, n_kv_head=4, head_dim=8, d_model=32, mlp_dim=128,
+                nested_c1=8, seq_len=12, vocab=50)
+    base.update(kw)
+    return small_preset(**base)
+
+
+def _inner_params(prm, c1):
+    inner = {"wte": np.ascontiguousarray(prm["wte"][:, :c1]),
+             "lm_head": np.ascontiguousarray(prm["lm_head"][:, :c1]),
+             "resid_lambda": prm["resid_lambda"], "x0_lambda": prm["x0_lambda"]}
+    for n in ("wq", "wk", "wv", "wo", "w1", "w2"):
+        inner[n] = [blocks[0] for blocks in prm[n]]
+    return inner
+
+
+def pin_nested_inner_equals_standalone():
+    """[F]: the top-left corner of the nested network is the smaller model -- the kfront=1
+    losses and logits of one pass of the full model equal, bitwise, those of the standalone
+    inner model (width c1, the first heads, the inner MLP width, W_E and W_U restricted to
+    the first c1 columns, the diagonal blocks of every linear)."""
+    p = _nest_preset()
+    prm = dense_params(p)
+    rows = _tokens(p)
+    tok, tgt = rows[:, :-1], rows[:, 1:]
+    got = _fwd(p, prm, tok, tgt, want_logits=True)
+    c1 = p.nested_c1
+    inner = p.with_(nested_c1=0, d_model=c1, n_head=p.n_head * c1 // p.d_model,
+                    n_kv_head=p.n_kv_head * c1 // p.d_model, mlp_dim=p.mlp_dim * c1 // p.d_model)
+    ref = _fwd(inner, _inner_params(prm, c1), tok, tgt, want_logits=True)
+    assert np.array_equal(got["logits_k1"], ref["logits"])
+    assert np.array_equal(got["losses_k1"], ref["losses"]) and got["mean_k1"] == ref["mean"]
+    assert not np.allclose(got["losses"], got["losses_k1"])
+
+
+def pin_nested_one_block_is_plain():
+    """With a single block (c1 = C) the nested forward is the plain model, bitwise."""
+    p = _nest_preset(nested_c1=32)
+    prm = dense_params(p)
+    rows = _tokens(p)
+    tok, tgt = rows[:, :-1], rows[:, 1:]
+    got = _fwd(p, prm, tok, tgt, want_logits=True)
+    plain = dict(prm)
+    for n in ("wq", "wk", "wv", "wo", "w1", "w2"):
+        plain[n] = [blocks[0] for blocks in prm[n]]
+    ref = _fwd(p.with_(nested_c1=0), plain, tok, tgt, want_logits=True)
+    assert np.array_equal(got["logits"], ref["logits"]) and np.array_equal(got["losses"], ref["losses"])
+
+
+def pin_blocktri_zero_padded_dense():
+    """[F]: a block lower triangular linear is the dense product with the upper block zero."""
+    rng = np.random.default_rng(12)
+    o1, o2, i1, i2 = 3, 5, 4, 6
+    w1, w2 = rng.standard_normal((o1, i1)), rng.standard_normal((o2, i1 + i2))
+    dense = np.zeros((o1 + o2, i1 + i2))
+    dense[:o1, :i1], dense[o1:, :] = w1, w2
+    x = rng.standard_normal((7, i1 + i2))
+    assert np.allclose(oracle.blocktri_linear(x, [w1, w2], i1), x @ dense.T, rtol=1e-13, atol=1e-13)
+
+
+def pin_prefix_rms_norm():
+    """PrefixRMSNorm: the first block is RMSNorm of the prefix (unit RMS, blind to the rest:
+    changing the second block leaves it bitwise unchanged); with a zero prefix the second
+    block is x2 / RMS(x) over all C dims, whose RMS over its own C - c1 dims is sqrt(C/(C-c1))."""
+    rng = np.random.default_rng(13)
+    C, c1 = 12, 4
+    x = rng.standard_normal((6, C)) * rng.uniform(0.1, 10, (6, 1))
+    y = oracle.prefix_rms_norm(x, c1, 0.0)
+    assert np.allclose(np.mean(y[:, :c1] ** 2, axis=-1), 1.0, rtol=0, atol=1e-12)
+    x2 = x.copy()
+    x2[:, c1:] *= 7.0
+    assert np.array_equal(oracle.prefix_rms_norm(x2, c1, 0.0)[:, :c1], y[:, :c1])
+    z = x.copy()
+    z[:, :c1] = 0.0
+    yz = oracle.prefix_rms_norm(z, c1, 1e-30)   # tiny eps: the zero prefix itself stays finite
+    assert np.allclose(np.sqrt(np.mean(yz[:, c1:] ** 2, axis=-1)), math.sqrt(C / (C - c1)), rtol=1e-12)
+
+
+def pin_nested_filtration():
+    """Changing only weights that act on or produce the second block (row block 2 of every
+    linear, the lm_head's later columns) leaves the kfront=1 losses bitwise unchanged."""
+    p = _nest_preset()
+    prm = dense_params(p)
+    rows = _tokens(p)
+    tok, tgt = rows[:, :-1], rows[:, 1:]
+    a = _fwd(p, prm, tok, tgt)
+    prm2 = dict(prm)
+    for n in ("wq", "wk", "wv", "wo", "w1", "w2"):
+        prm2[n] = [[b0, 3.0 * b1] for b0, b1 in prm[n]]
+    prm2["lm_head"] = prm["lm_head"].copy()
+    prm2["lm_head"][:, p.nested_c1:] *= -2.0
+    b = _fwd(p, prm2, tok, tgt)
+    assert np.array_equal(a["losses_k1"], b["losses_k1"])
+    assert not np.allclose(a["losses"], b["losses"])
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

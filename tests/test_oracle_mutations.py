@@ -13,7 +13,8 @@ import oracle_pins as P
 _orig = {n: getattr(oracle, n) for n in ("apply_rope", "visible_mask", "relu_squared", "softcap",
                                           "token_losses", "rms_norm", "attention", "block", "linear",
                                           "has_ve", "value_embed_mix", "softplus",
-                                          "attention_with_prior")}
+                                          "attention_with_prior", "prefix_rms_norm",
+                                          "blocktri_linear")}
 
 
 def _rope_sign(u, cos, sin):
@@ -196,6 +197,21 @@ def _routing_reversed(monkeypatch):
     monkeypatch.setattr(oracle, "block", blk)
 
 
+def _prefix_norm_own_rms(u, c1, eps=0.0):
+    first = _orig["rms_norm"](np.ascontiguousarray(u[..., :c1]), eps)
+    if c1 == u.shape[-1]:
+        return first
+    return np.concatenate([first, _orig["rms_norm"](np.ascontiguousarray(u[..., c1:]), eps)], axis=-1)
+
+
+def _blocktri_no_lower_block(x, blocks, in1):
+    w1, w2 = blocks
+    y1 = np.ascontiguousarray(x[..., :in1]) @ w1.T
+    if w2.shape[0] == 0:
+        return y1
+    return np.concatenate([y1, x[..., in1:] @ w2[:, in1:].T], axis=-1)
+
+
 MUTATIONS = {
     "rope_sign": (lambda mp: mp.setattr(oracle, "apply_rope", _rope_sign), [P.pin_rope_worked_example]),
     "rope_interleaved": (lambda mp: mp.setattr(oracle, "apply_rope", _rope_interleaved),
@@ -229,6 +245,10 @@ MUTATIONS = {
     "prior_from_pass_two": (lambda mp: mp.setattr(oracle, "attention_with_prior", _prior_from_pass_two),
                             [P.pin_looped_prior_comes_from_pass_one, P.pin_looped_augmented_width]),
     "routing_reversed": (_routing_reversed, [P.pin_looped_equal_passes_closed_form]),
+    "prefix_norm_block2_own_rms": (lambda mp: mp.setattr(oracle, "prefix_rms_norm", _prefix_norm_own_rms),
+                                   [P.pin_prefix_rms_norm]),
+    "blocktri_without_lower_block": (lambda mp: mp.setattr(oracle, "blocktri_linear", _blocktri_no_lower_block),
+                                     [P.pin_blocktri_zero_padded_dense]),
 }
 
 
