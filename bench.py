@@ -37,13 +37,23 @@ def _attn_flops(p, w, prior=False):
     return (6 if prior else 4) * p.n_head * p.head_dim * avg
 
 
+def live_fraction(p):
+    """Share of a nested linear's weights that are live (block lower triangular, inner share
+    r = c1/C of both dimensions): 1 - r + r^2; 1 for a dense model."""
+    r = getattr(p, "nested_c1", 0) / p.d_model
+    return 1.0 - r + r * r if r else 1.0
+
+
 def flops_per_token(p, windows):
-    """Algorithmic forward FLOPs per token: every linear (2 per multiply-add) plus attention
-    over the visible keys only.  Looped trunk: pass 1 needs L-1 full layers and the last
-    layer's projection (its q, k), pass 2 all L layers with the prior."""
+    """Algorithmic forward FLOPs per token: every linear (2 per multiply-add; nested models:
+    the live blocks only) plus attention over the visible keys only.  Looped trunk: pass 1
+    needs L-1 full layers and the last layer's projection (its q, k), pass 2 all L layers with
+    the prior.  Nested models count the lm_head once: the kfront=1 logits are a column prefix
+    of the same product."""
     C, H, Hkv, D, F, V = p.d_model, p.n_head, p.n_kv_head, p.head_dim, p.mlp_dim, p.vocab
-    qkv = 2 * C * (H + 2 * Hkv) * D
-    lin = qkv + 2 * (H * D * C + 2 * C * F)
+    live = live_fraction(p)
+    qkv = 2 * C * (H + 2 * Hkv) * D * live
+    lin = qkv + 2 * (H * D * C + 2 * C * F) * live
     L = p.n_layer
     if getattr(p, "looped", False):
         pass1 = (L - 1) * lin + qkv + sum(_attn_flops(p, w) for w in windows[:-1])
@@ -65,8 +75,11 @@ def flops_per_launch(p, windows):
         att = [_attn_flops(p, w) for w in windows[:-1]] + [_attn_flops(p, w, True) for w in windows]
     else:
         att = [_attn_flops(p, w) for w in windows]
-    return {1: 2.0 * M * C * (H + 2 * Hkv) * D, 2: M * sum(att) / len(att), 3: 2.0 * M * H * D * C,
-            4: 2.0 * M * C * F, 5: 2.0 * M * F * C, 6: 2.0 * M * C * V}
+    live = live_fraction(p)
+    # nested: the two lm_head launches (full, then the inner K-prefix) are averaged
+    head = M * V * (C + p.nested_c1) if getattr(p, "nested_c1", 0) else 2.0 * M * C * V
+    return {1: 2.0 * M * C * (H + 2 * Hkv) * D * live, 2: M * sum(att) / len(att),
+            3: 2.0 * M * H * D * C * live, 4: 2.0 * M * C * F * live, 5: 2.0 * M * F * C * live, 6: head}
 
 
 def measured_traffic(root, kind):
@@ -136,16 +149,26 @@ def main():
     loss = torch.empty((B, T), dtype=torch.float32, device=dev)
     mean = torch.empty(1, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
+    nested = bool(getattr(p, "nested_c1", 0))
+    if nested:  # both losses of the nested model (full and kfront=1) come from every step
+        loss1 = torch.empty((B, T), dtype=torch.float32, device=dev)
+        mean1 = torch.empty(1, dtype=torch.float32, device=dev)
+
+    def fwd(timing=None):
+        if nested:
+            return model.forward_nested(t_tok, t_tgt, loss, mean, None, loss1, mean1, None, stream, timing)
+        return model.forward(t_tok, t_tgt, loss, mean, None, stream, timing=timing)
 
     def step():
-        st = model.forward(t_tok, t_tgt, loss, mean, None, stream)
+        st = fwd()
         if st != gf.GPT_OK:
             raise RuntimeError(gf.gpt_status_string(st))
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    print(f"[bench] warmup done, mean loss {mean.item():.4f}", file=sys.stderr, flush=True)
+    print(f"[bench] warmup done, mean loss {mean.item():.4f}"
+          + (f", kfront=1 mean loss {mean1.item():.4f}" if nested else ""), file=sys.stderr, flush=True)
 
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -168,8 +191,8 @@ def main():
     L = p.n_layer
     if getattr(p, "looped", False):  # pass 1 stops after its last layer's projection
         per_step = {1: 2 * L, 2: 2 * L - 1, 3: 2 * L - 1, 4: 2 * L - 1, 5: 2 * L - 1, 6: 1}
-    else:
-        per_step = {1: L, 2: L, 3: L, 4: L, 5: L, 6: 1}
+    else:  # nested: one pair covers both row blocks of a step; the lm_head runs twice
+        per_step = {1: L, 2: L, 3: L, 4: L, 5: L, 6: 2 if nested else 1}
     fpl = flops_per_launch(p, windows)
     kern = {}
     for kind in KINDS:
@@ -182,7 +205,7 @@ def main():
         for i in range(args.kernel_steps):  # one slice of event pairs per step
             sl = slice(i * per_step[kind], (i + 1) * per_step[kind])
             t = gf.launch_timing(kind, evb[sl], eve[sl])
-            st = model.forward(t_tok, t_tgt, loss, mean, None, stream, timing=t)
+            st = fwd(t)
             if st != gf.GPT_OK:
                 raise RuntimeError(gf.gpt_status_string(st))
             assert t.recorded == per_step[kind]

@@ -26,7 +26,8 @@ GPT_F32, GPT_BF16 = 0, 1
  GPT_KERNEL_LM_HEAD) = 1, 2, 3, 4, 5, 6
 
 EXPORTED = [
-    "gpt_validate", "gpt_workspace_bytes", "gpt_fwd_loss", "gpt_fwd_loss_timed", "gpt_device_status",
+    "gpt_validate", "gpt_workspace_bytes", "gpt_fwd_loss", "gpt_fwd_loss_timed", "gpt_fwd_loss_nested",
+    "gpt_device_status",
     "gpt_status_string",
     "gpt_op_embed_norm", "gpt_op_mix_norm", "gpt_op_rope_table", "gpt_op_qk_rope_norm",
     "gpt_op_linear", "gpt_op_qkv", "gpt_op_attention", "gpt_op_lm_head_ce_workspace",
@@ -43,6 +44,7 @@ class gpt_cfg(ctypes.Structure):
         ("softcap", ctypes.c_float), ("rope_base", ctypes.c_float), ("attn_scale", ctypes.c_float),
         ("norm_eps", ctypes.c_float), ("dtype", ctypes.c_int32),
         ("has_ve", ctypes.POINTER(ctypes.c_uint8)), ("looped", ctypes.c_int32),
+        ("nested_c1", ctypes.c_int32),
     ]
 
 
@@ -83,6 +85,8 @@ def _load() -> ctypes.CDLL:
         "gpt_fwd_loss": (I, [ctypes.POINTER(gpt_cfg), ctypes.POINTER(gpt_weights), P, P, P, P, P, P, S, P]),
         "gpt_fwd_loss_timed": (I, [ctypes.POINTER(gpt_cfg), ctypes.POINTER(gpt_weights), P, P, P, P, P, P, S, P,
                                    ctypes.POINTER(gpt_launch_timing)]),
+        "gpt_fwd_loss_nested": (I, [ctypes.POINTER(gpt_cfg), ctypes.POINTER(gpt_weights), P, P, P, P, P, P, P, P,
+                                    P, S, P, ctypes.POINTER(gpt_launch_timing)]),
         "gpt_device_status": (I, [P, P]),
         "gpt_status_string": (ctypes.c_char_p, [I]),
         "gpt_op_embed_norm": (I, [I, P, P, P, P, P, P, P, I, I, I, F, P, P]),
@@ -166,7 +170,7 @@ def make_cfg(p: Any, batch: Optional[int] = None, windows: Optional[Sequence[int
                 p.softcap, p.rope_base, p.attn_scale, p.norm_eps,
                 GPT_BF16 if p.dtype == "bf16" else GPT_F32,
                 None if ve is None else ctypes.cast(ve, ctypes.POINTER(ctypes.c_uint8)),
-                1 if getattr(p, "looped", False) else 0)
+                1 if getattr(p, "looped", False) else 0, int(getattr(p, "nested_c1", 0) or 0))
     c._win, c._ve = win, ve
     return c
 
@@ -198,6 +202,15 @@ def gpt_fwd_loss_timed(cfg: gpt_cfg, weights: gpt_weights, tokens, targets, loss
                                       _ptr(loss), _ptr(mean_loss), _ptr(logits), _ptr(workspace),
                                       workspace_bytes, _stream(stream),
                                       None if timing is None else ctypes.byref(timing))
+
+
+def gpt_fwd_loss_nested(cfg: gpt_cfg, weights: gpt_weights, tokens, targets, loss, mean_loss, logits,
+                        loss_k1, mean_k1, logits_k1, workspace, workspace_bytes: int, stream=None,
+                        timing: Optional[gpt_launch_timing] = None) -> int:
+    return _load().gpt_fwd_loss_nested(ctypes.byref(cfg), ctypes.byref(weights), _ptr(tokens), _ptr(targets),
+                                       _ptr(loss), _ptr(mean_loss), _ptr(logits), _ptr(loss_k1),
+                                       _ptr(mean_k1), _ptr(logits_k1), _ptr(workspace), workspace_bytes,
+                                       _stream(stream), None if timing is None else ctypes.byref(timing))
 
 
 def launch_timing(kind: int, begin_events, end_events) -> gpt_launch_timing:
@@ -276,7 +289,9 @@ class DeviceModel:
     ``weights`` is any object with attributes wte, lm_head, resid_lambda, x0_lambda and
     per-layer lists wq, wk, wv, wo, w1, w2 (numpy arrays: uint16 bf16 bits or float32), plus
     per-layer ve and ve_gate lists when the configuration has value embeddings, and
-    pass_emb ([2, C]) and gate_logit ([L] float32) for the looped trunk.
+    pass_emb ([2, C]) and gate_logit ([L] float32) for the looped trunk.  For a nested
+    configuration each per-layer linear is its two row blocks [block1, block2]; they are
+    uploaded back to back into one buffer, the storage gpt_weights documents.
     """
 
     def __init__(self, p: Any, weights: Any, batch: Optional[int] = None, device: str = "cuda",
@@ -295,8 +310,12 @@ class DeviceModel:
             "x0_lambda": torch.from_numpy(np.asarray(weights.x0_lambda, np.float32)).to(device),
         }
         arrs = {}
+        nested = bool(getattr(p, "nested_c1", 0))
         for n in ("wq", "wk", "wv", "wo", "w1", "w2"):
-            self.t[n] = [to_device(m, dt, device) for m in getattr(weights, n)]
+            mats = getattr(weights, n)
+            if nested:
+                mats = [np.concatenate([np.ravel(b) for b in blocks]) for blocks in mats]
+            self.t[n] = [to_device(m, dt, device) for m in mats]
             arrs[n] = (ctypes.c_void_p * p.n_layer)(*[m.data_ptr() for m in self.t[n]])
         ve_ptr = gate_ptr = None
         if getattr(p, "value_embeds", False):
@@ -333,6 +352,28 @@ class DeviceModel:
                                       self.ws_ptr, self.ws_bytes, stream, timing)
         return gpt_fwd_loss(self.cfg, self.w, tokens, targets, loss, mean, logits, self.ws_ptr,
                             self.ws_bytes, stream)
+
+    def forward_nested(self, tokens, targets=None, loss=None, mean=None, logits=None, loss_k1=None,
+                       mean_k1=None, logits_k1=None, stream=None,
+                       timing: Optional[gpt_launch_timing] = None) -> int:
+        """Enqueue gpt_fwd_loss_nested (full model and kfront=1 outputs from one pass)."""
+        return gpt_fwd_loss_nested(self.cfg, self.w, tokens, targets, loss, mean, logits, loss_k1,
+                                   mean_k1, logits_k1, self.ws_ptr, self.ws_bytes, stream, timing)
+
+    def call_nested(self, tokens, targets=None, want_logits: bool = False):
+        """Allocate outputs, run gpt_fwd_loss_nested, and return a dict with loss, mean, logits
+        and loss_k1, mean_k1, logits_k1 (None where not computed)."""
+        import torch
+        B, T, V = self.batch, self.p.seq_len, self.p.vocab
+        dev = tokens.device
+        out = {}
+        for sfx in ("", "_k1"):
+            out["loss" + sfx] = torch.empty((B, T), dtype=torch.float32, device=dev) if targets is not None else None
+            out["mean" + sfx] = torch.empty(1, dtype=torch.float32, device=dev) if targets is not None else None
+            out["logits" + sfx] = torch.empty((B, T, V), dtype=torch.float32, device=dev) if want_logits else None
+        _check(self.forward_nested(tokens, targets, out["loss"], out["mean"], out["logits"], out["loss_k1"],
+                                   out["mean_k1"], out["logits_k1"]), "gpt_fwd_loss_nested")
+        return out
 
     def __call__(self, tokens, targets=None, want_logits: bool = False):
         """Allocate outputs, run, and return (loss [B,T], mean [1], logits or None)."""

@@ -64,7 +64,28 @@ gpt_status validate(const gpt_cfg* c) {
   }
   if (c->looped != 0 && c->looped != 1) return GPT_E_INVALID_ARG;
   if (c->looped && c->dtype == GPT_BF16 && c->head_dim != 128) return GPT_E_UNSUPPORTED;
+  if (c->nested_c1 != 0) {
+    const long c1 = c->nested_c1, C = c->d_model;
+    if (c1 < 0 || c1 > C) return GPT_E_INVALID_ARG;
+    // every partitioned dimension splits exactly in the proportion c1 : C
+    if ((c->n_head * c1) % C || (c->n_kv_head * c1) % C || (c->mlp_dim * c1) % C)
+      return GPT_E_INVALID_ARG;
+    if (c->looped || any_ve(c)) return GPT_E_UNSUPPORTED;
+    if (c1 % 64 || (c->mlp_dim * c1 / C) % 64) return GPT_E_UNSUPPORTED;
+    if (c->dtype == GPT_BF16 && ((c->n_head * c1 / C * c->head_dim) % 128 ||
+                                 (c->n_kv_head * c1 / C * c->head_dim) % 128))
+      return GPT_E_UNSUPPORTED;
+  }
   return GPT_OK;
+}
+
+// Shares of the inner block of a nested model (validated exact).
+struct Split {
+  int c1, h1, hkv1, f1;
+};
+Split split_of(const gpt_cfg* c) {
+  const long c1 = c->nested_c1, C = c->d_model;
+  return {(int)c1, (int)(c->n_head * c1 / C), (int)(c->n_kv_head * c1 / C), (int)(c->mlp_dim * c1 / C)};
 }
 
 Layout plan(const gpt_cfg* c) {
@@ -147,8 +168,11 @@ gpt_status lm_head_ce(bool bf, const void* xf, const void* wu, const int32_t* ta
                       const int32_t* tokens, int M, int C, int V, float cap, float* loss,
                       float* mean, float* logits, float* partial, float* tgt, int nnb,
                       unsigned* flags, hipStream_t s, const Timer& tm, const float* rs_ssp = nullptr,
-                      float eps = 0.f) {
-  GemmArgs g = gemm_args(xf, C, wu, V, C, M, nullptr, 0);
+                      float eps = 0.f, int K = 0) {
+  // K < C: the product over input columns [0, K) only (xf and wu keep their row stride C)
+  if (K <= 0) K = C;
+  GemmArgs g = gemm_args(xf, C, wu, V, K, M, nullptr, 0);
+  g.ldb = C;
   if (rs_ssp) { g.rs_ssp = rs_ssp; g.rs_n = C / gemm_resid_slice_cols(M, C); g.rs_c = (float)C; g.eps = eps; }
   g.targets = targets; g.partial = partial; g.tgt_logit = tgt; g.logits = logits;
   g.nnb = nnb; g.cap = cap;
@@ -160,6 +184,117 @@ gpt_status lm_head_ce(bool bf, const void* xf, const void* wu, const int32_t* ta
   }
   return GPT_OK;
 }
+
+// Row block r (0 or 1) of a nested linear [out, in] with inner shares (o1, i1): its first
+// element (row block 2 follows row block 1).
+const void* row_block(const void* base, int r, int o1, int i1, size_t es) {
+  return r == 0 ? base : (const char*)base + (size_t)o1 * i1 * es;
+}
+
+// The layers of a nested (two-block) model, from the embedding to the final PrefixRMSNorm'd
+// stream in xn ("Fully Nested Transformers", opening section: block lower triangular linears
+// and PrefixRMSNorm).  Row block 1 of every linear is a GEMM over the inner input columns
+// [0, in1) writing the inner output columns; row block 2 a GEMM over all input columns writing
+// the rest.  Each output element is written by exactly one of the two, so residual epilogues
+// (and the next layer's x0 mix in the MLP down-projection) apply per element unchanged.  Every
+// norm is materialised by the row kernel (a PrefixRMSNorm is not a row scale of the product).
+gpt_status nested_layers(const gpt_cfg* c, const gpt_weights* w, const int32_t* tokens,
+                         const Split& sp, const Layout& L, char* ws, const Timer& tm,
+                         hipStream_t s) {
+  const bool bf = c->dtype == GPT_BF16;
+  const size_t es = bf ? 2 : 4;
+  const int B = c->batch, T = c->seq_len, M = B * T, C = c->d_model, H = c->n_head;
+  const int Hkv = c->n_kv_head, D = c->head_dim, F = c->mlp_dim, V = c->vocab;
+  const int c1 = sp.c1, h1 = sp.h1, hkv1 = sp.hkv1, f1 = sp.f1;
+  const float eps = c->norm_eps;
+  unsigned* flags = (unsigned*)(ws + L.flags);
+  float* x = (float*)(ws + L.x);
+  float* x0 = (float*)(ws + L.x0);
+  void* xn = ws + L.xn;
+  void* qk = ws + L.qk;
+  void* vt = ws + L.vt;
+  void* o = ws + L.o;
+  void* hbuf = ws + L.h;
+  const float2* cs = (const float2*)(ws + L.cs);
+  float* ssp = (float*)(ws + L.ssp);
+  const int nqk = (H + Hkv) * D, nqkv = (H + 2 * Hkv) * D;
+  auto gemm2 = [&](Epi e, const GemmArgs& g1, const GemmArgs& g2) -> hipError_t {
+    hipError_t r = g1.N > 0 ? gemm(bf, e, g1, s) : hipSuccess;
+    if (r == hipSuccess && g2.N > 0) r = gemm(bf, e, g2, s);
+    return r;
+  };
+  CK(launch_embed_norm(tokens, w->wte, bf, w->resid_lambda, w->x0_lambda, x0, x, xn, M, C, V,
+                       eps, flags, s, nullptr, c1));
+  for (int l = 0; l < c->n_layer; ++l) {
+    const int win = c->window[l] < T ? c->window[l] : T;
+    const void* wq[2] = {row_block(w->wq[l], 0, h1 * D, c1, es), row_block(w->wq[l], 1, h1 * D, c1, es)};
+    const void* wk[2] = {row_block(w->wk[l], 0, hkv1 * D, c1, es), row_block(w->wk[l], 1, hkv1 * D, c1, es)};
+    const void* wv[2] = {row_block(w->wv[l], 0, hkv1 * D, c1, es), row_block(w->wv[l], 1, hkv1 * D, c1, es)};
+    const void* wo[2] = {row_block(w->wo[l], 0, c1, h1 * D, es), row_block(w->wo[l], 1, c1, h1 * D, es)};
+    const void* w1[2] = {row_block(w->w1[l], 0, f1, c1, es), row_block(w->w1[l], 1, f1, c1, es)};
+    const void* w2[2] = {row_block(w->w2[l], 0, c1, f1, es), row_block(w->w2[l], 1, c1, f1, es)};
+    if (bf) {
+      // q/k/v: one GEMM per row block over its three segments; the epilogue places q and k
+      // heads at their model-wide columns and v heads at their model-wide head index
+      GemmArgs g[2];
+      for (int r = 0; r < 2; ++r) {
+        const int hq = r ? H - h1 : h1, hk = r ? Hkv - hkv1 : hkv1;
+        g[r] = gemm_args(xn, C, wq[r], (hq + 2 * hk) * D, r ? C : c1, M, qk, nqk);
+        g[r].B1 = wk[r]; g[r].B2 = wv[r]; g[r].nseg0 = hq * D; g[r].nseg1 = hk * D;
+        g[r].vt = vt; g[r].T = T; g[r].D = D; g[r].Hkv = Hkv; g[r].nqk = (hq + hk) * D; g[r].eps = eps;
+        g[r].q_off = r ? h1 * D : 0;
+        g[r].k_off = H * D + (r ? hkv1 * D : 0);
+        g[r].v_head_off = r ? hkv1 : 0;
+        if (D == 128) g[r].cs = cs;
+      }
+      TIMED(tm, GPT_KERNEL_QKV, gemm2(EPI_QKV, g[0], g[1]));
+      if (D != 128) CK(launch_qk_rope_norm(qk, true, nqk, cs, M, T, H + Hkv, D, eps, s));
+      TIMED(tm, GPT_KERNEL_ATTENTION, launch_attn_bf16(qk, vt, o, B, T, H, Hkv, D, win,
+                                                       c->attn_scale, s));
+    } else {
+      // q/k/v into the [q | k | v] rows: one GEMM per (projection, row block)
+      const void* wp[3][2] = {{wq[0], wq[1]}, {wk[0], wk[1]}, {wv[0], wv[1]}};
+      const int n1[3] = {h1 * D, hkv1 * D, hkv1 * D}, n[3] = {H * D, Hkv * D, Hkv * D};
+      const int base[3] = {0, H * D, (H + Hkv) * D};
+      for (int j = 0; j < 3; ++j) {
+        float* out = (float*)qk + base[j];
+        CK(gemm2(EPI_STORE, gemm_args(xn, C, wp[j][0], n1[j], c1, M, out, nqkv),
+                 gemm_args(xn, C, wp[j][1], n[j] - n1[j], C, M, out + n1[j], nqkv)));
+      }
+      CK(launch_qk_rope_norm(qk, false, nqkv, cs, M, T, H + Hkv, D, eps, s));
+      CK(launch_attn_f32((const float*)qk, (float*)o, B, T, H, Hkv, D, win, c->attn_scale, s));
+    }
+    // x += o W_O^T: inner rows read the inner heads' outputs
+    TIMED(tm, GPT_KERNEL_ATTN_OUT,
+          gemm2(EPI_RESID, gemm_args(o, H * D, wo[0], c1, h1 * D, M, x, C),
+                gemm_args(o, H * D, wo[1], C - c1, H * D, M, x + c1, C)));
+    CK(launch_mix_norm(x, x0, w->resid_lambda, w->x0_lambda, l, false, xn, bf, M, C, eps, s, c1));
+    // h = relu(xn W_1^T)^2
+    char* hb = (char*)hbuf;
+    TIMED(tm, GPT_KERNEL_MLP_UP,
+          gemm2(EPI_RELU2, gemm_args(xn, C, w1[0], f1, c1, M, hb, F),
+                gemm_args(xn, C, w1[1], F - f1, C, M, hb + (size_t)f1 * es, F)));
+    // x += h W_2^T; the bf16 epilogue also applies the next layer's x0 mix
+    const bool more = l + 1 < c->n_layer;
+    GemmArgs gd[2] = {gemm_args(hbuf, F, w2[0], c1, f1, M, x, C),
+                      gemm_args(hbuf, F, w2[1], C - c1, F, M, x + c1, C)};
+    if (bf && more)
+      for (int r = 0; r < 2; ++r) {
+        const int c0 = r ? c1 : 0;  // first output column of the launch
+        gd[r].xb = (bf16_t*)xn + c0; gd[r].ssp = ssp; gd[r].col_off = c0;
+        gd[r].x0 = x0 + c0; gd[r].lam = w->resid_lambda; gd[r].mu = w->x0_lambda; gd[r].layer = l + 1;
+      }
+    TIMED(tm, GPT_KERNEL_MLP_DOWN, gemm2(EPI_RESID, gd[0], gd[1]));
+    CK(launch_mix_norm(x, x0, w->resid_lambda, w->x0_lambda, l + 1, more && !bf, xn, bf, M, C, eps,
+                       s, c1));
+  }
+  return GPT_OK;
+}
+
+gpt_status run(const gpt_cfg* c, const gpt_weights* w, const int32_t* tokens,
+               const int32_t* targets, float* loss, float* mean_loss, float* logits,
+               float* loss1, float* mean1, float* logits1, void* workspace,
+               size_t workspace_bytes, void* stream, gpt_launch_timing* timing);
 
 }  // namespace
 
@@ -183,6 +318,28 @@ gpt_status gpt_fwd_loss_timed(const gpt_cfg* c, const gpt_weights* w, const int3
                               const int32_t* targets, float* loss, float* mean_loss,
                               float* logits, void* workspace, size_t workspace_bytes,
                               void* stream, gpt_launch_timing* timing) {
+  return run(c, w, tokens, targets, loss, mean_loss, logits, nullptr, nullptr, nullptr, workspace,
+             workspace_bytes, stream, timing);
+}
+
+gpt_status gpt_fwd_loss_nested(const gpt_cfg* c, const gpt_weights* w, const int32_t* tokens,
+                               const int32_t* targets, float* loss, float* mean_loss,
+                               float* logits, float* loss_k1, float* mean_k1, float* logits_k1,
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               gpt_launch_timing* timing) {
+  if (!c || c->nested_c1 == 0) return GPT_E_INVALID_ARG;
+  return run(c, w, tokens, targets, loss, mean_loss, logits, loss_k1, mean_k1, logits_k1,
+             workspace, workspace_bytes, stream, timing);
+}
+
+}  // extern "C"
+
+namespace {
+
+gpt_status run(const gpt_cfg* c, const gpt_weights* w, const int32_t* tokens,
+               const int32_t* targets, float* loss, float* mean_loss, float* logits,
+               float* loss1, float* mean1, float* logits1, void* workspace,
+               size_t workspace_bytes, void* stream, gpt_launch_timing* timing) {
   if (timing) {
     if (timing->kind < GPT_KERNEL_QKV || timing->kind > GPT_KERNEL_LM_HEAD || timing->capacity < 0 ||
         (timing->capacity > 0 && (!timing->begin || !timing->end)))
@@ -210,6 +367,10 @@ gpt_status gpt_fwd_loss_timed(const gpt_cfg* c, const gpt_weights* w, const int3
     return GPT_E_INVALID_ARG;
   if (targets && (!loss || !mean_loss)) return GPT_E_INVALID_ARG;
   if (!targets && !logits) return GPT_E_INVALID_ARG;
+  if (!loss1 != !mean1 || (loss1 && !targets) || (loss1 && !aligned(loss1, 4)) ||
+      (mean1 && !aligned(mean1, 4)) || (logits1 && !aligned(logits1, 4)))
+    return GPT_E_INVALID_ARG;
+  const bool want1 = loss1 || logits1;
   const void* ptrs16[] = {w->wte, w->lm_head};
   for (const void* p : ptrs16)
     if (!aligned(p, 16)) return GPT_E_INVALID_ARG;
@@ -252,6 +413,16 @@ gpt_status gpt_fwd_loss_timed(const gpt_cfg* c, const gpt_weights* w, const int3
   // stops after the last layer's projection, the only part of it pass 2 reads); pass 1 adds
   // the layer's cached prior to its attention logits.  Otherwise there is one pass.
   const size_t es = bf ? 2 : 4;
+  if (c->nested_c1) {
+    const Split sp = split_of(c);
+    if (gpt_status e = nested_layers(c, w, tokens, sp, L, ws, tm, s); e != GPT_OK) return e;
+    // the final (prefix-)normalised stream is in xn: full model, then the inner model
+    gpt_status e = lm_head_ce(bf, xn, w->lm_head, targets, tokens, M, C, V, c->softcap, loss,
+                              mean_loss, logits, partial, tgt, L.nnb, flags, s, tm);
+    if (e != GPT_OK || !want1) return e;
+    return lm_head_ce(bf, xn, w->lm_head, loss1 ? targets : nullptr, tokens, M, C, V, c->softcap,
+                      loss1, mean1, logits1, partial, tgt, L.nnb, flags, s, tm, nullptr, 0.f, sp.c1);
+  }
   const size_t qk1_layer = (size_t)M * (bf ? nqk : nqkv) * es;
   for (int pass = c->looped ? 0 : 1; pass < 2; ++pass) {
     const bool capture = c->looped && pass == 0, prior = c->looped && pass == 1;
@@ -269,7 +440,7 @@ gpt_status gpt_fwd_loss_timed(const gpt_cfg* c, const gpt_weights* w, const int3
         // fp32, apply the next layer's x0 mix, and emit bf16(x) plus per-slice sums of squares.
         bf16_t* xb = (bf16_t*)xn;
         GemmArgs g = gemm_args(xn, C, w->wq[l], nqkv, C, M, qk_l, nqk);
-        g.B1 = w->wk[l]; g.B2 = w->wv[l]; g.nseg0 = H * D; g.nseg1 = Hkv * D;
+        g.B1 = w->wk[l]; g.B2 = w->wv[l]; g.nseg0 = H * D; g.nseg1 = Hkv * D; g.k_off = H * D;
         g.vt = vt; g.T = T; g.D = D; g.Hkv = Hkv; g.nqk = nqk; g.eps = eps;
         const bool fused = D == 128;
         if (fused) g.cs = cs;
@@ -328,6 +499,10 @@ gpt_status gpt_fwd_loss_timed(const gpt_cfg* c, const gpt_weights* w, const int3
   return lm_head_ce(bf, xn, w->lm_head, targets, tokens, M, C, V, c->softcap, loss, mean_loss,
                     logits, partial, tgt, L.nnb, flags, s, tm);
 }
+
+}  // namespace
+
+extern "C" {
 
 gpt_status gpt_device_status(void* workspace, void* stream) {
   if (!workspace) return GPT_E_INVALID_ARG;
@@ -411,7 +586,7 @@ gpt_status gpt_op_qkv(const void* xn, const void* wq, const void* wk, const void
   if (cs && (D != 128 || T % 32)) return GPT_E_UNSUPPORTED;  // fused epilogue: whole heads, 32-row groups
   const int M = B * T, nqk = (H + Hkv) * D, nqkv = (H + 2 * Hkv) * D;
   GemmArgs g = gemm_args(xn, C, wq, nqkv, C, M, qk, nqk);
-  g.B1 = wk; g.B2 = wv; g.nseg0 = H * D; g.nseg1 = Hkv * D;
+  g.B1 = wk; g.B2 = wv; g.nseg0 = H * D; g.nseg1 = Hkv * D; g.k_off = H * D;
   g.vt = vt; g.T = T; g.D = D; g.Hkv = Hkv; g.nqk = nqk;
   g.cs = (const float2*)cs; g.eps = eps;
   CK(launch_gemm_bf16(EPI_QKV, g, (hipStream_t)stream));

@@ -132,10 +132,16 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
   static_assert(AI % 2 == 0, "A row blocks per wave must be even");
   const int wids = __builtin_amdgcn_readfirstlane(wid);
   const int pb = (wids * BI) & 1;  // parity of this wave's first B row block (0 when BI is even)
-  // A and B share their row pitch (lda == ldb, checked by the launcher).
-  int va[2];
+  // The 256x384 tiles assume A and B share their row pitch (the launcher checks lda == ldb);
+  // the other tiles keep a second offset pair for B.
+  constexpr bool SAME_LD = BN == 384;
+  int va[2], vb[2];
 #pragma unroll
-  for (int p = 0; p < 2; ++p) va[p] = ((lane >> 3) * lda + (((lane & 7) ^ (lane >> 3) ^ p) << 3)) * 2;
+  for (int p = 0; p < 2; ++p) {
+    const int c = ((lane & 7) ^ (lane >> 3) ^ p) << 3;
+    va[p] = ((lane >> 3) * lda + c) * 2;
+    vb[p] = SAME_LD ? va[p] : ((lane >> 3) * ldb + c) * 2;
+  }
   typedef __attribute__((address_space(3))) void* lds_ptr_t;
 #define GEMM_ISSUE(buf, k0)                                                                   \
   do {                                                                                       \
@@ -146,7 +152,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
     _Pragma("unroll") for (int i = 0; i < BI; ++i)                                           \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb,                                          \
         (lds_ptr_t)(Bs + (buf) * BN * BK + (wids * BI + i) * 512), 16,                      \
-        (BI % 2 == 0 ? va[i & 1] : (((pb + i) & 1) ? va[1] : va[0])),                        \
+        (BI % 2 == 0 ? vb[i & 1] : (((pb + i) & 1) ? vb[1] : vb[0])),                        \
         (k0) * 2 + (wids * BI + i) * 16 * ldb, 0, 0);                                        \
   } while (0)
 
@@ -467,7 +473,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
             if (g.ve != nullptr) {
               // Value embedding: lane L's gate is row L % 32 of this group's; each lane then
               // adds g * ve[token] for its 16 rows and 4 columns.
-              const int gg = (wcol0 - g.nqk) / g.D, ldve = g.Hkv * g.D;
+              const int gg = g.v_head_off + (wcol0 - g.nqk) / g.D, ldve = g.Hkv * g.D;
               const int grp0 = m0 + wm * TM + fm * 32;
               const int lrow = lane & 31;
               float logit = 0.f;
@@ -507,15 +513,16 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
           const int row0 = m0 + wm * TM + fm * 32;
           if (live && is_qk) {
+            const int qc = wcol0 < g.nseg0 ? g.q_off + wcol0 : g.k_off + (wcol0 - g.nseg0);
 #pragma unroll
             for (int k = 0; k < 8; ++k) {  // 32 rows x 16 chunks
               const int idx = lane + 64 * k, lr = idx >> 4, ch = idx & 15;
               if (row0 + lr < M)
-                *(bf16x8*)(qk + (size_t)(row0 + lr) * g.ldo + wcol0 + ch * 8) = *(const bf16x8*)(stg + lr * LQ + ch * 8);
+                *(bf16x8*)(qk + (size_t)(row0 + lr) * g.ldo + qc + ch * 8) = *(const bf16x8*)(stg + lr * LQ + ch * 8);
             }
           } else if (live) {
             // 32 consecutive rows are 32 consecutive positions of one sequence (T % 32 == 0)
-            const int bb = row0 / g.T, t0 = row0 - bb * g.T, gg = (wcol0 - g.nqk) / g.D;
+            const int bb = row0 / g.T, t0 = row0 - bb * g.T, gg = g.v_head_off + (wcol0 - g.nqk) / g.D;
             bf16* const vb = vt + ((size_t)(bb * g.Hkv + gg) * g.D) * g.T + t0;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {  // 128 d rows x 4 chunks of 8 positions
@@ -534,15 +541,16 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
       const int col = cbase + fn * 32;
       if (col >= N) continue;
       if (col < g.nqk) {
+        const int qcol = col < g.nseg0 ? g.q_off + col : g.k_off + (col - g.nseg0);
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int row = rbase + fm * 32 + 8 * (r >> 2) + (r & 3);
-            if (row < M) qk[(size_t)row * g.ldo + col] = (bf16)acc[fm][fn][r];
+            if (row < M) qk[(size_t)row * g.ldo + qcol] = (bf16)acc[fm][fn][r];
           }
       } else {
-        const int vc = col - g.nqk, gg = vc / g.D, d = vc - gg * g.D;
+        const int vc = col - g.nqk, gl = vc / g.D, d = vc - gl * g.D, gg = g.v_head_off + gl;
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -628,8 +636,13 @@ hipError_t run_bf16(Epi epi, const GemmArgs& a, hipStream_t s) {
       else if (a.lam == nullptr) GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_RESID_PROD>), grid, NT, s, a);
       else GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_RESID_MIX>), grid, NT, s, a);
       break;
-    case EPI_QKV: GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_QKV>), grid, NT, s, a); break;
-    case EPI_CE: GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_CE>), grid, NT, s, a); break;
+    case EPI_QKV:
+    case EPI_CE:
+      // the tile plan gives these epilogues 256-wide or 128-wide tiles only
+      if constexpr (BN != 256 && BN != 128) return hipErrorInvalidValue;
+      else if (epi == EPI_QKV) GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_QKV>), grid, NT, s, a);
+      else GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_CE>), grid, NT, s, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -772,10 +785,15 @@ GemmArgs shift_cols(const GemmArgs& a, Epi epi, int c0) {
     if (a.xb) b.xb = a.xb + c0;
     if (a.x0) b.x0 = a.x0 + c0;
     b.col_off = a.col_off + c0;
+  } else if (epi == EPI_QKV) {
+    // the output base stays; the first remaining segment is addressed as the q segment and
+    // is placed where it belonged (v columns are placed by head index)
+    b.nqk = a.nqk - c0;
+    if (c0 <= a.nseg0) b.q_off = a.q_off + c0;
+    else if (c0 < a.nqk) b.q_off = a.k_off + (c0 - a.nseg0);
   } else {
     b.out = (bf16*)a.out + c0;
   }
-  if (epi == EPI_QKV) b.nqk = a.nqk - c0;
   return b;
 }
 
@@ -810,7 +828,7 @@ struct Plan {
   int split_cols;  // 256x256 plan: columns of the leading part (0 = no split)
 };
 
-Plan plan_gemm(Epi epi, int M, int N, int nseg0, int nseg1, int ncu) {
+Plan plan_gemm(Epi epi, int M, int N, int nseg0, int nseg1, int ncu, bool same_ld = true) {
   auto seg_ok_n = [&](int bn) {
     const int e0 = nseg0, e1 = nseg0 + nseg1;
     return (e0 >= N || e0 % bn == 0) && (e1 >= N || e1 % bn == 0);
@@ -833,7 +851,7 @@ Plan plan_gemm(Epi epi, int M, int N, int nseg0, int nseg1, int ncu) {
       const double c = rounds(nbm * (N / 192)) * 0.75 / 0.9;
       if (c <= cost) { cost = c; p = Plan{Tiles::T192, 0}; }
     }
-    if (N % 384 == 0 && seg_ok_n(384)) {
+    if (N % 384 == 0 && seg_ok_n(384) && same_ld) {
       const double c = rounds(nbm * (N / 384)) * 1.5;
       if (c <= cost) { cost = c; p = Plan{Tiles::T384, 0}; }
     }
@@ -852,10 +870,10 @@ int gemm_resid_slice_cols(int M, int N) {
 }
 
 hipError_t launch_gemm_bf16(Epi epi, const GemmArgs& a, hipStream_t s) {
-  if (a.K % BK || a.M <= 0 || a.N <= 0 || a.lda != a.ldb) return hipErrorInvalidValue;
+  if (a.K % BK || a.M <= 0 || a.N <= 0) return hipErrorInvalidValue;
   if (epi == EPI_CE) return run_bf16<256, 256, 2, 4>(epi, a, s);  // must match gemm_bf16_ce_blocks
   if (epi == EPI_QKV && a.cs != nullptr && a.D != 128) return hipErrorInvalidValue;
-  const Plan p = plan_gemm(epi, a.M, a.N, a.nseg0, a.nseg1, cu_count());
+  const Plan p = plan_gemm(epi, a.M, a.N, a.nseg0, a.nseg1, cu_count(), a.lda == a.ldb);
   if (p.tiles == Tiles::T384) return run_bf16<256, 384, 2, 4>(epi, a, s);  // slices of 96 columns
   if (p.tiles == Tiles::T192) return run_bf16<256, 192, 4, 2>(epi, a, s);  // slices of 96 columns
   if (!seg_ok(a, 256)) return seg_ok(a, 128) ? run_narrow(epi, a, s) : hipErrorInvalidValue;

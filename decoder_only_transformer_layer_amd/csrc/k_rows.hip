@@ -4,7 +4,11 @@
 //
 // Sources: "The Mathematics of Karpathy's nanochat", sections "High-Level Forward Pass" (embed,
 // norm, keep x0), "RMS Normalization", "Residual Stream with Learnable Scalars" (x <- lambda x +
-// mu x0), "Rotary Position Embeddings (RoPE)" and "QK-Norm with Sharpening".
+// mu x0), "Rotary Position Embeddings (RoPE)" and "QK-Norm with Sharpening"; the two-block
+// PrefixRMSNorm of the nested model: "Fully Nested Transformers", opening section.  The prefix
+// statistic is the same lane-ordered partial sum over columns [0, c1) that a row of width c1
+// accumulates, so the first block of a nested row normalises exactly as a standalone row of
+// that width does.
 #include "common.h"
 #include "kernels.h"
 
@@ -35,7 +39,7 @@ template <typename WT, typename AT, int NCH>
 __global__ __launch_bounds__(256) void embed_norm_kernel(
     const int32_t* __restrict__ tokens, const WT* __restrict__ wte, const float* __restrict__ lam,
     const float* __restrict__ mu, float* __restrict__ x0, float* __restrict__ x, AT* __restrict__ xn,
-    int M, int C, int V, float eps, unsigned* __restrict__ flags, const WT* __restrict__ pe) {
+    int M, int C, int V, float eps, unsigned* __restrict__ flags, const WT* __restrict__ pe, int c1) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
   if (row >= M) return;
@@ -46,7 +50,7 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(
   }
   const WT* src = wte + (size_t)t * C;
   float v[NCH][4];
-  float ss = 0.f;
+  float ss = 0.f, ss1 = 0.f;
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int i = (c * 64 + lane) * 4;
@@ -58,38 +62,47 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(
 #pragma unroll
         for (int k = 0; k < 4; ++k) v[c][k] += pv[k];
       }
-      ss += v[c][0] * v[c][0] + v[c][1] * v[c][1] + v[c][2] * v[c][2] + v[c][3] * v[c][3];
+      const float q = v[c][0] * v[c][0] + v[c][1] * v[c][1] + v[c][2] * v[c][2] + v[c][3] * v[c][3];
+      ss += q;
+      if (i < c1) ss1 += q;
     }
   }
   ss = wave_sum(ss);
-  const float r0 = rsqrtf(ss / (float)C + eps);
+  ss1 = c1 < C ? wave_sum(ss1) : ss;
+  const float r0 = rsqrtf(ss / (float)C + eps), r01 = rsqrtf(ss1 / (float)c1 + eps);
   const float a = lam[0], b = mu[0];
-  float ss2 = 0.f;
+  float ss2 = 0.f, ss21 = 0.f;
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int i = (c * 64 + lane) * 4;
     if (i < C) {
       float e0[4], e1[4];
+      const float rr = i < c1 ? r01 : r0;
+      float q = 0.f;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        e0[k] = v[c][k] * r0;
+        e0[k] = v[c][k] * rr;
         e1[k] = a * e0[k] + b * e0[k];
-        ss2 += e1[k] * e1[k];
+        q += e1[k] * e1[k];
         v[c][k] = e1[k];
       }
+      ss2 += q;
+      if (i < c1) ss21 += q;
       store4(x0 + (size_t)row * C + i, e0);
       store4(x + (size_t)row * C + i, e1);
     }
   }
   ss2 = wave_sum(ss2);
-  const float r1 = rsqrtf(ss2 / (float)C + eps);
+  ss21 = c1 < C ? wave_sum(ss21) : ss2;
+  const float r1 = rsqrtf(ss2 / (float)C + eps), r11 = rsqrtf(ss21 / (float)c1 + eps);
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int i = (c * 64 + lane) * 4;
     if (i < C) {
       float e[4];
+      const float rr = i < c1 ? r11 : r1;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) e[k] = v[c][k] * r1;
+      for (int k = 0; k < 4; ++k) e[k] = v[c][k] * rr;
       store4(xn + (size_t)row * C + i, e);
     }
   }
@@ -98,7 +111,7 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(
 template <typename AT, int NCH, bool MIX>
 __global__ __launch_bounds__(256) void mix_norm_kernel(
     float* __restrict__ x, const float* __restrict__ x0, const float* __restrict__ lam,
-    const float* __restrict__ mu, int layer, AT* __restrict__ xn, int M, int C, float eps) {
+    const float* __restrict__ mu, int layer, AT* __restrict__ xn, int M, int C, float eps, int c1) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
   if (row >= M) return;
@@ -106,7 +119,7 @@ __global__ __launch_bounds__(256) void mix_norm_kernel(
   float a = 1.f, b = 0.f;
   if (MIX) { a = lam[layer]; b = mu[layer]; }
   float v[NCH][4];
-  float ss = 0.f;
+  float ss = 0.f, ss1 = 0.f;
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int i = (c * 64 + lane) * 4;
@@ -119,18 +132,22 @@ __global__ __launch_bounds__(256) void mix_norm_kernel(
         for (int k = 0; k < 4; ++k) v[c][k] = a * v[c][k] + b * w[k];
         store4(xr + i, v[c]);
       }
-      ss += v[c][0] * v[c][0] + v[c][1] * v[c][1] + v[c][2] * v[c][2] + v[c][3] * v[c][3];
+      const float q = v[c][0] * v[c][0] + v[c][1] * v[c][1] + v[c][2] * v[c][2] + v[c][3] * v[c][3];
+      ss += q;
+      if (i < c1) ss1 += q;
     }
   }
   ss = wave_sum(ss);
-  const float r = rsqrtf(ss / (float)C + eps);
+  ss1 = c1 < C ? wave_sum(ss1) : ss;
+  const float r = rsqrtf(ss / (float)C + eps), r1 = rsqrtf(ss1 / (float)c1 + eps);
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int i = (c * 64 + lane) * 4;
     if (i < C) {
       float e[4];
+      const float rr = i < c1 ? r1 : r;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) e[k] = v[c][k] * r;
+      for (int k = 0; k < 4; ++k) e[k] = v[c][k] * rr;
       store4(xn + (size_t)row * C + i, e);
     }
   }
@@ -216,35 +233,38 @@ hipError_t launch_rope_table(float2* cs, int T, int D, float base, hipStream_t s
 
 hipError_t launch_embed_norm(const int32_t* tokens, const void* wte, bool wbf16, const float* lam,
                              const float* mu, float* x0, float* x, void* xn, int M, int C, int V,
-                             float eps, unsigned* flags, hipStream_t s, const void* pe) {
-  if (C % 4) return hipErrorInvalidValue;
+                             float eps, unsigned* flags, hipStream_t s, const void* pe, int c1) {
+  if (c1 <= 0) c1 = C;
+  if (C % 4 || c1 % 4 || c1 > C) return hipErrorInvalidValue;
   const int grid = (M + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
   return dispatch_nch(C, [&](auto nch) {
     constexpr int N = decltype(nch)::value;
     if (wbf16)
       embed_norm_kernel<bf16, bf16, N><<<grid, 256, 0, s>>>(tokens, (const bf16*)wte, lam, mu, x0, x,
                                                             (bf16*)xn, M, C, V, eps, flags,
-                                                            (const bf16*)pe);
+                                                            (const bf16*)pe, c1);
     else
       embed_norm_kernel<float, float, N><<<grid, 256, 0, s>>>(tokens, (const float*)wte, lam, mu, x0,
                                                               x, (float*)xn, M, C, V, eps, flags,
-                                                              (const float*)pe);
+                                                              (const float*)pe, c1);
     return hipGetLastError();
   });
 }
 
 hipError_t launch_mix_norm(float* x, const float* x0, const float* lam, const float* mu, int layer,
-                           bool mix, void* xn, bool xbf16, int M, int C, float eps, hipStream_t s) {
-  if (C % 4) return hipErrorInvalidValue;
+                           bool mix, void* xn, bool xbf16, int M, int C, float eps, hipStream_t s,
+                           int c1) {
+  if (c1 <= 0) c1 = C;
+  if (C % 4 || c1 % 4 || c1 > C) return hipErrorInvalidValue;
   const int grid = (M + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
   return dispatch_nch(C, [&](auto nch) {
     constexpr int N = decltype(nch)::value;
     if (xbf16) {
-      if (mix) mix_norm_kernel<bf16, N, true><<<grid, 256, 0, s>>>(x, x0, lam, mu, layer, (bf16*)xn, M, C, eps);
-      else mix_norm_kernel<bf16, N, false><<<grid, 256, 0, s>>>(x, x0, lam, mu, layer, (bf16*)xn, M, C, eps);
+      if (mix) mix_norm_kernel<bf16, N, true><<<grid, 256, 0, s>>>(x, x0, lam, mu, layer, (bf16*)xn, M, C, eps, c1);
+      else mix_norm_kernel<bf16, N, false><<<grid, 256, 0, s>>>(x, x0, lam, mu, layer, (bf16*)xn, M, C, eps, c1);
     } else {
-      if (mix) mix_norm_kernel<float, N, true><<<grid, 256, 0, s>>>(x, x0, lam, mu, layer, (float*)xn, M, C, eps);
-      else mix_norm_kernel<float, N, false><<<grid, 256, 0, s>>>(x, x0, lam, mu, layer, (float*)xn, M, C, eps);
+      if (mix) mix_norm_kernel<float, N, true><<<grid, 256, 0, s>>>(x, x0, lam, mu, layer, (float*)xn, M, C, eps, c1);
+      else mix_norm_kernel<float, N, false><<<grid, 256, 0, s>>>(x, x0, lam, mu, layer, (float*)xn, M, C, eps, c1);
     }
     return hipGetLastError();
   });

@@ -34,16 +34,22 @@ extern thread_local LaunchEvents launch_events;
 // cos/sin table cs[t * (D/2) + j] = (cos phi, sin phi), phi = t * base^(-2j/D), in fp64 then fp32.
 hipError_t launch_rope_table(float2* cs, int T, int D, float base, hipStream_t s);
 
+// Every norm below takes c1 (0 < c1 <= C, a multiple of 4; 0 means C): with c1 < C it is the
+// two-block PrefixRMSNorm -- columns [0, c1) divided by the RMS of columns [0, c1), the rest by
+// the RMS of the whole row.  c1 = C (or 0) is the plain RMSNorm.
+
 // x0 = RMSNorm(wte[tokens] (+ pe)); x = lam[0] x0 + mu[0] x0; xn = RMSNorm(x).
 // wbf16 selects bf16 (else fp32) embedding storage and xn type; pe (optional, [C], the
 // embedding's type) is added to every embedding row before the norm.
 hipError_t launch_embed_norm(const int32_t* tokens, const void* wte, bool wbf16, const float* lam,
                              const float* mu, float* x0, float* x, void* xn, int M, int C, int V,
-                             float eps, unsigned* flags, hipStream_t s, const void* pe = nullptr);
+                             float eps, unsigned* flags, hipStream_t s, const void* pe = nullptr,
+                             int c1 = 0);
 
 // If mix: x = lam[layer] x + mu[layer] x0 (in place).  Then xn = RMSNorm(x).
 hipError_t launch_mix_norm(float* x, const float* x0, const float* lam, const float* mu, int layer,
-                           bool mix, void* xn, bool xbf16, int M, int C, float eps, hipStream_t s);
+                           bool mix, void* xn, bool xbf16, int M, int C, float eps, hipStream_t s,
+                           int c1 = 0);
 
 // fp32 path value embedding, in place on the v columns of qkv [M][ld] (v head h at column
 // voff + h*D): v += 3 sigmoid(xn[m][0:12] . gate[h]) * ve[tokens[m]][h*D : (h+1)*D].
@@ -67,6 +73,10 @@ struct GemmArgs {
   int M, N, K;
   void* out; int ldo;                     // STORE/RELU2: act [M, ldo]; RESID: float [M, ldo] (+=); QKV: qk
   void* vt; int T, D, Hkv, nqk;           // QKV (bf16 only): columns >= nqk stored transposed to vt [B][Hkv][D][T]
+  // QKV output placement: GEMM column c < nseg0 (q) goes to qk column q_off + c, c in
+  // [nseg0, nqk) (k) to k_off + (c - nseg0), v columns to KV head v_head_off + (c - nqk) / D.
+  // gemm_args() sets the identity (0, nseg0, 0); nested models launch their blocks separately.
+  int q_off, k_off, v_head_off;
   const float2* cs;                       // QKV: if set (head_dim 128), RoPE table [T][D/2] -> the q/k
   float eps;                              //      heads get RoPE + RMSNorm in the epilogue
   // QKV with cs set: if ve is set, every v head h of row m gets
@@ -93,7 +103,7 @@ struct GemmArgs {
 };
 
 // bf16 inputs, fp32 accumulation on MFMA.  Returns hipErrorInvalidValue for shapes the
-// tiling does not cover (K % 64, segment sizes, lda != ldb).
+// tiling does not cover (K % 64, segment sizes).
 hipError_t launch_gemm_bf16(Epi epi, const GemmArgs& a, hipStream_t s);
 // Number of column blocks the CE epilogue of launch_gemm_bf16 produces for N columns.
 int gemm_bf16_ce_blocks(int N);

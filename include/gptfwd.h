@@ -81,11 +81,30 @@ typedef struct {
                            RMSNorm(W_E[t] + pass_emb[p]); pass-2 layer l adds
                            softplus(gate_logit[l]) * attn_scale * <q1, k1> of pass-1 layer l to
                            its logits; the loss comes from pass 2.  GPT_BF16 needs head_dim 128. */
+  int32_t nested_c1;    /* 0, or the width c1 of the inner block of a two-block nested model
+                           (StairFormer, "Fully Nested Transformers", opening section and
+                           "Reproducing the main experiment"): every per-layer linear is block
+                           lower triangular, every RMSNorm on the residual stream a PrefixRMSNorm
+                           (columns [0, c1) normed by their own RMS, the rest by the whole row's),
+                           so columns [0, c1) of the stream evolve as a standalone model of width
+                           c1 would.  Every partitioned dimension splits in the proportion
+                           c1 : d_model: the inner block holds the first H1 = n_head*c1/d_model
+                           query heads, Hkv1 = n_kv_head*c1/d_model KV heads and F1 =
+                           mlp_dim*c1/d_model hidden units.  Needs 0 < c1 <= d_model, c1 and F1
+                           multiples of 64, exact splits, no value embeddings and looped = 0; for
+                           GPT_BF16 also H1*head_dim and Hkv1*head_dim multiples of 128. */
 } gpt_cfg;
 
 /* Weights: borrowed device memory of type cfg->dtype (float or bf16), row-major [out, in].
  * Per-layer matrices are given as HOST arrays of n_layer device pointers.  Every device
- * pointer must be 16-byte aligned. */
+ * pointer must be 16-byte aligned.
+ *
+ * Nested models (cfg->nested_c1 > 0) store only the live blocks of each block lower triangular
+ * linear [out, in] with inner shares out1, in1 ("Fully Nested Transformers", section "What's
+ * here": only live weights are stored): row block 1 [out1, in1] row-major, immediately
+ * followed by row block 2 [out - out1, in] row-major.  (out1, in1) is (H1*D, c1) for wq,
+ * (Hkv1*D, c1) for wk and wv, (c1, H1*D) for wo, (F1, c1) for w1 and (c1, F1) for w2.  wte and
+ * lm_head stay dense [vocab, d_model]; the inner model reads their first c1 columns. */
 typedef struct {
   const void *wte;            /* [vocab, d_model] token embedding W_E */
   const void *lm_head;        /* [vocab, d_model] unembedding W_U (untied) */
@@ -173,6 +192,21 @@ gpt_status gpt_fwd_loss_timed(const gpt_cfg *cfg, const gpt_weights *w, const in
                               const int32_t *targets, float *loss, float *mean_loss,
                               float *logits, void *workspace, size_t workspace_bytes,
                               void *stream, gpt_launch_timing *timing);
+
+/* Nested models: the full model's outputs (as gpt_fwd_loss) and, from the same single pass,
+ * those of the inner model -- the kfront=1 submodel of "Fully Nested Transformers", section
+ * "Reproducing the main experiment": the cross-entropy of cap * tanh(z1 / cap) with z1 the
+ * first c1 columns of the final PrefixRMSNorm'd stream against the first c1 columns of
+ * lm_head.  loss_k1 [B, T], mean_k1 [1] and logits_k1 [B, T, vocab] follow the rules of loss,
+ * mean_loss and logits; the k1 outputs may all be NULL (then this is gpt_fwd_loss_timed).
+ * GPT_E_INVALID_ARG if cfg->nested_c1 == 0.  `timing` as in gpt_fwd_loss_timed (NULL: none);
+ * the inner and outer row-block launches of one step share a pair, and the two lm_head passes
+ * take one pair each (full model first). */
+gpt_status gpt_fwd_loss_nested(const gpt_cfg *cfg, const gpt_weights *w, const int32_t *tokens,
+                               const int32_t *targets, float *loss, float *mean_loss,
+                               float *logits, float *loss_k1, float *mean_k1, float *logits_k1,
+                               void *workspace, size_t workspace_bytes, void *stream,
+                               gpt_launch_timing *timing);
 
 /* Synchronise `stream`, then report whether any gpt_fwd_loss call that used this workspace saw
  * an out-of-range token or target id since the workspace's last call began (GPT_OK or

@@ -51,7 +51,7 @@ def _cfg(**kw):
 
 
 def test_validate_presets(lib):
-    for name in ("tiny", "d12", "d24", "d24gve", "d24loop"):
+    for name in ("tiny", "d12", "d24", "d24gve", "d24loop", "d24nest"):
         c = gf.make_cfg(gptdata.preset(name))
         assert gf.gpt_validate(c) == gf.GPT_OK, name
         assert gf.gpt_workspace_bytes(c) > 0
@@ -162,6 +162,46 @@ def test_looped_validation(lib):
     F = 0x200000
     assert lib.gpt_fwd_loss(ctypes.byref(c), ctypes.byref(w), F, F, F, F, None, 0x10000000, need,
                             None) == gf.GPT_E_INVALID_ARG
+
+
+def test_nested_validation(lib):
+    """Nested models: exact proportional splits, a 64-multiple inner width, 128-column inner
+    q/k/v segments on bf16, no value embeddings or looped trunk; the nested entry point
+    rejects a plain model and inconsistent kfront=1 outputs before any launch."""
+    p = gptdata.preset("d24nest")
+    assert gf.gpt_validate(gf.make_cfg(p)) == gf.GPT_OK
+    assert gf.gpt_validate(gf.make_cfg(p.with_(nested_c1=p.d_model))) == gf.GPT_OK    # one block
+    assert gf.gpt_validate(gf.make_cfg(p.with_(nested_c1=-64))) == gf.GPT_E_INVALID_ARG
+    assert gf.gpt_validate(gf.make_cfg(p.with_(nested_c1=2 * p.d_model))) == gf.GPT_E_INVALID_ARG
+    assert gf.gpt_validate(gf.make_cfg(p.with_(nested_c1=352))) == gf.GPT_E_INVALID_ARG  # 24*352 % 1536
+    # exact splits, but an inner width of 32 columns
+    odd = p.with_(d_model=960, n_head=30, n_kv_head=30, mlp_dim=3840, nested_c1=32, dtype="f32")
+    assert gf.gpt_validate(gf.make_cfg(odd)) == gf.GPT_E_UNSUPPORTED
+    assert gf.gpt_validate(gf.make_cfg(odd.with_(nested_c1=64))) == gf.GPT_OK
+    # bf16: 2 inner heads of 64 = 128 columns is fine, 1 inner KV head of 64 is not
+    q = p.with_(n_head=24, n_kv_head=12, nested_c1=128)
+    assert gf.gpt_validate(gf.make_cfg(q)) == gf.GPT_E_UNSUPPORTED
+    assert gf.gpt_validate(gf.make_cfg(q.with_(dtype="f32"))) == gf.GPT_OK
+    assert gf.gpt_validate(gf.make_cfg(p.with_(value_embeds=True))) == gf.GPT_E_UNSUPPORTED
+    assert gf.gpt_validate(gf.make_cfg(p.with_(looped=True, head_dim=128, n_head=12, n_kv_head=12))) \
+        == gf.GPT_E_UNSUPPORTED
+    c = gf.make_cfg(p)
+    w = _weights(c.n_layer)
+    need = gf.gpt_workspace_bytes(c)
+    F = 0x200000
+
+    def call(cfg=c, loss1=F, mean1=F, logits1=None, targets=F):
+        return lib.gpt_fwd_loss_nested(ctypes.byref(cfg), ctypes.byref(w), F, targets, F, F, None,
+                                       loss1, mean1, logits1, 0x10000000, need, None, None)
+    plain = gf.make_cfg(gptdata.preset("d24"))
+    assert call(cfg=plain) == gf.GPT_E_INVALID_ARG
+    assert call(mean1=None) == gf.GPT_E_INVALID_ARG          # loss_k1 without mean_k1
+    assert call(loss1=None) == gf.GPT_E_INVALID_ARG
+    assert call(loss1=F + 2) == gf.GPT_E_INVALID_ARG         # misaligned
+    assert lib.gpt_fwd_loss_nested(ctypes.byref(c), ctypes.byref(w), F, None, None, None, F, F, F, None,
+                                   0x10000000, need, None, None) == gf.GPT_E_INVALID_ARG  # k1 loss, no targets
+    assert lib.gpt_fwd_loss_nested(ctypes.byref(c), ctypes.byref(w), F, F, F, F, None, F, F, None,
+                                   None, need, None, None) == gf.GPT_E_WORKSPACE
 
 
 def test_fwd_loss_timed_argument_errors(lib):
