@@ -24,6 +24,8 @@ Sources (cited by page title and section):
   [F]  "Fully Nested Transformers" -- the StairFormer description: block lower
        triangular weights, PrefixRMSNorm, per-block heads, kfront submodel
        forward, prefix cross-entropy.
+  [M]  also section "Inference: Generating Text" (the autoregressive loop) and
+       its "Sampling Controls" (temperature, top-k filtering, greedy at 0).
 
 Readings where the pages are silent or disagree (each frozen as a config field
 so the oracle and the GPU path cannot silently diverge):
@@ -54,6 +56,14 @@ so the oracle and the GPU path cannot silently diverge):
     every RMSNorm is the PrefixRMSNorm (block-1 coordinates over the RMS of
     dims [0, c1), block-2 coordinates over the RMS of all dims); the lm_head is
     shared, kfront=1 reading input columns [0, c1).  No value embeddings.
+  * sampling: the logits sampled from are the softcapped ones (the page's
+    worked example samples "logits (after softcapping)"); top-k keeps every
+    token whose logit is >= the k-th largest (ties at the threshold stay, as
+    the page's masking of values below the k-th one does); a draw with
+    temperature > 0 is the inverse CDF of the kept tokens' softmax(z / tau)
+    in vocabulary order at a uniform u in [0, 1) supplied by the caller (the
+    page's multinomial draw with its random number made an input); temperature
+    0 is the argmax, the first index among equal maxima.
   * value embeddings (when cfg.value_embeds): the gate reads the first 12
     channels of the attention block's normalised input x_tilde (the input of
     the Q/K/V projections), and the mixed value v + g * e is what attention
@@ -76,7 +86,7 @@ __all__ = [
     "attention", "linear", "relu_squared", "softcap", "token_losses",
     "mean_loss", "has_ve", "value_embed_mix", "softplus", "attention_with_prior", "block",
     "forward_row", "forward", "prefix_rms_norm", "blocktri_linear", "forward_nested_row",
-    "forward_nested",
+    "forward_nested", "top_k_keep", "sample_next", "generate",
 ]
 
 
@@ -536,3 +546,59 @@ def forward(cfg: Any, params: Any, tokens: np.ndarray, targets: Optional[np.ndar
     if want_logits:
         res["logits"] = np.stack(out_z)
     return res
+
+
+# ----------------------------------------------------------------------------- generation
+
+def top_k_keep(z: np.ndarray, k: Optional[int]) -> np.ndarray:
+    """[M] "Sampling Controls", top-k filtering: the tokens kept for sampling -- every v with
+    z_v >= the k-th largest logit (all of them when k is None or k >= V)."""
+    z = np.asarray(z)
+    if k is None or k >= z.shape[-1]:
+        return np.ones(z.shape, dtype=bool)
+    if k < 1:
+        raise ValueError("top_k must be >= 1")
+    kth = np.sort(z)[::-1][k - 1]
+    return z >= kth
+
+
+def sample_next(zhat: np.ndarray, top_k: Optional[int], temperature: float, u: float) -> int:
+    """One draw of the next token from the softcapped logits of one position ([M] "Sampling
+    Controls"): temperature 0 is the argmax (first index on ties); otherwise
+    P(v) = exp(z_v / tau) / sum_{kept v'} exp(z_v' / tau) over the top-k kept tokens, and the
+    token is the first v in vocabulary order whose cumulative probability exceeds u."""
+    z = np.asarray(zhat, dtype=np.float64)
+    if temperature == 0.0:
+        return int(np.argmax(z))
+    if not temperature > 0.0:
+        raise ValueError("temperature must be >= 0")
+    keep = top_k_keep(z, top_k)
+    s = np.where(keep, z / temperature, -np.inf)
+    e = np.exp(s - np.max(s))
+    cdf = np.cumsum(e / np.sum(e))
+    idx = int(np.searchsorted(cdf, u, side="right"))   # first index with cdf > u
+    idx = min(idx, z.shape[-1] - 1)
+    while not keep[idx]:          # u within rounding of 1: the last kept token
+        idx -= 1
+    return idx
+
+
+def generate(cfg: Any, params: Any, prompt: np.ndarray, n_new: int, top_k: Optional[int],
+             temperature: float, u: np.ndarray, windows: Optional[Sequence[int]] = None
+             ) -> Dict[str, Any]:
+    """[M] "Inference: Generating Text": from a prompt [B, P], n_new times run the full
+    forward on the sequence so far, take the softcapped logits at the last position and
+    append one sampled token per row (u [n_new, B] are the draws).  The forward's windows
+    are those of a sequence of cfg.seq_len tokens (the model's configuration), applied to the
+    sequence so far.  Returns the tokens [B, P + n_new] and the logits each step sampled from
+    [n_new, B, V]."""
+    seq = np.array(prompt, dtype=np.int64)
+    if windows is None:
+        windows = layer_windows(cfg.window_pattern, cfg.short_window, cfg.seq_len, cfg.n_layer)
+    steps = []
+    for i in range(n_new):
+        z = forward(cfg, params, seq, want_logits=True, windows=windows)["logits"][:, -1, :]
+        nxt = [sample_next(z[b], top_k, temperature, float(u[i][b])) for b in range(seq.shape[0])]
+        seq = np.concatenate([seq, np.array(nxt, dtype=np.int64)[:, None]], axis=1)
+        steps.append(z)
+    return {"tokens": seq, "logits": np.stack(steps)}

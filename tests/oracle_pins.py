@@ -700,4 +700,91 @@ def pin_nested_filtration():
     assert not np.allclose(a["losses"], b["losses"])
 
 
+# ----------------------------------------------------------------------------- generation
+
+def pin_sampling_worked_example_greedy():
+    """[M] "Inference: Generating Text" worked example: at temperature 0 the draw is the
+    largest logit ("announced"), whatever u and top-k are."""
+    e = EX["sampling"]
+    z = np.array(e["logits"])
+    for u in (0.0, 0.3, 0.999):
+        for k in (None, 1, 3):
+            assert oracle.sample_next(z, k, 0.0, u) == e["greedy"]
+
+
+def pin_greedy_first_index_on_ties():
+    """Temperature 0 is the argmax; among equal maxima the first index (brute force)."""
+    rng = np.random.default_rng(21)
+    for _ in range(50):
+        z = rng.integers(-3, 4, size=9).astype(np.float64)
+        best = 0
+        for i in range(9):
+            if z[i] > z[best]:
+                best = i
+        assert oracle.sample_next(z, None, 0.0, 0.5) == best
+
+
+def pin_sampling_closed_form_probabilities():
+    """[M] "Sampling Controls": with logits tau*ln(1, 2, 4) (+ any shift) the temperature
+    softmax is (1/7, 2/7, 4/7) exactly, so midpoints of a uniform grid of 7000 draws split
+    1000 / 2000 / 4000 (the inverse CDF in vocabulary order)."""
+    tau = 0.8
+    z = tau * np.log(np.array([1.0, 2.0, 4.0])) + 3.25
+    n = 7000
+    counts = np.zeros(3, dtype=int)
+    for i in range(n):
+        counts[oracle.sample_next(z, None, tau, (i + 0.5) / n)] += 1
+    assert counts.tolist() == [1000, 2000, 4000], counts
+
+
+def pin_sampling_temperature_scale_invariance():
+    """Only z / tau matters: scaling logits and temperature together leaves every draw."""
+    rng = np.random.default_rng(22)
+    z = rng.standard_normal(40) * 3
+    for u in rng.random(200):
+        assert oracle.sample_next(z, 7, 0.7, u) == oracle.sample_next(2.5 * z, 7, 1.75, u)
+
+
+def pin_top_k_keeps_ties():
+    """[M] "Sampling Controls" top-k: tokens below the k-th largest logit are removed, so logits
+    equal to it stay; with two equal maxima and k = 1 both are drawn, each for half of u."""
+    z = np.array([1.0, 3.0, 3.0, 2.0])
+    assert oracle.top_k_keep(z, 1).tolist() == [False, True, True, False]
+    assert oracle.top_k_keep(z, 3).tolist() == [False, True, True, True]
+    assert oracle.top_k_keep(z, None).all() and oracle.top_k_keep(z, 4).all()
+    for tau in (0.3, 1.0, 5.0):
+        assert oracle.sample_next(z, 1, tau, 0.25) == 1 and oracle.sample_next(z, 1, tau, 0.75) == 2
+
+
+def pin_top_k_one_is_greedy():
+    """Top-1 sampling at any temperature and u is the argmax (distinct logits)."""
+    rng = np.random.default_rng(23)
+    for _ in range(100):
+        z = rng.standard_normal(30)
+        assert oracle.sample_next(z, 1, float(rng.uniform(0.1, 3)), float(rng.random())) == int(np.argmax(z))
+
+
+def pin_inverse_cdf_strict_boundary():
+    """Two equal logits: the cumulative probability of token 0 is exactly 1/2, and the draw is
+    the first token whose cumulative probability exceeds u, so u = 1/2 draws token 1."""
+    z = np.array([0.5, 0.5])
+    assert oracle.sample_next(z, None, 1.0, 0.4999) == 0
+    assert oracle.sample_next(z, None, 1.0, 0.5) == 1
+
+
+def pin_generation_logits_are_one_forward():
+    """Causality: the logits that each generation step samples from equal the logits at the
+    same positions of one forward pass over the final sequence."""
+    p = small_preset(n_layer=2, seq_len=16, vocab=40, short_window=5)
+    prm = dense_params(p)
+    rng = np.random.default_rng(24)
+    prompt = rng.integers(0, p.vocab, size=(2, 5))
+    u = rng.random((6, 2))
+    g = oracle.generate(p, prm, prompt, 6, top_k=10, temperature=0.9, u=u)
+    full = oracle.forward(p, prm, g["tokens"][:, :-1], want_logits=True,
+                          windows=oracle.layer_windows(p.window_pattern, p.short_window, p.seq_len, p.n_layer))
+    for i in range(6):
+        assert np.allclose(g["logits"][i], full["logits"][:, 4 + i, :], rtol=1e-10, atol=1e-12)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -14,7 +14,7 @@ _orig = {n: getattr(oracle, n) for n in ("apply_rope", "visible_mask", "relu_squ
                                           "token_losses", "rms_norm", "attention", "block", "linear",
                                           "has_ve", "value_embed_mix", "softplus",
                                           "attention_with_prior", "prefix_rms_norm",
-                                          "blocktri_linear")}
+                                          "blocktri_linear", "top_k_keep", "sample_next")}
 
 
 def _rope_sign(u, cos, sin):
@@ -204,6 +204,32 @@ def _prefix_norm_own_rms(u, c1, eps=0.0):
     return np.concatenate([first, _orig["rms_norm"](np.ascontiguousarray(u[..., c1:]), eps)], axis=-1)
 
 
+def _top_k_drops_ties(z, k):
+    """Exactly k tokens kept (a stable sort decides among equal logits)."""
+    z = np.asarray(z)
+    if k is None or k >= z.shape[-1]:
+        return np.ones(z.shape, dtype=bool)
+    keep = np.zeros(z.shape, dtype=bool)
+    keep[np.argsort(-z, kind="stable")[:k]] = True
+    return keep
+
+
+def _sampler(temperature_op="div", greedy_last=False, strict=True):
+    """A sampler with one planted mistake selected by the arguments."""
+    def sample(zhat, top_k, temperature, u):
+        z = np.asarray(zhat, dtype=np.float64)
+        if temperature == 0.0:
+            return int(len(z) - 1 - np.argmax(z[::-1])) if greedy_last else int(np.argmax(z))
+        keep = oracle.top_k_keep(z, top_k)
+        zs = z * temperature if temperature_op == "mul" else z / temperature
+        s = np.where(keep, zs, -np.inf)
+        e = np.exp(s - np.max(s))
+        cdf = np.cumsum(e / np.sum(e))
+        idx = int(np.searchsorted(cdf, u, side="right" if strict else "left"))
+        return min(idx, z.shape[-1] - 1)
+    return sample
+
+
 def _blocktri_no_lower_block(x, blocks, in1):
     w1, w2 = blocks
     y1 = np.ascontiguousarray(x[..., :in1]) @ w1.T
@@ -249,6 +275,13 @@ MUTATIONS = {
                                    [P.pin_prefix_rms_norm]),
     "blocktri_without_lower_block": (lambda mp: mp.setattr(oracle, "blocktri_linear", _blocktri_no_lower_block),
                                      [P.pin_blocktri_zero_padded_dense]),
+    "top_k_drops_ties": (lambda mp: mp.setattr(oracle, "top_k_keep", _top_k_drops_ties), [P.pin_top_k_keeps_ties]),
+    "temperature_multiplies": (lambda mp: mp.setattr(oracle, "sample_next", _sampler(temperature_op="mul")),
+                               [P.pin_sampling_closed_form_probabilities]),
+    "greedy_last_index": (lambda mp: mp.setattr(oracle, "sample_next", _sampler(greedy_last=True)),
+                          [P.pin_greedy_first_index_on_ties]),
+    "cdf_not_strict": (lambda mp: mp.setattr(oracle, "sample_next", _sampler(strict=False)),
+                       [P.pin_inverse_cdf_strict_boundary]),
 }
 
 
