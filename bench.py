@@ -100,6 +100,52 @@ def measured_traffic(root, kind):
         return None
 
 
+def decode_bench(gf, p, model, steps):
+    """Time gpt_decode_step for the preset's rows at the last cache position (every layer attends
+    over its whole window), eagerly and replayed from a HIP graph.  Algorithmic bytes per step:
+    every weight once (the linears, W_U and B rows of W_E) plus the cached keys and values each
+    layer attends to."""
+    import torch
+    B, T, C, H, Hkv, D, F, V, L = (p.batch, p.seq_len, p.d_model, p.n_head, p.n_kv_head, p.head_dim,
+                                   p.mlp_dim, p.vocab, p.n_layer)
+    d = gf.Decoder(model)
+    windows = gf.layer_windows(p.window_pattern, p.short_window, T, L)
+    cur = torch.zeros(B, dtype=torch.int32, device="cuda")
+    pos = torch.full((B,), T - 1, dtype=torch.int32, device="cuda")
+    out = torch.empty((B, V), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        if d.step(cur, pos, out) != gf.GPT_OK:
+            raise RuntimeError("decode step failed")
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        d.step(cur, pos, out)
+    e1.record()
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / steps
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        d.step(cur, pos, out)
+    g.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_ms = e0.elapsed_time(e1) / steps
+    es = 2 if p.dtype == "bf16" else 4
+    weights = (L * (C * (H + 2 * Hkv) * D + H * D * C + 2 * C * F) + V * C + B * C) * es
+    kv = sum(2 * B * Hkv * min(w, T) * D * es for w in windows)
+    gbs = (weights + kv) / (graph_ms * 1e-3) / 1e9
+    print(f"[bench] decode: {eager_ms:.3f} ms/step eager, {graph_ms:.3f} ms/step graph "
+          f"({B} rows at position {T - 1}), {gbs:.0f} GB/s algorithmic", file=sys.stderr, flush=True)
+    return {"rows": B, "position": T - 1, "ms_per_step_eager": round(eager_ms, 4),
+            "ms_per_step_graph": round(graph_ms, 4), "tokens_per_s_graph": round(B / (graph_ms * 1e-3), 1),
+            "bytes_per_step": weights + kv, "achieved_gbs": round(gbs, 1), "peak_gbs": PEAK_HBM_GBS}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -111,6 +157,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-steps", type=int, default=3,
                     help="measurement steps per kernel kind for the per-kernel event timing")
+    ap.add_argument("--decode-steps", type=int, default=20,
+                    help="timed decode steps (one token per row, full cache); 0 skips the decode line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy (a known-size reference "
                          "for HBM traffic counters)")
@@ -222,6 +270,10 @@ def main():
         f"{n} {k['avg_us']:.1f} us x{k['launches_per_step']} ({k['tflops']:.0f} TF/s)" for n, k in kern.items()),
         file=sys.stderr, flush=True)
 
+    dec = None
+    if args.decode_steps > 0 and not nested and not getattr(p, "looped", False) and not p.value_embeds:
+        dec = decode_bench(gf, p, model, args.decode_steps)
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -265,6 +317,7 @@ def main():
                      "frac": round(k_tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(ROOT, dk),
                      "avg_launch_us": dom["avg_us"], "flops_per_launch": fpl[dk]},
         "kernels": kern,
+        "decode": dec,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -27,8 +27,8 @@ GPT_F32, GPT_BF16 = 0, 1
 
 EXPORTED = [
     "gpt_validate", "gpt_workspace_bytes", "gpt_fwd_loss", "gpt_fwd_loss_timed", "gpt_fwd_loss_nested",
-    "gpt_device_status",
-    "gpt_status_string",
+    "gpt_device_status", "gpt_status_string",
+    "gpt_kv_cache_bytes", "gpt_decode_workspace_bytes", "gpt_decode_step", "gpt_sample",
     "gpt_op_embed_norm", "gpt_op_mix_norm", "gpt_op_rope_table", "gpt_op_qk_rope_norm",
     "gpt_op_linear", "gpt_op_qkv", "gpt_op_attention", "gpt_op_lm_head_ce_workspace",
     "gpt_op_lm_head_ce",
@@ -88,6 +88,10 @@ def _load() -> ctypes.CDLL:
         "gpt_fwd_loss_nested": (I, [ctypes.POINTER(gpt_cfg), ctypes.POINTER(gpt_weights), P, P, P, P, P, P, P, P,
                                     P, S, P, ctypes.POINTER(gpt_launch_timing)]),
         "gpt_device_status": (I, [P, P]),
+        "gpt_kv_cache_bytes": (S, [ctypes.POINTER(gpt_cfg)]),
+        "gpt_decode_workspace_bytes": (S, [ctypes.POINTER(gpt_cfg)]),
+        "gpt_decode_step": (I, [ctypes.POINTER(gpt_cfg), ctypes.POINTER(gpt_weights), P, P, P, P, P, S, P]),
+        "gpt_sample": (I, [P, I, I, I, F, P, P, P]),
         "gpt_status_string": (ctypes.c_char_p, [I]),
         "gpt_op_embed_norm": (I, [I, P, P, P, P, P, P, P, I, I, I, F, P, P]),
         "gpt_op_mix_norm": (I, [I, P, P, P, P, I, I, P, I, I, F, P]),
@@ -223,6 +227,26 @@ def launch_timing(kind: int, begin_events, end_events) -> gpt_launch_timing:
                           ctypes.cast(e, ctypes.POINTER(ctypes.c_void_p)), 0)
     t._keep = (b, e)  # the arrays must outlive the call
     return t
+
+
+def gpt_kv_cache_bytes(cfg: gpt_cfg) -> int:
+    return _load().gpt_kv_cache_bytes(ctypes.byref(cfg))
+
+
+def gpt_decode_workspace_bytes(cfg: gpt_cfg) -> int:
+    return _load().gpt_decode_workspace_bytes(ctypes.byref(cfg))
+
+
+def gpt_decode_step(cfg: gpt_cfg, weights: gpt_weights, tokens, pos, kv_cache, logits, workspace,
+                    workspace_bytes: int, stream=None) -> int:
+    return _load().gpt_decode_step(ctypes.byref(cfg), ctypes.byref(weights), _ptr(tokens), _ptr(pos),
+                                   _ptr(kv_cache), _ptr(logits), _ptr(workspace), workspace_bytes,
+                                   _stream(stream))
+
+
+def gpt_sample(logits, batch: int, vocab: int, top_k: int, temperature: float, u, out, stream=None) -> int:
+    return _load().gpt_sample(_ptr(logits), batch, vocab, top_k, temperature, _ptr(u), _ptr(out),
+                              _stream(stream))
 
 
 def gpt_device_status(workspace, stream=None) -> int:
@@ -385,6 +409,35 @@ class DeviceModel:
         logits = torch.empty((B, T, V), dtype=torch.float32, device=dev) if want_logits else None
         _check(self.forward(tokens, targets, loss, mean, logits), "gpt_fwd_loss")
         return loss, mean, logits
+
+    def device_status(self) -> int:
+        return gpt_device_status(self.ws_ptr)
+
+
+class Decoder:
+    """Decode-step state over the weights of a DeviceModel: a KV cache for `batch` rows of up to
+    the preset's seq_len positions and the step's workspace (both device buffers owned here).
+    Every call only enqueues work on the current (or given) stream."""
+
+    def __init__(self, model: DeviceModel):
+        import torch
+        self.m = model
+        self.cfg = model.cfg
+        _check(gpt_validate(self.cfg), "gpt_validate")
+        self.cache_bytes = gpt_kv_cache_bytes(self.cfg)
+        self.ws_bytes = gpt_decode_workspace_bytes(self.cfg)
+        if self.cache_bytes == 0 or self.ws_bytes == 0:
+            raise GptError(GPT_E_UNSUPPORTED, "decode configuration")
+        dev = model.ws.device
+        self.cache = torch.empty(self.cache_bytes + 256, dtype=torch.uint8, device=dev)
+        self.cache_ptr = self.cache.data_ptr() + (-self.cache.data_ptr()) % 256
+        self.ws = torch.empty(self.ws_bytes + 256, dtype=torch.uint8, device=dev)
+        self.ws_ptr = self.ws.data_ptr() + (-self.ws.data_ptr()) % 256
+
+    def step(self, tokens, pos, logits, stream=None) -> int:
+        """Enqueue gpt_decode_step: tokens, pos device int32 [B]; logits device fp32 [B, V]."""
+        return gpt_decode_step(self.cfg, self.m.w, tokens, pos, self.cache_ptr, logits, self.ws_ptr,
+                               self.ws_bytes, stream)
 
     def device_status(self) -> int:
         return gpt_device_status(self.ws_ptr)

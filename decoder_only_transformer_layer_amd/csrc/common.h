@@ -17,6 +17,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // 16-byte copy
 // Error bits raised by kernels into the workspace flag word.
 #define GPT_FLAG_BAD_TOKEN 1u
 #define GPT_FLAG_BAD_TARGET 2u
+#define GPT_FLAG_BAD_POS 4u
 
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }

@@ -504,6 +504,147 @@ gpt_status run(const gpt_cfg* c, const gpt_weights* w, const int32_t* tokens,
 
 extern "C" {
 
+// ------------------------------------------------------------------------------- decoding
+
+static gpt_status validate_decode(const gpt_cfg* c) {
+  const gpt_status st = validate(c);
+  if (st != GPT_OK) return st;
+  if (c->batch > 32 || c->seq_len > 8192 || c->n_head / c->n_kv_head > 8) return GPT_E_UNSUPPORTED;
+  if (any_ve(c) || c->looped || c->nested_c1) return GPT_E_UNSUPPORTED;
+  return GPT_OK;
+}
+
+// K splits of the decode step's products (bf16): the q/k/v projection, the attention output
+// projection and the MLP down-projection split K when N alone gives too few blocks; their
+// consumers (the RoPE/append kernel, the residual norms) sum the partial tiles.
+struct DecodeSplits {
+  int qkv, out, down;
+};
+
+static DecodeSplits decode_splits(const gpt_cfg* c) {
+  if (c->dtype != GPT_BF16) return {1, 1, 1};
+  const int C = c->d_model, H = c->n_head, Hkv = c->n_kv_head, D = c->head_dim, F = c->mlp_dim;
+  return {gemv_splits((H + 2 * Hkv) * D, C), gemv_splits(C, H * D), gemv_splits(C, F)};
+}
+
+struct DecodeLayout {
+  size_t flags, x, x0, xn, y, q, o, h, part, gpart, total;
+};
+
+static DecodeLayout decode_plan(const gpt_cfg* c) {
+  DecodeLayout L{};
+  const size_t B = c->batch, C = c->d_model, H = c->n_head, Hkv = c->n_kv_head, D = c->head_dim;
+  const size_t F = c->mlp_dim, es = c->dtype == GPT_BF16 ? 2 : 4;
+  const DecodeSplits ks = decode_splits(c);
+  const size_t ro = (size_t)(ks.out > ks.down ? ks.out : ks.down) * B * C;  // residual partials
+  size_t off = 0;
+  L.flags = off; off += up(64);
+  L.x = off; off += up(B * C * 4);
+  L.x0 = off; off += up(B * C * 4);
+  L.xn = off; off += up(B * C * es);
+  L.y = off; off += up((size_t)ks.qkv * B * (H + 2 * Hkv) * D * 4);
+  L.q = off; off += up(B * H * D * es);
+  L.o = off; off += up(B * H * D * es);
+  L.h = off; off += up(B * F * es);
+  L.part = off; off += up(B * H * (size_t)decode_attn_chunks(c->seq_len) * (D + 2) * 4);
+  L.gpart = off; off += up(ro * 4);
+  L.total = off;
+  return L;
+}
+
+size_t gpt_kv_cache_bytes(const gpt_cfg* c) {
+  if (validate_decode(c) != GPT_OK) return 0;
+  const size_t es = c->dtype == GPT_BF16 ? 2 : 4;
+  return (size_t)c->n_layer * 2 * c->batch * c->n_kv_head * c->seq_len * c->head_dim * es;
+}
+
+size_t gpt_decode_workspace_bytes(const gpt_cfg* c) {
+  if (validate_decode(c) != GPT_OK) return 0;
+  return decode_plan(c).total;
+}
+
+gpt_status gpt_decode_step(const gpt_cfg* c, const gpt_weights* w, const int32_t* tokens,
+                           const int32_t* pos, void* kv_cache, float* logits, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  gpt_status st = validate_decode(c);
+  if (st != GPT_OK) return st;
+  if (!w || !tokens || !pos || !logits) return GPT_E_INVALID_ARG;
+  if (!w->wte || !w->lm_head || !w->resid_lambda || !w->x0_lambda || !w->wq || !w->wk || !w->wv ||
+      !w->wo || !w->w1 || !w->w2)
+    return GPT_E_INVALID_ARG;
+  for (int l = 0; l < c->n_layer; ++l)
+    if (!w->wq[l] || !w->wk[l] || !w->wv[l] || !w->wo[l] || !w->w1[l] || !w->w2[l] ||
+        !aligned(w->wq[l], 16) || !aligned(w->wk[l], 16) || !aligned(w->wv[l], 16) ||
+        !aligned(w->wo[l], 16) || !aligned(w->w1[l], 16) || !aligned(w->w2[l], 16))
+      return GPT_E_INVALID_ARG;
+  if (!aligned(w->wte, 16) || !aligned(w->lm_head, 16) || !aligned(tokens, 4) || !aligned(pos, 4) ||
+      !aligned(logits, 4))
+    return GPT_E_INVALID_ARG;
+  if (!kv_cache || !aligned(kv_cache, ALIGN)) return GPT_E_INVALID_ARG;
+  const DecodeLayout L = decode_plan(c);
+  if (!workspace || workspace_bytes < L.total || !aligned(workspace, ALIGN)) return GPT_E_WORKSPACE;
+
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf = c->dtype == GPT_BF16;
+  const int B = c->batch, T = c->seq_len, C = c->d_model, H = c->n_head, Hkv = c->n_kv_head;
+  const int D = c->head_dim, F = c->mlp_dim, V = c->vocab;
+  const size_t es = bf ? 2 : 4;
+  const float eps = c->norm_eps;
+  char* ws = (char*)workspace;
+  unsigned* flags = (unsigned*)(ws + L.flags);
+  float* x = (float*)(ws + L.x);
+  float* x0 = (float*)(ws + L.x0);
+  void* xn = ws + L.xn;
+  float* y = (float*)(ws + L.y);
+  void* q = ws + L.q;
+  void* o = ws + L.o;
+  void* hb = ws + L.h;
+  const int nqkv = (H + 2 * Hkv) * D;
+  const size_t cache_half = (size_t)B * Hkv * T * D * es;  // k or v of one layer
+
+  float* gpart = (float*)(ws + L.gpart);
+  const DecodeSplits ks = decode_splits(c);
+  CK(launch_clear_u32(flags, 16, s));
+  CK(launch_embed_norm(tokens, w->wte, bf, w->resid_lambda, w->x0_lambda, x0, x, xn, B, C, V, eps,
+                       flags, s));
+  for (int l = 0; l < c->n_layer; ++l) {
+    char* kc = (char*)kv_cache + (size_t)l * 2 * cache_half;
+    char* vc = kc + cache_half;
+    const int win = c->window[l] < T ? c->window[l] : T;
+    // q/k/v (K-split partials in y), then RoPE + QK-norm and the cache append
+    CK(launch_gemv(bf, DEC_STORE, xn, C, B, w->wq[l], w->wk[l], w->wv[l], H * D, Hkv * D, nqkv, C,
+                   y, nqkv, s, ks.qkv, y));
+    CK(launch_rope_append(bf, y, nqkv, ks.qkv, pos, B, T, H, Hkv, D, eps, c->rope_base, q, kc, vc,
+                          flags, s));
+    CK(launch_decode_attn(bf, q, kc, vc, pos, B, T, H, Hkv, D, win, c->attn_scale, o,
+                          (float*)(ws + L.part), s));
+    // x += o W_O^T (partials summed by the norm kernel), xn = RMSNorm(x)
+    CK(launch_gemv(bf, DEC_RESID, o, H * D, B, w->wo[l], w->wo[l], w->wo[l], C, 0, C, H * D, x, C, s,
+                   ks.out, gpart));
+    CK(launch_mix_norm(x, x0, w->resid_lambda, w->x0_lambda, l, false, xn, bf, B, C, eps, s, 0,
+                       ks.out > 1 ? gpart : nullptr, ks.out));
+    CK(launch_gemv(bf, DEC_RELU2, xn, C, B, w->w1[l], w->w1[l], w->w1[l], F, 0, F, C, hb, F, s));
+    // x += h W_2^T, then the next layer's x0 mix and norm (or the final norm)
+    CK(launch_gemv(bf, DEC_RESID, hb, F, B, w->w2[l], w->w2[l], w->w2[l], C, 0, C, F, x, C, s,
+                   ks.down, gpart));
+    const bool more = l + 1 < c->n_layer;
+    CK(launch_mix_norm(x, x0, w->resid_lambda, w->x0_lambda, l + 1, more, xn, bf, B, C, eps, s, 0,
+                       ks.down > 1 ? gpart : nullptr, ks.down));
+  }
+  CK(launch_gemv(bf, DEC_LOGITS, xn, C, B, w->lm_head, w->lm_head, w->lm_head, V, 0, V, C, logits,
+                 V, s, 1, nullptr, c->softcap, pos, tokens, T, V));
+  return GPT_OK;
+}
+
+gpt_status gpt_sample(const float* logits, int32_t batch, int32_t vocab, int32_t top_k,
+                      float temperature, const float* u, int32_t* out, void* stream) {
+  if (!logits || !u || !out || batch < 1 || vocab < 1) return GPT_E_INVALID_ARG;
+  if (!(temperature >= 0.f) || !isfinite(temperature)) return GPT_E_INVALID_ARG;
+  if ((long)batch * vocab > (1L << 31)) return GPT_E_UNSUPPORTED;
+  CK(launch_sample(logits, batch, vocab, top_k, temperature, u, out, (hipStream_t)stream));
+  return GPT_OK;
+}
+
 gpt_status gpt_device_status(void* workspace, void* stream) {
   if (!workspace) return GPT_E_INVALID_ARG;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return GPT_E_HIP;
@@ -519,7 +660,7 @@ const char* gpt_status_string(gpt_status s) {
     case GPT_E_UNSUPPORTED: return "configuration not supported by the kernels";
     case GPT_E_WORKSPACE: return "workspace missing, too small or misaligned";
     case GPT_E_HIP: return "HIP launch or runtime error";
-    case GPT_E_DEVICE_INPUT: return "token or target id out of range";
+    case GPT_E_DEVICE_INPUT: return "token, target id or position out of range";
   }
   return "unknown status";
 }

@@ -1,0 +1,555 @@
+// Decode-step kernels: one new token per row against a KV cache, and sampling of the next token.
+//
+// Sources: "The Mathematics of Karpathy's nanochat", section "Inference: Generating Text" (the
+// autoregressive loop: logits at the last position, then a draw) and its "Sampling Controls"
+// (temperature, top-k filtering, greedy at temperature 0).  A step at position t computes what
+// the full forward computes at position t -- attention is causal, so the keys and values of
+// positions < t are those cached by earlier steps ("Scaled Dot-Product Attention with Sliding
+// Window": query t sees keys j <= t with t - j < w).
+//
+// With B rows the weight products are [B, K] x [N, K]^T: every weight is read once per step and
+// used B times, so they stream at HBM speed.  Even so, the products run on MFMA: at B = 8 a VALU
+// product needs 8 multiply-adds per 2-byte weight, more than the vector units retire at HBM rate.
+#include "common.h"
+#include "kernels.h"
+
+namespace gptk {
+namespace {
+
+constexpr int GV_ROWS = 32;   // weight rows per block (one 32x32 MFMA output tile, batch in N)
+constexpr int GV_WAVES = 4;   // wavefronts per block
+constexpr int GV_KB = 64;     // K per wavefront step: four 32x32x16 MFMAs
+constexpr int GV_TARGET_BLOCKS = 1024;
+
+// Per-(row b, column n) epilogue of a decode-step product.
+struct GvEpi {
+  int kind;           // DEC_* below
+  void* out; int ldo; // STORE: f32; RELU2: activation type; RESID: f32 (x += v); LOGITS: f32
+  float cap;
+  const int32_t* pos; const int32_t* tokens; int T; int V;  // LOGITS: rows with bad input -> NaN
+};
+
+template <typename AT>
+__device__ __forceinline__ void gv_apply(const GvEpi& e, int b, int n, float v) {
+  const size_t o = (size_t)b * e.ldo + n;
+  switch (e.kind) {
+    case DEC_STORE: ((float*)e.out)[o] = v; break;
+    case DEC_RELU2: { const float r = fmaxf(v, 0.f); ((AT*)e.out)[o] = from_f32<AT>(r * r); } break;
+    case DEC_RESID: ((float*)e.out)[o] += v; break;
+    case DEC_LOGITS: {
+      const int p = e.pos[b], t = e.tokens[b];
+      const bool bad = p < 0 || p >= e.T || t < 0 || t >= e.V;
+      ((float*)e.out)[o] = bad ? __builtin_nanf("") : e.cap * tanhf(v / e.cap);
+    } break;
+  }
+}
+
+// bf16 weights and activations: y[b][n] = sum_k act[b][k] W[n][k] for b < B <= 32.  A block
+// owns 32 weight rows (three row segments W0 | W1 | W2 with boundaries on multiples of 32) and
+// one of KS contiguous ranges of 64-column K steps; its wavefronts take the range's steps in
+// turn.  In a step, lane l (row l % 32, half g = l / 32) holds W[row][kb + 32g + 8m .. +8] for
+// MFMA m = 0..3 and the batch operand holds act[b = l % 32][the same columns], so each MFMA sums
+// 16 columns and the four cover the step.  The wavefronts' tiles are summed through LDS in a
+// fixed order.  With KS > 1 the block stores its tile as partial[ks][b][n] and the consumer of
+// the product sums the KS tiles in split order (no block waits on another); with KS = 1 the
+// epilogue is applied here.
+__global__ __launch_bounds__(GV_WAVES * 64) void gemv_bf16_kernel(
+    const bf16* __restrict__ act, int lda, int B, const bf16* __restrict__ W0,
+    const bf16* __restrict__ W1, const bf16* __restrict__ W2, int nseg0, int nseg1, int N, int K,
+    int KS, float* __restrict__ partial, GvEpi e) {
+  __shared__ float red[GV_WAVES][64 * 16];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int rb = blockIdx.x / KS, ks = blockIdx.x % KS;
+  const int n0 = rb * GV_ROWS;
+  const bf16* W;
+  int r0;
+  if (n0 < nseg0) { W = W0; r0 = n0; }
+  else if (n0 < nseg0 + nseg1) { W = W1; r0 = n0 - nseg0; }
+  else { W = W2; r0 = n0 - nseg0 - nseg1; }
+  const int row = lane & 31, g = lane >> 5;
+  const bool row_ok = n0 + row < N, b_ok = row < B;  // the batch operand's lane row is b
+  const bf16* wp = W + (size_t)(r0 + row) * K + 32 * g;
+  const bf16* ap = act + (size_t)row * lda + 32 * g;
+  const int nks = K / GV_KB, s0 = (int)((long)ks * nks / KS), s1 = (int)((long)(ks + 1) * nks / KS);
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  const bf16x8 zero = {};
+  for (int st = s0 + wid; st < s1; st += GV_WAVES) {
+    const int kb = st * GV_KB;
+    bf16x8 wa[4], xb[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      wa[m] = row_ok ? *(const bf16x8*)(wp + kb + 8 * m) : zero;
+      xb[m] = b_ok ? *(const bf16x8*)(ap + kb + 8 * m) : zero;
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[m], xb[m], acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) red[wid][lane * 16 + r] = acc[r];
+  __syncthreads();
+  float v[64 * 16 / (GV_WAVES * 64)];
+#pragma unroll
+  for (int i = 0; i < 64 * 16 / (GV_WAVES * 64); ++i) {
+    const int idx = threadIdx.x + i * GV_WAVES * 64;
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < GV_WAVES; ++w) t += red[w][idx];
+    v[i] = t;
+  }
+  auto coords = [&](int idx, int& b, int& n) {
+    const int l = idx >> 4, r = idx & 15;
+    n = n0 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+    b = l & 31;
+  };
+  if (KS > 1) {
+#pragma unroll
+    for (int i = 0; i < 64 * 16 / (GV_WAVES * 64); ++i) {
+      int b, n;
+      coords(threadIdx.x + i * GV_WAVES * 64, b, n);
+      if (b < B && n < N) partial[((size_t)ks * B + b) * N + n] = v[i];
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 64 * 16 / (GV_WAVES * 64); ++i) {
+    int b, n;
+    coords(threadIdx.x + i * GV_WAVES * 64, b, n);
+    if (b < B && n < N) gv_apply<bf16>(e, b, n, v[i]);
+  }
+}
+
+// fp32 weights and activations: one wavefront per output column n, lanes over K, all B rows.
+__global__ __launch_bounds__(256) void gemv_f32_kernel(const float* __restrict__ act, int lda, int B,
+                                                       const float* __restrict__ W0,
+                                                       const float* __restrict__ W1,
+                                                       const float* __restrict__ W2, int nseg0,
+                                                       int nseg1, int N, int K, GvEpi e) {
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= N) return;
+  const float* w;
+  if (n < nseg0) w = W0 + (size_t)n * K;
+  else if (n < nseg0 + nseg1) w = W1 + (size_t)(n - nseg0) * K;
+  else w = W2 + (size_t)(n - nseg0 - nseg1) * K;
+  for (int b = 0; b < B; ++b) {
+    const float* a = act + (size_t)b * lda;
+    float s = 0.f;
+    for (int k = lane; k < K; k += 64) s = fmaf(a[k], w[k], s);
+    s = wave_sum(s);
+    if (lane == 0) gv_apply<float>(e, b, n, s);
+  }
+}
+
+// q/k/v of the step's token: RoPE at position pos[b] and per-head RMSNorm on the q and k heads
+// (fp32, then one rounding to the cache type), q_hat to qout [B, H*D], k_hat and v into the
+// cache at position pos[b].  One wavefront per (row, head) of the H + 2*Hkv heads; lane p
+// rotates the pair (p, p + D/2).  The angle is formed as the forward's RoPE table forms it
+// (fp64 power, cosine and sine, rounded to fp32).
+template <typename AT>
+__global__ __launch_bounds__(256) void rope_append_kernel(
+    const float* __restrict__ y, int ldy, int KS, size_t kstride, const int32_t* __restrict__ pos,
+    int B, int T, int H, int Hkv, int D, float eps, double base, AT* __restrict__ qout,
+    AT* __restrict__ kc, AT* __restrict__ vc, unsigned* __restrict__ flags) {
+  const int lane = threadIdx.x & 63;
+  const int nh = H + 2 * Hkv;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= B * nh) return;
+  const int b = w / nh, hh = w % nh, half = D >> 1;
+  const int t = pos[b];
+  if (t < 0 || t >= T) {
+    if (lane == 0 && hh == 0) atomicOr(flags, GPT_FLAG_BAD_POS);
+    return;
+  }
+  const float* src = y + (size_t)b * ldy + (size_t)hh * D;
+  auto val = [&](int d) {  // the product's value: its K-split partial tiles summed in order
+    float v = src[d];
+    for (int k = 1; k < KS; ++k) v += src[k * kstride + d];
+    return v;
+  };
+  if (hh >= H + Hkv) {  // v: copied into the cache
+    const int g = hh - H - Hkv;
+    AT* dst = vc + (((size_t)b * Hkv + g) * T + t) * D;
+    for (int d = lane; d < D; d += 64) dst[d] = from_f32<AT>(val(d));
+    return;
+  }
+  float y1 = 0.f, y2 = 0.f;
+  if (lane < half) {
+    const double omega = pow(base, -2.0 * (double)lane / (double)D);
+    const double phi = (double)t * omega;
+    const float c = (float)cos(phi), s = (float)sin(phi);
+    const float u1 = val(lane), u2 = val(lane + half);
+    y1 = u1 * c + u2 * s;
+    y2 = -u1 * s + u2 * c;
+  }
+  const float ss = wave_sum(y1 * y1 + y2 * y2);
+  const float r = rsqrtf(ss / (float)D + eps);
+  AT* dst = hh < H ? qout + (size_t)b * H * D + (size_t)hh * D
+                   : kc + (((size_t)b * Hkv + (hh - H)) * T + t) * D;
+  if (lane < half) {
+    dst[lane] = from_f32<AT>(y1 * r);
+    dst[lane + half] = from_f32<AT>(y2 * r);
+  }
+}
+
+// Attention of the step's queries over cached keys j in [lo, t], lo = max(0, t - w + 1), split
+// over chunks of DA_CHUNK keys (flash-decoding): block (row b, KV head g, chunk c) scores the
+// chunk's keys against the G = H/Hkv query heads that read KV head g (each key and value row is
+// read once for the whole group), and writes per head the chunk's max m_c, sum l_c = sum_j
+// exp(s_j - m_c) and unnormalised output O_c = sum_j exp(s_j - m_c) v_j (fp32).  The combine
+// kernel merges the chunks: o = sum_c e^(m_c - m) O_c / sum_c e^(m_c - m) l_c.  Query head h
+// reads KV head h*Hkv/H, i.e. the group of head h is h / G.
+constexpr int DA_THREADS = 256;
+constexpr int DA_CHUNK = 128;       // keys per block: two threads per key in the score pass
+constexpr int DA_MAX_GROUP = 8;     // query heads per KV head
+
+__device__ __forceinline__ void load8(const bf16* p, float v[8]) {
+  const bf16x8 t = *(const bf16x8*)p;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (float)t[i];
+}
+__device__ __forceinline__ void load8(const float* p, float v[8]) {
+  const f32x4 a = *(const f32x4*)p, c = *(const f32x4*)(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[i + 4] = c[i]; }
+}
+
+template <typename AT, int D>
+__global__ __launch_bounds__(DA_THREADS) void decode_attn_chunk_kernel(
+    const AT* __restrict__ q, const AT* __restrict__ kc, const AT* __restrict__ vc,
+    const int32_t* __restrict__ pos, int T, int H, int Hkv, int window, float scale, int nch,
+    float* __restrict__ part) {
+  __shared__ float qs[DA_MAX_GROUP][D];
+  __shared__ float sc[DA_MAX_GROUP][DA_CHUNK];
+  __shared__ float ml[DA_MAX_GROUP][2];
+  __shared__ float red[4][DA_MAX_GROUP][D];
+  const int c = blockIdx.y, bg = blockIdx.x, b = bg / Hkv, g = bg % Hkv;
+  const int G = H / Hkv, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int t = pos[b];
+  const bool ok = t >= 0 && t < T;
+  const int lo = ok ? (t - window + 1 > 0 ? t - window + 1 : 0) : 0;
+  const int j0 = lo + c * DA_CHUNK;
+  const int nk = ok ? min(DA_CHUNK, t + 1 - j0) : 0;  // keys of this chunk (<= 0: none)
+  // part layout per (b, h, chunk): [m, l, O[0..D)]
+  auto slot = [&](int gi) { return part + (((size_t)b * H + g * G + gi) * nch + c) * (D + 2); };
+  if (nk <= 0) {
+    for (int i = tid; i < G * (D + 2); i += DA_THREADS) {
+      const int gi = i / (D + 2), e = i % (D + 2);
+      slot(gi)[e] = e == 0 ? -INFINITY : 0.f;
+    }
+    return;
+  }
+  for (int i = tid; i < G * D; i += DA_THREADS)
+    qs[i / D][i % D] = to_f32(q[(size_t)b * H * D + (size_t)(g * G + i / D) * D + i % D]);
+  __syncthreads();
+  // scores: thread (key j = tid / 2, half = tid % 2) over D/2 dimensions, halves joined by a shuffle
+  {
+    const int j = tid >> 1, hf = tid & 1;
+    const AT* kr = kc + (((size_t)b * Hkv + g) * T + (j0 + (j < nk ? j : 0))) * D + hf * (D / 2);
+    float kv[D / 2];
+#pragma unroll
+    for (int i = 0; i < D / 2; ++i) kv[i] = to_f32(kr[i]);
+    for (int gi = 0; gi < G; ++gi) {
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < D / 2; ++i) s = fmaf(qs[gi][hf * (D / 2) + i], kv[i], s);
+      s += __shfl_xor(s, 1);
+      if (hf == 0 && j < DA_CHUNK) sc[gi][j] = j < nk ? s * scale : -INFINITY;
+    }
+  }
+  __syncthreads();
+  // per head: chunk max and sum (one wavefront per head, two keys per lane)
+  for (int gi = wid; gi < G; gi += DA_THREADS / 64) {
+    const float a = sc[gi][lane], bb = sc[gi][lane + 64];
+    const float m = wave_max(fmaxf(a, bb));
+    const float pa = expf(a - m), pb = expf(bb - m);
+    sc[gi][lane] = pa;
+    sc[gi][lane + 64] = pb;
+    const float l = wave_sum(pa + pb);
+    if (lane == 0) { ml[gi][0] = m; ml[gi][1] = l; }
+  }
+  __syncthreads();
+  // O = sum_j p_j v_j: thread (8-dimension octet, key part) reads 8 values of a row at once;
+  // the value rows are read once for all heads of the group.  Parts are summed by shuffles
+  // within a wavefront, then the 4 wavefronts through LDS, in a fixed order.
+  {
+    constexpr int OCT = D / 8, PARTS = DA_THREADS / OCT;  // D=128: 16 x 16; D=64: 8 x 32
+    const int oc = tid % OCT, pt = tid / OCT;
+    float acc[DA_MAX_GROUP][8];
+#pragma unroll
+    for (int gi = 0; gi < DA_MAX_GROUP; ++gi)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[gi][i] = 0.f;
+    const AT* vb = vc + (((size_t)b * Hkv + g) * T + j0) * D + oc * 8;
+#pragma unroll
+    for (int k = 0; k < DA_CHUNK / PARTS; ++k) {
+      const int j = pt + k * PARTS;
+      if (j < nk) {
+        float vv[8];
+        load8(vb + (size_t)j * D, vv);
+#pragma unroll
+        for (int gi = 0; gi < DA_MAX_GROUP; ++gi)
+          if (gi < G) {
+            const float pj = sc[gi][j];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[gi][i] = fmaf(pj, vv[i], acc[gi][i]);
+          }
+      }
+    }
+#pragma unroll
+    for (int gi = 0; gi < DA_MAX_GROUP; ++gi)
+      if (gi < G)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float a = acc[gi][i];
+#pragma unroll
+        for (int o = OCT; o < 64; o <<= 1) a += __shfl_xor(a, o);
+        acc[gi][i] = a;
+      }
+    if (lane < OCT)
+#pragma unroll
+      for (int gi = 0; gi < DA_MAX_GROUP; ++gi)
+        if (gi < G)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) red[wid][gi][oc * 8 + i] = acc[gi][i];
+    __syncthreads();
+  }
+  for (int i = tid; i < G * (D + 2); i += DA_THREADS) {
+    const int gi = i / (D + 2), e = i % (D + 2);
+    float v;
+    if (e == 0) v = ml[gi][0];
+    else if (e == 1) v = ml[gi][1];
+    else v = ((red[0][gi][e - 2] + red[1][gi][e - 2]) + red[2][gi][e - 2]) + red[3][gi][e - 2];
+    slot(gi)[e] = v;
+  }
+}
+
+// o[b][h] = merge of the chunks' partial softmax results (fixed chunk order); rows with an
+// invalid position get zeros (their logits are NaN).  The chunks' (m, l) are staged in LDS
+// first so the output loop's loads are independent.
+constexpr int DA_MAX_CHUNKS = 64;  // 8192 keys / 128
+
+template <typename AT, int D>
+__global__ __launch_bounds__(D) void decode_attn_combine_kernel(const float* __restrict__ part,
+                                                                int nch, int H, AT* __restrict__ o) {
+  __shared__ float wgt[DA_MAX_CHUNKS], lsum[DA_MAX_CHUNKS];
+  const int bh = blockIdx.x, d = threadIdx.x;
+  const float* p = part + (size_t)bh * nch * (D + 2);
+  for (int c = d; c < nch; c += D) { wgt[c] = p[c * (D + 2)]; lsum[c] = p[c * (D + 2) + 1]; }
+  __syncthreads();
+  float m = -INFINITY;
+  for (int c = 0; c < nch; ++c) m = fmaxf(m, wgt[c]);
+  float l = 0.f, acc = 0.f;
+  if (m != -INFINITY)
+    for (int c = 0; c < nch; ++c) {
+      const float e = expf(wgt[c] - m);
+      l = fmaf(e, lsum[c], l);
+      acc = fmaf(e, p[c * (D + 2) + 2 + d], acc);
+    }
+  o[(size_t)bh * D + d] = from_f32<AT>(l > 0.f ? acc / l : 0.f);
+}
+
+// ---------------------------------------------------------------------------------- sampling
+constexpr int SMP_THREADS = 1024;
+
+__device__ __forceinline__ unsigned order_key(float f) {  // monotone map float -> uint32
+  const unsigned u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Block-wide sum of one value per thread (fixed order); every thread receives the total.
+__device__ float block_sum(float v, float* scratch) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) scratch[wid] = v;
+  __syncthreads();
+  float s = 0.f;
+  for (int w = 0; w < SMP_THREADS / 64; ++w) s += scratch[w];
+  return s;
+}
+
+// One block per row.  Temperature 0: the first index of the largest logit.  Otherwise the
+// k-th largest logit (exact radix select over the order-preserving 32-bit keys, 8 bits per
+// pass) bounds the kept set {v : z_v >= z_(k)}; p_v = exp((z_v - max) / tau) over it; the token
+// is the first v, in vocabulary order, whose running sum exceeds u * sum_v p_v.  Each thread
+// owns a contiguous run of the vocabulary; runs are summed by a block scan, so the total and
+// the running sums come from the same additions.
+__global__ __launch_bounds__(SMP_THREADS) void sample_kernel(const float* __restrict__ logits,
+                                                             int V, int top_k, float temperature,
+                                                             const float* __restrict__ u,
+                                                             int32_t* __restrict__ out) {
+  __shared__ unsigned hist[256];
+  __shared__ float scratch[SMP_THREADS / 64];
+  __shared__ float runs[SMP_THREADS];
+  __shared__ unsigned sel[2];
+  __shared__ unsigned long long best, last_kept;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const float* z = logits + (size_t)b * V;
+  const int per = (V + SMP_THREADS - 1) / SMP_THREADS;
+  const int v0 = tid * per, v1 = min(V, v0 + per);
+  if (temperature == 0.f) {  // argmax, first index on ties: max of (key, ~index)
+    unsigned long long m = 0;
+    for (int v = v0; v < v1; ++v) {
+      const unsigned long long c = ((unsigned long long)order_key(z[v]) << 32) | (unsigned)(~v);
+      m = c > m ? c : m;
+    }
+    if (tid == 0) best = 0;
+    __syncthreads();
+    atomicMax(&best, m);
+    __syncthreads();
+    if (tid == 0) out[b] = (int32_t)(~(unsigned)(best & 0xffffffffu));
+    return;
+  }
+  // threshold key of the k-th largest logit (0 = keep all)
+  unsigned thr = 0;
+  if (top_k > 0 && top_k < V) {
+    unsigned prefix = 0, mask = 0;
+    int need = top_k;  // rank still to find among keys matching the prefix
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int i = tid; i < 256; i += SMP_THREADS) hist[i] = 0;
+      __syncthreads();
+      for (int v = v0; v < v1; ++v) {
+        const unsigned k = order_key(z[v]);
+        if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255], 1u);
+      }
+      __syncthreads();
+      if (tid == 0) {  // digit holding the need-th largest, scanning from the top
+        int acc = 0, dgt = 255;
+        for (; dgt > 0; --dgt) {
+          if (acc + (int)hist[dgt] >= need) break;
+          acc += hist[dgt];
+        }
+        sel[0] = (unsigned)dgt;
+        sel[1] = (unsigned)(need - acc);
+      }
+      __syncthreads();
+      prefix |= sel[0] << shift;
+      mask |= 255u << shift;
+      need = (int)sel[1];
+      __syncthreads();
+    }
+    thr = prefix;  // every bit decided: the exact key of the k-th largest
+  }
+  float mloc = -INFINITY;
+  for (int v = v0; v < v1; ++v) mloc = fmaxf(mloc, z[v]);
+  mloc = wave_max(mloc);
+  __syncthreads();
+  if ((tid & 63) == 0) scratch[tid >> 6] = mloc;
+  __syncthreads();
+  float mx = scratch[0];
+  for (int w = 1; w < SMP_THREADS / 64; ++w) mx = fmaxf(mx, scratch[w]);
+  const float inv_t = 1.f / temperature;
+  float run = 0.f;
+  for (int v = v0; v < v1; ++v)
+    if (order_key(z[v]) >= thr) run += expf((z[v] - mx) * inv_t);
+  __syncthreads();
+  runs[tid] = run;
+  __syncthreads();
+  // exclusive scan of the runs (thread 0, fixed order; 1024 additions)
+  if (tid == 0) {
+    float acc = 0.f;
+    for (int i = 0; i < SMP_THREADS; ++i) { const float r = runs[i]; runs[i] = acc; acc += r; }
+    scratch[0] = acc;
+    best = ~0ull;
+    last_kept = 0ull;
+  }
+  __syncthreads();
+  const float total = scratch[0], target = u[b] * total;
+  float s = runs[tid];
+  int pick = -1, last = -1;
+  for (int v = v0; v < v1; ++v) {
+    if (order_key(z[v]) < thr) continue;
+    last = v;
+    s += expf((z[v] - mx) * inv_t);
+    if (s > target) { pick = v; break; }
+  }
+  if (pick >= 0) atomicMin(&best, (unsigned long long)pick);
+  if (last >= 0) atomicMax(&last_kept, (unsigned long long)last + 1);
+  __syncthreads();
+  // no running sum exceeded u * total (u * total rounded up to the total): the last kept token
+  if (tid == 0) out[b] = best != ~0ull ? (int32_t)best : (int32_t)last_kept - 1;
+}
+
+}  // namespace
+
+// K splits of a product: enough blocks to keep every CU busy, each wavefront with >= 1 step.
+int gemv_splits(int N, int K) {
+  const int nrb = (N + GV_ROWS - 1) / GV_ROWS, nks = K / GV_KB;
+  int ks = (GV_TARGET_BLOCKS + nrb - 1) / nrb;
+  ks = ks < nks / GV_WAVES ? ks : nks / GV_WAVES;
+  return ks > 1 ? ks : 1;
+}
+
+hipError_t launch_gemv(bool bf, int kind, const void* act, int lda, int B, const void* W0,
+                       const void* W1, const void* W2, int nseg0, int nseg1, int N, int K,
+                       void* out, int ldo, hipStream_t s, int KS, float* partial, float cap,
+                       const int32_t* pos, const int32_t* tokens, int T, int V) {
+  if (B < 1 || B > 32 || N < 1 || K < 1 || K % GV_KB || KS < 1) return hipErrorInvalidValue;
+  if ((nseg0 < N && nseg0 % GV_ROWS) || (nseg0 + nseg1 < N && (nseg0 + nseg1) % GV_ROWS))
+    return hipErrorInvalidValue;  // interior segment boundaries on block boundaries
+  GvEpi e{kind, out, ldo, cap, pos, tokens, T, V};
+  if (bf) {
+    if (KS > 1 && !partial) return hipErrorInvalidValue;
+    const int grid = (N + GV_ROWS - 1) / GV_ROWS * KS;
+    gemv_bf16_kernel<<<grid, GV_WAVES * 64, 0, s>>>((const bf16*)act, lda, B, (const bf16*)W0,
+                                                    (const bf16*)W1, (const bf16*)W2, nseg0, nseg1,
+                                                    N, K, KS, partial, e);
+  } else {
+    if (KS != 1) return hipErrorInvalidValue;
+    gemv_f32_kernel<<<(N + 3) / 4, 256, 0, s>>>((const float*)act, lda, B, (const float*)W0,
+                                                (const float*)W1, (const float*)W2, nseg0, nseg1,
+                                                N, K, e);
+  }
+  return hipGetLastError();
+}
+
+
+hipError_t launch_rope_append(bool bf, const float* y, int ldy, int KS, const int32_t* pos, int B,
+                              int T, int H, int Hkv, int D, float eps, float base, void* qout,
+                              void* kc, void* vc, unsigned* flags, hipStream_t s) {
+  const int grid = (B * (H + 2 * Hkv) + 3) / 4;
+  const size_t kstride = (size_t)B * ldy;
+  if (bf)
+    rope_append_kernel<bf16><<<grid, 256, 0, s>>>(y, ldy, KS, kstride, pos, B, T, H, Hkv, D, eps,
+                                                  (double)base, (bf16*)qout, (bf16*)kc, (bf16*)vc,
+                                                  flags);
+  else
+    rope_append_kernel<float><<<grid, 256, 0, s>>>(y, ldy, KS, kstride, pos, B, T, H, Hkv, D, eps,
+                                                   (double)base, (float*)qout, (float*)kc,
+                                                   (float*)vc, flags);
+  return hipGetLastError();
+}
+
+int decode_attn_chunks(int T) { return (T + DA_CHUNK - 1) / DA_CHUNK; }
+
+hipError_t launch_decode_attn(bool bf, const void* q, const void* kc, const void* vc,
+                              const int32_t* pos, int B, int T, int H, int Hkv, int D, int window,
+                              float scale, void* o, float* part, hipStream_t s) {
+  if ((D != 64 && D != 128) || H % Hkv || H / Hkv > DA_MAX_GROUP || decode_attn_chunks(T) > DA_MAX_CHUNKS)
+    return hipErrorInvalidValue;
+  const int w = window < T ? window : T;
+  const int nch = (w + DA_CHUNK - 1) / DA_CHUNK;  // chunks a window spans (partials laid out per nch)
+  const dim3 grid(B * Hkv, nch);
+#define GPTK_DA(AT, DD)                                                                              \
+  do {                                                                                               \
+    decode_attn_chunk_kernel<AT, DD><<<grid, DA_THREADS, 0, s>>>((const AT*)q, (const AT*)kc,         \
+                                                                 (const AT*)vc, pos, T, H, Hkv, w,    \
+                                                                 scale, nch, part);                  \
+    decode_attn_combine_kernel<AT, DD><<<B * H, DD, 0, s>>>(part, nch, H, (AT*)o);                   \
+  } while (0)
+  if (bf) { if (D == 128) GPTK_DA(bf16, 128); else GPTK_DA(bf16, 64); }
+  else { if (D == 128) GPTK_DA(float, 128); else GPTK_DA(float, 64); }
+#undef GPTK_DA
+  return hipGetLastError();
+}
+
+hipError_t launch_sample(const float* logits, int B, int V, int top_k, float temperature,
+                         const float* u, int32_t* out, hipStream_t s) {
+  if (B < 1 || V < 1) return hipErrorInvalidValue;
+  sample_kernel<<<B, SMP_THREADS, 0, s>>>(logits, V, top_k, temperature, u, out);
+  return hipGetLastError();
+}
+
+}  // namespace gptk

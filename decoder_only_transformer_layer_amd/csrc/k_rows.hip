@@ -153,6 +153,18 @@ __global__ __launch_bounds__(256) void mix_norm_kernel(
   }
 }
 
+// x[i] += sum_k add[k][i] (K-split partial products, summed in split order), 4 elements a thread.
+__global__ __launch_bounds__(256) void add_partials_kernel(float* __restrict__ x,
+                                                           const float* __restrict__ add, int ks,
+                                                           size_t stride, int n4) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  f32x4 y = *(const f32x4*)(add + 4 * (size_t)i);
+  for (int k = 1; k < ks; ++k) y += *(const f32x4*)(add + k * stride + 4 * (size_t)i);
+  f32x4* xp = (f32x4*)(x + 4 * (size_t)i);
+  *xp = *xp + y;
+}
+
 __global__ void rope_table_kernel(float2* __restrict__ cs, int T, int half, double base) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= T * half) return;
@@ -253,7 +265,14 @@ hipError_t launch_embed_norm(const int32_t* tokens, const void* wte, bool wbf16,
 
 hipError_t launch_mix_norm(float* x, const float* x0, const float* lam, const float* mu, int layer,
                            bool mix, void* xn, bool xbf16, int M, int C, float eps, hipStream_t s,
-                           int c1) {
+                           int c1, const float* add, int add_ks) {
+  if (add != nullptr) {  // x += the K-split partial products, summed in split order
+    if (C % 4 || add_ks < 1) return hipErrorInvalidValue;
+    const int n4 = M * C / 4;
+    add_partials_kernel<<<(n4 + 255) / 256, 256, 0, s>>>(x, add, add_ks, (size_t)M * C, n4);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (c1 <= 0) c1 = C;
   if (C % 4 || c1 % 4 || c1 > C) return hipErrorInvalidValue;
   const int grid = (M + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;

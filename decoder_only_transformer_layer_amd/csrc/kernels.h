@@ -46,10 +46,11 @@ hipError_t launch_embed_norm(const int32_t* tokens, const void* wte, bool wbf16,
                              float eps, unsigned* flags, hipStream_t s, const void* pe = nullptr,
                              int c1 = 0);
 
-// If mix: x = lam[layer] x + mu[layer] x0 (in place).  Then xn = RMSNorm(x).
+// x += sum_k add[k] (add: optional [add_ks][M][C] partials, summed in order), then if mix:
+// x = lam[layer] x + mu[layer] x0 (in place).  Then xn = RMSNorm(x).
 hipError_t launch_mix_norm(float* x, const float* x0, const float* lam, const float* mu, int layer,
                            bool mix, void* xn, bool xbf16, int M, int C, float eps, hipStream_t s,
-                           int c1 = 0);
+                           int c1 = 0, const float* add = nullptr, int add_ks = 0);
 
 // fp32 path value embedding, in place on the v columns of qkv [M][ld] (v head h at column
 // voff + h*D): v += 3 sigmoid(xn[m][0:12] . gate[h]) * ve[tokens[m]][h*D : (h+1)*D].
@@ -61,6 +62,41 @@ hipError_t launch_ve_mix_f32(float* qkv, int ld, int voff, const float* xn, int 
 // position row % T, then per-head RMSNorm.
 hipError_t launch_qk_rope_norm(void* qk, bool bf16, int ld, const float2* cs, int M, int T,
                                int nheads, int D, float eps, hipStream_t s);
+
+// ---- decode step (k_decode.hip) ------------------------------------------------------------
+// Products of the decode step: y[b][n] = sum_k act[b][k] W[n][k] for b < B <= 32 (act rows
+// lda apart; W the row segments W0 | W1 | W2 split at nseg0, nseg0 + nseg1, multiples of 32;
+// K a multiple of 64), then per element: DEC_STORE out_f32 = y; DEC_RELU2 out_act =
+// relu(y)^2; DEC_RESID out_f32 += y; DEC_LOGITS out_f32 = cap tanh(y / cap), NaN for rows whose
+// pos is outside [0, T) or whose token is outside [0, V).
+enum DecEpi { DEC_STORE = 0, DEC_RELU2 = 1, DEC_RESID = 2, DEC_LOGITS = 3 };
+// KS > 1 (bf16 only) splits K over KS blocks per row block: the product then only stores its
+// KS partial tiles in partial[KS][B][N] (no epilogue) and the consumer sums them in order.
+int gemv_splits(int N, int K);
+hipError_t launch_gemv(bool bf16, int kind, const void* act, int lda, int B, const void* W0,
+                       const void* W1, const void* W2, int nseg0, int nseg1, int N, int K,
+                       void* out, int ldo, hipStream_t s, int KS = 1, float* partial = nullptr,
+                       float cap = 0.f, const int32_t* pos = nullptr,
+                       const int32_t* tokens = nullptr, int T = 0, int V = 0);
+// RoPE at pos[b] + per-head RMSNorm of the q and k heads of y [KS][B][ldy] (fp32 K-split
+// partials summed in order; heads q | k | v), q_hat to qout [B, H*D], k_hat and v to the caches
+// [B, Hkv, T, D] at position pos[b]; a row with pos outside [0, T) writes nothing and raises
+// GPT_FLAG_BAD_POS.
+hipError_t launch_rope_append(bool bf16, const float* y, int ldy, int KS, const int32_t* pos, int B,
+                              int T, int H, int Hkv, int D, float eps, float base, void* qout,
+                              void* kc, void* vc, unsigned* flags, hipStream_t s);
+// o [B, H*D] = attention of q [B, H*D] over cached keys/values [B, Hkv, T, D] at positions
+// [max(0, pos - window + 1), pos] of each row; part is scratch of
+// B * H * decode_attn_chunks(T) * (D + 2) floats.
+int decode_attn_chunks(int T);
+hipError_t launch_decode_attn(bool bf16, const void* q, const void* kc, const void* vc,
+                              const int32_t* pos, int B, int T, int H, int Hkv, int D, int window,
+                              float scale, void* o, float* part, hipStream_t s);
+// One token per row from logits [B, V]: argmax if temperature == 0, else the inverse CDF at
+// u[b] of softmax(z / temperature) over the top_k largest logits (ties kept; top_k <= 0 or
+// >= V keeps all), in vocabulary order.
+hipError_t launch_sample(const float* logits, int B, int V, int top_k, float temperature,
+                         const float* u, int32_t* out, hipStream_t s);
 
 // ---- GEMMs (k_gemm.hip) --------------------------------------------------------------------
 enum Epi { EPI_STORE = 0, EPI_RELU2 = 1, EPI_RESID = 2, EPI_QKV = 3, EPI_CE = 4 };

@@ -208,9 +208,51 @@ gpt_status gpt_fwd_loss_nested(const gpt_cfg *cfg, const gpt_weights *w, const i
                                void *workspace, size_t workspace_bytes, void *stream,
                                gpt_launch_timing *timing);
 
-/* Synchronise `stream`, then report whether any gpt_fwd_loss call that used this workspace saw
- * an out-of-range token or target id since the workspace's last call began (GPT_OK or
- * GPT_E_DEVICE_INPUT; GPT_E_HIP if synchronising failed). */
+/* ---- Decoding ("The Mathematics of Karpathy's nanochat", section "Inference: Generating
+ * Text": an autoregressive loop that takes the logits at the last position and samples the
+ * next token).  gpt_decode_step runs the forward pass for ONE new token per row at position
+ * pos[b], reading the keys and values of positions < pos[b] from a KV cache that earlier steps
+ * of the same row filled and writing those of pos[b] into it; its logits are those the full
+ * forward gives at position pos[b] of the sequence so far (attention is causal).  Here
+ * cfg->batch is the number of rows (1..32) and cfg->seq_len the cache capacity T (<= 8192;
+ * at most 8 query heads per KV head);
+ * the per-layer windows apply as in the forward.  Base models only: no value embeddings,
+ * looped trunk or nested model (GPT_E_UNSUPPORTED).
+ *
+ * KV cache layout (device, cfg->dtype, caller-owned, contents before a row's first step do not
+ * matter): for layer l, k_hat at [l][0][b][g][t][d] and v at [l][1][b][g][t][d], dimensions
+ * [n_layer][2][batch][n_kv_head][seq_len][head_dim]; k_hat is the RoPE'd, normalised key. */
+size_t gpt_kv_cache_bytes(const gpt_cfg *cfg);         /* 0 if cfg does not validate for decoding */
+size_t gpt_decode_workspace_bytes(const gpt_cfg *cfg); /* 0 likewise */
+
+/*   tokens     device int32 [B]: the token at position pos[b] of row b, in [0, vocab)
+ *   pos        device int32 [B]: its position, in [0, seq_len)
+ *   kv_cache   device, gpt_kv_cache_bytes(cfg), 256-byte aligned
+ *   logits     device fp32 [B, vocab] out: softcapped logits zhat at pos[b]
+ *   workspace  device, gpt_decode_workspace_bytes(cfg), 256-byte aligned (contents on entry do
+ *              not matter)
+ * Enqueues only (no host synchronisation, no allocation), so a step can be captured in a HIP
+ * graph and replayed with new tokens/pos values.  A row whose token or position is out of range
+ * gets NaN logits, writes nothing into the cache, and gpt_device_status(workspace) reports
+ * GPT_E_DEVICE_INPUT. */
+gpt_status gpt_decode_step(const gpt_cfg *cfg, const gpt_weights *w, const int32_t *tokens,
+                           const int32_t *pos, void *kv_cache, float *logits, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/* Sampling controls of the same section: for each row b of logits [batch, vocab] (device fp32),
+ * out[b] (device int32) = the first index of the largest logit if temperature == 0; otherwise
+ * the tokens whose logit is >= the top_k-th largest are kept (ties at the threshold stay;
+ * top_k <= 0 or >= vocab keeps all), p_v = exp((z_v - max z) / temperature) over them, and
+ * out[b] is the first token in vocabulary order whose running sum of p exceeds u[b] * sum p
+ * (u device fp32 [batch], uniform draws in [0, 1) supplied by the caller: the library draws no
+ * random numbers).  GPT_E_INVALID_ARG for a negative or non-finite temperature, batch < 1 or
+ * vocab < 1, or NULL pointers. */
+gpt_status gpt_sample(const float *logits, int32_t batch, int32_t vocab, int32_t top_k,
+                      float temperature, const float *u, int32_t *out, void *stream);
+
+/* Synchronise `stream`, then report whether any gpt_fwd_loss (or gpt_decode_step) call that
+ * used this workspace saw an out-of-range token, target id or position since the workspace's
+ * last call began (GPT_OK or GPT_E_DEVICE_INPUT; GPT_E_HIP if synchronising failed). */
 gpt_status gpt_device_status(void *workspace, void *stream);
 
 /* Static description of a status code (never NULL). */

@@ -204,6 +204,46 @@ def test_nested_validation(lib):
                                    None, need, None, None) == gf.GPT_E_WORKSPACE
 
 
+def test_decode_validation_and_argument_errors(lib):
+    """Decoding: base models with 1..32 rows and a cache of <= 8192 positions; every
+    host-detectable error returns before any launch (fake device addresses are never touched)."""
+    p = gptdata.preset("d24")
+    c = gf.make_cfg(p)
+    assert gf.gpt_kv_cache_bytes(c) == 24 * 2 * 8 * 12 * 2048 * 128 * 2
+    assert gf.gpt_decode_workspace_bytes(c) > 0
+    for bad in (p.with_(batch=33), p.with_(seq_len=16384), gptdata.preset("d24gve"),
+                gptdata.preset("d24loop"), gptdata.preset("d24nest")):
+        assert gf.gpt_kv_cache_bytes(gf.make_cfg(bad)) == 0
+        assert gf.gpt_decode_workspace_bytes(gf.make_cfg(bad)) == 0
+    w = _weights(c.n_layer)
+    need = gf.gpt_decode_workspace_bytes(c)
+    F, CACHE, WS = 0x200000, 0x40000000, 0x10000000
+
+    def call(cfg=c, tokens=F, pos=F, cache=CACHE, logits=F, ws=WS, wsb=need):
+        return lib.gpt_decode_step(ctypes.byref(cfg), ctypes.byref(w), tokens, pos, cache, logits, ws,
+                                   wsb, None)
+    assert call(tokens=None) == gf.GPT_E_INVALID_ARG
+    assert call(pos=None) == gf.GPT_E_INVALID_ARG
+    assert call(pos=F + 2) == gf.GPT_E_INVALID_ARG
+    assert call(logits=None) == gf.GPT_E_INVALID_ARG
+    assert call(cache=None) == gf.GPT_E_INVALID_ARG
+    assert call(cache=CACHE + 16) == gf.GPT_E_INVALID_ARG       # not 256-aligned
+    assert call(ws=None) == gf.GPT_E_WORKSPACE
+    assert call(wsb=need - 1) == gf.GPT_E_WORKSPACE
+    assert call(cfg=gf.make_cfg(p.with_(batch=33))) == gf.GPT_E_UNSUPPORTED
+    assert call(cfg=gf.make_cfg(gptdata.preset("d24gve"))) == gf.GPT_E_UNSUPPORTED
+    S = lambda **kw: lib.gpt_sample(kw.get("logits", F), kw.get("b", 2), kw.get("v", 100), kw.get("k", 5),
+                                    kw.get("t", 1.0), kw.get("u", F), kw.get("out", F), None)
+    assert S(logits=None) == gf.GPT_E_INVALID_ARG
+    assert S(u=None) == gf.GPT_E_INVALID_ARG
+    assert S(out=None) == gf.GPT_E_INVALID_ARG
+    assert S(b=0) == gf.GPT_E_INVALID_ARG
+    assert S(v=0) == gf.GPT_E_INVALID_ARG
+    assert S(t=-0.5) == gf.GPT_E_INVALID_ARG
+    assert S(t=float("nan")) == gf.GPT_E_INVALID_ARG
+    assert S(t=float("inf")) == gf.GPT_E_INVALID_ARG
+
+
 def test_fwd_loss_timed_argument_errors(lib):
     """The timing record is checked before anything else; a bad one never reaches a launch."""
     c = _cfg()

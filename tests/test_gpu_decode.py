@@ -1,0 +1,243 @@
+"""Decoding through the C ABI (gpt_decode_step, gpt_sample) against the oracle.
+
+A decode step at position t must give the logits that the oracle's full forward gives at
+position t of the same sequence ("The Mathematics of Karpathy's nanochat", section "Inference:
+Generating Text": the next token comes from the logits at the last position; attention is causal,
+so the cached keys and values of earlier positions are all a step needs).  Bars as for the
+forward: fp32 logits within 1e-3 of the largest |logit|; bf16 logits |error| RMS <= 6e-3 and max
+<= 3e-2.  The sampler is compared token by token with oracle.sample_next on the same logits and
+draws; where they differ, the GPU's token must still be a valid draw: kept by top-k, with u within
+rounding (1e-5) of its cumulative-probability interval.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import decoder_only_transformer_layer_amd as gf
+import gptdata
+import oracle
+from gpu_helpers import params_of, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode_all(p, w, tok, lag=None, windows=None):
+    """Feed tok [B, T] through T decode steps; row b's position at step s is s - lag[b] (rows
+    that have not started repeat position 0).  Returns the logits [B, T, V] by position."""
+    torch = torch_mod()
+    B, T = tok.shape
+    m = gf.DeviceModel(p, w, batch=B, windows=windows)
+    d = gf.Decoder(m)
+    lag = np.zeros(B, dtype=np.int64) if lag is None else np.asarray(lag)
+    t_tok = torch.from_numpy(tok.astype(np.int32)).cuda()
+    logits = torch.empty((B, p.vocab), dtype=torch.float32, device="cuda")
+    out = np.zeros((B, T, p.vocab))
+    steps = T + int(lag.max())
+    for s in range(steps):
+        pos = np.clip(s - lag, 0, T - 1).astype(np.int32)
+        t_pos = torch.from_numpy(pos).cuda()
+        cur = t_tok[torch.arange(B, device="cuda"), t_pos.long()].contiguous()
+        assert d.step(cur, t_pos, logits) == gf.GPT_OK
+        z = logits.cpu().numpy().astype(np.float64)
+        for b in range(B):
+            if s - lag[b] >= 0 and s - lag[b] < T:
+                out[b, s - lag[b]] = z[b]
+    torch.cuda.synchronize()
+    assert d.device_status() == gf.GPT_OK
+    return out
+
+
+def test_decode_matches_forward_fp32():
+    """fp32, GQA 2:1, head_dim 64, windows 16 / full; row 1 runs two positions behind row 0."""
+    p = gptdata.Preset(name="dec32", n_layer=2, d_model=128, n_head=2, n_kv_head=1, head_dim=64,
+                       mlp_dim=512, vocab=500, seq_len=48, batch=2, dtype="f32", short_window=16,
+                       lambda_range=(0.9, 1.1), mu_range=(0.0, 0.2), seed=51)
+    w, tok, _ = gptdata.make_inputs(p)
+    got = _decode_all(p, w, tok, lag=[0, 2])
+    ref = oracle.forward(p, params_of(w), tok, want_logits=True)["logits"]
+    err = np.max(np.abs(got - ref)) / np.max(np.abs(ref))
+    print(f"  decode fp32: logits err/max {err:.2e}")
+    assert err <= 1e-3
+
+
+def _check_bf16_logits(got, ref):
+    d = got - ref
+    rms, mx = float(np.sqrt(np.mean(d * d))), float(np.max(np.abs(d)))
+    print(f"  logits |err| rms {rms:.3e} max {mx:.3e}")
+    assert rms <= 6e-3 and mx <= 3e-2
+
+
+def test_decode_matches_forward_bf16():
+    """bf16, GQA 4:2, head_dim 128, windows 32 / 64 / full over 128 positions, 3 rows."""
+    p = gptdata.Preset(name="dec16", n_layer=3, d_model=256, n_head=4, n_kv_head=2, head_dim=128,
+                       mlp_dim=1024, vocab=1000, seq_len=128, batch=3, dtype="bf16", short_window=32,
+                       lambda_range=(0.9, 1.1), mu_range=(0.0, 0.2), seed=53)
+    w, tok, _ = gptdata.make_inputs(p)
+    windows = [32, 64, 128]
+    got = _decode_all(p, w, tok, windows=windows)
+    ref = oracle.forward(p, params_of(w), tok, want_logits=True, windows=windows)["logits"]
+    _check_bf16_logits(got, ref)
+
+
+def test_decode_d24_positions():
+    """d24 weights, 2 rows, the whole 2048-token cache: logits at positions 0, 511, 1023, 1024,
+    1500 and 2047 of row 0 against one oracle forward of that row."""
+    p = gptdata.preset("d24").with_(batch=2)
+    w, tok, _ = gptdata.make_inputs(p)
+    torch = torch_mod()
+    m = gf.DeviceModel(p, w, batch=2)
+    d = gf.Decoder(m)
+    t_tok = torch.from_numpy(tok).cuda()
+    logits = torch.empty((2, p.vocab), dtype=torch.float32, device="cuda")
+    check = [0, 511, 1023, 1024, 1500, 2047]
+    got = {}
+    for s in range(p.seq_len):
+        t_pos = torch.full((2,), s, dtype=torch.int32, device="cuda")
+        assert d.step(t_tok[:, s].contiguous(), t_pos, logits) == gf.GPT_OK
+        if s in check:
+            got[s] = logits[0].cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+    assert d.device_status() == gf.GPT_OK
+    ref = oracle.forward(p, params_of(w), tok[:1], want_logits=True)["logits"][0]
+    _check_bf16_logits(np.stack([got[s] for s in check]), ref[check])
+
+
+def test_decode_bad_inputs():
+    """An out-of-range token or position gives NaN logits for that row only and a device error;
+    the other rows are unaffected."""
+    p = gptdata.Preset(name="decbad", n_layer=2, d_model=128, n_head=2, n_kv_head=2, head_dim=64,
+                       mlp_dim=256, vocab=300, seq_len=64, batch=3, dtype="bf16", short_window=32,
+                       seed=55)
+    w, tok, _ = gptdata.make_inputs(p)
+    torch = torch_mod()
+    m = gf.DeviceModel(p, w, batch=3)
+    d = gf.Decoder(m)
+    logits = torch.empty((3, p.vocab), dtype=torch.float32, device="cuda")
+    cur = torch.tensor([tok[0, 0], p.vocab + 5, tok[2, 0]], dtype=torch.int32, device="cuda")
+    pos = torch.tensor([0, 0, 0], dtype=torch.int32, device="cuda")
+    assert d.step(cur, pos, logits) == gf.GPT_OK
+    z = logits.cpu().numpy()
+    assert np.all(np.isnan(z[1])) and np.all(np.isfinite(z[[0, 2]]))
+    assert d.device_status() == gf.GPT_E_DEVICE_INPUT
+    cur = torch.from_numpy(tok[:, 0].copy()).cuda()
+    pos = torch.tensor([0, p.seq_len, -1], dtype=torch.int32, device="cuda")
+    assert d.step(cur, pos, logits) == gf.GPT_OK
+    z = logits.cpu().numpy()
+    assert np.all(np.isfinite(z[0])) and np.all(np.isnan(z[1:]))
+    assert d.device_status() == gf.GPT_E_DEVICE_INPUT
+    ref = oracle.forward(p, params_of(w), tok[:1, :1], want_logits=True)["logits"][0, 0]
+    assert np.max(np.abs(z[0] - ref)) <= 3e-2
+
+
+def _valid_draw(z, k, tau, u, tok):
+    """The GPU's token is a valid draw at u: kept by top-k and u within 1e-5 of its interval of
+    the (fp64) cumulative distribution in vocabulary order."""
+    keep = oracle.top_k_keep(z, k if k and k > 0 else None)
+    if not keep[tok]:
+        return False
+    s = np.where(keep, z / tau, -np.inf)
+    e = np.exp(s - np.max(s))
+    cdf = np.cumsum(e / e.sum())
+    lo = cdf[tok - 1] if tok > 0 else 0.0
+    return lo - 1e-5 <= u <= cdf[tok] + 1e-5
+
+
+@pytest.mark.parametrize("V", [100, 5003, 32768])
+def test_sampler_matches_oracle(V):
+    """Greedy with planted ties, top-k = 1, 7, 50, all (0 and V), temperatures 0.5 / 1 / 2."""
+    torch = torch_mod()
+    rng = np.random.default_rng(V)
+    B = 6
+    z = (rng.standard_normal((B, V)) * 2.5).astype(np.float32)
+    z[0, [3, V - 1]] = z[0].max() + 1.0     # equal maxima: greedy takes the first
+    z[1, 10:14] = 4.0                         # ties at a top-k threshold
+    z[1, 14:] = np.minimum(z[1, 14:], 3.0)
+    z[1, :10] = np.minimum(z[1, :10], 3.0)
+    t_z = torch.from_numpy(z).cuda()
+    out = torch.empty(B, dtype=torch.int32, device="cuda")
+    mism = 0
+    for k in (0, 1, 2, 7, 50, V):
+        for tau in (0.0, 0.5, 1.0, 2.0):
+            for trial in range(3):
+                u = rng.random(B).astype(np.float32)
+                t_u = torch.from_numpy(u).cuda()
+                assert gf.gpt_sample(t_z, B, V, k, tau, t_u, out) == gf.GPT_OK
+                got = out.cpu().numpy()
+                for b in range(B):
+                    zb = z[b].astype(np.float64)
+                    ref = oracle.sample_next(zb, k if k > 0 else None, tau, float(u[b]))
+                    if got[b] != ref:
+                        mism += 1
+                        assert tau > 0 and _valid_draw(zb, k, tau, float(u[b]), int(got[b])), (k, tau, b)
+    print(f"  V={V}: {mism} boundary-rounding differences")
+    assert mism <= 2
+
+
+def test_greedy_generation_matches_oracle():
+    """fp32 model: decode + greedy sampling for 12 new tokens after a 6-token prompt, against the
+    oracle's generate (full forward per step)."""
+    torch = torch_mod()
+    p = gptdata.Preset(name="gen32", n_layer=2, d_model=128, n_head=2, n_kv_head=2, head_dim=64,
+                       mlp_dim=512, vocab=200, seq_len=32, batch=2, dtype="f32", short_window=8,
+                       seed=57)
+    w, tok, _ = gptdata.make_inputs(p)
+    prompt, n_new = tok[:, :6], 12
+    ref = oracle.generate(p, params_of(w), prompt, n_new, top_k=None, temperature=0.0,
+                          u=np.zeros((n_new, 2)))
+    m = gf.DeviceModel(p, w, batch=2)
+    d = gf.Decoder(m)
+    logits = torch.empty((2, p.vocab), dtype=torch.float32, device="cuda")
+    nxt = torch.empty(2, dtype=torch.int32, device="cuda")
+    u = torch.zeros(2, dtype=torch.float32, device="cuda")
+    seq = [torch.from_numpy(prompt[:, i].astype(np.int32)).cuda() for i in range(prompt.shape[1])]
+    for s in range(prompt.shape[1] + n_new - 1):
+        pos = torch.full((2,), s, dtype=torch.int32, device="cuda")
+        assert d.step(seq[s], pos, logits) == gf.GPT_OK
+        if s >= prompt.shape[1] - 1:
+            assert gf.gpt_sample(logits, 2, p.vocab, 0, 0.0, u, nxt) == gf.GPT_OK
+            seq.append(nxt.clone())
+    got = torch.stack(seq, dim=1).cpu().numpy()
+    assert np.array_equal(got, ref["tokens"]), (got, ref["tokens"])
+
+
+def test_decode_step_graph_replay():
+    """A decode step captured once in a HIP graph and replayed for successive positions (new
+    token and position values written between replays, with eager work in between) gives, at
+    every replay, the logits of the same steps run eagerly."""
+    torch = torch_mod()
+    p = gptdata.Preset(name="decgraph", n_layer=2, d_model=256, n_head=2, n_kv_head=2, head_dim=128,
+                       mlp_dim=1024, vocab=700, seq_len=64, batch=2, dtype="bf16", short_window=16,
+                       seed=59)
+    w, tok, _ = gptdata.make_inputs(p)
+    n = 12
+    eager = []
+    m = gf.DeviceModel(p, w, batch=2)
+    d = gf.Decoder(m)
+    logits = torch.empty((2, p.vocab), dtype=torch.float32, device="cuda")
+    for s in range(n):
+        t_pos = torch.full((2,), s, dtype=torch.int32, device="cuda")
+        assert d.step(torch.from_numpy(tok[:, s].copy()).cuda(), t_pos, logits) == gf.GPT_OK
+        eager.append(logits.cpu().numpy().copy())
+    d2 = gf.Decoder(m)   # fresh cache
+    cur = torch.zeros(2, dtype=torch.int32, device="cuda")
+    pos = torch.zeros(2, dtype=torch.int32, device="cuda")
+    out = torch.empty((2, p.vocab), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):        # warm-up launch outside the capture
+        assert d2.step(cur, pos, out) == gf.GPT_OK
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        assert d2.step(cur, pos, out) == gf.GPT_OK
+    for s in range(n):
+        cur.copy_(torch.from_numpy(tok[:, s].copy()))
+        pos.fill_(s)
+        g.replay()
+        torch.cuda.synchronize()
+        junk = torch.randn(1000, device="cuda").sum()   # eager work between replays
+        assert np.array_equal(out.cpu().numpy(), eager[s]), s
+        del junk
+    assert d2.device_status() == gf.GPT_OK
