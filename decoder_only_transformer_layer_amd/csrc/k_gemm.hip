@@ -378,43 +378,83 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // Row sum of squares of this lane's row over the wavefront's slice: 8-lane butterfly.
+      auto put_ss = [&](int row, float ss) {
+        ss += __shfl_xor(ss, 1);
+        ss += __shfl_xor(ss, 2);
+        ss += __shfl_xor(ss, 4);
+        if ((lane & 7) == 0 && slice_live && row < M) g.ssp[(size_t)slice * M + row] = ss;
+      };
+      if (interior && vec) {
+        // The x (and x0) chunks of the next 8 rows are loaded before this 8 rows' stores
+        // are issued (the compiler cannot move a load of x past a store to x), so two row
+        // groups' loads are in flight instead of one chunk's.
+        f32x4 xv[2][FN], x0v[2][FN];
+        auto prefetch = [&](int j) {
+          const size_t ro = (size_t)(m0 + wm * TM + fm * 32 + lr + 8 * j) * g.ldo + n0 + wn * TN + lc;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = m0 + wm * TM + fm * 32 + lr + 8 * j;
-        float ss = 0.f;
+          for (int c = 0; c < FN; ++c) {
+            xv[j & 1][c] = *(const f32x4*)(out + ro + 32 * c);
+            if (mix) x0v[j & 1][c] = *(const f32x4*)(g.x0 + ro + 32 * c);
+          }
+        };
+        prefetch(0);
 #pragma unroll
-        for (int c = 0; c < FN; ++c) {
-          const int col = n0 + wn * TN + 32 * c + lc;
-          const f32x4 a = *(const f32x4*)(stg + (lr + 8 * j) * LDP + 32 * c + lc);
-          const size_t o = (size_t)row * g.ldo + col;
-          if ((interior || (row < M && col + 4 <= N)) && vec) {
-            f32x4 v = *(const f32x4*)(out + o) + a;
-            if (mix) v = lam * v + mu * *(const f32x4*)(g.x0 + o);
-            *(f32x4*)(out + o) = v;
+        for (int j = 0; j < 4; ++j) {
+          if (j + 1 < 4) prefetch(j + 1);
+          const int row = m0 + wm * TM + fm * 32 + lr + 8 * j;
+          const size_t ro = (size_t)row * g.ldo + n0 + wn * TN + lc;
+          float ss = 0.f;
+#pragma unroll
+          for (int c = 0; c < FN; ++c) {
+            const f32x4 a = *(const f32x4*)(stg + (lr + 8 * j) * LDP + 32 * c + lc);
+            f32x4 v = xv[j & 1][c] + a;
+            if (mix) v = lam * v + mu * x0v[j & 1][c];
+            *(f32x4*)(out + ro + 32 * c) = v;
             if (prod) {
               bf16x4 h;
 #pragma unroll
               for (int e = 0; e < 4; ++e) h[e] = (bf16)v[e];
-              *(bf16x4*)(g.xb + o) = h;
+              *(bf16x4*)(g.xb + ro + 32 * c) = h;
               ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
             }
-          } else if (row < M) {
+          }
+          if (prod) put_ss(row, ss);
+        }
+      } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              if (col + e < N) {
-                float v = out[o + e] + a[e];
-                if (mix) v = lam * v + mu * g.x0[o + e];
-                out[o + e] = v;
-                if (prod) { g.xb[o + e] = (bf16)v; ss += v * v; }
+        for (int j = 0; j < 4; ++j) {
+          const int row = m0 + wm * TM + fm * 32 + lr + 8 * j;
+          float ss = 0.f;
+#pragma unroll
+          for (int c = 0; c < FN; ++c) {
+            const int col = n0 + wn * TN + 32 * c + lc;
+            const f32x4 a = *(const f32x4*)(stg + (lr + 8 * j) * LDP + 32 * c + lc);
+            const size_t o = (size_t)row * g.ldo + col;
+            if (row < M && col + 4 <= N && vec) {
+              f32x4 v = *(const f32x4*)(out + o) + a;
+              if (mix) v = lam * v + mu * *(const f32x4*)(g.x0 + o);
+              *(f32x4*)(out + o) = v;
+              if (prod) {
+                bf16x4 h;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) h[e] = (bf16)v[e];
+                *(bf16x4*)(g.xb + o) = h;
+                ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+              }
+            } else if (row < M) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                if (col + e < N) {
+                  float v = out[o + e] + a[e];
+                  if (mix) v = lam * v + mu * g.x0[o + e];
+                  out[o + e] = v;
+                  if (prod) { g.xb[o + e] = (bf16)v; ss += v * v; }
+                }
               }
             }
           }
-        }
-        if (prod) {
-          ss += __shfl_xor(ss, 1);
-          ss += __shfl_xor(ss, 2);
-          ss += __shfl_xor(ss, 4);
-          if ((lane & 7) == 0 && slice_live && row < M) g.ssp[(size_t)slice * M + row] = ss;
+          if (prod) put_ss(row, ss);
         }
       }
       __builtin_amdgcn_wave_barrier();  // reads of this group precede the next group's writes
