@@ -29,6 +29,7 @@ EXPORTED = [
     "gpt_validate", "gpt_workspace_bytes", "gpt_fwd_loss", "gpt_fwd_loss_timed", "gpt_fwd_loss_nested",
     "gpt_device_status", "gpt_status_string",
     "gpt_kv_cache_bytes", "gpt_decode_workspace_bytes", "gpt_decode_step", "gpt_sample",
+    "gpt_prefill_workspace_bytes", "gpt_prefill",
     "gpt_op_embed_norm", "gpt_op_mix_norm", "gpt_op_rope_table", "gpt_op_qk_rope_norm",
     "gpt_op_linear", "gpt_op_qkv", "gpt_op_attention", "gpt_op_lm_head_ce_workspace",
     "gpt_op_lm_head_ce",
@@ -92,6 +93,8 @@ def _load() -> ctypes.CDLL:
         "gpt_decode_workspace_bytes": (S, [ctypes.POINTER(gpt_cfg)]),
         "gpt_decode_step": (I, [ctypes.POINTER(gpt_cfg), ctypes.POINTER(gpt_weights), P, P, P, P, P, S, P]),
         "gpt_sample": (I, [P, I, I, I, F, P, P, P]),
+        "gpt_prefill_workspace_bytes": (S, [ctypes.POINTER(gpt_cfg)]),
+        "gpt_prefill": (I, [ctypes.POINTER(gpt_cfg), ctypes.POINTER(gpt_weights), P, I, P, P, P, P, S, P]),
         "gpt_status_string": (ctypes.c_char_p, [I]),
         "gpt_op_embed_norm": (I, [I, P, P, P, P, P, P, P, I, I, I, F, P, P]),
         "gpt_op_mix_norm": (I, [I, P, P, P, P, I, I, P, I, I, F, P]),
@@ -242,6 +245,16 @@ def gpt_decode_step(cfg: gpt_cfg, weights: gpt_weights, tokens, pos, kv_cache, l
     return _load().gpt_decode_step(ctypes.byref(cfg), ctypes.byref(weights), _ptr(tokens), _ptr(pos),
                                    _ptr(kv_cache), _ptr(logits), _ptr(workspace), workspace_bytes,
                                    _stream(stream))
+
+
+def gpt_prefill_workspace_bytes(cfg: gpt_cfg) -> int:
+    return _load().gpt_prefill_workspace_bytes(ctypes.byref(cfg))
+
+
+def gpt_prefill(cfg: gpt_cfg, weights: gpt_weights, tokens, prompt_len: int, lens, kv_cache, logits,
+                workspace, workspace_bytes: int, stream=None) -> int:
+    return _load().gpt_prefill(ctypes.byref(cfg), ctypes.byref(weights), _ptr(tokens), prompt_len, _ptr(lens),
+                               _ptr(kv_cache), _ptr(logits), _ptr(workspace), workspace_bytes, _stream(stream))
 
 
 def gpt_sample(logits, batch: int, vocab: int, top_k: int, temperature: float, u, out, stream=None) -> int:
@@ -410,6 +423,15 @@ class DeviceModel:
         _check(self.forward(tokens, targets, loss, mean, logits), "gpt_fwd_loss")
         return loss, mean, logits
 
+    def prefill(self, tokens, prompt_len: int, logits, lens=None, stream=None) -> int:
+        """Enqueue gpt_prefill on tokens [B, prompt_len] (device int32, contiguous); the forward
+        uses the DeviceModel's workspace."""
+        need = gpt_prefill_workspace_bytes(self.cfg)
+        if self.m.ws_bytes < need:
+            raise GptError(GPT_E_WORKSPACE, "prefill workspace")
+        return gpt_prefill(self.cfg, self.m.w, tokens, prompt_len, lens, self.cache_ptr, logits,
+                           self.m.ws_ptr, self.m.ws_bytes, stream)
+
     def device_status(self) -> int:
         return gpt_device_status(self.ws_ptr)
 
@@ -438,6 +460,15 @@ class Decoder:
         """Enqueue gpt_decode_step: tokens, pos device int32 [B]; logits device fp32 [B, V]."""
         return gpt_decode_step(self.cfg, self.m.w, tokens, pos, self.cache_ptr, logits, self.ws_ptr,
                                self.ws_bytes, stream)
+
+    def prefill(self, tokens, prompt_len: int, logits, lens=None, stream=None) -> int:
+        """Enqueue gpt_prefill on tokens [B, prompt_len] (device int32, contiguous); the forward
+        uses the DeviceModel's workspace."""
+        need = gpt_prefill_workspace_bytes(self.cfg)
+        if self.m.ws_bytes < need:
+            raise GptError(GPT_E_WORKSPACE, "prefill workspace")
+        return gpt_prefill(self.cfg, self.m.w, tokens, prompt_len, lens, self.cache_ptr, logits,
+                           self.m.ws_ptr, self.m.ws_bytes, stream)
 
     def device_status(self) -> int:
         return gpt_device_status(self.ws_ptr)

@@ -21,8 +21,17 @@ inline size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 struct Layout {
-  size_t flags, x, x0, xn, qk, vt, o, h, cs, ssp, partial, tgt, qk1, total;
+  size_t flags, x, x0, xn, qk, vt, o, h, cs, ssp, partial, tgt, qk1, last, total;
   int nnb;
+};
+
+// Prefill (gpt_prefill): the forward's layers also fill the decode cache (capacity T rows per
+// (row, KV head)); the outputs are the logits at each row's last prompt position.
+struct Prefill {
+  void* cache;
+  int T;
+  const int32_t* lens;
+  float* logits;
 };
 
 constexpr int VE_GATE_CH = 12;  // input channels of the value-embedding gate
@@ -116,6 +125,7 @@ Layout plan(const gpt_cfg* c) {
   // looped trunk: every pass-1 layer's q, k (bf16: the qk layout; fp32: the whole qkv rows)
   L.qk1 = off;
   if (c->looped) off += up((size_t)c->n_layer * M * (bf ? (H + Hkv) * D * 2 : (H + 2 * Hkv) * D * 4));
+  L.last = off; off += up((size_t)c->batch * C * 4);  // prefill: each row's last position, normed
   L.total = off;
   return L;
 }
@@ -294,7 +304,8 @@ gpt_status nested_layers(const gpt_cfg* c, const gpt_weights* w, const int32_t* 
 gpt_status run(const gpt_cfg* c, const gpt_weights* w, const int32_t* tokens,
                const int32_t* targets, float* loss, float* mean_loss, float* logits,
                float* loss1, float* mean1, float* logits1, void* workspace,
-               size_t workspace_bytes, void* stream, gpt_launch_timing* timing);
+               size_t workspace_bytes, void* stream, gpt_launch_timing* timing,
+               const Prefill* pf = nullptr);
 
 }  // namespace
 
@@ -339,7 +350,8 @@ namespace {
 gpt_status run(const gpt_cfg* c, const gpt_weights* w, const int32_t* tokens,
                const int32_t* targets, float* loss, float* mean_loss, float* logits,
                float* loss1, float* mean1, float* logits1, void* workspace,
-               size_t workspace_bytes, void* stream, gpt_launch_timing* timing) {
+               size_t workspace_bytes, void* stream, gpt_launch_timing* timing,
+               const Prefill* pf) {
   if (timing) {
     if (timing->kind < GPT_KERNEL_QKV || timing->kind > GPT_KERNEL_LM_HEAD || timing->capacity < 0 ||
         (timing->capacity > 0 && (!timing->begin || !timing->end)))
@@ -366,7 +378,7 @@ gpt_status run(const gpt_cfg* c, const gpt_weights* w, const int32_t* tokens,
                     !aligned(w->gate_logit, 4)))
     return GPT_E_INVALID_ARG;
   if (targets && (!loss || !mean_loss)) return GPT_E_INVALID_ARG;
-  if (!targets && !logits) return GPT_E_INVALID_ARG;
+  if (!targets && !logits && !pf) return GPT_E_INVALID_ARG;
   if (!loss1 != !mean1 || (loss1 && !targets) || (loss1 && !aligned(loss1, 4)) ||
       (mean1 && !aligned(mean1, 4)) || (logits1 && !aligned(logits1, 4)))
     return GPT_E_INVALID_ARG;
@@ -451,6 +463,11 @@ gpt_status run(const gpt_cfg* c, const gpt_weights* w, const int32_t* tokens,
         }
         TIMED(tm, GPT_KERNEL_QKV, launch_gemm_bf16(EPI_QKV, g, s));
         if (!fused) CK(launch_qk_rope_norm(qk_l, true, nqk, cs, M, T, H + Hkv, D, eps, s));
+        if (pf) {
+          char* kc = (char*)pf->cache + (size_t)l * 2 * B * Hkv * pf->T * D * 2;
+          CK(launch_cache_fill(true, qk_l, nqk, H * D, vt, 0, B, T, pf->T, Hkv, D, kc,
+                               kc + (size_t)B * Hkv * pf->T * D * 2, s));
+        }
         if (capture && l + 1 == c->n_layer) break;
         TIMED(tm, GPT_KERNEL_ATTENTION, launch_attn_bf16(qk_l, vt, o, B, T, H, Hkv, D, win,
                                                          c->attn_scale, s, qk1_l, gl, l));
@@ -477,6 +494,11 @@ gpt_status run(const gpt_cfg* c, const gpt_weights* w, const int32_t* tokens,
                                (const float*)w->ve[l], (const float*)w->ve_gate[l], M, Hkv, D, s));
         // RoPE + QK-norm on the q and k heads
         CK(launch_qk_rope_norm(qk_l, false, nqkv, cs, M, T, H + Hkv, D, eps, s));
+        if (pf) {
+          char* kc = (char*)pf->cache + (size_t)l * 2 * B * Hkv * pf->T * D * 4;
+          CK(launch_cache_fill(false, qk_l, nqkv, H * D, qk_l, (H + Hkv) * D, B, T, pf->T, Hkv, D,
+                               kc, kc + (size_t)B * Hkv * pf->T * D * 4, s));
+        }
         if (capture && l + 1 == c->n_layer) break;
         // windowed causal attention
         CK(launch_attn_f32((const float*)qk_l, (float*)o, B, T, H, Hkv, D, win, c->attn_scale, s,
@@ -492,6 +514,13 @@ gpt_status run(const gpt_cfg* c, const gpt_weights* w, const int32_t* tokens,
         CK(launch_mix_norm(x, x0, w->resid_lambda, w->x0_lambda, l + 1, more, xn, false, M, C, eps, s));
       }
     }
+  }
+  if (pf) {  // logits at each row's last prompt position: its normed row times W_U^T
+    void* last = ws + L.last;
+    CK(launch_last_row_norm(bf, x, pf->lens, B, T, C, eps, last, flags, s));
+    CK(launch_gemv(bf, DEC_LOGITS, last, C, B, w->lm_head, w->lm_head, w->lm_head, V, 0, V, C,
+                   pf->logits, V, s, 1, nullptr, c->softcap));
+    return GPT_OK;
   }
   if (bf)
     return lm_head_ce(bf, xn, w->lm_head, targets, tokens, M, C, V, c->softcap, loss, mean_loss,
@@ -634,6 +663,30 @@ gpt_status gpt_decode_step(const gpt_cfg* c, const gpt_weights* w, const int32_t
   CK(launch_gemv(bf, DEC_LOGITS, xn, C, B, w->lm_head, w->lm_head, w->lm_head, V, 0, V, C, logits,
                  V, s, 1, nullptr, c->softcap, pos, tokens, T, V));
   return GPT_OK;
+}
+
+size_t gpt_prefill_workspace_bytes(const gpt_cfg* c) {
+  if (validate_decode(c) != GPT_OK) return 0;
+  return plan(c).total;  // the forward over up to seq_len positions
+}
+
+gpt_status gpt_prefill(const gpt_cfg* c, const gpt_weights* w, const int32_t* tokens,
+                       int32_t prompt_len, const int32_t* lens, void* kv_cache, float* logits,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  gpt_status st = validate_decode(c);
+  if (st != GPT_OK) return st;
+  if (prompt_len < 1 || prompt_len > c->seq_len) return GPT_E_INVALID_ARG;
+  if (!kv_cache || !aligned(kv_cache, ALIGN) || !logits || !aligned(logits, 4) ||
+      (lens && !aligned(lens, 4)))
+    return GPT_E_INVALID_ARG;
+  gpt_cfg f = *c;  // the forward over the prompt positions
+  f.seq_len = prompt_len;
+  st = validate(&f);
+  if (st != GPT_OK) return st;
+  if (!workspace || workspace_bytes < gpt_prefill_workspace_bytes(c)) return GPT_E_WORKSPACE;
+  const Prefill pf{kv_cache, c->seq_len, lens, logits};
+  return run(&f, w, tokens, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+             workspace, workspace_bytes, stream, nullptr, &pf);
 }
 
 gpt_status gpt_sample(const float* logits, int32_t batch, int32_t vocab, int32_t top_k,

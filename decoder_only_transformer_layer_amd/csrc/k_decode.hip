@@ -37,8 +37,11 @@ __device__ __forceinline__ void gv_apply(const GvEpi& e, int b, int n, float v) 
     case DEC_RELU2: { const float r = fmaxf(v, 0.f); ((AT*)e.out)[o] = from_f32<AT>(r * r); } break;
     case DEC_RESID: ((float*)e.out)[o] += v; break;
     case DEC_LOGITS: {
-      const int p = e.pos[b], t = e.tokens[b];
-      const bool bad = p < 0 || p >= e.T || t < 0 || t >= e.V;
+      bool bad = false;
+      if (e.pos != nullptr) {
+        const int p = e.pos[b], t = e.tokens[b];
+        bad = p < 0 || p >= e.T || t < 0 || t >= e.V;
+      }
       ((float*)e.out)[o] = bad ? __builtin_nanf("") : e.cap * tanhf(v / e.cap);
     } break;
   }
@@ -350,6 +353,67 @@ __global__ __launch_bounds__(D) void decode_attn_combine_kernel(const float* __r
   o[(size_t)bh * D + d] = from_f32<AT>(l > 0.f ? acc / l : 0.f);
 }
 
+// ----------------------------------------------------------------------------------- prefill
+// The decode cache from one forward pass over P positions: k_hat rows (and, on the fp32 path,
+// v rows) are copied from the forward's row-major [B*P][ld] projection at column col0 + g*D
+// into [B][Hkv][T][D]; 16 bytes per thread.
+template <typename AT>
+__global__ __launch_bounds__(256) void cache_fill_rows_kernel(const AT* __restrict__ src, int ld,
+                                                              int col0, AT* __restrict__ dst, int B,
+                                                              int P, int T, int Hkv, int D) {
+  constexpr int E = 16 / sizeof(AT);
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  const int per_row = Hkv * D / E;
+  if (idx >= (long)B * P * per_row) return;
+  const int c = (int)(idx % per_row), bt = (int)(idx / per_row), b = bt / P, t = bt % P;
+  const int g = c / (D / E), d = (c % (D / E)) * E;
+  *(u32x4*)(dst + (((size_t)b * Hkv + g) * T + t) * D + d) =
+      *(const u32x4*)(src + (size_t)bt * ld + col0 + g * D + d);
+}
+
+// bf16 path: v of the forward is stored transposed, [B][Hkv][D][P]; 64x64 tiles go through LDS
+// to [B][Hkv][T][D].
+__global__ __launch_bounds__(256) void cache_fill_vt_kernel(const bf16* __restrict__ vt,
+                                                            bf16* __restrict__ dst, int P, int T,
+                                                            int D) {
+  __shared__ bf16 tile[64][64 + 2];
+  const int bg = blockIdx.z, d0 = blockIdx.y * 64, t0 = blockIdx.x * 64;
+  const bf16* s = vt + (size_t)bg * D * P;
+  bf16* o = dst + (size_t)bg * T * D;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int dd = i / 64, tt = i % 64;
+    if (d0 + dd < D && t0 + tt < P) tile[dd][tt] = s[(size_t)(d0 + dd) * P + t0 + tt];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int tt = i / 64, dd = i % 64;
+    if (d0 + dd < D && t0 + tt < P) o[(size_t)(t0 + tt) * D + d0 + dd] = tile[dd][tt];
+  }
+}
+
+// Row b's last prompt position r = b*P + len_b - 1 (len_b = lens[b], or P), RMS-normalised in
+// fp32 from the residual stream x and rounded once to the activation type; an invalid length
+// raises GPT_FLAG_BAD_POS and gives a NaN row (so its logits are NaN).
+template <typename AT>
+__global__ __launch_bounds__(64) void last_row_norm_kernel(const float* __restrict__ x,
+                                                           const int32_t* __restrict__ lens, int P,
+                                                           int C, float eps, AT* __restrict__ out,
+                                                           unsigned* __restrict__ flags) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int len = lens != nullptr ? lens[b] : P;
+  AT* o = out + (size_t)b * C;
+  if (len < 1 || len > P) {
+    if (lane == 0) atomicOr(flags, GPT_FLAG_BAD_POS);
+    for (int i = lane; i < C; i += 64) o[i] = from_f32<AT>(__builtin_nanf(""));
+    return;
+  }
+  const float* xr = x + ((size_t)b * P + len - 1) * C;
+  float ss = 0.f;
+  for (int i = lane; i < C; i += 64) ss += xr[i] * xr[i];
+  const float r = rsqrtf(wave_sum(ss) / (float)C + eps);
+  for (int i = lane; i < C; i += 64) o[i] = from_f32<AT>(xr[i] * r);
+}
+
 // ---------------------------------------------------------------------------------- sampling
 constexpr int SMP_THREADS = 1024;
 
@@ -542,6 +606,29 @@ hipError_t launch_decode_attn(bool bf, const void* q, const void* kc, const void
   if (bf) { if (D == 128) GPTK_DA(bf16, 128); else GPTK_DA(bf16, 64); }
   else { if (D == 128) GPTK_DA(float, 128); else GPTK_DA(float, 64); }
 #undef GPTK_DA
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_fill(bool bf, const void* qk, int ld, int kcol0, const void* vsrc,
+                             int vcol0, int B, int P, int T, int Hkv, int D, void* kc, void* vc,
+                             hipStream_t s) {
+  const long n = (long)B * P * Hkv * D / (bf ? 8 : 4);
+  const int grid = (int)((n + 255) / 256);
+  if (bf) {
+    cache_fill_rows_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)qk, ld, kcol0, (bf16*)kc, B, P, T, Hkv, D);
+    const dim3 g2((P + 63) / 64, (D + 63) / 64, B * Hkv);
+    cache_fill_vt_kernel<<<g2, 256, 0, s>>>((const bf16*)vsrc, (bf16*)vc, P, T, D);
+  } else {
+    cache_fill_rows_kernel<float><<<grid, 256, 0, s>>>((const float*)qk, ld, kcol0, (float*)kc, B, P, T, Hkv, D);
+    cache_fill_rows_kernel<float><<<grid, 256, 0, s>>>((const float*)vsrc, ld, vcol0, (float*)vc, B, P, T, Hkv, D);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_last_row_norm(bool bf, const float* x, const int32_t* lens, int B, int P, int C,
+                                float eps, void* out, unsigned* flags, hipStream_t s) {
+  if (bf) last_row_norm_kernel<bf16><<<B, 64, 0, s>>>(x, lens, P, C, eps, (bf16*)out, flags);
+  else last_row_norm_kernel<float><<<B, 64, 0, s>>>(x, lens, P, C, eps, (float*)out, flags);
   return hipGetLastError();
 }
 

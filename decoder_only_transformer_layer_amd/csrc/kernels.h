@@ -92,6 +92,15 @@ int decode_attn_chunks(int T);
 hipError_t launch_decode_attn(bool bf16, const void* q, const void* kc, const void* vc,
                               const int32_t* pos, int B, int T, int H, int Hkv, int D, int window,
                               float scale, void* o, float* part, hipStream_t s);
+// Prefill: the decode cache [B][Hkv][T][D] from one forward pass over P <= T positions.  k_hat
+// rows come from qk [B*P][ld] at column kcol0 + g*D; v from vsrc -- bf16: the forward's
+// transposed [B][Hkv][D][P]; fp32: rows of [B*P][ld] at column vcol0 + g*D.
+hipError_t launch_cache_fill(bool bf16, const void* qk, int ld, int kcol0, const void* vsrc,
+                             int vcol0, int B, int P, int T, int Hkv, int D, void* kc, void* vc,
+                             hipStream_t s);
+// out [B, C] = RMSNorm of x row b*P + lens[b] - 1 (lens NULL: P); bad lengths -> NaN row + flag.
+hipError_t launch_last_row_norm(bool bf16, const float* x, const int32_t* lens, int B, int P, int C,
+                                float eps, void* out, unsigned* flags, hipStream_t s);
 // One token per row from logits [B, V]: argmax if temperature == 0, else the inverse CDF at
 // u[b] of softmax(z / temperature) over the top_k largest logits (ties kept; top_k <= 0 or
 // >= V keeps all), in vocabulary order.

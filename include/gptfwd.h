@@ -239,6 +239,20 @@ gpt_status gpt_decode_step(const gpt_cfg *cfg, const gpt_weights *w, const int32
                            const int32_t *pos, void *kv_cache, float *logits, void *workspace,
                            size_t workspace_bytes, void *stream);
 
+/* Prefill: fill the KV cache from ONE forward pass over a prompt batch tokens [B, prompt_len]
+ * (device int32, prompt_len <= seq_len; GPT_BF16 needs prompt_len % 64 == 0, as the forward
+ * does) instead of prompt_len decode steps, and return in logits [B, vocab] (device fp32) the
+ * softcapped logits at each row's last prompt position, len_b - 1, with len_b = lens[b] (device
+ * int32 [B], 1 <= len_b <= prompt_len; NULL: every row has prompt_len tokens).  Positions
+ * [0, prompt_len) of every row are written to the cache; decoding a row continues at pos =
+ * len_b, whose steps overwrite the padded positions before any query can see them, so ragged
+ * prompts share one padded batch.  A row with an invalid length gets NaN logits and raises the
+ * device input flag.  The workspace is gpt_prefill_workspace_bytes(cfg) (the forward's). */
+size_t gpt_prefill_workspace_bytes(const gpt_cfg *cfg); /* 0 if cfg does not validate for decoding */
+gpt_status gpt_prefill(const gpt_cfg *cfg, const gpt_weights *w, const int32_t *tokens,
+                       int32_t prompt_len, const int32_t *lens, void *kv_cache, float *logits,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
 /* Sampling controls of the same section: for each row b of logits [batch, vocab] (device fp32),
  * out[b] (device int32) = the first index of the largest logit if temperature == 0; otherwise
  * the tokens whose logit is >= the top_k-th largest are kept (ties at the threshold stay;

@@ -232,6 +232,18 @@ def test_decode_validation_and_argument_errors(lib):
     assert call(wsb=need - 1) == gf.GPT_E_WORKSPACE
     assert call(cfg=gf.make_cfg(p.with_(batch=33))) == gf.GPT_E_UNSUPPORTED
     assert call(cfg=gf.make_cfg(gptdata.preset("d24gve"))) == gf.GPT_E_UNSUPPORTED
+    pw = gf.gpt_prefill_workspace_bytes(c)
+    assert pw == gf.gpt_workspace_bytes(c) > 0
+    Pf = lambda cfg=c, plen=64, tokens=F, cache=CACHE, logits=F, ws=WS, wsb=pw: lib.gpt_prefill(
+        ctypes.byref(cfg), ctypes.byref(w), tokens, plen, None, cache, logits, ws, wsb, None)
+    assert Pf(plen=0) == gf.GPT_E_INVALID_ARG
+    assert Pf(plen=p.seq_len + 64) == gf.GPT_E_INVALID_ARG
+    assert Pf(plen=100) == gf.GPT_E_UNSUPPORTED           # bf16 forward needs a multiple of 64
+    assert Pf(cache=CACHE + 16) == gf.GPT_E_INVALID_ARG
+    assert Pf(logits=None) == gf.GPT_E_INVALID_ARG
+    assert Pf(tokens=None) == gf.GPT_E_INVALID_ARG
+    assert Pf(wsb=pw - 1) == gf.GPT_E_WORKSPACE
+    assert Pf(cfg=gf.make_cfg(gptdata.preset("d24gve"))) == gf.GPT_E_UNSUPPORTED
     S = lambda **kw: lib.gpt_sample(kw.get("logits", F), kw.get("b", 2), kw.get("v", 100), kw.get("k", 5),
                                     kw.get("t", 1.0), kw.get("u", F), kw.get("out", F), None)
     assert S(logits=None) == gf.GPT_E_INVALID_ARG

@@ -241,3 +241,61 @@ def test_decode_step_graph_replay():
         assert np.array_equal(out.cpu().numpy(), eager[s]), s
         del junk
     assert d2.device_status() == gf.GPT_OK
+
+
+def _prefill_then_decode(p, w, tok, P, lens, n_steps, windows=None):
+    """Prefill positions [0, P) of every row (row b's prompt is its first lens[b] tokens), then
+    decode n_steps more tokens per row from position lens[b].  Returns the prefill logits [B, V]
+    and the decode logits [n_steps, B, V]."""
+    torch = torch_mod()
+    B = tok.shape[0]
+    m = gf.DeviceModel(p, w, batch=B, windows=windows)
+    d = gf.Decoder(m)
+    t_tok = torch.from_numpy(tok.astype(np.int32)).cuda()
+    t_lens = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    logits = torch.empty((B, p.vocab), dtype=torch.float32, device="cuda")
+    assert d.prefill(t_tok[:, :P].contiguous(), P, logits, lens=t_lens) == gf.GPT_OK
+    first = logits.cpu().numpy().astype(np.float64)
+    assert m.device_status() == gf.GPT_OK
+    steps = []
+    for s in range(n_steps):
+        pos = t_lens + s
+        cur = t_tok[torch.arange(B, device="cuda"), pos.long()].contiguous()
+        assert d.step(cur, pos.contiguous(), logits) == gf.GPT_OK
+        steps.append(logits.cpu().numpy().astype(np.float64))
+    torch.cuda.synchronize()
+    assert d.device_status() == gf.GPT_OK
+    return first, np.stack(steps)
+
+
+def test_prefill_then_decode_fp32():
+    """fp32: prompts of 20 and 13 tokens in one padded batch of 20, then 10 decode steps each;
+    every logit vector against the oracle's forward of that row's sequence."""
+    p = gptdata.Preset(name="pre32", n_layer=2, d_model=128, n_head=2, n_kv_head=1, head_dim=64,
+                       mlp_dim=512, vocab=500, seq_len=48, batch=2, dtype="f32", short_window=16,
+                       lambda_range=(0.9, 1.1), mu_range=(0.0, 0.2), seed=61)
+    w, tok, _ = gptdata.make_inputs(p)
+    lens = [20, 13]
+    first, steps = _prefill_then_decode(p, w, tok, 20, lens, 10)
+    ref = oracle.forward(p, params_of(w), tok, want_logits=True)["logits"]   # causal: all positions
+    scale = np.max(np.abs(ref))
+    for b, n in enumerate(lens):
+        assert np.max(np.abs(first[b] - ref[b, n - 1])) / scale <= 1e-3
+        for s in range(10):
+            assert np.max(np.abs(steps[s, b] - ref[b, n + s])) / scale <= 1e-3
+
+
+def test_prefill_then_decode_bf16():
+    """bf16, GQA 4:2, head_dim 128, windows 32 / 64 / full: a padded batch of 64 with prompts of
+    64, 50 and 33 tokens, then 20 decode steps per row."""
+    p = gptdata.Preset(name="pre16", n_layer=3, d_model=256, n_head=4, n_kv_head=2, head_dim=128,
+                       mlp_dim=1024, vocab=1000, seq_len=128, batch=3, dtype="bf16", short_window=32,
+                       lambda_range=(0.9, 1.1), mu_range=(0.0, 0.2), seed=63)
+    w, tok, _ = gptdata.make_inputs(p)
+    windows = [32, 64, 128]
+    lens = [64, 50, 33]
+    first, steps = _prefill_then_decode(p, w, tok, 64, lens, 20, windows=windows)
+    ref = oracle.forward(p, params_of(w), tok, want_logits=True, windows=windows)["logits"]
+    got = np.concatenate([first[None]] + [steps[s][None] for s in range(20)])
+    want = np.stack([np.stack([ref[b, lens[b] - 1 + s] for b in range(3)]) for s in range(21)])
+    _check_bf16_logits(got, want)
