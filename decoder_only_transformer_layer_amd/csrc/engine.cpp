@@ -228,7 +228,10 @@ gpt_status nested_layers(const gpt_cfg* c, const gpt_weights* w, const int32_t* 
   const float2* cs = (const float2*)(ws + L.cs);
   float* ssp = (float*)(ws + L.ssp);
   const int nqk = (H + Hkv) * D, nqkv = (H + 2 * Hkv) * D;
+  // row block 1 (inner, g1) and row block 2 (outer, g2) of a linear: bf16 runs them as one
+  // grouped launch with the outer (longer-K) tiles dispatched first
   auto gemm2 = [&](Epi e, const GemmArgs& g1, const GemmArgs& g2) -> hipError_t {
+    if (bf) return launch_gemm_bf16_pair(e, g2, g1, s);
     hipError_t r = g1.N > 0 ? gemm(bf, e, g1, s) : hipSuccess;
     if (r == hipSuccess && g2.N > 0) r = gemm(bf, e, g2, s);
     return r;

@@ -66,8 +66,9 @@ __device__ __forceinline__ void tile_of(int pid, int nbm, int nbn, int& bm, int&
   bn = in / gsz;
 }
 
+// One output tile (pid = its index in the GEMM's tile order) of C = A B^T with epilogue EPI.
 template <int BM, int BN, int WM, int WN, int EPI>
-__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses device-only types (buffer resources)
   constexpr int NT = WM * WN * 64;
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
 
   const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
   int bm, bn;
-  tile_of<8>(blockIdx.x, nbm, nbn, bm, bn);
+  tile_of<8>(pid, nbm, nbn, bm, bn);
   const int m0 = bm * BM, n0 = bn * BN;
 
   // B row segment holding this column block (segment boundaries are multiples of BN).
@@ -663,6 +664,20 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
 #endif
 }
 
+template <int BM, int BN, int WM, int WN, int EPI>
+__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) {
+  gemm_tile<BM, BN, WM, WN, EPI>(g, blockIdx.x);
+}
+
+// Two independent GEMMs with the same tile shape and epilogue in one launch: blocks
+// [0, nb1) are the tiles of g1, the rest those of g2.  Blocks are dispatched in order, so g1
+// is the one with the longer K and g2's shorter tiles fill in behind it.
+template <int BM, int BN, int WM, int WN, int EPI>
+__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_pair_kernel(GemmArgs g1, GemmArgs g2, int nb1) {
+  if ((int)blockIdx.x < nb1) gemm_tile<BM, BN, WM, WN, EPI>(g1, blockIdx.x);
+  else gemm_tile<BM, BN, WM, WN, EPI>(g2, (int)blockIdx.x - nb1);
+}
+
 template <int BM, int BN, int WM, int WN>
 hipError_t run_bf16(Epi epi, const GemmArgs& a, hipStream_t s) {
   const int grid = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
@@ -684,6 +699,32 @@ hipError_t run_bf16(Epi epi, const GemmArgs& a, hipStream_t s) {
       else GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_CE>), grid, NT, s, a);
       break;
     default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN>
+hipError_t run_bf16_pair(Epi epi, const GemmArgs& a, const GemmArgs& b, hipStream_t s) {
+  const int na = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  const int grid = na + ((b.M + BM - 1) / BM) * ((b.N + BN - 1) / BN);
+  constexpr int NT = WM * WN * 64;
+  if constexpr (WM > 2) {  // the tall wavefront layouts serve the fused q/k/v epilogue only
+    if (epi != EPI_QKV) return hipErrorInvalidValue;
+    GPTK_LAUNCH((gemm_bf16_pair_kernel<BM, BN, WM, WN, EPI_QKV>), grid, NT, s, a, b, na);
+  } else {
+    switch (epi) {
+      case EPI_STORE: GPTK_LAUNCH((gemm_bf16_pair_kernel<BM, BN, WM, WN, EPI_STORE>), grid, NT, s, a, b, na); break;
+      case EPI_RELU2: GPTK_LAUNCH((gemm_bf16_pair_kernel<BM, BN, WM, WN, EPI_RELU2>), grid, NT, s, a, b, na); break;
+      case EPI_RESID:
+        if ((a.xb == nullptr) != (b.xb == nullptr) || (a.lam == nullptr) != (b.lam == nullptr))
+          return hipErrorInvalidValue;  // both halves take the same residual variant
+        if (a.xb == nullptr) GPTK_LAUNCH((gemm_bf16_pair_kernel<BM, BN, WM, WN, EPI_RESID>), grid, NT, s, a, b, na);
+        else if (a.lam == nullptr) GPTK_LAUNCH((gemm_bf16_pair_kernel<BM, BN, WM, WN, EPI_RESID_PROD>), grid, NT, s, a, b, na);
+        else GPTK_LAUNCH((gemm_bf16_pair_kernel<BM, BN, WM, WN, EPI_RESID_MIX>), grid, NT, s, a, b, na);
+        break;
+      case EPI_QKV: GPTK_LAUNCH((gemm_bf16_pair_kernel<BM, BN, WM, WN, EPI_QKV>), grid, NT, s, a, b, na); break;
+      default: return hipErrorInvalidValue;
+    }
   }
   return hipGetLastError();
 }
@@ -927,6 +968,20 @@ hipError_t launch_gemm_bf16(Epi epi, const GemmArgs& a, hipStream_t s) {
     return run_narrow(epi, shift_cols(a, epi, p.split_cols), s);
   }
   return run_main(epi, a, s);
+}
+
+hipError_t launch_gemm_bf16_pair(Epi epi, const GemmArgs& a, const GemmArgs& b, hipStream_t s) {
+  if (a.N <= 0) return launch_gemm_bf16(epi, b, s);
+  if (b.N <= 0) return launch_gemm_bf16(epi, a, s);
+  if (a.K % BK || b.K % BK || a.M <= 0 || b.M <= 0 || epi == EPI_CE) return hipErrorInvalidValue;
+  const bool fused = epi == EPI_QKV && (a.cs != nullptr || b.cs != nullptr);
+  if (fused && (a.cs == nullptr || b.cs == nullptr || a.D != 128 || b.D != 128)) return hipErrorInvalidValue;
+  if (seg_ok(a, 256) && seg_ok(b, 256))
+    return fused ? run_bf16_pair<256, 256, 4, 2>(epi, a, b, s) : run_bf16_pair<256, 256, 2, 4>(epi, a, b, s);
+  if (seg_ok(a, 128) && seg_ok(b, 128))
+    return fused ? run_bf16_pair<256, 128, 4, 1>(epi, a, b, s) : run_bf16_pair<256, 128, 2, 2>(epi, a, b, s);
+  const hipError_t e = launch_gemm_bf16(epi, a, s);
+  return e != hipSuccess ? e : launch_gemm_bf16(epi, b, s);
 }
 
 hipError_t launch_gemm_f32(Epi epi, const GemmArgs& a, hipStream_t s) {

@@ -157,6 +157,9 @@ int gemm_bf16_ce_blocks(int N);
 int gemm_resid_slice_cols(int M, int N);
 // fp32 SIMT GEMM (small configurations).
 hipError_t launch_gemm_f32(Epi epi, const GemmArgs& a, hipStream_t s);
+// bf16: two independent GEMMs (same epilogue kind) in one launch, a's tiles dispatched first
+// (give a the longer K); N <= 0 in either runs the other alone.
+hipError_t launch_gemm_bf16_pair(Epi epi, const GemmArgs& a, const GemmArgs& b, hipStream_t s);
 int gemm_f32_ce_blocks(int N);
 
 // ---- attention (k_attn.hip) ----------------------------------------------------------------
