@@ -258,10 +258,9 @@ gpt_status nested_layers(const gpt_cfg* c, const gpt_weights* w, const int32_t* 
         g[r].q_off = r ? h1 * D : 0;
         g[r].k_off = H * D + (r ? hkv1 * D : 0);
         g[r].v_head_off = r ? hkv1 : 0;
-        if (D == 128) g[r].cs = cs;
+        g[r].cs = cs;  // fused RoPE + QK-norm (head_dim 64 or 128)
       }
       TIMED(tm, GPT_KERNEL_QKV, gemm2(EPI_QKV, g[0], g[1]));
-      if (D != 128) CK(launch_qk_rope_norm(qk, true, nqk, cs, M, T, H + Hkv, D, eps, s));
       TIMED(tm, GPT_KERNEL_ATTENTION, launch_attn_bf16(qk, vt, o, B, T, H, Hkv, D, win,
                                                        c->attn_scale, s));
     } else {
@@ -457,15 +456,13 @@ gpt_status run(const gpt_cfg* c, const gpt_weights* w, const int32_t* tokens,
         GemmArgs g = gemm_args(xn, C, w->wq[l], nqkv, C, M, qk_l, nqk);
         g.B1 = w->wk[l]; g.B2 = w->wv[l]; g.nseg0 = H * D; g.nseg1 = Hkv * D; g.k_off = H * D;
         g.vt = vt; g.T = T; g.D = D; g.Hkv = Hkv; g.nqk = nqk; g.eps = eps;
-        const bool fused = D == 128;
-        if (fused) g.cs = cs;
+        g.cs = cs;  // RoPE + QK-norm in the GEMM epilogue (head_dim 64 or 128)
         if (l > 0) { g.rs_ssp = ssp; g.rs_n = nsl; g.rs_c = (float)C; }  // layer 0 reads normed xn
         if (c->has_ve && c->has_ve[l]) {  // validated: D == 128, so the fused epilogue adds it
           g.ve = (const bf16_t*)w->ve[l]; g.ve_gate = (const bf16_t*)w->ve_gate[l];
           g.tokens = tokens; g.vocab = V;
         }
         TIMED(tm, GPT_KERNEL_QKV, launch_gemm_bf16(EPI_QKV, g, s));
-        if (!fused) CK(launch_qk_rope_norm(qk_l, true, nqk, cs, M, T, H + Hkv, D, eps, s));
         if (pf) {
           char* kc = (char*)pf->cache + (size_t)l * 2 * B * Hkv * pf->T * D * 2;
           CK(launch_cache_fill(true, qk_l, nqk, H * D, vt, 0, B, T, pf->T, Hkv, D, kc,
@@ -780,7 +777,7 @@ gpt_status gpt_op_qkv(const void* xn, const void* wq, const void* wk, const void
       !(eps >= 0.f))
     return GPT_E_INVALID_ARG;
   if (C % 64 || T % 4 || (H * D) % 128 || (Hkv * D) % 128) return GPT_E_UNSUPPORTED;
-  if (cs && (D != 128 || T % 32)) return GPT_E_UNSUPPORTED;  // fused epilogue: whole heads, 32-row groups
+  if (cs && T % 32) return GPT_E_UNSUPPORTED;  // fused epilogue: whole heads, 32-row groups
   const int M = B * T, nqk = (H + Hkv) * D, nqkv = (H + 2 * Hkv) * D;
   GemmArgs g = gemm_args(xn, C, wq, nqkv, C, M, qk, nqk);
   g.B1 = wk; g.B2 = wv; g.nseg0 = H * D; g.nseg1 = Hkv * D; g.k_off = H * D;

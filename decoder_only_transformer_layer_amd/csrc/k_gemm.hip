@@ -466,7 +466,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
     const int wcol0 = n0 + wn * TN;  // q, k and v segments are multiples of TN columns
     if constexpr (TN == 128) {
       if (g.cs != nullptr) {
-        // This wavefront owns one whole 128-wide head (q, k or v) for its TM rows.  Each
+        // This wavefront owns one whole 128-wide head (or two 64-wide ones) for its TM rows.  Each
         // 32-row group is finished in registers, staged through wavefront-private LDS as
         // bf16 and written back with 16-byte stores: q/k rows row-major, v transposed.
         // RoPE pairs (j, j+64) of a q/k head are tiles fn and fn+2 of the same lane; the
@@ -481,7 +481,33 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
         __syncthreads();  // every wavefront is done with the operand tiles
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
-          if (is_qk) {
+          if (is_qk && g.D == 64) {
+            // two 64-wide heads: head h is tiles 2h and 2h+1, RoPE pairs (j, j+32) one lane's
+            // tiles 2h, 2h+1, and each head's sum of squares its own 32-lane butterfly
+#pragma unroll
+            for (int hc = 0; hc < 2; ++hc) {
+              float2 c[8];
+#pragma unroll
+              for (int q = 0; q < 8; ++q) {
+                const int r = 8 * hc + q;
+                const int t = (rbase + fm * 32 + 8 * (r >> 2) + (r & 3)) % g.T;
+                c[q] = g.cs[t * 32 + rl];
+              }
+#pragma unroll
+              for (int q = 0; q < 8; ++q) {
+                const int r = 8 * hc + q;
+                bf16* const sr = stg + (8 * (r >> 2) + 4 * hl + (r & 3)) * LQ + rl;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                  const float u1 = acc[fm][2 * h][r], u2 = acc[fm][2 * h + 1][r];
+                  const float y1 = u1 * c[q].x + u2 * c[q].y, y2 = -u1 * c[q].y + u2 * c[q].x;
+                  const float sc = rsqrtf(sum32(y1 * y1 + y2 * y2) * (1.0f / 64.0f) + g.eps);
+                  sr[64 * h] = (bf16)(y1 * sc);
+                  sr[64 * h + 32] = (bf16)(y2 * sc);
+                }
+              }
+            }
+          } else if (is_qk) {
 #pragma unroll
             for (int hc = 0; hc < 2; ++hc) {
               float2 c[2][8];
@@ -953,7 +979,7 @@ int gemm_resid_slice_cols(int M, int N) {
 hipError_t launch_gemm_bf16(Epi epi, const GemmArgs& a, hipStream_t s) {
   if (a.K % BK || a.M <= 0 || a.N <= 0) return hipErrorInvalidValue;
   if (epi == EPI_CE) return run_bf16<256, 256, 2, 4>(epi, a, s);  // must match gemm_bf16_ce_blocks
-  if (epi == EPI_QKV && a.cs != nullptr && a.D != 128) return hipErrorInvalidValue;
+  if (epi == EPI_QKV && a.cs != nullptr && a.D != 128 && a.D != 64) return hipErrorInvalidValue;
   const Plan p = plan_gemm(epi, a.M, a.N, a.nseg0, a.nseg1, cu_count(), a.lda == a.ldb);
   if (p.tiles == Tiles::T384) return run_bf16<256, 384, 2, 4>(epi, a, s);  // slices of 96 columns
   if (p.tiles == Tiles::T192) return run_bf16<256, 192, 4, 2>(epi, a, s);  // slices of 96 columns
@@ -975,7 +1001,8 @@ hipError_t launch_gemm_bf16_pair(Epi epi, const GemmArgs& a, const GemmArgs& b, 
   if (b.N <= 0) return launch_gemm_bf16(epi, a, s);
   if (a.K % BK || b.K % BK || a.M <= 0 || b.M <= 0 || epi == EPI_CE) return hipErrorInvalidValue;
   const bool fused = epi == EPI_QKV && (a.cs != nullptr || b.cs != nullptr);
-  if (fused && (a.cs == nullptr || b.cs == nullptr || a.D != 128 || b.D != 128)) return hipErrorInvalidValue;
+  if (fused && (a.cs == nullptr || b.cs == nullptr || a.D != b.D || (a.D != 128 && a.D != 64)))
+    return hipErrorInvalidValue;
   if (seg_ok(a, 256) && seg_ok(b, 256))
     return fused ? run_bf16_pair<256, 256, 4, 2>(epi, a, b, s) : run_bf16_pair<256, 256, 2, 4>(epi, a, b, s);
   if (seg_ok(a, 128) && seg_ok(b, 128))

@@ -56,8 +56,7 @@ gpt_status gpt_op_linear(int32_t dtype, int32_t epi, const void *a, const void *
  * xn [B*T, C]; q and k go to qk [B*T, (H+Hkv)*D] row-major, v to vt [B, Hkv, D, T].  If cs (a
  * table from gpt_op_rope_table) is non-NULL, every q and k head is rotated and RMS-normalised
  * (eps inside the root) in fp32 before rounding, exactly as gpt_op_qk_rope_norm would do to the
- * unrounded projection; this fused form needs D == 128 and T % 32 == 0 (else
- * GPT_E_UNSUPPORTED).  C % 64 == 0, T % 4 == 0 and (H*D) % 128 == (Hkv*D) % 128 == 0 always. */
+ * unrounded projection; this fused form needs T % 32 == 0 (else GPT_E_UNSUPPORTED).  C % 64 == 0, T % 4 == 0 and (H*D) % 128 == (Hkv*D) % 128 == 0 always. */
 gpt_status gpt_op_qkv(const void *xn, const void *wq, const void *wk, const void *wv, int32_t B,
                       int32_t T, int32_t C, int32_t H, int32_t Hkv, int32_t D, const float *cs,
                       float eps, void *qk, void *vt, void *stream);

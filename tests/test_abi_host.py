@@ -288,9 +288,9 @@ def test_op_argument_errors(lib):
     assert lib.gpt_op_embed_norm(1, F, F, F, F, F, F, F, 4, 6, 10, 1e-6, F, None) == gf.GPT_E_INVALID_ARG
     assert lib.gpt_op_qk_rope_norm(1, F, 100, F, 4, 4, 1, 256, 1e-6, None) == gf.GPT_E_INVALID_ARG
     assert lib.gpt_op_rope_table(F, 4, 7, 1e5, None) == gf.GPT_E_INVALID_ARG
-    # fused QKV epilogue (RoPE table given): head_dim 128 and T % 32 == 0 only
+    # fused QKV epilogue (RoPE table given): T % 32 == 0 only (head_dim 64 and 128)
     assert lib.gpt_op_qkv(F, F, F, F, 1, 100, 256, 2, 2, 128, F, 1e-6, F, F, None) == gf.GPT_E_UNSUPPORTED
-    assert lib.gpt_op_qkv(F, F, F, F, 1, 128, 256, 2, 2, 64, F, 1e-6, F, F, None) == gf.GPT_E_UNSUPPORTED
+    assert lib.gpt_op_qkv(F, F, F, F, 1, 100, 256, 2, 2, 64, F, 1e-6, F, F, None) == gf.GPT_E_UNSUPPORTED
     assert lib.gpt_op_lm_head_ce_workspace(1, 16, 1) == 0
     need = lib.gpt_op_lm_head_ce_workspace(1, 16, 100)
     assert need > 0
