@@ -153,16 +153,46 @@ __global__ __launch_bounds__(256) void mix_norm_kernel(
   }
 }
 
-// x[i] += sum_k add[k][i] (K-split partial products, summed in split order), 4 elements a thread.
-__global__ __launch_bounds__(256) void add_partials_kernel(float* __restrict__ x,
+// One block per row (few rows, long partial sums): x += sum_k add[k] (K-split partial
+// products, summed in a fixed order), then the optional x0 mix, then xn = RMSNorm(x).  Each
+// thread owns 4-element chunks; the row's sum of squares is reduced over the block.
+template <typename AT>
+__global__ __launch_bounds__(256) void add_mix_norm_kernel(float* __restrict__ x,
                                                            const float* __restrict__ add, int ks,
-                                                           size_t stride, int n4) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= n4) return;
-  f32x4 y = *(const f32x4*)(add + 4 * (size_t)i);
-  for (int k = 1; k < ks; ++k) y += *(const f32x4*)(add + k * stride + 4 * (size_t)i);
-  f32x4* xp = (f32x4*)(x + 4 * (size_t)i);
-  *xp = *xp + y;
+                                                           const float* __restrict__ x0,
+                                                           const float* __restrict__ lam,
+                                                           const float* __restrict__ mu, int layer,
+                                                           bool mix, AT* __restrict__ xn, int M,
+                                                           int C, float eps) {
+  __shared__ float red[4];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  float* xr = x + (size_t)row * C;
+  const float a = mix ? lam[layer] : 1.f, b = mix ? mu[layer] : 0.f;
+  float ss = 0.f;
+  for (int i = 4 * tid; i < C; i += 4 * 256) {
+    // four independent partial sums (splits k = j mod 4) so that the loads overlap
+    f32x4 y4[4] = {};
+    int k = 0;
+    for (; k + 4 <= ks; k += 4) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y4[j] += *(const f32x4*)(add + ((size_t)(k + j) * M + row) * C + i);
+    }
+    for (; k < ks; ++k) y4[k & 3] += *(const f32x4*)(add + ((size_t)k * M + row) * C + i);
+    const f32x4 y = (y4[0] + y4[1]) + (y4[2] + y4[3]);
+    f32x4 v = *(const f32x4*)(xr + i) + y;
+    if (mix) v = a * v + b * *(const f32x4*)(x0 + (size_t)row * C + i);
+    *(f32x4*)(xr + i) = v;
+    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  }
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  const float r = rsqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)C + eps);
+  for (int i = 4 * tid; i < C; i += 4 * 256) {
+    const f32x4 v = *(const f32x4*)(xr + i);
+    float e[4] = {v[0] * r, v[1] * r, v[2] * r, v[3] * r};
+    store4(xn + (size_t)row * C + i, e);
+  }
 }
 
 __global__ void rope_table_kernel(float2* __restrict__ cs, int T, int half, double base) {
@@ -266,12 +296,13 @@ hipError_t launch_embed_norm(const int32_t* tokens, const void* wte, bool wbf16,
 hipError_t launch_mix_norm(float* x, const float* x0, const float* lam, const float* mu, int layer,
                            bool mix, void* xn, bool xbf16, int M, int C, float eps, hipStream_t s,
                            int c1, const float* add, int add_ks) {
-  if (add != nullptr) {  // x += the K-split partial products, summed in split order
-    if (C % 4 || add_ks < 1) return hipErrorInvalidValue;
-    const int n4 = M * C / 4;
-    add_partials_kernel<<<(n4 + 255) / 256, 256, 0, s>>>(x, add, add_ks, (size_t)M * C, n4);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  if (add != nullptr) {  // x += the K-split partial products (summed in split order), fused
+    if (C % 4 || add_ks < 1 || (c1 > 0 && c1 != C)) return hipErrorInvalidValue;
+    if (xbf16)
+      add_mix_norm_kernel<bf16><<<M, 256, 0, s>>>(x, add, add_ks, x0, lam, mu, layer, mix, (bf16*)xn, M, C, eps);
+    else
+      add_mix_norm_kernel<float><<<M, 256, 0, s>>>(x, add, add_ks, x0, lam, mu, layer, mix, (float*)xn, M, C, eps);
+    return hipGetLastError();
   }
   if (c1 <= 0) c1 = C;
   if (C % 4 || c1 % 4 || c1 > C) return hipErrorInvalidValue;
