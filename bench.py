@@ -146,6 +146,53 @@ def decode_bench(gf, p, model, steps):
             "bytes_per_step": weights + kv, "achieved_gbs": round(gbs, 1), "peak_gbs": PEAK_HBM_GBS}
 
 
+def gemm_compare(gf, p, reps=20):
+    """The preset's linear shapes (M = B*T rows) through gpt_op_linear with the plain store
+    epilogue and through torch's F.linear (the ROCm dense-GEMM library) on the same bf16 operands
+    in the same [out, in] weight layout: a yardstick for the GEMM main loop, outside the
+    throughput region."""
+    import torch
+    M, C, F, V = p.batch * p.seq_len, p.d_model, p.mlp_dim, p.vocab
+    qkv = (p.n_head + 2 * p.n_kv_head) * p.head_dim
+    shapes = [("qkv", qkv, C), ("attn_out", C, p.n_head * p.head_dim), ("mlp_up", F, C),
+              ("mlp_down", C, F), ("lm_head", V, C)]
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(0)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out = []
+    for name, N, K in shapes:
+        a = torch.randn(M, K, device=dev, generator=gen).to(torch.bfloat16)
+        wt = (torch.randn(N, K, device=dev, generator=gen) / math.sqrt(K)).to(torch.bfloat16)
+        y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        if gf.gpt_op_linear(gf.GPT_BF16, 0, a, wt, M, N, K, y) != gf.GPT_OK:
+            raise RuntimeError(f"gpt_op_linear failed on {name}")
+        ref = torch.nn.functional.linear(a, wt)
+        torch.cuda.synchronize()
+        rel = ((y.float() - ref.float()).abs().max() / ref.float().abs().max()).item()
+        t_own = timed(lambda: gf.gpt_op_linear(gf.GPT_BF16, 0, a, wt, M, N, K, y))
+        t_lib = timed(lambda: torch.nn.functional.linear(a, wt))
+        fl = 2.0 * M * N * K
+        print(f"[bench] gemm {name} {M}x{N}x{K}: own {t_own * 1e3:.1f} us ({fl / t_own / 1e9:.0f} TF/s), "
+              f"library {t_lib * 1e3:.1f} us ({fl / t_lib / 1e9:.0f} TF/s), max rel diff {rel:.1e}",
+              file=sys.stderr, flush=True)
+        out.append({"gemm": name, "M": M, "N": N, "K": K, "own_us": round(t_own * 1e3, 1),
+                    "library_us": round(t_lib * 1e3, 1)})
+        del a, wt, y, ref
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -162,6 +209,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy (a known-size reference "
                          "for HBM traffic counters)")
+    ap.add_argument("--gemm-compare", action="store_true",
+                    help="also time the preset's linear shapes (store epilogue) against torch's "
+                         "F.linear")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -274,6 +324,8 @@ def main():
     if args.decode_steps > 0 and not nested and not getattr(p, "looped", False) and not p.value_embeds:
         dec = decode_bench(gf, p, model, args.decode_steps)
 
+    gcmp = gemm_compare(gf, p) if args.gemm_compare and p.dtype == "bf16" else None
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -318,6 +370,7 @@ def main():
                      "avg_launch_us": dom["avg_us"], "flops_per_launch": fpl[dk]},
         "kernels": kern,
         "decode": dec,
+        "gemm_vs_library": gcmp,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

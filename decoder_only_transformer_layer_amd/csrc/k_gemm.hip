@@ -32,6 +32,10 @@ constexpr int BK = 64;
 // Kernel-internal residual variants: + bf16 copy and row sums of squares; + next-layer mix.
 constexpr int EPI_RESID_PROD = 5, EPI_RESID_MIX = 6;
 template <int E> constexpr bool is_resid = E == EPI_RESID || E == EPI_RESID_PROD || E == EPI_RESID_MIX;
+// Kernel-internal cross-entropy variant that also writes the raw logits (a separate kernel:
+// the extra stores' addressing would otherwise cost the main loop registers).
+constexpr int EPI_CE_LOGITS = 7;
+template <int E> constexpr bool is_ce = E == EPI_CE || E == EPI_CE_LOGITS;
 
 // s_waitcnt immediate waiting until at most n vector-memory operations are outstanding
 // (gfx9 encoding: vmcnt[3:0] at bits 3:0 and vmcnt[5:4] at bits 15:14; expcnt and lgkmcnt
@@ -633,7 +637,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
           }
       }
     }
-  } else if constexpr (EPI == EPI_CE) {
+  } else if constexpr (is_ce<EPI>) {
     // Per row: sum over this block's columns of exp(zhat - cap).  Each lane sums its FN
     // columns, a 32-lane butterfly sums a wavefront's TN columns, and the WN wavefronts that
     // share a row combine through LDS (free after the main loop's final barrier).  Targets of
@@ -665,7 +669,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
         }
     };
     if (interior) ce(std::false_type{}); else ce(std::true_type{});
-    if (g.logits != nullptr) {  // raw logits (softcapped afterwards by the logits pass)
+    if constexpr (EPI == EPI_CE_LOGITS) {  // raw logits (softcapped afterwards by the logits pass)
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -718,11 +722,15 @@ hipError_t run_bf16(Epi epi, const GemmArgs& a, hipStream_t s) {
       else GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_RESID_MIX>), grid, NT, s, a);
       break;
     case EPI_QKV:
-    case EPI_CE:
-      // the tile plan gives these epilogues 256-wide or 128-wide tiles only
+      // the tile plan gives this epilogue 256-wide or 128-wide tiles only
       if constexpr (BN != 256 && BN != 128) return hipErrorInvalidValue;
-      else if (epi == EPI_QKV) GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_QKV>), grid, NT, s, a);
-      else GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_CE>), grid, NT, s, a);
+      else GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_QKV>), grid, NT, s, a);
+      break;
+    case EPI_CE:
+      // 256x384 tiles only: the partial-sum layout has one column per 384-wide block
+      if constexpr (BN != 384) return hipErrorInvalidValue;
+      else if (a.logits == nullptr) GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_CE>), grid, NT, s, a);
+      else GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_CE_LOGITS>), grid, NT, s, a);
       break;
     default: return hipErrorInvalidValue;
   }
@@ -970,7 +978,7 @@ Plan plan_gemm(Epi epi, int M, int N, int nseg0, int nseg1, int ncu, bool same_l
 
 thread_local LaunchEvents launch_events;
 
-int gemm_bf16_ce_blocks(int N) { return (N + 255) / 256; }
+int gemm_bf16_ce_blocks(int N) { return (N + 383) / 384; }
 
 int gemm_resid_slice_cols(int M, int N) {
   return plan_gemm(EPI_RESID, M, N, N, 0, cu_count()).tiles == Tiles::T256 ? 64 : 96;
@@ -978,7 +986,10 @@ int gemm_resid_slice_cols(int M, int N) {
 
 hipError_t launch_gemm_bf16(Epi epi, const GemmArgs& a, hipStream_t s) {
   if (a.K % BK || a.M <= 0 || a.N <= 0) return hipErrorInvalidValue;
-  if (epi == EPI_CE) return run_bf16<256, 256, 2, 4>(epi, a, s);  // must match gemm_bf16_ce_blocks
+  if (epi == EPI_CE) {  // 256x384 tiles, as gemm_bf16_ce_blocks counts them
+    if (a.lda != a.ldb) return hipErrorInvalidValue;
+    return run_bf16<256, 384, 2, 4>(epi, a, s);
+  }
   if (epi == EPI_QKV && a.cs != nullptr && a.D != 128 && a.D != 64) return hipErrorInvalidValue;
   const Plan p = plan_gemm(epi, a.M, a.N, a.nseg0, a.nseg1, cu_count(), a.lda == a.ldb);
   if (p.tiles == Tiles::T384) return run_bf16<256, 384, 2, 4>(epi, a, s);  // slices of 96 columns
