@@ -239,6 +239,31 @@ def test_attention_bf16(H, Hkv, D, window):
         assert err.mean() < 3e-3, (b, err.mean())
 
 
+@pytest.mark.parametrize("B,H,Hkv,window", [(2, 16, 16, 256), (4, 12, 4, 5000)])
+def test_attention_bf16_many_heads(B, H, Hkv, window):
+    """Grids of many (batch, head) pairs: 32 pairs with a 256-key window (every query block
+    spans a window edge), and 48 pairs with GQA (3 query heads per KV head) and full windows.
+    Every head against the oracle."""
+    torch = torch_mod()
+    rng = np.random.default_rng(B * 100 + H)
+    T, D = 512, 64
+    q, k, v = _attn_inputs(rng, B, T, H, Hkv, D)
+    qk, qk64 = bf16_dev(np.concatenate([q, k], axis=2).reshape(B * T, (H + Hkv) * D).astype(np.float32))
+    vt, vt64 = bf16_dev(np.ascontiguousarray(v.transpose(0, 2, 3, 1)).astype(np.float32))
+    o = empty((B * T, H * D), "bf16")
+    scale = 1.0 / math.sqrt(D)
+    _ok(gf.gpt_op_attention(BF, qk, vt, o, B, T, H, Hkv, D, window, scale), "attention")
+    _sync()
+    got = to_host(o).reshape(B, T, H, D)
+    x = qk64.reshape(B, T, H + Hkv, D)
+    v64 = vt64.transpose(0, 3, 1, 2)
+    for b in range(B):
+        ref = oracle.attention(x[b, :, :H], x[b, :, H:], v64[b], window, scale)
+        err = np.abs(got[b] - ref)
+        assert err.max() < 2.5e-2, (b, err.max())
+        assert err.mean() < 3e-3, (b, err.mean())
+
+
 def test_attention_sharp_scale_and_f32():
     """Page 5's reading of the logit scale (1.15^2, no 1/sqrt(d)) and the fp32 kernel."""
     torch = torch_mod()
