@@ -56,11 +56,12 @@ __device__ __forceinline__ void gv_apply(const GvEpi& e, int b, int n, float v) 
 // fixed order.  With KS > 1 the block stores its tile as partial[ks][b][n] and the consumer of
 // the product sums the KS tiles in split order (no block waits on another); with KS = 1 the
 // epilogue is applied here.
-__global__ __launch_bounds__(GV_WAVES * 64) void gemv_bf16_kernel(
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(
     const bf16* __restrict__ act, int lda, int B, const bf16* __restrict__ W0,
     const bf16* __restrict__ W1, const bf16* __restrict__ W2, int nseg0, int nseg1, int N, int K,
     int KS, float* __restrict__ partial, GvEpi e) {
-  __shared__ float red[GV_WAVES][64 * 16];
+  __shared__ float red[NW][64 * 16];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int rb = blockIdx.x / KS, ks = blockIdx.x % KS;
   const int n0 = rb * GV_ROWS;
@@ -78,27 +79,41 @@ __global__ __launch_bounds__(GV_WAVES * 64) void gemv_bf16_kernel(
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
   const bf16x8 zero = {};
-  for (int st = s0 + wid; st < s1; st += GV_WAVES) {
+  // This wavefront's K steps s0 + wid, s0 + wid + NW, ...: double-buffered, the loads of
+  // the next step issued before the MFMAs of the current one (two named register sets, loop
+  // unrolled by two).
+  bf16x8 wa0[4], xb0[4], wa1[4], xb1[4];
+  auto load = [&](int st, bf16x8 (&wa)[4], bf16x8 (&xb)[4]) {
     const int kb = st * GV_KB;
-    bf16x8 wa[4], xb[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       wa[m] = row_ok ? *(const bf16x8*)(wp + kb + 8 * m) : zero;
       xb[m] = b_ok ? *(const bf16x8*)(ap + kb + 8 * m) : zero;
     }
+  };
+  auto mma = [&](const bf16x8 (&wa)[4], const bf16x8 (&xb)[4]) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[m], xb[m], acc, 0, 0, 0);
+  };
+  int st = s0 + wid;
+  if (st < s1) load(st, wa0, xb0);
+  for (; st < s1; st += 2 * NW) {
+    if (st + NW < s1) load(st + NW, wa1, xb1);
+    mma(wa0, xb0);
+    if (st + NW >= s1) break;
+    if (st + 2 * NW < s1) load(st + 2 * NW, wa0, xb0);
+    mma(wa1, xb1);
   }
 #pragma unroll
   for (int r = 0; r < 16; ++r) red[wid][lane * 16 + r] = acc[r];
   __syncthreads();
-  float v[64 * 16 / (GV_WAVES * 64)];
+  float v[64 * 16 / (NW * 64)];
 #pragma unroll
-  for (int i = 0; i < 64 * 16 / (GV_WAVES * 64); ++i) {
-    const int idx = threadIdx.x + i * GV_WAVES * 64;
+  for (int i = 0; i < 64 * 16 / (NW * 64); ++i) {
+    const int idx = threadIdx.x + i * NW * 64;
     float t = 0.f;
 #pragma unroll
-    for (int w = 0; w < GV_WAVES; ++w) t += red[w][idx];
+    for (int w = 0; w < NW; ++w) t += red[w][idx];
     v[i] = t;
   }
   auto coords = [&](int idx, int& b, int& n) {
@@ -108,17 +123,17 @@ __global__ __launch_bounds__(GV_WAVES * 64) void gemv_bf16_kernel(
   };
   if (KS > 1) {
 #pragma unroll
-    for (int i = 0; i < 64 * 16 / (GV_WAVES * 64); ++i) {
+    for (int i = 0; i < 64 * 16 / (NW * 64); ++i) {
       int b, n;
-      coords(threadIdx.x + i * GV_WAVES * 64, b, n);
+      coords(threadIdx.x + i * NW * 64, b, n);
       if (b < B && n < N) partial[((size_t)ks * B + b) * N + n] = v[i];
     }
     return;
   }
 #pragma unroll
-  for (int i = 0; i < 64 * 16 / (GV_WAVES * 64); ++i) {
+  for (int i = 0; i < 64 * 16 / (NW * 64); ++i) {
     int b, n;
-    coords(threadIdx.x + i * GV_WAVES * 64, b, n);
+    coords(threadIdx.x + i * NW * 64, b, n);
     if (b < B && n < N) gv_apply<bf16>(e, b, n, v[i]);
   }
 }
@@ -150,6 +165,7 @@ __global__ __launch_bounds__(256) void gemv_f32_kernel(const float* __restrict__
 // cache at position pos[b].  One wavefront per (row, head) of the H + 2*Hkv heads; lane p
 // rotates the pair (p, p + D/2).  The angle is formed as the forward's RoPE table forms it
 // (fp64 power, cosine and sine, rounded to fp32).
+constexpr int RA_KB = 16;  // partial tiles loaded together
 template <typename AT>
 __global__ __launch_bounds__(256) void rope_append_kernel(
     const float* __restrict__ y, int ldy, int KS, size_t kstride, const int32_t* __restrict__ pos,
@@ -166,15 +182,36 @@ __global__ __launch_bounds__(256) void rope_append_kernel(
     return;
   }
   const float* src = y + (size_t)b * ldy + (size_t)hh * D;
-  auto val = [&](int d) {  // the product's value: its K-split partial tiles summed in order
-    float v = src[d];
-    for (int k = 1; k < KS; ++k) v += src[k * kstride + d];
-    return v;
+  // The product's values at d0 and d1 (< D; d1 = -1: none): their K-split partial tiles summed
+  // in split order, all tiles loaded before the first add so that the loads overlap.
+  auto val2 = [&](int d0, int d1, float& v0, float& v1) {
+    v0 = 0.f;
+    v1 = 0.f;
+    for (int k0 = 0; k0 < KS; k0 += RA_KB) {
+      float t0[RA_KB], t1[RA_KB];
+#pragma unroll
+      for (int k = 0; k < RA_KB; ++k)
+        if (k0 + k < KS) {
+          t0[k] = src[(size_t)(k0 + k) * kstride + d0];
+          t1[k] = d1 >= 0 ? src[(size_t)(k0 + k) * kstride + d1] : 0.f;
+        }
+#pragma unroll
+      for (int k = 0; k < RA_KB; ++k)
+        if (k0 + k < KS) {
+          v0 = (k0 + k == 0) ? t0[k] : v0 + t0[k];
+          v1 = (k0 + k == 0) ? t1[k] : v1 + t1[k];
+        }
+    }
   };
   if (hh >= H + Hkv) {  // v: copied into the cache
     const int g = hh - H - Hkv;
     AT* dst = vc + (((size_t)b * Hkv + g) * T + t) * D;
-    for (int d = lane; d < D; d += 64) dst[d] = from_f32<AT>(val(d));
+    for (int d = lane; d < D; d += 128) {
+      float v0, v1;
+      val2(d, d + 64 < D ? d + 64 : -1, v0, v1);
+      dst[d] = from_f32<AT>(v0);
+      if (d + 64 < D) dst[d + 64] = from_f32<AT>(v1);
+    }
     return;
   }
   float y1 = 0.f, y2 = 0.f;
@@ -182,7 +219,8 @@ __global__ __launch_bounds__(256) void rope_append_kernel(
     const double omega = pow(base, -2.0 * (double)lane / (double)D);
     const double phi = (double)t * omega;
     const float c = (float)cos(phi), s = (float)sin(phi);
-    const float u1 = val(lane), u2 = val(lane + half);
+    float u1, u2;
+    val2(lane, lane + half, u1, u2);
     y1 = u1 * c + u2 * s;
     y2 = -u1 * s + u2 * c;
   }
@@ -557,9 +595,9 @@ hipError_t launch_gemv(bool bf, int kind, const void* act, int lda, int B, const
   if (bf) {
     if (KS > 1 && !partial) return hipErrorInvalidValue;
     const int grid = (N + GV_ROWS - 1) / GV_ROWS * KS;
-    gemv_bf16_kernel<<<grid, GV_WAVES * 64, 0, s>>>((const bf16*)act, lda, B, (const bf16*)W0,
-                                                    (const bf16*)W1, (const bf16*)W2, nseg0, nseg1,
-                                                    N, K, KS, partial, e);
+    gemv_bf16_kernel<GV_WAVES><<<grid, GV_WAVES * 64, 0, s>>>(
+        (const bf16*)act, lda, B, (const bf16*)W0, (const bf16*)W1, (const bf16*)W2, nseg0, nseg1,
+        N, K, KS, partial, e);
   } else {
     if (KS != 1) return hipErrorInvalidValue;
     gemv_f32_kernel<<<(N + 3) / 4, 256, 0, s>>>((const float*)act, lda, B, (const float*)W0,

@@ -155,43 +155,62 @@ __global__ __launch_bounds__(256) void mix_norm_kernel(
 
 // One block per row (few rows, long partial sums): x += sum_k add[k] (K-split partial
 // products, summed in a fixed order), then the optional x0 mix, then xn = RMSNorm(x).  Each
-// thread owns 4-element chunks; the row's sum of squares is reduced over the block.
+// thread owns up to AMN_NP 4-element chunks (one when C <= 4 * blockDim).  A chunk's partial
+// products are loaded AMN_KB at a time, all before any is added, so their round trips overlap;
+// the sum runs over four interleaved accumulators (split k into k mod 4, combined pairwise), and
+// the updated chunks stay in registers through the block's sum of squares.
+constexpr int AMN_KB = 32, AMN_NP = 2, AMN_NTH = 512;
 template <typename AT>
-__global__ __launch_bounds__(256) void add_mix_norm_kernel(float* __restrict__ x,
-                                                           const float* __restrict__ add, int ks,
-                                                           const float* __restrict__ x0,
-                                                           const float* __restrict__ lam,
-                                                           const float* __restrict__ mu, int layer,
-                                                           bool mix, AT* __restrict__ xn, int M,
-                                                           int C, float eps) {
-  __shared__ float red[4];
-  const int row = blockIdx.x, tid = threadIdx.x;
+__global__ __launch_bounds__(AMN_NTH) void add_mix_norm_kernel(float* __restrict__ x,
+                                                            const float* __restrict__ add, int ks,
+                                                            const float* __restrict__ x0,
+                                                            const float* __restrict__ lam,
+                                                            const float* __restrict__ mu, int layer,
+                                                            bool mix, AT* __restrict__ xn, int M,
+                                                            int C, float eps) {
+  __shared__ float red[AMN_NTH / 64];
+  const int row = blockIdx.x, tid = threadIdx.x, nth = blockDim.x;
   float* xr = x + (size_t)row * C;
   const float a = mix ? lam[layer] : 1.f, b = mix ? mu[layer] : 0.f;
+  f32x4 v[AMN_NP];
   float ss = 0.f;
-  for (int i = 4 * tid; i < C; i += 4 * 256) {
-    // four independent partial sums (splits k = j mod 4) so that the loads overlap
-    f32x4 y4[4] = {};
-    int k = 0;
-    for (; k + 4 <= ks; k += 4) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) y4[j] += *(const f32x4*)(add + ((size_t)(k + j) * M + row) * C + i);
+  for (int p = 0; p < AMN_NP; ++p) {
+    const int i = 4 * (tid + p * nth);
+    if (i < C) {
+      const f32x4 xv = *(const f32x4*)(xr + i);
+      const f32x4 x0v = mix ? *(const f32x4*)(x0 + (size_t)row * C + i) : f32x4{};
+      f32x4 y4[4] = {};
+      for (int k0 = 0; k0 < ks; k0 += AMN_KB) {
+        f32x4 t[AMN_KB];
+#pragma unroll
+        for (int k = 0; k < AMN_KB; ++k)
+          if (k0 + k < ks) t[k] = *(const f32x4*)(add + ((size_t)(k0 + k) * M + row) * C + i);
+#pragma unroll
+        for (int k = 0; k < AMN_KB; ++k)
+          if (k0 + k < ks) y4[k & 3] += t[k];  // AMN_KB is a multiple of 4: (k0 + k) & 3 == k & 3
+      }
+      const f32x4 y = (y4[0] + y4[1]) + (y4[2] + y4[3]);
+      f32x4 w = xv + y;
+      if (mix) w = a * w + b * x0v;
+      *(f32x4*)(xr + i) = w;
+      ss += w[0] * w[0] + w[1] * w[1] + w[2] * w[2] + w[3] * w[3];
+      v[p] = w;
     }
-    for (; k < ks; ++k) y4[k & 3] += *(const f32x4*)(add + ((size_t)k * M + row) * C + i);
-    const f32x4 y = (y4[0] + y4[1]) + (y4[2] + y4[3]);
-    f32x4 v = *(const f32x4*)(xr + i) + y;
-    if (mix) v = a * v + b * *(const f32x4*)(x0 + (size_t)row * C + i);
-    *(f32x4*)(xr + i) = v;
-    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
   }
   ss = wave_sum(ss);
   if ((tid & 63) == 0) red[tid >> 6] = ss;
   __syncthreads();
-  const float r = rsqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)C + eps);
-  for (int i = 4 * tid; i < C; i += 4 * 256) {
-    const f32x4 v = *(const f32x4*)(xr + i);
-    float e[4] = {v[0] * r, v[1] * r, v[2] * r, v[3] * r};
-    store4(xn + (size_t)row * C + i, e);
+  float tot = 0.f;
+  for (int j = 0; j < (nth >> 6); ++j) tot += red[j];
+  const float r = rsqrtf(tot / (float)C + eps);
+#pragma unroll
+  for (int p = 0; p < AMN_NP; ++p) {
+    const int i = 4 * (tid + p * nth);
+    if (i < C) {
+      float e[4] = {v[p][0] * r, v[p][1] * r, v[p][2] * r, v[p][3] * r};
+      store4(xn + (size_t)row * C + i, e);
+    }
   }
 }
 
@@ -297,11 +316,12 @@ hipError_t launch_mix_norm(float* x, const float* x0, const float* lam, const fl
                            bool mix, void* xn, bool xbf16, int M, int C, float eps, hipStream_t s,
                            int c1, const float* add, int add_ks) {
   if (add != nullptr) {  // x += the K-split partial products (summed in split order), fused
-    if (C % 4 || add_ks < 1 || (c1 > 0 && c1 != C)) return hipErrorInvalidValue;
+    if (C % 4 || add_ks < 1 || (c1 > 0 && c1 != C) || C > 4 * AMN_NTH * AMN_NP) return hipErrorInvalidValue;
+    const int chunks = C / 4, nth = chunks <= AMN_NTH ? (chunks + 63) / 64 * 64 : AMN_NTH;
     if (xbf16)
-      add_mix_norm_kernel<bf16><<<M, 256, 0, s>>>(x, add, add_ks, x0, lam, mu, layer, mix, (bf16*)xn, M, C, eps);
+      add_mix_norm_kernel<bf16><<<M, nth, 0, s>>>(x, add, add_ks, x0, lam, mu, layer, mix, (bf16*)xn, M, C, eps);
     else
-      add_mix_norm_kernel<float><<<M, 256, 0, s>>>(x, add, add_ks, x0, lam, mu, layer, mix, (float*)xn, M, C, eps);
+      add_mix_norm_kernel<float><<<M, nth, 0, s>>>(x, add, add_ks, x0, lam, mu, layer, mix, (float*)xn, M, C, eps);
     return hipGetLastError();
   }
   if (c1 <= 0) c1 = C;
