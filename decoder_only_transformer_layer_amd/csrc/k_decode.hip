@@ -49,7 +49,7 @@ __device__ __forceinline__ void gv_apply(const GvEpi& e, int b, int n, float v) 
 
 // bf16 weights and activations: y[b][n] = sum_k act[b][k] W[n][k] for b < B <= 32.  A block
 // owns 32 weight rows (three row segments W0 | W1 | W2 with boundaries on multiples of 32) and
-// one of KS contiguous ranges of 64-column K steps; its wavefronts take the range's steps in
+// one of KS contiguous ranges of 64-column K steps; its NW wavefronts (GV_WAVES at launch) take the range's steps in
 // turn.  In a step, lane l (row l % 32, half g = l / 32) holds W[row][kb + 32g + 8m .. +8] for
 // MFMA m = 0..3 and the batch operand holds act[b = l % 32][the same columns], so each MFMA sums
 // 16 columns and the four cover the step.  The wavefronts' tiles are summed through LDS in a
