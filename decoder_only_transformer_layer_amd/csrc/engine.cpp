@@ -187,7 +187,7 @@ gpt_status lm_head_ce(bool bf, const void* xf, const void* wu, const int32_t* ta
   g.targets = targets; g.partial = partial; g.tgt_logit = tgt; g.logits = logits;
   g.nnb = nnb; g.cap = cap;
   TIMED(tm, GPT_KERNEL_LM_HEAD, gemm(bf, EPI_CE, g, s));
-  if (logits) CK(launch_softcap(logits, (size_t)M * V, cap, s));
+  if (logits && !bf) CK(launch_softcap(logits, (size_t)M * V, cap, s));  // bf16: written softcapped
   if (targets) {
     CK(launch_ce_finalize(partial, nnb, tgt, targets, tokens, M, V, cap, loss, flags, s));
     CK(launch_ce_mean(loss, targets, M, mean, s));

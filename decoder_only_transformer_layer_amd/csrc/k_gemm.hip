@@ -6,7 +6,7 @@
 //   QKV    - q/k columns row-major, v columns transposed to [B][Hkv][D][T] (bf16 path)
 //   CE     - softcap, per-row partial sum of exp(zhat - cap) per column block, and the target's
 //            raw logit; the [M, V] logits are never written unless the caller asks for them
-//            (then raw, softcapped afterwards by launch_softcap).
+//            (then already softcapped).
 //
 // Sources: "The Mathematics of Karpathy's nanochat", sections "Causal Self-Attention"
 // (projections, no bias), "Output Projection", "Feed-Forward Network (MLP)" (ReLU^2, 4x),
@@ -46,12 +46,6 @@ constexpr int lgkmcnt_0 = 0xC07F;
 
 __device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-// exp(zhat - cap) for zhat = cap * tanh(z / cap), written without cancellation:
-// zhat - cap = -2 cap / (1 + exp(2 z / cap)).
-__device__ __forceinline__ float ce_term(float z, float two_over_cap_log2e, float m2cap_log2e) {
-  const float e = exp2_fast(z * two_over_cap_log2e);
-  return exp2_fast(m2cap_log2e * rcp_fast(1.0f + e));
-}
 
 // Block -> output tile.  Workgroups are dispatched round-robin over the 8 XCDs (each with its
 // own L2), so block ids are first regrouped so that XCD x owns a contiguous 1/8 of the tile
@@ -642,15 +636,23 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
     // columns, a 32-lane butterfly sums a wavefront's TN columns, and the WN wavefronts that
     // share a row combine through LDS (free after the main loop's final barrier).  Targets of
     // the block's rows are staged in LDS so that the target-logit pick-up is a predicated store.
+    // With q = 1 / (1 + exp(2z / cap)): zhat = cap (1 - 2q) and exp(zhat - cap) = exp(-2 cap q),
+    // the latter without the cancellation of subtracting cap from zhat.
+    // EPI_CE_LOGITS also writes zhat: each 32-row group of the wavefront's tile is staged in LDS
+    // past red and tgt and written back row-contiguous, 16 bytes per lane.
+    constexpr bool LOGITS = EPI == EPI_CE_LOGITS;
     float* red = (float*)lds;                    // [BM][WN]
     int* tgt = (int*)(lds) + BM * WN;            // [BM]
+    constexpr int LDP = TN + 4, STG0 = (BM * WN + BM + 63) / 64 * 64;  // staging pitch, offset (floats)
+    static_assert(!LOGITS || (STG0 + WM * WN * 32 * LDP) * 4 <= (int)sizeof(lds), "logits staging exceeds LDS");
+    float* const stg = (float*)lds + STG0 + wid * 32 * LDP;
     const float cap = g.cap;
     const float k1 = 2.0f / cap * GPT_LOG2E, k2 = -2.0f * cap * GPT_LOG2E;
     for (int i = tid; i < BM; i += NT) tgt[i] = (g.targets != nullptr && m0 + i < M) ? g.targets[m0 + i] : -1;
     __syncthreads();
     auto ce = [&](auto checked) {
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
+      for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int rloc = wm * TM + fm * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
@@ -659,27 +661,42 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
 #pragma unroll
           for (int fn = 0; fn < FN; ++fn) {
             const float z = acc[fm][fn][r];
-            const float e = ce_term(z, k1, k2);
-            s += (!decltype(checked)::value || cbase + fn * 32 < N) ? e : 0.f;
+            const float q = rcp_fast(1.0f + exp2_fast(z * k1));
+            s += (!decltype(checked)::value || cbase + fn * 32 < N) ? exp2_fast(k2 * q) : 0.f;
             // raw logit; the loss kernel applies the softcap to it
             if (ycol == fn * 32) g.tgt_logit[m0 + rloc] = z;
+            if constexpr (LOGITS) stg[(8 * (r >> 2) + 4 * hl + (r & 3)) * LDP + fn * 32 + rl] = cap - 2.0f * cap * q;
           }
           s = sum32(s);
           if (rl == 0) red[rloc * WN + wn] = s;
         }
+        if constexpr (LOGITS) {
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          constexpr int CPR = TN / 4;  // 4-float chunks per staged row
+          const bool vec = (N & 3) == 0;
+#pragma unroll
+          for (int k = 0; k < 32 * CPR / 64; ++k) {
+            const int idx = lane + 64 * k, lr = idx / CPR, ch = idx % CPR;
+            const int row = m0 + wm * TM + fm * 32 + lr, col = n0 + wn * TN + ch * 4;
+            if (row < M) {
+              const f32x4 v = *(const f32x4*)(stg + lr * LDP + ch * 4);
+              float* const op = g.logits + (size_t)row * N + col;
+              if (vec && col + 4 <= N) {
+                *(f32x4*)op = v;
+              } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  if (col + e < N) op[e] = v[e];
+              }
+            }
+          }
+          __builtin_amdgcn_wave_barrier();  // reads of this group precede the next group's writes
+        }
+      }
     };
     if (interior) ce(std::false_type{}); else ce(std::true_type{});
-    if constexpr (EPI == EPI_CE_LOGITS) {  // raw logits (softcapped afterwards by the logits pass)
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = rbase + fm * 32 + 8 * (r >> 2) + (r & 3), col = cbase + fn * 32;
-            if (row < M && col < N) g.logits[(size_t)row * N + col] = acc[fm][fn][r];
-          }
-    }
     __syncthreads();
     for (int rloc = tid; rloc < BM; rloc += NT) {
       const int row = m0 + rloc;
@@ -727,10 +744,17 @@ hipError_t run_bf16(Epi epi, const GemmArgs& a, hipStream_t s) {
       else GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_QKV>), grid, NT, s, a);
       break;
     case EPI_CE:
-      // 256x384 tiles only: the partial-sum layout has one column per 384-wide block
-      if constexpr (BN != 384) return hipErrorInvalidValue;
-      else if (a.logits == nullptr) GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_CE>), grid, NT, s, a);
-      else GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_CE_LOGITS>), grid, NT, s, a);
+      // 384-wide blocks only (the partial-sum layout has one column per block): 256-row tiles
+      // for the loss alone, 128-row tiles when the logits are written too
+      if constexpr (BN != 384) {
+        return hipErrorInvalidValue;
+      } else if constexpr (BM == 256) {
+        if (a.logits != nullptr) return hipErrorInvalidValue;
+        GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_CE>), grid, NT, s, a);
+      } else {
+        if (a.logits == nullptr) return hipErrorInvalidValue;
+        GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_CE_LOGITS>), grid, NT, s, a);
+      }
       break;
     default: return hipErrorInvalidValue;
   }
@@ -986,9 +1010,11 @@ int gemm_resid_slice_cols(int M, int N) {
 
 hipError_t launch_gemm_bf16(Epi epi, const GemmArgs& a, hipStream_t s) {
   if (a.K % BK || a.M <= 0 || a.N <= 0) return hipErrorInvalidValue;
-  if (epi == EPI_CE) {  // 256x384 tiles, as gemm_bf16_ce_blocks counts them
+  if (epi == EPI_CE) {  // 384-wide column blocks, as gemm_bf16_ce_blocks counts them
     if (a.lda != a.ldb) return hipErrorInvalidValue;
-    return run_bf16<256, 384, 2, 4>(epi, a, s);
+    // Writing the logits too takes 128-row tiles: the staged stores' addressing would otherwise
+    // push the 256-row tiles' main loop past the register file.
+    return a.logits != nullptr ? run_bf16<128, 384, 2, 4>(epi, a, s) : run_bf16<256, 384, 2, 4>(epi, a, s);
   }
   if (epi == EPI_QKV && a.cs != nullptr && a.D != 128 && a.D != 64) return hipErrorInvalidValue;
   const Plan p = plan_gemm(epi, a.M, a.N, a.nseg0, a.nseg1, cu_count(), a.lda == a.ldb);
