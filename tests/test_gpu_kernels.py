@@ -292,8 +292,10 @@ def test_attention_sharp_scale_and_f32():
 # ----------------------------------------------------------------------------- lm_head + CE
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("M,C,V", [(300, 256, 1000), (256, 128, 4096)])
+@pytest.mark.parametrize("M,C,V", [(300, 256, 1000), (256, 128, 4096), (257, 192, 1003)])
 def test_lm_head_ce(dtype, M, C, V):
+    """(257, 192, 1003): ragged rows, and a vocabulary that is neither a multiple of the
+    384-wide column blocks nor of 4 (the logits' row pitch takes the element-wise stores)."""
     torch = torch_mod()
     rng = np.random.default_rng(M + V)
     xf_h = oracle.rms_norm(rng.standard_normal((M, C)), 0).astype(np.float32)
