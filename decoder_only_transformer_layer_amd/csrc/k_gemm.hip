@@ -766,7 +766,7 @@ hipError_t run_bf16_pair(Epi epi, const GemmArgs& a, const GemmArgs& b, hipStrea
   const int na = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   const int grid = na + ((b.M + BM - 1) / BM) * ((b.N + BN - 1) / BN);
   constexpr int NT = WM * WN * 64;
-  if constexpr (WM > 2) {  // the tall wavefront layouts serve the fused q/k/v epilogue only
+  if constexpr (WM > 2 && BN != 192) {  // tall 256/128-wide layouts: the fused q/k/v epilogue only
     if (epi != EPI_QKV) return hipErrorInvalidValue;
     GPTK_LAUNCH((gemm_bf16_pair_kernel<BM, BN, WM, WN, EPI_QKV>), grid, NT, s, a, b, na);
   } else {
@@ -780,7 +780,10 @@ hipError_t run_bf16_pair(Epi epi, const GemmArgs& a, const GemmArgs& b, hipStrea
         else if (a.lam == nullptr) GPTK_LAUNCH((gemm_bf16_pair_kernel<BM, BN, WM, WN, EPI_RESID_PROD>), grid, NT, s, a, b, na);
         else GPTK_LAUNCH((gemm_bf16_pair_kernel<BM, BN, WM, WN, EPI_RESID_MIX>), grid, NT, s, a, b, na);
         break;
-      case EPI_QKV: GPTK_LAUNCH((gemm_bf16_pair_kernel<BM, BN, WM, WN, EPI_QKV>), grid, NT, s, a, b, na); break;
+      case EPI_QKV:
+        if constexpr (BN == 192) return hipErrorInvalidValue;  // q/k/v take 256- or 128-wide tiles
+        else GPTK_LAUNCH((gemm_bf16_pair_kernel<BM, BN, WM, WN, EPI_QKV>), grid, NT, s, a, b, na);
+        break;
       default: return hipErrorInvalidValue;
     }
   }
@@ -1040,6 +1043,19 @@ hipError_t launch_gemm_bf16_pair(Epi epi, const GemmArgs& a, const GemmArgs& b, 
   const bool fused = epi == EPI_QKV && (a.cs != nullptr || b.cs != nullptr);
   if (fused && (a.cs == nullptr || b.cs == nullptr || a.D != b.D || (a.D != 128 && a.D != 64)))
     return hipErrorInvalidValue;
+  // 256x192 tiles (wavefront tiles of 64x96) instead of 256x256 when that fills the CUs in fewer
+  // rounds, at ~0.9 of the larger tiles' rate: e.g. the nested model's MLP-down and
+  // out-projection pairs at M = 8192 make exactly 256 tiles of 256x192 against 224 of 256x256,
+  // whose longest ones then set the time.
+  if (!fused && epi != EPI_QKV && a.N % 192 == 0 && b.N % 192 == 0 && seg_ok(a, 192) && seg_ok(b, 192)) {
+    const int ncu = cu_count();
+    auto rounds = [&](int bn) {
+      const long t = (long)((a.M + 255) / 256) * ((a.N + bn - 1) / bn) + (long)((b.M + 255) / 256) * ((b.N + bn - 1) / bn);
+      return (double)((t + ncu - 1) / ncu);
+    };
+    const double c256 = seg_ok(a, 256) && seg_ok(b, 256) ? rounds(256) : 1e30;
+    if (rounds(192) * 0.75 / 0.9 < c256) return run_bf16_pair<256, 192, 4, 2>(epi, a, b, s);
+  }
   if (seg_ok(a, 256) && seg_ok(b, 256))
     return fused ? run_bf16_pair<256, 256, 4, 2>(epi, a, b, s) : run_bf16_pair<256, 256, 2, 4>(epi, a, b, s);
   if (seg_ok(a, 128) && seg_ok(b, 128))
