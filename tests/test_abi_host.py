@@ -59,6 +59,8 @@ def test_validate_presets(lib):
 
 @pytest.mark.parametrize("field,value,status", [
     ("n_layer", 0, gf.GPT_E_INVALID_ARG),
+    ("batch", 0, gf.GPT_E_INVALID_ARG),             # empty inputs are rejected, not skipped
+    ("seq_len", 0, gf.GPT_E_INVALID_ARG),
     ("vocab", 1, gf.GPT_E_INVALID_ARG),
     ("n_kv_head", 5, gf.GPT_E_INVALID_ARG),        # 12 % 5 != 0
     ("softcap", 0.0, gf.GPT_E_INVALID_ARG),
