@@ -43,6 +43,12 @@ bool any_ve(const gpt_cfg* c) {
   return false;
 }
 
+// 32-bit index limits shared by the model and the per-step entry points: the RoPE table's entry
+// index (T * D/2), and one sequence's q/k rows in the bf16 attention, which its K tiles read
+// through a buffer resource of fewer than 2^31 bytes.
+bool rope_fits(long T, long D) { return T * (D / 2) <= INT32_MAX - 255; }
+bool attn_bf16_fits(long T, long H, long Hkv, long D) { return T * (H + Hkv) * D * 2 <= INT32_MAX; }
+
 gpt_status validate(const gpt_cfg* c) {
   if (!c) return GPT_E_INVALID_ARG;
   if (c->n_layer < 1 || c->d_model < 1 || c->n_head < 1 || c->n_kv_head < 1 || c->head_dim < 1 ||
@@ -63,8 +69,10 @@ gpt_status validate(const gpt_cfg* c) {
   if (c->head_dim != 64 && c->head_dim != 128) return GPT_E_UNSUPPORTED;
   if (c->d_model % 64 || c->mlp_dim % 64 || (c->n_head * c->head_dim) % 64) return GPT_E_UNSUPPORTED;
   if (c->d_model > 8192) return GPT_E_UNSUPPORTED;
+  if (!rope_fits(c->seq_len, c->head_dim)) return GPT_E_UNSUPPORTED;
   if (c->dtype == GPT_BF16) {
     if (c->seq_len % 64) return GPT_E_UNSUPPORTED;
+    if (!attn_bf16_fits(c->seq_len, c->n_head, c->n_kv_head, c->head_dim)) return GPT_E_UNSUPPORTED;
     if ((c->n_head * c->head_dim) % 128 || (c->n_kv_head * c->head_dim) % 128) return GPT_E_UNSUPPORTED;
   }
   if (any_ve(c)) {
@@ -745,6 +753,7 @@ gpt_status gpt_op_mix_norm(int32_t dtype, float* x, const float* x0, const float
 
 gpt_status gpt_op_rope_table(float* cs, int32_t T, int32_t D, float base, void* stream) {
   if (!cs || T < 1 || D < 2 || (D & 1) || !(base > 0.f)) return GPT_E_INVALID_ARG;
+  if (!rope_fits(T, D)) return GPT_E_UNSUPPORTED;
   CK(launch_rope_table((float2*)cs, T, D, base, (hipStream_t)stream));
   return GPT_OK;
 }
@@ -797,7 +806,7 @@ gpt_status gpt_op_attention(int32_t dtype, const void* qk, const void* vt, void*
   const int win = window < T ? window : T;
   if (dtype == GPT_BF16) {
     if (!vt) return GPT_E_INVALID_ARG;
-    if (T % 64) return GPT_E_UNSUPPORTED;
+    if (T % 64 || !attn_bf16_fits(T, H, Hkv, D)) return GPT_E_UNSUPPORTED;
     CK(launch_attn_bf16(qk, vt, o, B, T, H, Hkv, D, win, scale, (hipStream_t)stream));
   } else {
     CK(launch_attn_f32((const float*)qk, (float*)o, B, T, H, Hkv, D, win, scale, (hipStream_t)stream));

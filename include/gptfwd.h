@@ -55,7 +55,10 @@ typedef enum { GPT_F32 = 0, GPT_BF16 = 1 } gpt_dtype;
 /* Model and batch shape.  Supported: head_dim in {64, 128}; n_head % n_kv_head == 0;
  * d_model, n_head*head_dim and mlp_dim multiples of 64; vocab >= 2; for GPT_BF16 seq_len a
  * multiple of 64 and n_kv_head*head_dim a multiple of 128.  d_model <= 8192.  batch >= 1 and
- * seq_len >= 1: an empty batch is GPT_E_INVALID_ARG, not a call that does nothing. */
+ * seq_len >= 1: an empty batch is GPT_E_INVALID_ARG, not a call that does nothing.  32-bit
+ * limits (GPT_E_UNSUPPORTED beyond them): batch*seq_len <= 2^30, vocab*d_model <= 2^31,
+ * seq_len*head_dim/2 < 2^31, and for GPT_BF16 one sequence's q/k rows,
+ * seq_len*(n_head+n_kv_head)*head_dim*2 bytes, at most 2^31 - 1. */
 typedef struct {
   int32_t n_layer;      /* L */
   int32_t d_model;      /* C, residual width */

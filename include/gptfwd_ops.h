@@ -35,7 +35,8 @@ gpt_status gpt_op_mix_norm(int32_t dtype, float *x, const float *x0, const float
                            int32_t C, float eps, void *stream);
 
 /* RoPE table ("Rotary Position Embeddings (RoPE)", Frequency Construction):
- * cs fp32 [T, D/2, 2] out with (cos, sin) of t * base^(-2j/D), evaluated in fp64. */
+ * cs fp32 [T, D/2, 2] out with (cos, sin) of t * base^(-2j/D), evaluated in fp64.
+ * GPT_E_UNSUPPORTED when T * D/2 does not fit a 32-bit index. */
 gpt_status gpt_op_rope_table(float *cs, int32_t T, int32_t D, float base, void *stream);
 
 /* RoPE then per-head RMSNorm, in place ("Rotary Position Embeddings (RoPE)", Rotation
@@ -64,7 +65,8 @@ gpt_status gpt_op_qkv(const void *xn, const void *wq, const void *wk, const void
 /* Windowed causal attention ("Scaled Dot-Product Attention with Sliding Window") on already
  * rotated and normalised q, k.  GPT_BF16: q/k from qk [B*T, (H+Hkv)*D], v from vt
  * [B, Hkv, D, T]; GPT_F32: q/k/v from qk [B*T, (H+2*Hkv)*D] and vt ignored.  o [B*T, H*D] out.
- * Query head h reads KV head h*Hkv/H. */
+ * Query head h reads KV head h*Hkv/H.  D in {64, 128}.  GPT_BF16 also needs T % 64 == 0 and one
+ * sequence's q/k rows under 2^31 bytes (T * (H+Hkv) * D * 2), else GPT_E_UNSUPPORTED. */
 gpt_status gpt_op_attention(int32_t dtype, const void *qk, const void *vt, void *o, int32_t B,
                             int32_t T, int32_t H, int32_t Hkv, int32_t D, int32_t window,
                             float scale, void *stream);

@@ -71,6 +71,7 @@ def test_validate_presets(lib):
     ("d_model", 1000, gf.GPT_E_UNSUPPORTED),
     ("mlp_dim", 6100, gf.GPT_E_UNSUPPORTED),
     ("seq_len", 2000, gf.GPT_E_UNSUPPORTED),        # bf16 needs T % 64 == 0
+    ("seq_len", 1 << 19, gf.GPT_E_UNSUPPORTED),     # one row's q/k: 2^19 * 24 * 128 * 2 B > 2^31
 ])
 def test_validate_rejects(lib, field, value, status):
     c = _cfg(**{field: value})
@@ -290,6 +291,9 @@ def test_op_argument_errors(lib):
     assert lib.gpt_op_embed_norm(1, F, F, F, F, F, F, F, 4, 6, 10, 1e-6, F, None) == gf.GPT_E_INVALID_ARG
     assert lib.gpt_op_qk_rope_norm(1, F, 100, F, 4, 4, 1, 256, 1e-6, None) == gf.GPT_E_INVALID_ARG
     assert lib.gpt_op_rope_table(F, 4, 7, 1e5, None) == gf.GPT_E_INVALID_ARG
+    # 32-bit limits: RoPE table entries (T * D/2) and one sequence's bf16 q/k rows (< 2^31 bytes)
+    assert lib.gpt_op_rope_table(F, 1 << 25, 128, 1e5, None) == gf.GPT_E_UNSUPPORTED
+    assert lib.gpt_op_attention(1, F, F, F, 1, 1 << 19, 12, 12, 128, 8, 0.1, None) == gf.GPT_E_UNSUPPORTED
     # fused QKV epilogue (RoPE table given): T % 32 == 0 only (head_dim 64 and 128)
     assert lib.gpt_op_qkv(F, F, F, F, 1, 100, 256, 2, 2, 128, F, 1e-6, F, F, None) == gf.GPT_E_UNSUPPORTED
     assert lib.gpt_op_qkv(F, F, F, F, 1, 100, 256, 2, 2, 64, F, 1e-6, F, F, None) == gf.GPT_E_UNSUPPORTED
