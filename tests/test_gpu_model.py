@@ -183,6 +183,27 @@ def test_d24_bf16_bench_config(d24):
     assert err.max() <= 2e-2
 
 
+def test_d24_bf16_past_32bit_offsets(d24):
+    """B=176 at the d24 shape: 360,448 rows, so the MLP activations hold more than 2^31 elements
+    and the fp32 residual stream more than 2^31 bytes (14.6 GB of workspace).  Every loss must be
+    finite, and the oracle's 512-token prefixes of the first and the last row (the latter past
+    both 32-bit boundaries) must match."""
+    p0, w, _, _ = d24
+    p = p0.with_(batch=176)
+    tok, tgt = gptdata.make_tokens(p, np.random.default_rng(p.seed + 1))
+    _, got = _run(p, w, tok, tgt)
+    assert got["status"] == gf.GPT_OK
+    assert np.all(np.isfinite(got["losses"])) and math.isfinite(got["mean"])
+    prm = params_of(w)
+    pre = p0.with_(seq_len=512, batch=1)
+    wins = oracle.layer_windows(p0.window_pattern, p0.short_window, p0.seq_len, p0.n_layer)
+    for b in (0, p.batch - 1):
+        ref = oracle.forward(pre, prm, tok[b:b + 1, :512], tgt[b:b + 1, :512], windows=wins)
+        err = np.abs(got["losses"][b, :512] - ref["losses"][0])
+        print(f"  row {b} prefix: max |err| {err.max():.3e}")
+        assert err.max() <= 2e-2
+
+
 def test_launch_timing_hook_bf16():
     """gpt_fwd_loss_timed stamps one event pair per launch of the chosen kind and leaves the
     results bit-identical to gpt_fwd_loss."""
