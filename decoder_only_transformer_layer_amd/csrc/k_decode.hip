@@ -245,16 +245,19 @@ constexpr int DA_THREADS = 256;
 constexpr int DA_CHUNK = 128;       // keys per block: two threads per key in the score pass
 constexpr int DA_MAX_GROUP = 8;     // query heads per KV head
 
-__device__ __forceinline__ void load8(const bf16* p, float v[8]) {
-  const bf16x8 t = *(const bf16x8*)p;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = (float)t[i];
+
+// Eight consecutive elements as loaded (bf16 or fp32), converted only where used, so that all of
+// a thread's loads can be issued before the first of them is needed.
+template <typename AT> struct Raw8;
+template <> struct Raw8<bf16> { bf16x8 v; };
+template <> struct Raw8<float> { f32x4 a, b; };
+__device__ __forceinline__ void ld_raw(const bf16* p, Raw8<bf16>& r) { r.v = *(const bf16x8*)p; }
+__device__ __forceinline__ void ld_raw(const float* p, Raw8<float>& r) {
+  r.a = *(const f32x4*)p;
+  r.b = *(const f32x4*)(p + 4);
 }
-__device__ __forceinline__ void load8(const float* p, float v[8]) {
-  const f32x4 a = *(const f32x4*)p, c = *(const f32x4*)(p + 4);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[i + 4] = c[i]; }
-}
+__device__ __forceinline__ float raw_at(const Raw8<bf16>& r, int i) { return (float)r.v[i]; }
+__device__ __forceinline__ float raw_at(const Raw8<float>& r, int i) { return i < 4 ? r.a[i] : r.b[i - 4]; }
 
 template <typename AT, int D>
 __global__ __launch_bounds__(DA_THREADS) void decode_attn_chunk_kernel(
@@ -281,23 +284,37 @@ __global__ __launch_bounds__(DA_THREADS) void decode_attn_chunk_kernel(
     }
     return;
   }
+  // This thread's key half-row (score pass) and value rows (output pass) are requested first,
+  // together, then the queries: one memory round trip instead of three.  Keys past the chunk's
+  // end read the chunk's first key instead (their probability is 0).
+  constexpr int OCT = D / 8, PARTS = DA_THREADS / OCT;  // output pass: D=128: 16 x 16; D=64: 8 x 32
+  constexpr int VR = DA_CHUNK / PARTS;                  // value rows per thread
+  const int j = tid >> 1, hf = tid & 1;
+  const int oc = tid % OCT, pt = tid / OCT;
+  Raw8<AT> kraw[D / 16], vraw[VR];
+  {
+    const AT* kr = kc + (((size_t)b * Hkv + g) * T + (j0 + (j < nk ? j : 0))) * D + hf * (D / 2);
+#pragma unroll
+    for (int u = 0; u < D / 16; ++u) ld_raw(kr + 8 * u, kraw[u]);
+    const AT* vb = vc + (((size_t)b * Hkv + g) * T + j0) * D + oc * 8;
+#pragma unroll
+    for (int k = 0; k < VR; ++k) {
+      const int jv = pt + k * PARTS;
+      ld_raw(vb + (size_t)(jv < nk ? jv : 0) * D, vraw[k]);
+    }
+  }
   for (int i = tid; i < G * D; i += DA_THREADS)
     qs[i / D][i % D] = to_f32(q[(size_t)b * H * D + (size_t)(g * G + i / D) * D + i % D]);
   __syncthreads();
   // scores: thread (key j = tid / 2, half = tid % 2) over D/2 dimensions, halves joined by a shuffle
-  {
-    const int j = tid >> 1, hf = tid & 1;
-    const AT* kr = kc + (((size_t)b * Hkv + g) * T + (j0 + (j < nk ? j : 0))) * D + hf * (D / 2);
-    float kv[D / 2];
+  for (int gi = 0; gi < G; ++gi) {
+    float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < D / 2; ++i) kv[i] = to_f32(kr[i]);
-    for (int gi = 0; gi < G; ++gi) {
-      float s = 0.f;
+    for (int u = 0; u < D / 16; ++u)
 #pragma unroll
-      for (int i = 0; i < D / 2; ++i) s = fmaf(qs[gi][hf * (D / 2) + i], kv[i], s);
-      s += __shfl_xor(s, 1);
-      if (hf == 0 && j < DA_CHUNK) sc[gi][j] = j < nk ? s * scale : -INFINITY;
-    }
+      for (int i = 0; i < 8; ++i) s = fmaf(qs[gi][hf * (D / 2) + 8 * u + i], raw_at(kraw[u], i), s);
+    s += __shfl_xor(s, 1);
+    if (hf == 0 && j < DA_CHUNK) sc[gi][j] = j < nk ? s * scale : -INFINITY;
   }
   __syncthreads();
   // per head: chunk max and sum (one wavefront per head, two keys per lane)
@@ -315,26 +332,21 @@ __global__ __launch_bounds__(DA_THREADS) void decode_attn_chunk_kernel(
   // the value rows are read once for all heads of the group.  Parts are summed by shuffles
   // within a wavefront, then the 4 wavefronts through LDS, in a fixed order.
   {
-    constexpr int OCT = D / 8, PARTS = DA_THREADS / OCT;  // D=128: 16 x 16; D=64: 8 x 32
-    const int oc = tid % OCT, pt = tid / OCT;
     float acc[DA_MAX_GROUP][8];
 #pragma unroll
     for (int gi = 0; gi < DA_MAX_GROUP; ++gi)
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[gi][i] = 0.f;
-    const AT* vb = vc + (((size_t)b * Hkv + g) * T + j0) * D + oc * 8;
 #pragma unroll
-    for (int k = 0; k < DA_CHUNK / PARTS; ++k) {
-      const int j = pt + k * PARTS;
-      if (j < nk) {
-        float vv[8];
-        load8(vb + (size_t)j * D, vv);
+    for (int k = 0; k < VR; ++k) {
+      const int jv = pt + k * PARTS;
+      if (jv < nk) {
 #pragma unroll
         for (int gi = 0; gi < DA_MAX_GROUP; ++gi)
           if (gi < G) {
-            const float pj = sc[gi][j];
+            const float pj = sc[gi][jv];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[gi][i] = fmaf(pj, vv[i], acc[gi][i]);
+            for (int i = 0; i < 8; ++i) acc[gi][i] = fmaf(pj, raw_at(vraw[k], i), acc[gi][i]);
           }
       }
     }
