@@ -123,6 +123,30 @@ def _ptr(x: Any) -> Optional[int]:
     return x.data_ptr()
 
 
+def _require(t: Any, name: str, dtype: str, numel: int, optional: bool = True) -> None:
+    """Marshalling check of a tensor handed to the library by the DeviceModel / Decoder methods:
+    a torch tensor on a GPU with the given dtype ("int32" or "float32"), contiguous, holding
+    `numel` elements (the C functions read or write exactly that many).  None passes when
+    `optional`; an int is taken as a raw device address and passes unchecked."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name}: required")
+    if isinstance(t, int):
+        return
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor or a device address, got {type(t).__name__}")
+    if t.dtype != getattr(torch, dtype):
+        raise ValueError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{name}: expected {numel} elements, got {t.numel()}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor")
+
+
 def _stream(stream: Any) -> Optional[int]:
     if stream is None:
         import torch
@@ -383,7 +407,9 @@ class DeviceModel:
     def forward(self, tokens, targets=None, loss=None, mean=None, logits=None, stream=None,
                 timing: Optional[gpt_launch_timing] = None) -> int:
         """Enqueue gpt_fwd_loss (gpt_fwd_loss_timed if `timing` is given) on device tensors
-        (outputs preallocated by the caller)."""
+        (outputs preallocated by the caller): tokens, targets int32 [B, T]; loss fp32 [B, T];
+        mean fp32 [1]; logits fp32 [B, T, V]."""
+        self._check_io(tokens, targets, loss, mean, logits)
         if timing is not None:
             return gpt_fwd_loss_timed(self.cfg, self.w, tokens, targets, loss, mean, logits,
                                       self.ws_ptr, self.ws_bytes, stream, timing)
@@ -393,9 +419,20 @@ class DeviceModel:
     def forward_nested(self, tokens, targets=None, loss=None, mean=None, logits=None, loss_k1=None,
                        mean_k1=None, logits_k1=None, stream=None,
                        timing: Optional[gpt_launch_timing] = None) -> int:
-        """Enqueue gpt_fwd_loss_nested (full model and kfront=1 outputs from one pass)."""
+        """Enqueue gpt_fwd_loss_nested (full model and kfront=1 outputs from one pass); the _k1
+        outputs have the shapes of their full-model counterparts."""
+        self._check_io(tokens, targets, loss, mean, logits)
+        self._check_io(tokens, targets, loss_k1, mean_k1, logits_k1)
         return gpt_fwd_loss_nested(self.cfg, self.w, tokens, targets, loss, mean, logits, loss_k1,
                                    mean_k1, logits_k1, self.ws_ptr, self.ws_bytes, stream, timing)
+
+    def _check_io(self, tokens, targets, loss, mean, logits) -> None:
+        n = self.batch * self.p.seq_len
+        _require(tokens, "tokens", "int32", n, optional=False)
+        _require(targets, "targets", "int32", n)
+        _require(loss, "loss", "float32", n)
+        _require(mean, "mean", "float32", 1)
+        _require(logits, "logits", "float32", n * self.p.vocab)
 
     def call_nested(self, tokens, targets=None, want_logits: bool = False):
         """Allocate outputs, run gpt_fwd_loss_nested, and return a dict with loss, mean, logits
@@ -423,15 +460,6 @@ class DeviceModel:
         _check(self.forward(tokens, targets, loss, mean, logits), "gpt_fwd_loss")
         return loss, mean, logits
 
-    def prefill(self, tokens, prompt_len: int, logits, lens=None, stream=None) -> int:
-        """Enqueue gpt_prefill on tokens [B, prompt_len] (device int32, contiguous); the forward
-        uses the DeviceModel's workspace."""
-        need = gpt_prefill_workspace_bytes(self.cfg)
-        if self.m.ws_bytes < need:
-            raise GptError(GPT_E_WORKSPACE, "prefill workspace")
-        return gpt_prefill(self.cfg, self.m.w, tokens, prompt_len, lens, self.cache_ptr, logits,
-                           self.m.ws_ptr, self.m.ws_bytes, stream)
-
     def device_status(self) -> int:
         return gpt_device_status(self.ws_ptr)
 
@@ -458,12 +486,20 @@ class Decoder:
 
     def step(self, tokens, pos, logits, stream=None) -> int:
         """Enqueue gpt_decode_step: tokens, pos device int32 [B]; logits device fp32 [B, V]."""
+        B = self.m.batch
+        _require(tokens, "tokens", "int32", B, optional=False)
+        _require(pos, "pos", "int32", B, optional=False)
+        _require(logits, "logits", "float32", B * self.m.p.vocab, optional=False)
         return gpt_decode_step(self.cfg, self.m.w, tokens, pos, self.cache_ptr, logits, self.ws_ptr,
                                self.ws_bytes, stream)
 
     def prefill(self, tokens, prompt_len: int, logits, lens=None, stream=None) -> int:
         """Enqueue gpt_prefill on tokens [B, prompt_len] (device int32, contiguous); the forward
         uses the DeviceModel's workspace."""
+        B = self.m.batch
+        _require(tokens, "tokens", "int32", B * prompt_len, optional=False)
+        _require(logits, "logits", "float32", B * self.m.p.vocab, optional=False)
+        _require(lens, "lens", "int32", B)
         need = gpt_prefill_workspace_bytes(self.cfg)
         if self.m.ws_bytes < need:
             raise GptError(GPT_E_WORKSPACE, "prefill workspace")

@@ -311,3 +311,24 @@ def test_layer_windows_matches_pattern():
     assert gf.layer_windows("SSSL", 1024, 2048, 12)[-1] == 2048
     assert gf.layer_windows("SSSL", 128, 256, 2) == [128, 256]
     assert gf.layer_windows("SSSL", 1024, 2048, 5) == [1024, 1024, 1024, 2048, 2048]
+
+
+def test_binding_tensor_checks():
+    """The DeviceModel / Decoder methods reject tensors the C functions would read or write out
+    of bounds (wrong dtype, size or layout, host memory) before anything is enqueued."""
+    import torch
+    ok = torch.zeros(6, dtype=torch.int32)
+    gf._require(None, "targets", "int32", 6)                 # optional and absent
+    gf._require(0x200000, "tokens", "int32", 6)              # raw device address: unchecked
+    with pytest.raises(ValueError, match="required"):
+        gf._require(None, "tokens", "int32", 6, optional=False)
+    with pytest.raises(TypeError):
+        gf._require(ok.numpy(), "tokens", "int32", 6)
+    with pytest.raises(ValueError, match="int32"):
+        gf._require(ok.long(), "tokens", "int32", 6)
+    with pytest.raises(ValueError, match="elements"):
+        gf._require(ok[:5], "tokens", "int32", 6)
+    with pytest.raises(ValueError, match="contiguous"):
+        gf._require(torch.zeros((3, 4), dtype=torch.int32)[:, :2], "tokens", "int32", 6)
+    with pytest.raises(ValueError, match="GPU"):
+        gf._require(ok, "tokens", "int32", 6)
