@@ -265,14 +265,21 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
       // slices are stored slice-major ([slice][M]): consecutive threads read consecutive rows
       for (int i = tid; i < BM; i += NT) {
         const int row = m0 + i;
+        // Sixteen slices' loads are in flight together; slice j < n4 adds into s4[j % 4] and the
+        // rest into s4[0], each in increasing j.
         float s4[4] = {0.f, 0.f, 0.f, 0.f};
         if (row < M) {
-          int j = 0;
-          for (; j + 4 <= g.rs_n; j += 4) {
+          const int n4 = g.rs_n & ~3;
+          for (int j0 = 0; j0 < g.rs_n; j0 += 16) {
+            float v[16];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) s4[u] += g.rs_ssp[(size_t)(j + u) * M + row];
+            for (int u = 0; u < 16; ++u) v[u] = j0 + u < g.rs_n ? g.rs_ssp[(size_t)(j0 + u) * M + row] : 0.f;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+              if (j0 + u < n4) s4[u & 3] += v[u];
+              else if (j0 + u < g.rs_n) s4[0] += v[u];
+            }
           }
-          for (; j < g.rs_n; ++j) s4[0] += g.rs_ssp[(size_t)j * M + row];
         }
         rinv[i] = rsqrtf(((s4[0] + s4[1]) + (s4[2] + s4[3])) / g.rs_c + g.eps);
       }
