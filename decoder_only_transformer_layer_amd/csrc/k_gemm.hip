@@ -82,7 +82,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
 
   const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
   int bm, bn;
-  tile_of<8>(pid, nbm, nbn, bm, bn);
+  tile_of<4>(pid, nbm, nbn, bm, bn);  // 4 row blocks per group: ~0.6-0.9 % faster than 8 or 16 at d24
   const int m0 = bm * BM, n0 = bn * BN;
 
   // B row segment holding this column block (segment boundaries are multiples of BN).
