@@ -80,6 +80,20 @@ def test_decode_matches_forward_bf16():
     _check_bf16_logits(got, ref)
 
 
+def test_decode_group8_multichunk_bf16():
+    """bf16 at the largest query group the decode attention takes (8 query heads on one KV
+    head, head_dim 128), 320 cache positions so that windows of 200 and full span up to three
+    128-key chunks; row 1 runs three positions behind row 0."""
+    p = gptdata.Preset(name="dec8g", n_layer=2, d_model=256, n_head=8, n_kv_head=1, head_dim=128,
+                       mlp_dim=1024, vocab=700, seq_len=320, batch=2, dtype="bf16", short_window=200,
+                       lambda_range=(0.9, 1.1), mu_range=(0.0, 0.2), seed=57)
+    w, tok, _ = gptdata.make_inputs(p)
+    windows = [200, 320]
+    got = _decode_all(p, w, tok, lag=[0, 3], windows=windows)
+    ref = oracle.forward(p, params_of(w), tok, want_logits=True, windows=windows)["logits"]
+    _check_bf16_logits(got, ref)
+
+
 def test_decode_d24_positions():
     """d24 weights, 2 rows, the whole 2048-token cache: logits at positions 0, 511, 1023, 1024,
     1500 and 2047 of row 0 against one oracle forward of that row."""
