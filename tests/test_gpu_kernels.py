@@ -239,11 +239,12 @@ def test_attention_bf16(H, Hkv, D, window):
         assert err.mean() < 3e-3, (b, err.mean())
 
 
-@pytest.mark.parametrize("B,H,Hkv,window", [(2, 16, 16, 256), (4, 12, 4, 5000)])
+@pytest.mark.parametrize("B,H,Hkv,window", [(2, 16, 16, 256), (4, 12, 4, 5000), (2, 16, 2, 300)])
 def test_attention_bf16_many_heads(B, H, Hkv, window):
     """Grids of many (batch, head) pairs: 32 pairs with a 256-key window (every query block
-    spans a window edge), and 48 pairs with GQA (3 query heads per KV head) and full windows.
-    Every head against the oracle."""
+    spans a window edge), 48 pairs with GQA (3 query heads per KV head) and full windows, and
+    32 pairs with 8 query heads per KV head and a 300-key window.  Every head against the
+    oracle."""
     torch = torch_mod()
     rng = np.random.default_rng(B * 100 + H)
     T, D = 512, 64
