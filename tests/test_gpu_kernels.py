@@ -37,9 +37,11 @@ def _bf16_close(got, ref, rel=2 ** -8, atol=1e-5):
 # ----------------------------------------------------------------------------- GEMM
 
 # (16384, 1536): 256x384 tiles (one round); (8192, 768) and (1000, 576): 256x192 tiles, the
-# latter with ragged rows; (16384, 4608, ...) via QKV below: 256x256 with a 256x128 tail.
+# latter with ragged rows; (8192, 4352): 17 column blocks of 256 over 32 row blocks, split into
+# 16 blocks of 256x256 (two whole rounds) and a 256x128 column tail (the shifted output, and
+# residual, pointers of the tail); (16384, 4608, ...) via QKV below.
 @pytest.mark.parametrize("M,N,K", [(300, 384, 192), (512, 1000, 128), (8192, 8192, 64), (64, 128, 6144),
-                                   (16384, 1536, 64), (8192, 768, 128), (1000, 576, 64)])
+                                   (16384, 1536, 64), (8192, 768, 128), (1000, 576, 64), (8192, 4352, 64)])
 @pytest.mark.parametrize("epi", [0, 1, 2])
 def test_linear_bf16(M, N, K, epi):
     rng = np.random.default_rng(100 + M + N + K + epi)
