@@ -19,7 +19,7 @@ namespace {
 constexpr int GV_ROWS = 32;   // weight rows per block (one 32x32 MFMA output tile, batch in N)
 constexpr int GV_WAVES = 4;   // wavefronts per block
 constexpr int GV_KB = 64;     // K per wavefront step: four 32x32x16 MFMAs
-constexpr int GV_TARGET_BLOCKS = 1024;
+constexpr int GV_TARGET_BLOCKS = 2048;  // K splits aim at this many blocks (2048: 0.6 % faster d24 step than 1024)
 
 // Per-(row b, column n) epilogue of a decode-step product.
 struct GvEpi {
