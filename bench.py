@@ -193,14 +193,61 @@ def gemm_compare(gf, p, reps=20):
     return out
 
 
+def cpu_baseline(p, w, tok, tgt, windows, rows, budget_s):
+    """The oracle as it stands, in float32 (the dtype it offers for full-size runs), on whole
+    rows of the same batch, one after another until `rows` rows are done or `budget_s` seconds
+    have passed; its BLAS uses every thread it was given."""
+    import numpy as np
+    import oracle
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [0]) or None
+    except Exception:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    params = {
+        "wte": w.value(w.wte), "lm_head": w.value(w.lm_head),
+        "resid_lambda": w.resid_lambda, "x0_lambda": w.x0_lambda,
+        **{k: [w.value(a) for a in getattr(w, k)] for k in ("wq", "wk", "wv", "wo", "w1", "w2")},
+    }
+    if getattr(p, "value_embeds", False):
+        params.update(ve=[w.value(a) for a in w.ve], ve_gate=[w.value(a) for a in w.ve_gate])
+    if getattr(p, "looped", False):
+        params.update(pass_emb=w.value(w.pass_emb), gate_logit=w.gate_logit)
+    done, t_rows = 0, []
+    c0 = time.perf_counter()
+    for b in range(min(rows, p.batch)):
+        r0 = time.perf_counter()
+        oracle.forward(p, params, tok[b:b + 1], tgt[b:b + 1], dtype=np.float32, windows=windows)
+        t_rows.append(time.perf_counter() - r0)
+        done += 1
+        print(f"[bench] cpu oracle: row {b} in {t_rows[-1]:.1f}s", file=sys.stderr, flush=True)
+        if time.perf_counter() - c0 > budget_s:
+            break
+    cdt = time.perf_counter() - c0
+    n = done * p.seq_len
+    return {"value": round(n / cdt, 2), "unit": "tokens/s", "cores": blas or affinity or os.cpu_count(),
+            "kind": "oracle",
+            "sample": f"{done} of {p.batch} rows x {p.seq_len} tokens ({n} tokens), float32 NumPy oracle, "
+                      f"{cdt:.1f}s",
+            "cpu_count": os.cpu_count(), "cpu_affinity": affinity, "blas_threads": blas,
+            "seconds": round(cdt, 2), "seconds_per_row": [round(t, 2) for t in t_rows]}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="d24")
-    ap.add_argument("--cpu-tokens", type=int, default=2048,
-                    help="tokens of row 0 the CPU oracle evaluates (a causal prefix)")
+    ap.add_argument("--cpu-rows", type=int, default=8,
+                    help="whole rows of the batch the CPU oracle evaluates (default: all of d24's 8)")
+    ap.add_argument("--cpu-budget-s", type=float, default=240.0,
+                    help="stop the CPU oracle after the row that passes this many seconds")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-steps", type=int, default=3,
                     help="measurement steps per kernel kind for the per-kernel event timing")
@@ -268,21 +315,28 @@ def main():
     print(f"[bench] warmup done, mean loss {mean.item():.4f}"
           + (f", kfront=1 mean loss {mean1.item():.4f}" if nested else ""), file=sys.stderr, flush=True)
 
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # One event before every call and one after the last, all on the forward's stream: the first
+    # and the last bracket the whole region (the reported mean), consecutive pairs give each call.
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        evs[i].record(stream)
         step()
-    ev1.record(stream)
+    evs[-1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    per_call = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    ms_median = per_call[len(per_call) // 2] if len(per_call) % 2 else \
+        0.5 * (per_call[len(per_call) // 2 - 1] + per_call[len(per_call) // 2])
+    ms_min = per_call[0]
     tok_s = B * T / (ms / 1e3)
     fpt = flops_per_token(p, windows)
     assert gf.gpt_device_status(model.ws_ptr) == gf.GPT_OK
-    print(f"[bench] {args.steps} steps: {ms:.3f} ms/step (wall {wall / args.steps * 1e3:.3f}), "
-          f"{tok_s:,.0f} tok/s, {fpt * tok_s / 1e12:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    print(f"[bench] {args.steps} steps: {ms:.3f} ms/step (wall {wall / args.steps * 1e3:.3f}; per call "
+          f"median {ms_median:.3f}, min {ms_min:.3f}), {tok_s:,.0f} tok/s, {fpt * tok_s / 1e12:.1f} TFLOP/s",
+          file=sys.stderr, flush=True)
 
     # Per-kernel time inside the forward pass: kernel start/end stamps on HIP events, for every
     # launch of one kind, over separate measurement steps on the forward's own stream.
@@ -320,6 +374,11 @@ def main():
         f"{n} {k['avg_us']:.1f} us x{k['launches_per_step']} ({k['tflops']:.0f} TF/s)" for n, k in kern.items()),
         file=sys.stderr, flush=True)
 
+    traffic = measured_traffic(ROOT, dk)
+    traffic_src = ("stored: HBM bytes per dispatch from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) "
+                   "over this kernel source, profiles/gemm_traffic.json" if traffic is not None else
+                   "none: no counter record for this kernel source")
+
     dec = None
     if args.decode_steps > 0 and not nested and not getattr(p, "looped", False) and not p.value_embeds:
         dec = decode_bench(gf, p, model, args.decode_steps)
@@ -328,24 +387,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-        try:
-            from threadpoolctl import threadpool_info
-            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-        except Exception:
-            cores = os.cpu_count()
-        n = min(args.cpu_tokens, T)
-        params = {
-            "wte": w.value(w.wte), "lm_head": w.value(w.lm_head),
-            "resid_lambda": w.resid_lambda, "x0_lambda": w.x0_lambda,
-            **{k: [w.value(a) for a in getattr(w, k)] for k in ("wq", "wk", "wv", "wo", "w1", "w2")},
-        }
-        c0 = time.perf_counter()
-        oracle.forward(p, params, tok[:1, :n], tgt[:1, :n], windows=windows)
-        cdt = time.perf_counter() - c0
-        cpu = {"value": round(n / cdt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-               "sample": f"row 0, first {n} of {T} tokens (causal prefix), fp64 NumPy oracle, {cdt:.1f}s"}
-        print(f"[bench] cpu oracle: {n} tokens in {cdt:.1f}s", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(p, w, tok, tgt, windows, args.cpu_rows, args.cpu_budget_s)
 
     out = {
         "metric": "forward+loss tokens/sec at d24 T=2048 bf16; % of MFMA bf16 peak",
@@ -355,6 +397,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_median": round(ms_median, 4),
+        "ms_per_step_min": round(ms_min, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -366,7 +410,8 @@ def main():
                    "flops_per_token": round(fpt), "windows": "SSSL short 1024, last layer full"},
         "roofline": {"bound": "mfma", "kernel": KINDS[dk],
                      "achieved": round(k_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(k_tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(ROOT, dk),
+                     "frac": round(k_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "traffic_source": traffic_src,
                      "avg_launch_us": dom["avg_us"], "flops_per_launch": fpl[dk]},
         "kernels": kern,
         "decode": dec,
