@@ -22,12 +22,13 @@ LIB_PATH = os.path.join(_HERE, "libgptfwd.so")
 
 GPT_OK, GPT_E_INVALID_ARG, GPT_E_UNSUPPORTED, GPT_E_WORKSPACE, GPT_E_HIP, GPT_E_DEVICE_INPUT = 0, -1, -2, -3, -4, -5
 GPT_F32, GPT_BF16 = 0, 1
+GPT_NOALLOC_MAX_BYTES = 64 << 20  # the fixed workspace array of gpt_fwd_loss_noalloc
 (GPT_KERNEL_QKV, GPT_KERNEL_ATTENTION, GPT_KERNEL_ATTN_OUT, GPT_KERNEL_MLP_UP, GPT_KERNEL_MLP_DOWN,
  GPT_KERNEL_LM_HEAD) = 1, 2, 3, 4, 5, 6
 
 EXPORTED = [
     "gpt_validate", "gpt_workspace_bytes", "gpt_fwd_loss", "gpt_fwd_loss_timed", "gpt_fwd_loss_nested",
-    "gpt_device_status", "gpt_status_string",
+    "gpt_device_status", "gpt_status_string", "gpt_fwd_loss_noalloc",
     "gpt_kv_cache_bytes", "gpt_decode_workspace_bytes", "gpt_decode_step", "gpt_sample",
     "gpt_prefill_workspace_bytes", "gpt_prefill",
     "gpt_op_embed_norm", "gpt_op_mix_norm", "gpt_op_rope_table", "gpt_op_qk_rope_norm",
@@ -89,6 +90,7 @@ def _load() -> ctypes.CDLL:
         "gpt_fwd_loss_nested": (I, [ctypes.POINTER(gpt_cfg), ctypes.POINTER(gpt_weights), P, P, P, P, P, P, P, P,
                                     P, S, P, ctypes.POINTER(gpt_launch_timing)]),
         "gpt_device_status": (I, [P, P]),
+        "gpt_fwd_loss_noalloc": (I, [ctypes.POINTER(gpt_cfg), ctypes.POINTER(gpt_weights), P, P, P, P, P, P]),
         "gpt_kv_cache_bytes": (S, [ctypes.POINTER(gpt_cfg)]),
         "gpt_decode_workspace_bytes": (S, [ctypes.POINTER(gpt_cfg)]),
         "gpt_decode_step": (I, [ctypes.POINTER(gpt_cfg), ctypes.POINTER(gpt_weights), P, P, P, P, P, S, P]),
@@ -242,6 +244,12 @@ def gpt_fwd_loss_nested(cfg: gpt_cfg, weights: gpt_weights, tokens, targets, los
                                        _ptr(loss), _ptr(mean_loss), _ptr(logits), _ptr(loss_k1),
                                        _ptr(mean_k1), _ptr(logits_k1), _ptr(workspace), workspace_bytes,
                                        _stream(stream), None if timing is None else ctypes.byref(timing))
+
+
+def gpt_fwd_loss_noalloc(cfg: gpt_cfg, weights: gpt_weights, tokens, targets, loss, mean_loss, logits,
+                         stream=None) -> int:
+    return _load().gpt_fwd_loss_noalloc(ctypes.byref(cfg), ctypes.byref(weights), _ptr(tokens), _ptr(targets),
+                                        _ptr(loss), _ptr(mean_loss), _ptr(logits), _stream(stream))
 
 
 def launch_timing(kind: int, begin_events, end_events) -> gpt_launch_timing:
@@ -415,6 +423,12 @@ class DeviceModel:
                                       self.ws_ptr, self.ws_bytes, stream, timing)
         return gpt_fwd_loss(self.cfg, self.w, tokens, targets, loss, mean, logits, self.ws_ptr,
                             self.ws_bytes, stream)
+
+    def forward_noalloc(self, tokens, targets=None, loss=None, mean=None, logits=None, stream=None) -> int:
+        """gpt_fwd_loss_noalloc on device tensors (as forward): the library's fixed workspace
+        array instead of this model's."""
+        self._check_io(tokens, targets, loss, mean, logits)
+        return gpt_fwd_loss_noalloc(self.cfg, self.w, tokens, targets, loss, mean, logits, stream)
 
     def forward_nested(self, tokens, targets=None, loss=None, mean=None, logits=None, loss_k1=None,
                        mean_k1=None, logits_k1=None, stream=None,

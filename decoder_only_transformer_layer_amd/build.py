@@ -19,7 +19,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgptfwd.so")
 ARCH = "gfx950"
 
-SOURCES = ["k_rows.hip", "k_gemm.hip", "k_attn.hip", "k_loss.hip", "k_decode.hip", "engine.cpp"]
+SOURCES = ["k_rows.hip", "k_gemm.hip", "k_attn.hip", "k_loss.hip", "k_decode.hip", "noalloc.hip",
+           "engine.cpp"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",

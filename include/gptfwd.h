@@ -273,6 +273,23 @@ gpt_status gpt_sample(const float *logits, int32_t batch, int32_t vocab, int32_t
  * last call began (GPT_OK or GPT_E_DEVICE_INPUT; GPT_E_HIP if synchronising failed). */
 gpt_status gpt_device_status(void *workspace, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): gpt_fwd_loss with the workspace taken from a fixed
+ * array inside this library instead of an argument.  The array holds GPT_NOALLOC_MAX_BYTES
+ * (64 MiB) on every GPU the library runs on, from the first such call on that GPU until the
+ * process ends; configurations whose gpt_workspace_bytes() exceeds it are refused with
+ * GPT_E_WORKSPACE before any HIP call (a configuration that does not validate returns
+ * gpt_validate()'s status), and nothing is allocated, by this call or the forward pass.  The
+ * other arguments, their checks and the results are those of gpt_fwd_loss.  Every call on one
+ * GPU uses that GPU's single array, which keeps the last call's contents: calls that overlap on
+ * one GPU (different streams, or host threads) race, and must be ordered by the caller.  The
+ * array's device error flags are not readable through gpt_device_status(): out-of-range ids
+ * still show as NaN per-token losses. */
+#define GPT_NOALLOC_MAX_BYTES (64u << 20)
+gpt_status gpt_fwd_loss_noalloc(const gpt_cfg *cfg, const gpt_weights *w, const int32_t *tokens,
+                                const int32_t *targets, float *loss, float *mean_loss,
+                                float *logits, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *gpt_status_string(gpt_status s);
 

@@ -332,3 +332,17 @@ def test_binding_tensor_checks():
         gf._require(torch.zeros((3, 4), dtype=torch.int32)[:, :2], "tokens", "int32", 6)
     with pytest.raises(ValueError, match="GPU"):
         gf._require(ok, "tokens", "int32", 6)
+
+
+def test_noalloc_refuses_before_any_hip_call(lib):
+    """gpt_fwd_loss_noalloc checks the configuration and its workspace size on the host before
+    anything else: an invalid configuration reports gpt_validate's status, one whose workspace
+    exceeds the fixed array GPT_E_WORKSPACE (the pointers are never dereferenced)."""
+    w = gf.gpt_weights()
+    big = gf.make_cfg(gptdata.preset("d24"))
+    assert gf.gpt_workspace_bytes(big) > gf.GPT_NOALLOC_MAX_BYTES
+    assert gf.gpt_fwd_loss_noalloc(big, w, 16, 16, 16, 16, None, 0) == gf.GPT_E_WORKSPACE
+    bad = _cfg(head_dim=96)
+    assert gf.gpt_fwd_loss_noalloc(bad, w, 16, 16, 16, 16, None, 0) == gf.GPT_E_UNSUPPORTED
+    tiny = gf.make_cfg(gptdata.preset("tiny"))
+    assert 0 < gf.gpt_workspace_bytes(tiny) <= gf.GPT_NOALLOC_MAX_BYTES
