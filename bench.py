@@ -76,8 +76,8 @@ def flops_per_launch(p, windows):
     else:
         att = [_attn_flops(p, w) for w in windows]
     live = live_fraction(p)
-    # nested: the two lm_head launches (full, then the inner K-prefix) are averaged
-    head = M * V * (C + p.nested_c1) if getattr(p, "nested_c1", 0) else 2.0 * M * C * V
+    # nested: one lm_head pass gives both logits (the kfront=1 ones are its K-prefix)
+    head = 2.0 * M * C * V
     return {1: 2.0 * M * C * (H + 2 * Hkv) * D * live, 2: M * sum(att) / len(att),
             3: 2.0 * M * H * D * C * live, 4: 2.0 * M * C * F * live, 5: 2.0 * M * F * C * live, 6: head}
 
@@ -343,8 +343,8 @@ def main():
     L = p.n_layer
     if getattr(p, "looped", False):  # pass 1 stops after its last layer's projection
         per_step = {1: 2 * L, 2: 2 * L - 1, 3: 2 * L - 1, 4: 2 * L - 1, 5: 2 * L - 1, 6: 1}
-    else:  # nested: one pair covers both row blocks of a step; the lm_head runs twice
-        per_step = {1: L, 2: L, 3: L, 4: L, 5: L, 6: 2 if nested else 1}
+    else:  # nested: one pair covers both row blocks of a step, one lm_head pass both losses
+        per_step = {1: L, 2: L, 3: L, 4: L, 5: L, 6: 1}
     fpl = flops_per_launch(p, windows)
     kern = {}
     for kind in KINDS:

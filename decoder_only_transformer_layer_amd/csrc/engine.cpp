@@ -21,7 +21,7 @@ inline size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 struct Layout {
-  size_t flags, x, x0, xn, qk, vt, o, h, cs, ssp, partial, tgt, qk1, last, total;
+  size_t flags, x, x0, xn, qk, vt, o, h, cs, ssp, partial, tgt, qk1, last, partial1, tgt1, total;
   int nnb;
 };
 
@@ -134,6 +134,14 @@ Layout plan(const gpt_cfg* c) {
   L.qk1 = off;
   if (c->looped) off += up((size_t)c->n_layer * M * (bf ? (H + Hkv) * D * 2 : (H + 2 * Hkv) * D * 4));
   L.last = off; off += up((size_t)c->batch * C * 4);  // prefill: each row's last position, normed
+  // nested bf16: the kfront=1 cross-entropy sums taken inside the lm_head pass (per row, column
+  // block and wavefront) and the kfront=1 target logits
+  L.partial1 = off;
+  L.tgt1 = off;
+  if (c->nested_c1 && bf) {
+    off += up(M * (size_t)L.nnb * 4 * 4);
+    L.tgt1 = off; off += up(M * 4);
+  }
   L.total = off;
   return L;
 }
@@ -244,6 +252,25 @@ gpt_status nested_layers(const gpt_cfg* c, const gpt_weights* w, const int32_t* 
     if (r == hipSuccess && g2.N > 0) r = gemm(bf, e, g2, s);
     return r;
   };
+  // bf16: every PrefixRMSNorm after the embedding's is applied inside the GEMMs that consume it.
+  // The residual pairs (out-projection, MLP down) write bf16(x) and per-slice sums of squares
+  // (slices of sw columns; c1 is a whole number of slices); the inner row block of a consumer
+  // takes the prefix's RMS as a row scale, the outer one the two-part scale (GemmArgs::pre_k).
+  // The final norm, which the lm_head reads for both logits, is materialised.
+  int sw = 0;
+  if (bf) {
+    const GemmArgs a = gemm_args(o, H * D, w->wo[0], c1, h1 * D, M, x, C);
+    const GemmArgs b = gemm_args(o, H * D, w->wo[0], C - c1, H * D, M, x + c1, C);
+    sw = gemm_pair_resid_slice_cols(a, b);
+    if (sw <= 0 || c1 % sw || (C - c1) % sw) sw = 0;  // materialised norms instead
+  }
+  const bool fused = sw > 0;
+  // row scales of the two row blocks of a consumer of the (un-normalised) stream
+  auto scale_pair = [&](GemmArgs& in1, GemmArgs& in2) {
+    in1.rs_ssp = ssp; in1.rs_n = c1 / sw; in1.rs_c = (float)c1; in1.eps = eps;
+    in2.rs_ssp = ssp; in2.rs_n = C / sw; in2.rs_c = (float)C; in2.eps = eps;
+    in2.pre_k = c1; in2.pre_n = c1 / sw; in2.pre_c = (float)c1;
+  };
   CK(launch_embed_norm(tokens, w->wte, bf, w->resid_lambda, w->x0_lambda, x0, x, xn, M, C, V,
                        eps, flags, s, nullptr, c1));
   for (int l = 0; l < c->n_layer; ++l) {
@@ -268,6 +295,7 @@ gpt_status nested_layers(const gpt_cfg* c, const gpt_weights* w, const int32_t* 
         g[r].v_head_off = r ? hkv1 : 0;
         g[r].cs = cs;  // fused RoPE + QK-norm (head_dim 64 or 128)
       }
+      if (fused && l > 0) scale_pair(g[0], g[1]);  // layer 0 reads the embedding's normed stream
       TIMED(tm, GPT_KERNEL_QKV, gemm2(EPI_QKV, g[0], g[1]));
       TIMED(tm, GPT_KERNEL_ATTENTION, launch_attn_bf16(qk, vt, o, B, T, H, Hkv, D, win,
                                                        c->attn_scale, s));
@@ -285,15 +313,21 @@ gpt_status nested_layers(const gpt_cfg* c, const gpt_weights* w, const int32_t* 
       CK(launch_attn_f32((const float*)qk, (float*)o, B, T, H, Hkv, D, win, c->attn_scale, s));
     }
     // x += o W_O^T: inner rows read the inner heads' outputs
-    TIMED(tm, GPT_KERNEL_ATTN_OUT,
-          gemm2(EPI_RESID, gemm_args(o, H * D, wo[0], c1, h1 * D, M, x, C),
-                gemm_args(o, H * D, wo[1], C - c1, H * D, M, x + c1, C)));
-    CK(launch_mix_norm(x, x0, w->resid_lambda, w->x0_lambda, l, false, xn, bf, M, C, eps, s, c1));
+    GemmArgs go[2] = {gemm_args(o, H * D, wo[0], c1, h1 * D, M, x, C),
+                      gemm_args(o, H * D, wo[1], C - c1, H * D, M, x + c1, C)};
+    if (fused)
+      for (int r = 0; r < 2; ++r) {
+        const int c0 = r ? c1 : 0;
+        go[r].xb = (bf16_t*)xn + c0; go[r].ssp = ssp; go[r].col_off = c0;
+      }
+    TIMED(tm, GPT_KERNEL_ATTN_OUT, gemm2(EPI_RESID, go[0], go[1]));
+    if (!fused) CK(launch_mix_norm(x, x0, w->resid_lambda, w->x0_lambda, l, false, xn, bf, M, C, eps, s, c1));
     // h = relu(xn W_1^T)^2
     char* hb = (char*)hbuf;
-    TIMED(tm, GPT_KERNEL_MLP_UP,
-          gemm2(EPI_RELU2, gemm_args(xn, C, w1[0], f1, c1, M, hb, F),
-                gemm_args(xn, C, w1[1], F - f1, C, M, hb + (size_t)f1 * es, F)));
+    GemmArgs gu[2] = {gemm_args(xn, C, w1[0], f1, c1, M, hb, F),
+                      gemm_args(xn, C, w1[1], F - f1, C, M, hb + (size_t)f1 * es, F)};
+    if (fused) scale_pair(gu[0], gu[1]);
+    TIMED(tm, GPT_KERNEL_MLP_UP, gemm2(EPI_RELU2, gu[0], gu[1]));
     // x += h W_2^T; the bf16 epilogue also applies the next layer's x0 mix
     const bool more = l + 1 < c->n_layer;
     GemmArgs gd[2] = {gemm_args(hbuf, F, w2[0], c1, f1, M, x, C),
@@ -305,8 +339,9 @@ gpt_status nested_layers(const gpt_cfg* c, const gpt_weights* w, const int32_t* 
         gd[r].x0 = x0 + c0; gd[r].lam = w->resid_lambda; gd[r].mu = w->x0_lambda; gd[r].layer = l + 1;
       }
     TIMED(tm, GPT_KERNEL_MLP_DOWN, gemm2(EPI_RESID, gd[0], gd[1]));
-    CK(launch_mix_norm(x, x0, w->resid_lambda, w->x0_lambda, l + 1, more && !bf, xn, bf, M, C, eps,
-                       s, c1));
+    if (!fused || !more)
+      CK(launch_mix_norm(x, x0, w->resid_lambda, w->x0_lambda, l + 1, more && !bf, xn, bf, M, C, eps,
+                         s, c1));
   }
   return GPT_OK;
 }
@@ -438,7 +473,25 @@ gpt_status run(const gpt_cfg* c, const gpt_weights* w, const int32_t* tokens,
   if (c->nested_c1) {
     const Split sp = split_of(c);
     if (gpt_status e = nested_layers(c, w, tokens, sp, L, ws, tm, s); e != GPT_OK) return e;
-    // the final (prefix-)normalised stream is in xn: full model, then the inner model
+    // The final (prefix-)normalised stream is in xn.  Its first c1 columns are RMSNorm of the
+    // inner model's stream, so the product over K in [0, c1) is the kfront=1 logits and the one
+    // over all K the full model's: one lm_head pass (bf16, losses only) takes the kfront=1
+    // cross-entropy sums when its main loop reaches K = c1.  With logits requested, two passes.
+    if (bf && loss1 && !logits && !logits1 && sp.c1 < C) {
+      float* partial1 = (float*)(ws + L.partial1);
+      float* tgt1 = (float*)(ws + L.tgt1);
+      GemmArgs g = gemm_args(xn, C, w->lm_head, V, C, M, nullptr, 0);
+      g.ldb = C;
+      g.targets = targets; g.partial = partial; g.tgt_logit = tgt; g.nnb = L.nnb; g.cap = c->softcap;
+      g.partial1 = partial1; g.nnb1 = 4 * L.nnb; g.pre_k = sp.c1;
+      TIMED(tm, GPT_KERNEL_LM_HEAD, launch_gemm_bf16(EPI_CE, g, s));
+      CK(launch_prefix_target_logit(xn, w->lm_head, targets, M, C, sp.c1, V, tgt1, s));
+      CK(launch_ce_finalize(partial, L.nnb, tgt, targets, tokens, M, V, c->softcap, loss, flags, s));
+      CK(launch_ce_mean(loss, targets, M, mean_loss, s));
+      CK(launch_ce_finalize(partial1, 4 * L.nnb, tgt1, targets, tokens, M, V, c->softcap, loss1, flags, s));
+      CK(launch_ce_mean(loss1, targets, M, mean1, s));
+      return GPT_OK;
+    }
     gpt_status e = lm_head_ce(bf, xn, w->lm_head, targets, tokens, M, C, V, c->softcap, loss,
                               mean_loss, logits, partial, tgt, L.nnb, flags, s, tm);
     if (e != GPT_OK || !want1) return e;

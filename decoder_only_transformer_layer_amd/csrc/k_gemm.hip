@@ -35,7 +35,11 @@ template <int E> constexpr bool is_resid = E == EPI_RESID || E == EPI_RESID_PROD
 // Kernel-internal cross-entropy variant that also writes the raw logits (a separate kernel:
 // the extra stores' addressing would otherwise cost the main loop registers).
 constexpr int EPI_CE_LOGITS = 7;
-template <int E> constexpr bool is_ce = E == EPI_CE || E == EPI_CE_LOGITS;
+// Kernel-internal cross-entropy variant that also evaluates the cross-entropy terms of the
+// partial product over input columns [0, g.pre_k) (the nested model's kfront=1 logits) when the
+// main loop reaches that K (see GemmArgs::partial1).
+constexpr int EPI_CE_PREFIX = 8;
+template <int E> constexpr bool is_ce = E == EPI_CE || E == EPI_CE_LOGITS || E == EPI_CE_PREFIX;
 
 // s_waitcnt immediate waiting until at most n vector-memory operations are outstanding
 // (gfx9 encoding: vmcnt[3:0] at bits 3:0 and vmcnt[5:4] at bits 15:14; expcnt and lgkmcnt
@@ -64,15 +68,60 @@ __device__ __forceinline__ void tile_of(int pid, int nbm, int nbn, int& bm, int&
   bn = in / gsz;
 }
 
+// 1 / sqrt(sum_{j < n} ssp[j][row] / c + eps): the RMS scale of one row from the per-slice sums of
+// squares a residual producer wrote (slice-major, M per slice).  Sixteen slices' loads are in
+// flight together; slice j < n4 adds into s4[j % 4] and the rest into s4[0], each in increasing j.
+__device__ __forceinline__ float row_rinv(const float* ssp, int n, float c, float eps, int row, int M) {
+  float s4[4] = {0.f, 0.f, 0.f, 0.f};
+  const int n4 = n & ~3;
+  for (int j0 = 0; j0 < n; j0 += 16) {
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = j0 + u < n ? ssp[(size_t)(j0 + u) * M + row] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      if (j0 + u < n4) s4[u & 3] += v[u];
+      else if (j0 + u < n) s4[0] += v[u];
+    }
+  }
+  return rsqrtf(((s4[0] + s4[1]) + (s4[2] + s4[3])) / c + eps);
+}
+
+// The prefix's and the whole row's RMS scales in one pass over the row's slices: returns
+// (1/rms over slices [0, n1) of width c1, 1/rms over slices [0, n) of width c), each summed in
+// row_rinv's order.
+__device__ __forceinline__ float2 row_rinv2(const float* ssp, int n1, float c1, int n, float c, float eps,
+                                            int row, int M) {
+  float s4[4] = {0.f, 0.f, 0.f, 0.f}, p4[4] = {0.f, 0.f, 0.f, 0.f};
+  const int n4 = n & ~3, n14 = n1 & ~3;
+  for (int j0 = 0; j0 < n; j0 += 16) {
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = j0 + u < n ? ssp[(size_t)(j0 + u) * M + row] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int j = j0 + u;
+      if (j < n4) s4[u & 3] += v[u];
+      else if (j < n) s4[0] += v[u];
+      if (j < n14) p4[u & 3] += v[u];
+      else if (j < n1) p4[0] += v[u];
+    }
+  }
+  return make_float2(rsqrtf(((p4[0] + p4[1]) + (p4[2] + p4[3])) / c1 + eps),
+                     rsqrtf(((s4[0] + s4[1]) + (s4[2] + s4[3])) / c + eps));
+}
+
 // One output tile (pid = its index in the GEMM's tile order) of C = A B^T with epilogue EPI.
-template <int BM, int BN, int WM, int WN, int EPI>
+// PRE: the tile may take a PrefixRMSNorm'd A as a two-part row scale (GemmArgs::pre_k); the
+// kernel then holds BM more floats of LDS for the per-row factor.
+template <int BM, int BN, int WM, int WN, int EPI, bool PRE = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses device-only types (buffer resources)
   constexpr int NT = WM * WN * 64;
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
   static_assert(FM * 32 == TM && FN * 32 == TN, "wave tile must be a multiple of 32");
 
-  __shared__ __attribute__((aligned(16))) bf16 lds[2 * (BM + BN) * BK];
+  __shared__ __attribute__((aligned(16))) bf16 lds[2 * (BM + BN) * BK + (PRE ? 4 * BM : 0)];
   bf16* const As = lds;
   bf16* const Bs = lds + 2 * BM * BK;
 
@@ -141,6 +190,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
     va[p] = ((lane >> 3) * lda + c) * 2;
     vb[p] = SAME_LD ? va[p] : ((lane >> 3) * ldb + c) * 2;
   }
+  // The odd-BI tiles pick the B offset at run time: as named scalars (an array element selected
+  // at run time can end up in scratch memory).
+  const int vb0 = vb[0], vb1 = vb[1];
   typedef __attribute__((address_space(3))) void* lds_ptr_t;
 #define GEMM_ISSUE(buf, k0)                                                                   \
   do {                                                                                       \
@@ -151,7 +203,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
     _Pragma("unroll") for (int i = 0; i < BI; ++i)                                           \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb,                                          \
         (lds_ptr_t)(Bs + (buf) * BN * BK + (wids * BI + i) * 512), 16,                      \
-        (BI % 2 == 0 ? vb[i & 1] : (((pb + i) & 1) ? vb[1] : vb[0])),                        \
+        (BI % 2 == 0 ? vb[i & 1] : (((pb + i) & 1) ? vb1 : vb0)),                            \
         (k0) * 2 + (wids * BI + i) * 16 * ldb, 0, 0);                                        \
   } while (0)
 
@@ -182,19 +234,129 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
       for (int fn = 0; fn < FN; ++fn)
         acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fm], fb[fn], acc[fm][fn], 0, 0, 0);
   };
+  // PrefixRMSNorm'd A (nested models): the product over input columns [0, pre_k) carries the
+  // prefix's scale 1/rms_p, the rest the whole row's 1/rms_a.  Once the K steps below pre_k are
+  // done the accumulators are multiplied by pref[row] = (1/rms_p) / (1/rms_a); the epilogue's row
+  // scale then applies 1/rms_a to the sum.
+  // Thread i < BM owns tile row i: its (up to 16) slice sums are loaded with the first operand
+  // tiles and summed when the main loop reaches pre_k, so their latency hides behind the first K
+  // steps; then 1/rms_a goes where the epilogue's row scale reads it (the last BM floats of LDS).
+  // More than 16 slices: computed before the main loop instead.
+  float* const pref = (float*)(lds + 2 * (BM + BN) * BK);
+  const int kpre = (PRE && g.pre_k > 0) ? g.pre_k / BK : -1;
+  constexpr int PV = PRE ? 16 : 1;
+  float pv[PV];
+  const bool pv_held = PRE && kpre > 0 && g.rs_n <= 16;
+  auto prefix_factors = [&]() {
+    if constexpr (PRE) {
+      if (kpre > 0) {
+        float* const ra = (float*)lds + (sizeof(lds) / 4 - BM);
+        if (pv_held) {
+          const int row = m0 + tid;
+#pragma unroll
+          for (int u = 0; u < PV; ++u)
+            pv[u] = (tid < BM && row < M && u < g.rs_n) ? g.rs_ssp[(size_t)u * M + row] : 0.f;
+        } else {
+          for (int i = tid; i < BM; i += NT) {
+            const int row = m0 + i;
+            const float2 r = row < M ? row_rinv2(g.rs_ssp, g.pre_n, g.pre_c, g.rs_n, g.rs_c, g.eps, row, M)
+                                     : make_float2(0.f, 0.f);
+            pref[i] = r.x / r.y;
+            ra[i] = r.y;
+          }
+        }
+      }
+    }
+  };
+  // the held sums, in row_rinv's order (slice j < n4 into s4[j % 4], the rest into s4[0])
+  auto prefix_finish = [&]() {
+    if constexpr (PRE) {
+      if (pv_held) {
+        float* const ra = (float*)lds + (sizeof(lds) / 4 - BM);
+        if (tid < BM) {
+          float s4[4] = {0.f, 0.f, 0.f, 0.f}, p4[4] = {0.f, 0.f, 0.f, 0.f};
+          const int n4 = g.rs_n & ~3, n14 = g.pre_n & ~3;
+#pragma unroll
+          for (int u = 0; u < PV; ++u) {
+            if (u < n4) s4[u & 3] += pv[u];
+            else if (u < g.rs_n) s4[0] += pv[u];
+            if (u < n14) p4[u & 3] += pv[u];
+            else if (u < g.pre_n) p4[0] += pv[u];
+          }
+          const float rp = rsqrtf(((p4[0] + p4[1]) + (p4[2] + p4[3])) / g.pre_c + g.eps);
+          const float rr = rsqrtf(((s4[0] + s4[1]) + (s4[2] + s4[3])) / g.rs_c + g.eps);
+          pref[tid] = m0 + tid < M ? rp / rr : 0.f;
+          ra[tid] = m0 + tid < M ? rr : 0.f;
+        }
+        __syncthreads();
+      }
+    }
+  };
+  auto prefix_rescale = [&]() {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 f = *(const f32x4*)(pref + wm * TM + fm * 32 + 8 * j + 4 * hl);
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[fm][fn][4 * j + i] *= f[i];
+      }
+  };
+  // EPI_CE_PREFIX: the cross-entropy terms of the partial product over columns [0, pre_k), per
+  // row and wavefront (no LDS: the operand tiles occupy all of it), to partial1.
+  auto prefix_ce = [&]() {
+    if constexpr (EPI == EPI_CE_PREFIX) {
+      const float k1 = 2.0f / g.cap * GPT_LOG2E, k2 = -2.0f * g.cap * GPT_LOG2E;
+      const int cb = n0 + wn * TN + rl;
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float sum = 0.f;
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) {
+            const float q = rcp_fast(1.0f + exp2_fast(acc[fm][fn][r] * k1));
+            sum += cb + fn * 32 < N ? exp2_fast(k2 * q) : 0.f;
+          }
+          sum = sum32(sum);
+          const int row = m0 + wm * TM + fm * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (rl == 0 && row < M) g.partial1[(size_t)row * g.nnb1 + bn * WN + wn] = sum;
+        }
+    }
+  };
+  const int kce = EPI == EPI_CE_PREFIX ? g.pre_k / BK : -1;
   GEMM_ISSUE(0, 0);
   if (nk > 1) {
     GEMM_ISSUE(1, BK);
+    prefix_factors();
     __builtin_amdgcn_s_waitcnt(vmcnt_le(AI + BI));
   } else {
+    prefix_factors();
     __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
   }
   __syncthreads();
 #define PIN __builtin_amdgcn_sched_barrier(0)
+  // The K steps run as two loops with the same body: [0, ksplit) and [ksplit, nk), where ksplit
+  // is the K step at which the prefix row scale or the prefix cross-entropy applies (nk if none),
+  // so that the code between them stays out of the loops' register allocation.
+  const int ksplit = kpre > 0 ? kpre : (kce > 0 ? kce : nk);
+  auto at_split = [&]() {
+    if constexpr (PRE) {
+      if (kpre > 0) {
+        prefix_finish();
+        prefix_rescale();
+      }
+    }
+    if constexpr (EPI == EPI_CE_PREFIX) {
+      if (kce > 0) prefix_ce();
+    }
+  };
   if constexpr (!ROLL) {
     bf16x8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
     rda(As, 0, fa0); rdb(Bs, 0, fb0);
-    for (int kt = 0; kt < nk; ++kt) {
+    auto kstep = [&](int kt) {
       const int buf = kt & 1;
       const bf16* Ab = As + buf * BM * BK;
       const bf16* Bb = Bs + buf * BN * BK;
@@ -212,6 +374,31 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
       // The next substep-0 fragments were issued among those MFMAs; settling the LDS counter
       // here keeps the waitcnt pass from waiting on fresh reads at the loop top.
       __builtin_amdgcn_s_waitcnt(lgkmcnt_0);
+    };
+    if constexpr (PRE || EPI == EPI_CE_PREFIX) {
+      for (int kt = 0; kt < ksplit; ++kt) kstep(kt);
+      if (ksplit < nk) {
+        at_split();
+        for (int kt = ksplit; kt < nk; ++kt) kstep(kt);
+      }
+    } else {
+      for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        const bf16* Ab = As + buf * BM * BK;
+        const bf16* Bb = Bs + buf * BN * BK;
+        PIN; rda(Ab, 1, fa1); rdb(Bb, 1, fb1); PIN; mm(fa0, fb0);
+        PIN; rda(Ab, 2, fa0); rdb(Bb, 2, fb0); PIN; mm(fa1, fb1);
+        PIN; rda(Ab, 3, fa1); rdb(Bb, 3, fb1); PIN; mm(fa0, fb0);
+        PIN;
+        __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
+        __syncthreads();
+        PIN;
+        if (kt + 2 < nk) GEMM_ISSUE(buf, (kt + 2) * BK);
+        if (kt + 1 < nk) { rda(As + (buf ^ 1) * BM * BK, 0, fa0); rdb(Bs + (buf ^ 1) * BN * BK, 0, fb0); }
+        PIN; mm(fa1, fb1);
+        PIN;
+        __builtin_amdgcn_s_waitcnt(lgkmcnt_0);
+      }
     }
   } else {
     bf16x8 fa0[FM], fa1[FM], fb[FN];
@@ -229,7 +416,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
       }
     };
     rda(As, 0, fa0); rdb(Bs, 0, fb);
-    for (int kt = 0; kt < nk; ++kt) {
+    auto kstep = [&](int kt) {
       const int buf = kt & 1;
       const bf16* Ab = As + buf * BM * BK;
       const bf16* Bb = Bs + buf * BN * BK;
@@ -243,6 +430,29 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
       rda(As + (buf ^ 1) * BM * BK, 0, fa0);
       PIN; mmroll(fa1, Bs + (buf ^ 1) * BN * BK, 0);
       __builtin_amdgcn_s_waitcnt(lgkmcnt_0);
+    };
+    if constexpr (PRE || EPI == EPI_CE_PREFIX) {
+      for (int kt = 0; kt < ksplit; ++kt) kstep(kt);
+      if (ksplit < nk) {
+        at_split();
+        for (int kt = ksplit; kt < nk; ++kt) kstep(kt);
+      }
+    } else {
+      for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        const bf16* Ab = As + buf * BM * BK;
+        const bf16* Bb = Bs + buf * BN * BK;
+        PIN; rda(Ab, 1, fa1); PIN; mmroll(fa0, Bb, 1);
+        rda(Ab, 2, fa0); PIN; mmroll(fa1, Bb, 2);
+        rda(Ab, 3, fa1); PIN; mmroll(fa0, Bb, 3);
+        __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
+        __syncthreads();
+        PIN;
+        if (kt + 2 < nk) GEMM_ISSUE(buf, (kt + 2) * BK);
+        rda(As + (buf ^ 1) * BM * BK, 0, fa0);
+        PIN; mmroll(fa1, Bs + (buf ^ 1) * BN * BK, 0);
+        __builtin_amdgcn_s_waitcnt(lgkmcnt_0);
+      }
     }
   }
 #undef PIN
@@ -263,10 +473,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
       float* rinv = (float*)lds + (sizeof(lds) / 4 - BM);  // past any epilogue staging
       __syncthreads();  // every wavefront is done with the operand tiles
       // slices are stored slice-major ([slice][M]): consecutive threads read consecutive rows
-      for (int i = tid; i < BM; i += NT) {
+      // (a prefix-scaled tile has its 1/rms_a there already)
+      if (kpre <= 0) for (int i = tid; i < BM; i += NT) {
         const int row = m0 + i;
         // Sixteen slices' loads are in flight together; slice j < n4 adds into s4[j % 4] and the
-        // rest into s4[0], each in increasing j.
+        // rest into s4[0], each in increasing j (the order of row_rinv).
         float s4[4] = {0.f, 0.f, 0.f, 0.f};
         if (row < M) {
           const int n4 = g.rs_n & ~3;
@@ -461,6 +672,44 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
             }
           }
           if (prod) put_ss(row, ss);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();  // reads of this group precede the next group's writes
+    }
+  } else if constexpr (EPI == EPI_QKV && TN == 96) {
+    // v-only launches (every column a v column, nqk == 0, no value embeddings): each 32-row group
+    // of the wavefront's tile is staged through wavefront-private LDS transposed ([col][t], bf16)
+    // and written as 16-byte runs of 8 positions of v^T [B][Hkv][D][T].
+    bf16* vt = (bf16*)g.vt;
+    constexpr int LV = 32 + 8;  // staging pitch (bf16)
+    static_assert(WM * WN * TN * LV * 2 <= (int)sizeof(lds), "v staging exceeds LDS");
+    bf16* const stg = lds + wid * TN * LV;
+    __syncthreads();  // every wavefront is done with the operand tiles
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {  // rows 8j + 4hl + (0..3): four consecutive t
+          bf16x4 v4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v4[i] = (bf16)acc[fm][fn][4 * j + i];
+          *(bf16x4*)(stg + (fn * 32 + rl) * LV + 8 * j + 4 * hl) = v4;
+        }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // 32 consecutive rows are 32 consecutive positions of one sequence (T % 32 == 0)
+      const int row0 = m0 + wm * TM + fm * 32;
+      const int bb = row0 / g.T, t0 = row0 - bb * g.T;
+#pragma unroll
+      for (int k = 0; k < TN * 4 / 64; ++k) {  // TN columns x 4 runs of 8 positions
+        const int idx = lane + 64 * k, cl = idx >> 2, ch = idx & 3;
+        const int col = n0 + wn * TN + cl;
+        if (col < N && row0 + ch * 8 < M) {
+          const int gg = g.v_head_off + col / g.D, d = col - (col / g.D) * g.D;
+          *(bf16x8*)(vt + ((size_t)(bb * g.Hkv + gg) * g.D + d) * g.T + t0 + ch * 8) =
+              *(const bf16x8*)(stg + cl * LV + ch * 8);
         }
       }
       __builtin_amdgcn_wave_barrier();  // reads of this group precede the next group's writes
@@ -725,11 +974,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) 
 
 // Two independent GEMMs with the same tile shape and epilogue in one launch: blocks
 // [0, nb1) are the tiles of g1, the rest those of g2.  Blocks are dispatched in order, so g1
-// is the one with the longer K and g2's shorter tiles fill in behind it.
-template <int BM, int BN, int WM, int WN, int EPI>
+// is the one with the longer K and g2's shorter tiles fill in behind it.  PRE: either may take a
+// PrefixRMSNorm'd A (GemmArgs::pre_k).
+template <int BM, int BN, int WM, int WN, int EPI, bool PRE>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_pair_kernel(GemmArgs g1, GemmArgs g2, int nb1) {
-  if ((int)blockIdx.x < nb1) gemm_tile<BM, BN, WM, WN, EPI>(g1, blockIdx.x);
-  else gemm_tile<BM, BN, WM, WN, EPI>(g2, (int)blockIdx.x - nb1);
+  if ((int)blockIdx.x < nb1) gemm_tile<BM, BN, WM, WN, EPI, PRE>(g1, blockIdx.x);
+  else gemm_tile<BM, BN, WM, WN, EPI, PRE>(g2, (int)blockIdx.x - nb1);
 }
 
 template <int BM, int BN, int WM, int WN>
@@ -746,9 +996,16 @@ hipError_t run_bf16(Epi epi, const GemmArgs& a, hipStream_t s) {
       else GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_RESID_MIX>), grid, NT, s, a);
       break;
     case EPI_QKV:
-      // the tile plan gives this epilogue 256-wide or 128-wide tiles only
-      if constexpr (BN != 256 && BN != 128) return hipErrorInvalidValue;
-      else GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_QKV>), grid, NT, s, a);
+      // the tile plan gives this epilogue 256-wide or 128-wide tiles, and 384-wide ones to
+      // launches of v columns only (no value embeddings)
+      if constexpr (BN == 384) {
+        if (a.nqk != 0 || a.ve != nullptr || a.T % 32) return hipErrorInvalidValue;
+        GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_QKV>), grid, NT, s, a);
+      } else if constexpr (BN != 256 && BN != 128) {
+        return hipErrorInvalidValue;
+      } else {
+        GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_QKV>), grid, NT, s, a);
+      }
       break;
     case EPI_CE:
       // 384-wide blocks only (the partial-sum layout has one column per block): 256-row tiles
@@ -757,7 +1014,8 @@ hipError_t run_bf16(Epi epi, const GemmArgs& a, hipStream_t s) {
         return hipErrorInvalidValue;
       } else if constexpr (BM == 256) {
         if (a.logits != nullptr) return hipErrorInvalidValue;
-        GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_CE>), grid, NT, s, a);
+        if (a.partial1 != nullptr) GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_CE_PREFIX>), grid, NT, s, a);
+        else GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_CE>), grid, NT, s, a);
       } else {
         if (a.logits == nullptr) return hipErrorInvalidValue;
         GPTK_LAUNCH((gemm_bf16_kernel<BM, BN, WM, WN, EPI_CE_LOGITS>), grid, NT, s, a);
@@ -768,33 +1026,48 @@ hipError_t run_bf16(Epi epi, const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN>
-hipError_t run_bf16_pair(Epi epi, const GemmArgs& a, const GemmArgs& b, hipStream_t s) {
+template <int BM, int BN, int WM, int WN, bool PRE>
+hipError_t run_bf16_pair_pre(Epi epi, const GemmArgs& a, const GemmArgs& b, hipStream_t s) {
   const int na = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   const int grid = na + ((b.M + BM - 1) / BM) * ((b.N + BN - 1) / BN);
   constexpr int NT = WM * WN * 64;
   if constexpr (WM > 2 && BN != 192) {  // tall 256/128-wide layouts: the fused q/k/v epilogue only
     if (epi != EPI_QKV) return hipErrorInvalidValue;
-    GPTK_LAUNCH((gemm_bf16_pair_kernel<BM, BN, WM, WN, EPI_QKV>), grid, NT, s, a, b, na);
+    GPTK_LAUNCH((gemm_bf16_pair_kernel<BM, BN, WM, WN, EPI_QKV, PRE>), grid, NT, s, a, b, na);
+  } else if constexpr (PRE) {  // consumers of a PrefixRMSNorm'd input: ReLU^2 (MLP up) or q/k/v
+    switch (epi) {
+      case EPI_RELU2: GPTK_LAUNCH((gemm_bf16_pair_kernel<BM, BN, WM, WN, EPI_RELU2, PRE>), grid, NT, s, a, b, na); break;
+      case EPI_QKV:
+        if constexpr (BN == 192) return hipErrorInvalidValue;  // q/k/v take 256- or 128-wide tiles
+        else GPTK_LAUNCH((gemm_bf16_pair_kernel<BM, BN, WM, WN, EPI_QKV, PRE>), grid, NT, s, a, b, na);
+        break;
+      default: return hipErrorInvalidValue;
+    }
   } else {
     switch (epi) {
-      case EPI_STORE: GPTK_LAUNCH((gemm_bf16_pair_kernel<BM, BN, WM, WN, EPI_STORE>), grid, NT, s, a, b, na); break;
-      case EPI_RELU2: GPTK_LAUNCH((gemm_bf16_pair_kernel<BM, BN, WM, WN, EPI_RELU2>), grid, NT, s, a, b, na); break;
+      case EPI_STORE: GPTK_LAUNCH((gemm_bf16_pair_kernel<BM, BN, WM, WN, EPI_STORE, PRE>), grid, NT, s, a, b, na); break;
+      case EPI_RELU2: GPTK_LAUNCH((gemm_bf16_pair_kernel<BM, BN, WM, WN, EPI_RELU2, PRE>), grid, NT, s, a, b, na); break;
       case EPI_RESID:
         if ((a.xb == nullptr) != (b.xb == nullptr) || (a.lam == nullptr) != (b.lam == nullptr))
           return hipErrorInvalidValue;  // both halves take the same residual variant
-        if (a.xb == nullptr) GPTK_LAUNCH((gemm_bf16_pair_kernel<BM, BN, WM, WN, EPI_RESID>), grid, NT, s, a, b, na);
-        else if (a.lam == nullptr) GPTK_LAUNCH((gemm_bf16_pair_kernel<BM, BN, WM, WN, EPI_RESID_PROD>), grid, NT, s, a, b, na);
-        else GPTK_LAUNCH((gemm_bf16_pair_kernel<BM, BN, WM, WN, EPI_RESID_MIX>), grid, NT, s, a, b, na);
+        if (a.xb == nullptr) GPTK_LAUNCH((gemm_bf16_pair_kernel<BM, BN, WM, WN, EPI_RESID, PRE>), grid, NT, s, a, b, na);
+        else if (a.lam == nullptr) GPTK_LAUNCH((gemm_bf16_pair_kernel<BM, BN, WM, WN, EPI_RESID_PROD, PRE>), grid, NT, s, a, b, na);
+        else GPTK_LAUNCH((gemm_bf16_pair_kernel<BM, BN, WM, WN, EPI_RESID_MIX, PRE>), grid, NT, s, a, b, na);
         break;
       case EPI_QKV:
         if constexpr (BN == 192) return hipErrorInvalidValue;  // q/k/v take 256- or 128-wide tiles
-        else GPTK_LAUNCH((gemm_bf16_pair_kernel<BM, BN, WM, WN, EPI_QKV>), grid, NT, s, a, b, na);
+        else GPTK_LAUNCH((gemm_bf16_pair_kernel<BM, BN, WM, WN, EPI_QKV, PRE>), grid, NT, s, a, b, na);
         break;
       default: return hipErrorInvalidValue;
     }
   }
   return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN>
+hipError_t run_bf16_pair(Epi epi, const GemmArgs& a, const GemmArgs& b, hipStream_t s) {
+  if (a.pre_k > 0 || b.pre_k > 0) return run_bf16_pair_pre<BM, BN, WM, WN, true>(epi, a, b, s);
+  return run_bf16_pair_pre<BM, BN, WM, WN, false>(epi, a, b, s);
 }
 
 // ------------------------------------------------------------------------------ fp32 path
@@ -1022,11 +1295,49 @@ hipError_t launch_gemm_bf16(Epi epi, const GemmArgs& a, hipStream_t s) {
   if (a.K % BK || a.M <= 0 || a.N <= 0) return hipErrorInvalidValue;
   if (epi == EPI_CE) {  // 384-wide column blocks, as gemm_bf16_ce_blocks counts them
     if (a.lda != a.ldb) return hipErrorInvalidValue;
+    if (a.partial1 != nullptr && (a.logits != nullptr || a.pre_k <= 0 || a.pre_k % BK || a.pre_k >= a.K ||
+                                  a.nnb1 != 4 * a.nnb))
+      return hipErrorInvalidValue;
     // Writing the logits too takes 128-row tiles: the staged stores' addressing would otherwise
     // push the 256-row tiles' main loop past the register file.
     return a.logits != nullptr ? run_bf16<128, 384, 2, 4>(epi, a, s) : run_bf16<256, 384, 2, 4>(epi, a, s);
   }
   if (epi == EPI_QKV && a.cs != nullptr && a.D != 128 && a.D != 64) return hipErrorInvalidValue;
+  // Fused q/k/v: the q and k columns as one GEMM (256-wide tiles, whole heads per wavefront) and
+  // the v columns as another on 256x384 tiles when that takes fewer rounds of the CUs than one
+  // plan for all columns (e.g. d24: 3 rounds of q|k + 1 of v, against 4.5 for the whole).
+  if (epi == EPI_QKV && a.cs != nullptr && a.ve == nullptr && a.nqk > 0 && a.nqk < a.N &&
+      a.nqk % 256 == 0 && (a.N - a.nqk) % 384 == 0 && a.T % 32 == 0 && a.lda == a.ldb &&
+      seg_ok(a, 256)) {
+    const int ncu = cu_count();
+    auto cost = [&](const Plan& q, int n) {
+      const long nbm = (a.M + 255) / 256, t = nbm * (n / 256);
+      if (q.split_cols <= 0) return (double)((t + ncu - 1) / ncu);
+      const long c1 = q.split_cols / 256;
+      return (double)(nbm * c1 / ncu) + (double)((nbm * (n / 256 - c1) * 2 + ncu - 1) / ncu) * 0.5 / 0.75;
+    };
+    const Plan whole = plan_gemm(epi, a.M, a.N, a.nseg0, a.nseg1, ncu);
+    const Plan qk = plan_gemm(epi, a.M, a.nqk, a.nseg0, a.nseg1, ncu);
+    const long vt = (long)((a.M + 255) / 256) * ((a.N - a.nqk) / 384);
+    const double c_split = cost(qk, a.nqk) + (double)((vt + ncu - 1) / ncu) * 1.5;
+    if (whole.tiles == Tiles::T256 && qk.tiles == Tiles::T256 && c_split < cost(whole, a.N)) {
+      GemmArgs h = a;
+      h.N = a.nqk;
+      hipError_t e;
+      if (qk.split_cols > 0) {
+        GemmArgs head = h;
+        head.N = qk.split_cols;
+        if (head.nseg0 > head.N) head.nseg0 = head.N;
+        if (head.nseg0 + head.nseg1 > head.N) head.nseg1 = head.N - head.nseg0;
+        e = run_main(epi, head, s);
+        if (e == hipSuccess) e = run_narrow(epi, shift_cols(h, epi, qk.split_cols), s);
+      } else {
+        e = run_main(epi, h, s);
+      }
+      if (e != hipSuccess) return e;
+      return run_bf16<256, 384, 2, 4>(epi, shift_cols(a, epi, a.nqk), s);
+    }
+  }
   const Plan p = plan_gemm(epi, a.M, a.N, a.nseg0, a.nseg1, cu_count(), a.lda == a.ldb);
   if (p.tiles == Tiles::T384) return run_bf16<256, 384, 2, 4>(epi, a, s);  // slices of 96 columns
   if (p.tiles == Tiles::T192) return run_bf16<256, 192, 4, 2>(epi, a, s);  // slices of 96 columns
@@ -1043,17 +1354,13 @@ hipError_t launch_gemm_bf16(Epi epi, const GemmArgs& a, hipStream_t s) {
   return run_main(epi, a, s);
 }
 
-hipError_t launch_gemm_bf16_pair(Epi epi, const GemmArgs& a, const GemmArgs& b, hipStream_t s) {
-  if (a.N <= 0) return launch_gemm_bf16(epi, b, s);
-  if (b.N <= 0) return launch_gemm_bf16(epi, a, s);
-  if (a.K % BK || b.K % BK || a.M <= 0 || b.M <= 0 || epi == EPI_CE) return hipErrorInvalidValue;
+// Tile shape of a grouped pair (launch_gemm_bf16_pair): 256x192 tiles (wavefront tiles of 64x96)
+// instead of 256x256 when that fills the CUs in fewer rounds, at ~0.9 of the larger tiles' rate:
+// e.g. the nested model's MLP-down and out-projection pairs at M = 8192 make exactly 256 tiles
+// of 256x192 against 224 of 256x256, whose longest ones then set the time.
+enum class PairTiles { T192, T256, T128, SEPARATE };
+PairTiles plan_pair(Epi epi, const GemmArgs& a, const GemmArgs& b) {
   const bool fused = epi == EPI_QKV && (a.cs != nullptr || b.cs != nullptr);
-  if (fused && (a.cs == nullptr || b.cs == nullptr || a.D != b.D || (a.D != 128 && a.D != 64)))
-    return hipErrorInvalidValue;
-  // 256x192 tiles (wavefront tiles of 64x96) instead of 256x256 when that fills the CUs in fewer
-  // rounds, at ~0.9 of the larger tiles' rate: e.g. the nested model's MLP-down and
-  // out-projection pairs at M = 8192 make exactly 256 tiles of 256x192 against 224 of 256x256,
-  // whose longest ones then set the time.
   if (!fused && epi != EPI_QKV && a.N % 192 == 0 && b.N % 192 == 0 && seg_ok(a, 192) && seg_ok(b, 192)) {
     const int ncu = cu_count();
     auto rounds = [&](int bn) {
@@ -1061,14 +1368,42 @@ hipError_t launch_gemm_bf16_pair(Epi epi, const GemmArgs& a, const GemmArgs& b, 
       return (double)((t + ncu - 1) / ncu);
     };
     const double c256 = seg_ok(a, 256) && seg_ok(b, 256) ? rounds(256) : 1e30;
-    if (rounds(192) * 0.75 / 0.9 < c256) return run_bf16_pair<256, 192, 4, 2>(epi, a, b, s);
+    if (rounds(192) * 0.75 / 0.9 < c256) return PairTiles::T192;
   }
-  if (seg_ok(a, 256) && seg_ok(b, 256))
-    return fused ? run_bf16_pair<256, 256, 4, 2>(epi, a, b, s) : run_bf16_pair<256, 256, 2, 4>(epi, a, b, s);
-  if (seg_ok(a, 128) && seg_ok(b, 128))
-    return fused ? run_bf16_pair<256, 128, 4, 1>(epi, a, b, s) : run_bf16_pair<256, 128, 2, 2>(epi, a, b, s);
+  if (seg_ok(a, 256) && seg_ok(b, 256)) return PairTiles::T256;
+  if (seg_ok(a, 128) && seg_ok(b, 128)) return PairTiles::T128;
+  return PairTiles::SEPARATE;
+}
+
+hipError_t launch_gemm_bf16_pair(Epi epi, const GemmArgs& a, const GemmArgs& b, hipStream_t s) {
+  if (a.N <= 0) return launch_gemm_bf16(epi, b, s);
+  if (b.N <= 0) return launch_gemm_bf16(epi, a, s);
+  if (a.K % BK || b.K % BK || a.M <= 0 || b.M <= 0 || epi == EPI_CE) return hipErrorInvalidValue;
+  if ((a.pre_k > 0 && (a.pre_k % BK || a.rs_ssp == nullptr)) || (b.pre_k > 0 && (b.pre_k % BK || b.rs_ssp == nullptr)))
+    return hipErrorInvalidValue;
+  const bool fused = epi == EPI_QKV && (a.cs != nullptr || b.cs != nullptr);
+  if (fused && (a.cs == nullptr || b.cs == nullptr || a.D != b.D || (a.D != 128 && a.D != 64)))
+    return hipErrorInvalidValue;
+  switch (plan_pair(epi, a, b)) {
+    case PairTiles::T192: return run_bf16_pair<256, 192, 4, 2>(epi, a, b, s);
+    case PairTiles::T256:
+      return fused ? run_bf16_pair<256, 256, 4, 2>(epi, a, b, s) : run_bf16_pair<256, 256, 2, 4>(epi, a, b, s);
+    case PairTiles::T128:
+      return fused ? run_bf16_pair<256, 128, 4, 1>(epi, a, b, s) : run_bf16_pair<256, 128, 2, 2>(epi, a, b, s);
+    default: break;
+  }
+  if (a.pre_k > 0 || b.pre_k > 0) return hipErrorInvalidValue;  // the single-GEMM tiles take no prefix scale
   const hipError_t e = launch_gemm_bf16(epi, a, s);
   return e != hipSuccess ? e : launch_gemm_bf16(epi, b, s);
+}
+
+int gemm_pair_resid_slice_cols(const GemmArgs& a, const GemmArgs& b) {
+  switch (plan_pair(EPI_RESID, a, b)) {
+    case PairTiles::T192: return 96;   // 4 x 2 wavefronts of 64 x 96
+    case PairTiles::T256: return 64;   // 2 x 4 wavefronts of 128 x 64
+    case PairTiles::T128: return 64;   // 2 x 2 wavefronts of 128 x 64
+    default: return 0;                 // launched separately: slices of each GEMM's own plan
+  }
 }
 
 hipError_t launch_gemm_f32(Epi epi, const GemmArgs& a, hipStream_t s) {

@@ -61,6 +61,32 @@ __global__ __launch_bounds__(1024) void ce_mean_kernel(const float* __restrict__
   if (tid == 0) *mean = scnt[0] > 0 ? (float)(ssum[0] / (double)scnt[0]) : NAN;
 }
 
+// Raw logit of each row's target from the first c1 columns of the row and of the target's W_U
+// row (bf16 operands, fp32 sum), one wavefront per row: the kfront=1 logit of a nested model,
+// whose cross-entropy sums the lm_head pass takes at K = c1 ("Fully Nested Transformers": the
+// prefix cross-entropy).  Rows whose target is -1 or out of range get 0 (the loss kernel reports
+// them).
+__global__ __launch_bounds__(256) void prefix_target_logit_kernel(
+    const bf16* __restrict__ x, const bf16* __restrict__ wu, const int32_t* __restrict__ targets,
+    int M, int C, int c1, int V, float* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const int y = targets[row];
+  float s = 0.f;
+  if (y >= 0 && y < V) {
+    const bf16* xr = x + (size_t)row * C;
+    const bf16* wr = wu + (size_t)y * C;
+    for (int k = lane * 8; k < c1; k += 64 * 8) {
+      const bf16x8 a = *(const bf16x8*)(xr + k), b = *(const bf16x8*)(wr + k);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s = fmaf((float)a[e], (float)b[e], s);
+    }
+  }
+  s = wave_sum(s);
+  if (lane == 0) out[row] = s;
+}
+
 __global__ void softcap_kernel(float* __restrict__ z, size_t n, float cap) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) z[i] = cap * tanhf(z[i] / cap);
@@ -88,6 +114,14 @@ hipError_t launch_ce_finalize(const float* partial, int nnb, const float* tgt_lo
                               float* loss, unsigned* flags, hipStream_t s) {
   ce_finalize_kernel<<<(M + 3) / 4, 256, 0, s>>>(partial, nnb, tgt_logit, targets, tokens, M, V, cap,
                                                   loss, flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefix_target_logit(const void* x, const void* wu, const int32_t* targets, int M,
+                                      int C, int c1, int V, float* out, hipStream_t s) {
+  if (c1 % 8 || C % 8 || c1 > C) return hipErrorInvalidValue;
+  prefix_target_logit_kernel<<<(M + 3) / 4, 256, 0, s>>>((const bf16*)x, (const bf16*)wu, targets, M, C,
+                                                          c1, V, out);
   return hipGetLastError();
 }
 

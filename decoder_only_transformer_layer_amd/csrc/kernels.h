@@ -133,6 +133,10 @@ struct GemmArgs {
   // is multiplied by rsqrt(sum_j rs_ssp[j][row] / rs_c + eps) before the epilogue's own work,
   // i.e. the GEMM computes RMSNorm(A) W^T from A and its row sums of squares.
   const float* rs_ssp; int rs_n; float rs_c;
+  // Prefix row scale (pair launches only; consumers of a PrefixRMSNorm'd A, nested models): if
+  // pre_k > 0 (a multiple of 64, rs_ssp set), the product over input columns [0, pre_k) is scaled
+  // by rsqrt(sum_{j < pre_n} rs_ssp[j][row] / pre_c + eps) and the rest by the row scale above.
+  int pre_k, pre_n; float pre_c;
   // Residual producer (EPI_RESID, bf16 path): if xb is set, after x += acc the epilogue
   // optionally mixes x = lam[layer] x + mu[layer] x0 (when lam != NULL), stores x, a bf16 copy
   // of x to xb [M, ldo], and per-row sums of squares over each column slice of width
@@ -145,6 +149,11 @@ struct GemmArgs {
   float* logits;                          // CE: optional [M][N] raw fp32 logits (softcap applied later)
   int nnb;                                // CE: number of column blocks
   float cap;                              // CE: softcap
+  // CE (256-row tiles, no logits): if partial1 is set, the cross-entropy terms of the partial
+  // product over input columns [0, pre_k) (pre_k a multiple of 64, < K) are also summed, per row
+  // and wavefront: partial1[row][nnb1] with nnb1 = 4 * nnb (column block b, wavefront w at
+  // 4b + w); the targets' logits of that product are not picked up.
+  float* partial1; int nnb1;
 };
 
 // bf16 inputs, fp32 accumulation on MFMA.  Returns hipErrorInvalidValue for shapes the
@@ -155,6 +164,9 @@ int gemm_bf16_ce_blocks(int N);
 // Width of the column slices whose per-row sums of squares an M x N RESID GEMM with xb set
 // writes (ssp [N / width][M]); divides N whenever N % 64 == 0.
 int gemm_resid_slice_cols(int M, int N);
+// Width of the slices a RESID pair (launch_gemm_bf16_pair with xb set) writes for these two
+// GEMMs, or 0 if the pair would run as two separate launches.
+int gemm_pair_resid_slice_cols(const GemmArgs& a, const GemmArgs& b);
 // fp32 SIMT GEMM (small configurations).
 hipError_t launch_gemm_f32(Epi epi, const GemmArgs& a, hipStream_t s);
 // bf16: two independent GEMMs (same epilogue kind) in one launch, a's tiles dispatched first
@@ -181,6 +193,10 @@ hipError_t launch_attn_f32(const float* qkv, float* o, int B, int T, int H, int 
 hipError_t launch_ce_finalize(const float* partial, int nnb, const float* tgt_logit,
                               const int32_t* targets, const int32_t* tokens, int M, int V, float cap,
                               float* loss, unsigned* flags, hipStream_t s);
+// bf16: out[row] = sum_{k < c1} x[row][k] * wu[targets[row]][k] in fp32 (rows C apart; 0 where the
+// target is -1 or outside [0, V)): the raw target logit of the product over the first c1 columns.
+hipError_t launch_prefix_target_logit(const void* x, const void* wu, const int32_t* targets, int M,
+                                      int C, int c1, int V, float* out, hipStream_t s);
 // z = cap * tanh(z / cap) in place over n floats.
 hipError_t launch_softcap(float* z, size_t n, float cap, hipStream_t s);
 // Zero n 32-bit words with a kernel (no memset node, so the call stays graph-capturable).
