@@ -600,6 +600,8 @@ static gpt_status validate_decode(const gpt_cfg* c) {
   const gpt_status st = validate(c);
   if (st != GPT_OK) return st;
   if (c->batch > 32 || c->seq_len > 8192 || c->n_head / c->n_kv_head > 8) return GPT_E_UNSUPPORTED;
+  // bf16 products split K and the residual-norm kernel sums their partials, up to this width
+  if (c->dtype == GPT_BF16 && c->d_model > mix_norm_add_max_cols()) return GPT_E_UNSUPPORTED;
   if (any_ve(c) || c->looped || c->nested_c1) return GPT_E_UNSUPPORTED;
   return GPT_OK;
 }

@@ -207,6 +207,26 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
         (k0) * 2 + (wids * BI + i) * 16 * ldb, 0, 0);                                        \
   } while (0)
 
+  // Row-scale inputs staged early: a consumer of an un-normalised A (row scale from rs_ssp) has
+  // the slice sums of its tile rows copied into LDS by DMA during the second-to-last K step, into
+  // the buffer that step frees (the last step reads the other one), so the epilogue's row scale
+  // reads LDS instead of waiting on memory.  Interior row blocks with at most 16 slices; not the
+  // cross-entropy tiles (their epilogue holds too many registers already).
+  constexpr bool SS_OK = !is_resid<EPI> && !is_ce<EPI>;
+  const bool stage_ss = SS_OK && !PRE && g.rs_ssp != nullptr && nk >= 2 && g.rs_n <= 16 && m0 + BM <= M &&
+                        (long)g.rs_n * M * 4 < 0x7fffffffL;
+  const int ss_buf = nk & 1;  // the buffer the second-to-last K step frees
+#define SS_ISSUE(buf)                                                                         \
+  do {                                                                                       \
+    const __amdgpu_buffer_rsrc_t rss = __builtin_amdgcn_make_buffer_rsrc(                    \
+        (void*)(g.rs_ssp + m0), (short)0, (int)(((long)g.rs_n * M - m0) * 4), 0x00020000);   \
+    for (int j = wids; j < g.rs_n; j += NT / 64)                                              \
+      for (int q = 0; q < BM / 256; ++q)                                                      \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rss,                                         \
+          (lds_ptr_t)((float*)(As + (buf) * BM * BK) + j * BM + q * 256), 16, lane * 16,      \
+          (j * M + q * 256) * 4, 0, 0);                                                       \
+  } while (0)
+
   // Software pipeline over 16-wide k-substeps with two fragment register sets: the reads for
   // substep s+1 are issued before the MFMAs of substep s.  The barrier that retires a K step's
   // buffer sits before that step's last 16 MFMAs, whose operands are already in registers, so
@@ -368,6 +388,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
       __syncthreads();                          // everyone's too; buffer `buf` fully read
       PIN;
       if (kt + 2 < nk) GEMM_ISSUE(buf, (kt + 2) * BK);
+      else if (SS_OK && stage_ss && kt + 2 == nk) SS_ISSUE(buf);
       if (kt + 1 < nk) { rda(As + (buf ^ 1) * BM * BK, 0, fa0); rdb(Bs + (buf ^ 1) * BN * BK, 0, fb0); }
       PIN; mm(fa1, fb1);
       PIN;
@@ -394,6 +415,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
         __syncthreads();
         PIN;
         if (kt + 2 < nk) GEMM_ISSUE(buf, (kt + 2) * BK);
+      else if (SS_OK && stage_ss && kt + 2 == nk) SS_ISSUE(buf);
         if (kt + 1 < nk) { rda(As + (buf ^ 1) * BM * BK, 0, fa0); rdb(Bs + (buf ^ 1) * BN * BK, 0, fb0); }
         PIN; mm(fa1, fb1);
         PIN;
@@ -427,6 +449,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
       __syncthreads();                          // everyone's too; buffer `buf` fully read
       PIN;
       if (kt + 2 < nk) GEMM_ISSUE(buf, (kt + 2) * BK);
+      else if (SS_OK && stage_ss && kt + 2 == nk) SS_ISSUE(buf);
       rda(As + (buf ^ 1) * BM * BK, 0, fa0);
       PIN; mmroll(fa1, Bs + (buf ^ 1) * BN * BK, 0);
       __builtin_amdgcn_s_waitcnt(lgkmcnt_0);
@@ -449,6 +472,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
         __syncthreads();
         PIN;
         if (kt + 2 < nk) GEMM_ISSUE(buf, (kt + 2) * BK);
+      else if (SS_OK && stage_ss && kt + 2 == nk) SS_ISSUE(buf);
         rda(As + (buf ^ 1) * BM * BK, 0, fa0);
         PIN; mmroll(fa1, Bs + (buf ^ 1) * BN * BK, 0);
         __builtin_amdgcn_s_waitcnt(lgkmcnt_0);
@@ -457,6 +481,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
   }
 #undef PIN
 #undef GEMM_ISSUE
+#undef SS_ISSUE
 
   // ---------------------------------------------------------------- epilogues
   // acc[fm][fn][r] is C[row][col] with row = m0 + wm*TM + fm*32 + 8*(r/4) + 4*hl + r%4 and
@@ -474,7 +499,19 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
       __syncthreads();  // every wavefront is done with the operand tiles
       // slices are stored slice-major ([slice][M]): consecutive threads read consecutive rows
       // (a prefix-scaled tile has its 1/rms_a there already)
-      if (kpre <= 0) for (int i = tid; i < BM; i += NT) {
+      if (kpre <= 0 && stage_ss) {
+        // the slice sums staged in LDS by SS_ISSUE, summed in row_rinv's order
+        const float* ssl = (const float*)(As + ss_buf * BM * BK);
+        for (int i = tid; i < BM; i += NT) {
+          float s4[4] = {0.f, 0.f, 0.f, 0.f};
+          const int n4 = g.rs_n & ~3;
+          for (int j = 0; j < g.rs_n; ++j) {
+            if (j < n4) s4[j & 3] += ssl[j * BM + i];
+            else s4[0] += ssl[j * BM + i];
+          }
+          rinv[i] = rsqrtf(((s4[0] + s4[1]) + (s4[2] + s4[3])) / g.rs_c + g.eps);
+        }
+      } else if (kpre <= 0) for (int i = tid; i < BM; i += NT) {
         const int row = m0 + i;
         // Sixteen slices' loads are in flight together; slice j < n4 adds into s4[j % 4] and the
         // rest into s4[0], each in increasing j (the order of row_rinv).

@@ -312,6 +312,8 @@ hipError_t launch_embed_norm(const int32_t* tokens, const void* wte, bool wbf16,
   });
 }
 
+int mix_norm_add_max_cols() { return 4 * AMN_NTH * AMN_NP; }
+
 hipError_t launch_mix_norm(float* x, const float* x0, const float* lam, const float* mu, int layer,
                            bool mix, void* xn, bool xbf16, int M, int C, float eps, hipStream_t s,
                            int c1, const float* add, int add_ks) {

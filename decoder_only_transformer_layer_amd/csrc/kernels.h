@@ -51,6 +51,8 @@ hipError_t launch_embed_norm(const int32_t* tokens, const void* wte, bool wbf16,
 hipError_t launch_mix_norm(float* x, const float* x0, const float* lam, const float* mu, int layer,
                            bool mix, void* xn, bool xbf16, int M, int C, float eps, hipStream_t s,
                            int c1 = 0, const float* add = nullptr, int add_ks = 0);
+// Widest row (C) launch_mix_norm takes with partials to add (add != NULL).
+int mix_norm_add_max_cols();
 
 // fp32 path value embedding, in place on the v columns of qkv [M][ld] (v head h at column
 // voff + h*D): v += 3 sigmoid(xn[m][0:12] . gate[h]) * ve[tokens[m]][h*D : (h+1)*D].

@@ -219,7 +219,7 @@ gpt_status gpt_fwd_loss_nested(const gpt_cfg *cfg, const gpt_weights *w, const i
  * of the same row filled and writing those of pos[b] into it; its logits are those the full
  * forward gives at position pos[b] of the sequence so far (attention is causal).  Here
  * cfg->batch is the number of rows (1..32) and cfg->seq_len the cache capacity T (<= 8192;
- * at most 8 query heads per KV head);
+ * at most 8 query heads per KV head; with GPT_BF16, d_model <= 4096);
  * the per-layer windows apply as in the forward.  Base models only: no value embeddings,
  * looped trunk or nested model (GPT_E_UNSUPPORTED).
  *

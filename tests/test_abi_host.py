@@ -214,8 +214,12 @@ def test_decode_validation_and_argument_errors(lib):
     c = gf.make_cfg(p)
     assert gf.gpt_kv_cache_bytes(c) == 24 * 2 * 8 * 12 * 2048 * 128 * 2
     assert gf.gpt_decode_workspace_bytes(c) > 0
+    # bf16 d_model beyond the residual-norm kernel's 4096 columns: refused before any launch (the
+    # forward itself takes it)
+    wide = p.with_(d_model=8192, n_head=64, n_kv_head=64, mlp_dim=4 * 8192, n_layer=2)
+    assert gf.gpt_validate(gf.make_cfg(wide)) == gf.GPT_OK
     for bad in (p.with_(batch=33), p.with_(seq_len=16384), gptdata.preset("d24gve"),
-                gptdata.preset("d24loop"), gptdata.preset("d24nest")):
+                gptdata.preset("d24loop"), gptdata.preset("d24nest"), wide):
         assert gf.gpt_kv_cache_bytes(gf.make_cfg(bad)) == 0
         assert gf.gpt_decode_workspace_bytes(gf.make_cfg(bad)) == 0
     w = _weights(c.n_layer)
@@ -235,6 +239,7 @@ def test_decode_validation_and_argument_errors(lib):
     assert call(wsb=need - 1) == gf.GPT_E_WORKSPACE
     assert call(cfg=gf.make_cfg(p.with_(batch=33))) == gf.GPT_E_UNSUPPORTED
     assert call(cfg=gf.make_cfg(gptdata.preset("d24gve"))) == gf.GPT_E_UNSUPPORTED
+    assert call(cfg=gf.make_cfg(wide)) == gf.GPT_E_UNSUPPORTED
     pw = gf.gpt_prefill_workspace_bytes(c)
     assert pw == gf.gpt_workspace_bytes(c) > 0
     Pf = lambda cfg=c, plen=64, tokens=F, cache=CACHE, logits=F, ws=WS, wsb=pw: lib.gpt_prefill(
