@@ -134,13 +134,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
   tile_of<4>(pid, nbm, nbn, bm, bn);  // 4 row blocks per group: ~0.6-0.9 % faster than 8 or 16 at d24
   const int m0 = bm * BM, n0 = bn * BN;
 
-  // B row segment holding this column block (segment boundaries are multiples of BN).
-  const bf16* Bseg;
-  int nb0, nrows;
-  if (n0 < g.nseg0) { Bseg = (const bf16*)g.B0; nb0 = n0; nrows = g.nseg0; }
-  else if (n0 < g.nseg0 + g.nseg1) { Bseg = (const bf16*)g.B1; nb0 = n0 - g.nseg0; nrows = g.nseg1; }
-  else { Bseg = (const bf16*)g.B2; nb0 = n0 - g.nseg0 - g.nseg1; nrows = N - g.nseg0 - g.nseg1; }
-
   const bf16* const A = (const bf16*)g.A;
   const int lda = g.lda, ldb = g.ldb;
   const int nk = K / BK;
@@ -172,13 +165,25 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
   static_assert(AI * NW * 8 == BM && BI * NW * 8 == BN, "direct-LDS tiling mismatch");
   const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(A + (size_t)m0 * lda), (short)0, (int)min((size_t)(M - m0) * lda * 2, (size_t)0x7fffffff), 0x00020000);
+  const int wids = __builtin_amdgcn_readfirstlane(wid);
+  // B: each wave loads BN / NW consecutive rows of the tile, starting at row nw0.  Its resource
+  // starts there, in the row segment (B0 | B1 | B2) that holds them: segment boundaries are
+  // multiples of BN / NW rows, so a tile may straddle one while each wave's rows stay in one
+  // segment.  Rows past the segment's end (past N in the last tile) read as zero.
+  const int nw0 = n0 + wids * BI * 8;
+  const bf16* Bseg;
+  int nb0, nrows;
+  if (nw0 < g.nseg0) { Bseg = (const bf16*)g.B0; nb0 = nw0; nrows = g.nseg0; }
+  else if (nw0 < g.nseg0 + g.nseg1) { Bseg = (const bf16*)g.B1; nb0 = nw0 - g.nseg0; nrows = g.nseg1; }
+  else { Bseg = (const bf16*)g.B2; nb0 = nw0 - g.nseg0 - g.nseg1; nrows = N - g.nseg0 - g.nseg1; }
   const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(Bseg + (size_t)nb0 * ldb), (short)0, (int)min((size_t)(nrows - nb0) * ldb * 2, (size_t)0x7fffffff), 0x00020000);
+      (void*)(Bseg + (size_t)(nb0 < nrows ? nb0 : 0) * ldb), (short)0,
+      nb0 < nrows ? (int)min((size_t)(nrows - nb0) * ldb * 2, (size_t)0x7fffffff) : 0, 0x00020000);
   // Row block rb (8 rows) of an operand tile sits at row 8*rb: its lanes' chunk swizzle is
   // (lane & 7) ^ (lane >> 3) ^ (rb & 1), so two per-lane offsets serve every row block, and
-  // the row block's start and the K offset travel in the scalar soffset.
+  // the row block's start (relative to the wave's resource for B) and the K offset travel in
+  // the scalar soffset.
   static_assert(AI % 2 == 0, "A row blocks per wave must be even");
-  const int wids = __builtin_amdgcn_readfirstlane(wid);
   const int pb = (wids * BI) & 1;  // parity of this wave's first B row block (0 when BI is even)
   // The 256x384 tiles assume A and B share their row pitch (the launcher checks lda == ldb);
   // the other tiles keep a second offset pair for B.
@@ -204,7 +209,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb,                                          \
         (lds_ptr_t)(Bs + (buf) * BN * BK + (wids * BI + i) * 512), 16,                      \
         (BI % 2 == 0 ? vb[i & 1] : (((pb + i) & 1) ? vb1 : vb0)),                            \
-        (k0) * 2 + (wids * BI + i) * 16 * ldb, 0, 0);                                        \
+        (k0) * 2 + i * 16 * ldb, 0, 0);                                                      \
   } while (0)
 
   // Row-scale inputs staged early: a consumer of an un-normalised A (row scale from rs_ssp) has
@@ -1266,11 +1271,16 @@ hipError_t run_narrow(Epi epi, const GemmArgs& a, hipStream_t s) {
   return run_bf16<256, 128, 2, 2>(epi, a, s);
 }
 
-// Interior column-segment boundaries must fall on block-column boundaries.
-bool seg_ok(const GemmArgs& a, int bn) {
+// Interior column-segment boundaries (B0 | B1 | B2) must be multiples of `gran` columns.
+bool seg_ok(const GemmArgs& a, int gran) {
   const int e0 = a.nseg0, e1 = a.nseg0 + a.nseg1;
-  return (e0 >= a.N || e0 % bn == 0) && (e1 >= a.N || e1 % bn == 0);
+  return (e0 >= a.N || e0 % gran == 0) && (e1 >= a.N || e1 % gran == 0);
 }
+
+// Granularity the 256x256 and 256x128 tiles need of segment boundaries: each wave's share of
+// the B rows (32) lies in one segment, and with the fused q/k/v epilogue each wave's 128
+// columns (whole heads) are all q, all k or all v.
+int seg_gran(Epi epi, const GemmArgs& a) { return epi == EPI_QKV && a.cs != nullptr ? 128 : 32; }
 
 // Tile plan of one GEMM.  Candidates: 256x384 tiles (8 wavefronts of 128x96) and 256x192
 // tiles (8 wavefronts of 64x96) for the residual, ReLU^2 and store epilogues when N allows, and
@@ -1345,7 +1355,7 @@ hipError_t launch_gemm_bf16(Epi epi, const GemmArgs& a, hipStream_t s) {
   // plan for all columns (e.g. d24: 3 rounds of q|k + 1 of v, against 4.5 for the whole).
   if (epi == EPI_QKV && a.cs != nullptr && a.ve == nullptr && a.nqk > 0 && a.nqk < a.N &&
       a.nqk % 256 == 0 && (a.N - a.nqk) % 384 == 0 && a.T % 32 == 0 && a.lda == a.ldb &&
-      seg_ok(a, 256)) {
+      seg_ok(a, seg_gran(epi, a))) {
     const int ncu = cu_count();
     auto cost = [&](const Plan& q, int n) {
       const long nbm = (a.M + 255) / 256, t = nbm * (n / 256);
@@ -1378,7 +1388,7 @@ hipError_t launch_gemm_bf16(Epi epi, const GemmArgs& a, hipStream_t s) {
   const Plan p = plan_gemm(epi, a.M, a.N, a.nseg0, a.nseg1, cu_count(), a.lda == a.ldb);
   if (p.tiles == Tiles::T384) return run_bf16<256, 384, 2, 4>(epi, a, s);  // slices of 96 columns
   if (p.tiles == Tiles::T192) return run_bf16<256, 192, 4, 2>(epi, a, s);  // slices of 96 columns
-  if (!seg_ok(a, 256)) return seg_ok(a, 128) ? run_narrow(epi, a, s) : hipErrorInvalidValue;
+  if (!seg_ok(a, seg_gran(epi, a))) return hipErrorInvalidValue;
   if (p.split_cols > 0) {  // both parts keep 64-column wavefront slices
     GemmArgs head = a;
     head.N = p.split_cols;
@@ -1395,7 +1405,7 @@ hipError_t launch_gemm_bf16(Epi epi, const GemmArgs& a, hipStream_t s) {
 // instead of 256x256 when that fills the CUs in fewer rounds, at ~0.9 of the larger tiles' rate:
 // e.g. the nested model's MLP-down and out-projection pairs at M = 8192 make exactly 256 tiles
 // of 256x192 against 224 of 256x256, whose longest ones then set the time.
-enum class PairTiles { T192, T256, T128, SEPARATE };
+enum class PairTiles { T192, T256, SEPARATE };
 PairTiles plan_pair(Epi epi, const GemmArgs& a, const GemmArgs& b) {
   const bool fused = epi == EPI_QKV && (a.cs != nullptr || b.cs != nullptr);
   if (!fused && epi != EPI_QKV && a.N % 192 == 0 && b.N % 192 == 0 && seg_ok(a, 192) && seg_ok(b, 192)) {
@@ -1404,11 +1414,11 @@ PairTiles plan_pair(Epi epi, const GemmArgs& a, const GemmArgs& b) {
       const long t = (long)((a.M + 255) / 256) * ((a.N + bn - 1) / bn) + (long)((b.M + 255) / 256) * ((b.N + bn - 1) / bn);
       return (double)((t + ncu - 1) / ncu);
     };
-    const double c256 = seg_ok(a, 256) && seg_ok(b, 256) ? rounds(256) : 1e30;
+    const double c256 = seg_ok(a, seg_gran(epi, a)) && seg_ok(b, seg_gran(epi, b)) ? rounds(256) : 1e30;
     if (rounds(192) * 0.75 / 0.9 < c256) return PairTiles::T192;
   }
-  if (seg_ok(a, 256) && seg_ok(b, 256)) return PairTiles::T256;
-  if (seg_ok(a, 128) && seg_ok(b, 128)) return PairTiles::T128;
+  const int gran = fused ? 128 : 32;
+  if (seg_ok(a, gran) && seg_ok(b, gran)) return PairTiles::T256;
   return PairTiles::SEPARATE;
 }
 
@@ -1425,8 +1435,6 @@ hipError_t launch_gemm_bf16_pair(Epi epi, const GemmArgs& a, const GemmArgs& b, 
     case PairTiles::T192: return run_bf16_pair<256, 192, 4, 2>(epi, a, b, s);
     case PairTiles::T256:
       return fused ? run_bf16_pair<256, 256, 4, 2>(epi, a, b, s) : run_bf16_pair<256, 256, 2, 4>(epi, a, b, s);
-    case PairTiles::T128:
-      return fused ? run_bf16_pair<256, 128, 4, 1>(epi, a, b, s) : run_bf16_pair<256, 128, 2, 2>(epi, a, b, s);
     default: break;
   }
   if (a.pre_k > 0 || b.pre_k > 0) return hipErrorInvalidValue;  // the single-GEMM tiles take no prefix scale
@@ -1438,7 +1446,6 @@ int gemm_pair_resid_slice_cols(const GemmArgs& a, const GemmArgs& b) {
   switch (plan_pair(EPI_RESID, a, b)) {
     case PairTiles::T192: return 96;   // 4 x 2 wavefronts of 64 x 96
     case PairTiles::T256: return 64;   // 2 x 4 wavefronts of 128 x 64
-    case PairTiles::T128: return 64;   // 2 x 2 wavefronts of 128 x 64
     default: return 0;                 // launched separately: slices of each GEMM's own plan
   }
 }
