@@ -1267,7 +1267,12 @@ hipError_t run_main(Epi epi, const GemmArgs& a, hipStream_t s) {
 }
 
 hipError_t run_narrow(Epi epi, const GemmArgs& a, hipStream_t s) {
-  if (epi == EPI_QKV && a.cs != nullptr) return run_bf16<256, 128, 4, 1>(epi, a, s);
+  if (epi == EPI_QKV && a.cs != nullptr) {
+    // fused q/k/v: eight wavefronts of 32x128 (whole heads), two per SIMD
+    const int grid = ((a.M + 255) / 256) * ((a.N + 127) / 128);
+    GPTK_LAUNCH((gemm_bf16_kernel<256, 128, 8, 1, EPI_QKV>), grid, 512, s, a);
+    return hipGetLastError();
+  }
   return run_bf16<256, 128, 2, 2>(epi, a, s);
 }
 
