@@ -28,6 +28,34 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E bandwidth (published)
 
 
+def device_info():
+    """The GPU's compute-unit count and maximum shader clock as rocminfo reports them, and the
+    dense bf16 MFMA peak they imply (4096 FLOP per CU per clock on gfx950); None if rocminfo is
+    not available."""
+    import subprocess
+    try:
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=30).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    for agent in txt.split("*******")[1:]:
+        fields = {}
+        for line in agent.splitlines():
+            if ":" in line:
+                k, v = line.split(":", 1)
+                fields.setdefault(k.strip(), v.strip())
+        if fields.get("Device Type") != "GPU":
+            continue
+        try:
+            cus = int(fields["Compute Unit"])
+            mhz = int(fields["Max Clock Freq. (MHz)"].split()[0])
+        except (KeyError, ValueError, IndexError):
+            return None
+        return {"name": fields.get("Marketing Name", ""), "arch": fields.get("Name", ""),
+                "compute_units": cus, "max_sclk_mhz": mhz,
+                "peak_bf16_tflops_from_clock": round(cus * mhz * 1e6 * 4096 / 1e12, 1)}
+    return None
+
+
 def _attn_flops(p, w, prior=False):
     """Attention FLOPs per token of one layer: QK^T and PV over the visible keys (average over
     positions of min(t+1, w)); the looped prior adds a second QK^T of the same width."""
@@ -417,6 +445,7 @@ def main():
         "decode": dec,
         "gemm_vs_library": gcmp,
         "cpu_baseline": cpu,
+        "device": device_info(),
     }
     print(json.dumps(out), flush=True)
 
