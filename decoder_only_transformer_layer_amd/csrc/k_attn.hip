@@ -45,9 +45,9 @@ __device__ __forceinline__ int swzv(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 // also carry g * <q1, k1> from pass 1's q and k of this layer (qk1, the qk layout), g =
 // softplus(gate_logit[layer]).  This is attention over the augmented width [q, g q1] . [k, k1]:
 // K tiles hold both halves (k from qk, k1 from qk1), the query fragments both (q1 scaled by g
-// before rounding), so S^T takes 2 D/16 k-steps; V and everything after are unchanged.  The
-// doubled query fragments need more registers than two wavefronts per SIMD allow, so this form
-// runs 4 wavefronts (128 queries) per block.
+// before rounding), so S^T takes 2 D/16 k-steps; V and everything after are unchanged.  This
+// form also runs 8 wavefronts (two per SIMD; the doubled query fragments bring it to 254 VGPRs)
+// and a 3-stage ring of 48 KB stages.
 constexpr int STG = 3;
 
 template <int D, int NW, bool PRIOR, bool BOUNDED>
@@ -369,8 +369,8 @@ hipError_t launch_attn_bf16(const void* qk, const void* vt, void* o, int B, int 
   // looped prior within +-scale * D * (1 + g).
   if (qk1 != nullptr) {  // looped pass 2: prior from pass 1
     if (D != 128 || gate_logit == nullptr) return hipErrorInvalidValue;
-    const dim3 grid(((T + 127) / 128) * H * B);
-    GPTK_LAUNCH((attn_bf16_kernel<128, 4, true, false>), grid, 256, s, q, v, out, B, T, H, Hkv, window, sl2,
+    const dim3 grid(((T + 255) / 256) * H * B);
+    GPTK_LAUNCH((attn_bf16_kernel<128, 8, true, false>), grid, 512, s, q, v, out, B, T, H, Hkv, window, sl2,
                 (const bf16*)qk1, gate_logit, layer);
     return hipGetLastError();
   }
