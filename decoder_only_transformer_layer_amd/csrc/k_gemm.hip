@@ -1291,7 +1291,8 @@ int seg_gran(Epi epi, const GemmArgs& a) { return epi == EPI_QKV && a.cs != null
 // tiles (8 wavefronts of 64x96) for the residual, ReLU^2 and store epilogues when N allows, and
 // 256x256 tiles (8 wavefronts), the latter with the columns split when the tile count leaves a
 // partial last round on the CUs: a leading part whose 256x256 tiles fill whole rounds and a
-// tail of 256x128 tiles (4 wavefronts), so the partial round costs half a tile per CU.
+// tail of 256x128 tiles (8 wavefronts of 32x128 with the fused q/k/v epilogue, else 4 of
+// 128x64), so the partial round costs half a tile per CU.
 // Cost = rounds x tile area / relative efficiency (256x128 and 256x192 tiles run at about 3/4
 // and 9/10 of the larger tiles' rate, their wavefront tiles re-reading LDS more per MFMA); the
 // cheapest plan wins, wider tiles on a tie.  E.g. 16384 x 1536 takes one round of 256 tiles of
