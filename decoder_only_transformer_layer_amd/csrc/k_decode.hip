@@ -472,18 +472,6 @@ __device__ __forceinline__ unsigned order_key(float f) {  // monotone map float 
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Block-wide sum of one value per thread (fixed order); every thread receives the total.
-__device__ float block_sum(float v, float* scratch) {
-  v = wave_sum(v);
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  __syncthreads();
-  if (lane == 0) scratch[wid] = v;
-  __syncthreads();
-  float s = 0.f;
-  for (int w = 0; w < SMP_THREADS / 64; ++w) s += scratch[w];
-  return s;
-}
-
 // One block per row.  Temperature 0: the first index of the largest logit.  Otherwise the
 // k-th largest logit (exact radix select over the order-preserving 32-bit keys, 8 bits per
 // pass) bounds the kept set {v : z_v >= z_(k)}; p_v = exp((z_v - max) / tau) over it; the token

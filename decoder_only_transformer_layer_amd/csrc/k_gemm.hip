@@ -68,28 +68,12 @@ __device__ __forceinline__ void tile_of(int pid, int nbm, int nbn, int& bm, int&
   bn = in / gsz;
 }
 
-// 1 / sqrt(sum_{j < n} ssp[j][row] / c + eps): the RMS scale of one row from the per-slice sums of
-// squares a residual producer wrote (slice-major, M per slice).  Sixteen slices' loads are in
-// flight together; slice j < n4 adds into s4[j % 4] and the rest into s4[0], each in increasing j.
-__device__ __forceinline__ float row_rinv(const float* ssp, int n, float c, float eps, int row, int M) {
-  float s4[4] = {0.f, 0.f, 0.f, 0.f};
-  const int n4 = n & ~3;
-  for (int j0 = 0; j0 < n; j0 += 16) {
-    float v[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) v[u] = j0 + u < n ? ssp[(size_t)(j0 + u) * M + row] : 0.f;
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      if (j0 + u < n4) s4[u & 3] += v[u];
-      else if (j0 + u < n) s4[0] += v[u];
-    }
-  }
-  return rsqrtf(((s4[0] + s4[1]) + (s4[2] + s4[3])) / c + eps);
-}
-
-// The prefix's and the whole row's RMS scales in one pass over the row's slices: returns
-// (1/rms over slices [0, n1) of width c1, 1/rms over slices [0, n) of width c), each summed in
-// row_rinv's order.
+// The prefix's and the whole row's RMS scales from the per-slice sums of squares a residual
+// producer wrote (slice-major, M per slice), in one pass over the row's slices: returns
+// (1/sqrt(sum_{j < n1} ssp[j][row] / c1 + eps), 1/sqrt(sum_{j < n} ssp[j][row] / c + eps)).
+// The row-sum order used everywhere: sixteen slices' loads in flight together, slice j below
+// the largest multiple of 4 adds into s4[j % 4] and the rest into s4[0], each in increasing j,
+// then (s4[0] + s4[1]) + (s4[2] + s4[3]).
 __device__ __forceinline__ float2 row_rinv2(const float* ssp, int n1, float c1, int n, float c, float eps,
                                             int row, int M) {
   float s4[4] = {0.f, 0.f, 0.f, 0.f}, p4[4] = {0.f, 0.f, 0.f, 0.f};
@@ -293,7 +277,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
       }
     }
   };
-  // the held sums, in row_rinv's order (slice j < n4 into s4[j % 4], the rest into s4[0])
+  // the held sums, in the row-sum order of row_rinv2 (slice j < n4 into s4[j % 4], the rest into s4[0])
   auto prefix_finish = [&]() {
     if constexpr (PRE) {
       if (pv_held) {
@@ -505,7 +489,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
       // slices are stored slice-major ([slice][M]): consecutive threads read consecutive rows
       // (a prefix-scaled tile has its 1/rms_a there already)
       if (kpre <= 0 && stage_ss) {
-        // the slice sums staged in LDS by SS_ISSUE, summed in row_rinv's order
+        // the slice sums staged in LDS by SS_ISSUE, summed in row_rinv2's row-sum order
         const float* ssl = (const float*)(As + ss_buf * BM * BK);
         for (int i = tid; i < BM; i += NT) {
           float s4[4] = {0.f, 0.f, 0.f, 0.f};
@@ -519,7 +503,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
       } else if (kpre <= 0) for (int i = tid; i < BM; i += NT) {
         const int row = m0 + i;
         // Sixteen slices' loads are in flight together; slice j < n4 adds into s4[j % 4] and the
-        // rest into s4[0], each in increasing j (the order of row_rinv).
+        // rest into s4[0], each in increasing j (row_rinv2's row-sum order).
         float s4[4] = {0.f, 0.f, 0.f, 0.f};
         if (row < M) {
           const int n4 = g.rs_n & ~3;
