@@ -80,6 +80,20 @@ def test_decode_matches_forward_bf16():
     _check_bf16_logits(got, ref)
 
 
+def test_decode_matches_forward_bf16_d64():
+    """bf16 at head_dim 64 (the 64-wide RoPE/QK-norm, the chunk kernel's 8 x 32 output layout),
+    MHA with 6 heads, windows 40 / full over 192 positions (two 128-key chunks), 2 rows, row 1
+    one position behind row 0."""
+    p = gptdata.Preset(name="dec64", n_layer=2, d_model=384, n_head=6, n_kv_head=6, head_dim=64,
+                       mlp_dim=1536, vocab=900, seq_len=192, batch=2, dtype="bf16", short_window=40,
+                       lambda_range=(0.9, 1.1), mu_range=(0.0, 0.2), seed=61)
+    w, tok, _ = gptdata.make_inputs(p)
+    windows = [40, 192]
+    got = _decode_all(p, w, tok, lag=[0, 1], windows=windows)
+    ref = oracle.forward(p, params_of(w), tok, want_logits=True, windows=windows)["logits"]
+    _check_bf16_logits(got, ref)
+
+
 def test_decode_group8_multichunk_bf16():
     """bf16 at the largest query group the decode attention takes (8 query heads on one KV
     head, head_dim 128), 320 cache positions so that windows of 200 and full span up to three
