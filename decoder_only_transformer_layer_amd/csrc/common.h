@@ -41,8 +41,10 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // Sum over each aligned group of 32 lanes, broadcast to the group: DPP butterflies within
 // 16-lane rows (xor 1, xor 2, half-row mirror, row mirror) then a swizzle across the two rows.
+// Every lane's source exists in these patterns, so bound_ctrl changes no value; it lets the
+// compiler fold each move into the add that uses it (one v_add_f32_dpp per step).
 template <int CTRL> __device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float sum32(float v) {
   v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]

@@ -95,6 +95,16 @@ __device__ __forceinline__ float2 row_rinv2(const float* ssp, int n1, float c1, 
                      rsqrtf(((s4[0] + s4[1]) + (s4[2] + s4[3])) / c + eps));
 }
 
+// RoPE-pair column order of a fused q|k tile of 384 columns (three 128-wide heads) on 64x192
+// wavefront tiles: wavefront wn's fragments 2q and 2q+1 (32 columns each) hold, lane rl, the
+// halves d = j and d = j + 64 of rotation pair P = 96 wn + 32 q + rl of the tile (head P / 64,
+// j = P % 64).  Returns the tile-relative weight row (head * 128 + d) of tile column l.
+__host__ __device__ __forceinline__ int qk_pair_row(int l) {
+  const int wn = l / 192, f = (l % 192) / 32, r = l % 32;
+  const int p = 96 * wn + 32 * (f >> 1) + r;
+  return 128 * (p >> 6) + (p & 63) + 64 * (f & 1);
+}
+
 // One output tile (pid = its index in the GEMM's tile order) of C = A B^T with epilogue EPI.
 // PRE: the tile may take a PrefixRMSNorm'd A as a two-part row scale (GemmArgs::pre_k); the
 // kernel then holds BM more floats of LDS for the per-row factor.
@@ -154,7 +164,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
   // starts there, in the row segment (B0 | B1 | B2) that holds them: segment boundaries are
   // multiples of BN / NW rows, so a tile may straddle one while each wave's rows stay in one
   // segment.  Rows past the segment's end (past N in the last tile) read as zero.
-  const int nw0 = n0 + wids * BI * 8;
+  // Fused q|k tiles of the 64x192-wavefront layout (QKP) take their B rows in RoPE-pair order
+  // instead: every 8-row block of the tile's LDS rows is 8 consecutive weight rows of the tile
+  // (qk_pair_row), so the wave's resource starts at the tile's first row (the launcher keeps
+  // q|k tiles inside one segment) and each block's row offset travels in the soffset.
+  constexpr bool QKP = EPI == EPI_QKV && BN == 384 && WN == 2;
+  bool perm = false;
+  int nw0 = n0 + wids * BI * 8;
+  int boff[QKP ? BI : 1];
+  if constexpr (QKP) {
+    perm = g.cs != nullptr && n0 < g.nqk;
+    if (perm) nw0 = n0;
+#pragma unroll
+    for (int i = 0; i < BI; ++i) boff[i] = perm ? qk_pair_row((wids * BI + i) * 8) * ldb * 2 : i * 16 * ldb;
+  }
   const bf16* Bseg;
   int nb0, nrows;
   if (nw0 < g.nseg0) { Bseg = (const bf16*)g.B0; nb0 = nw0; nrows = g.nseg0; }
@@ -193,7 +216,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb,                                          \
         (lds_ptr_t)(Bs + (buf) * BN * BK + (wids * BI + i) * 512), 16,                      \
         (BI % 2 == 0 ? vb[i & 1] : (((pb + i) & 1) ? vb1 : vb0)),                            \
-        (k0) * 2 + i * 16 * ldb, 0, 0);                                                      \
+        (k0) * 2 + (QKP ? boff[QKP ? i : 0] : i * 16 * ldb), 0, 0);                         \
   } while (0)
 
   // Row-scale inputs staged early: a consumer of an un-normalised A (row scale from rs_ssp) has
@@ -411,6 +434,42 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
         __builtin_amdgcn_s_waitcnt(lgkmcnt_0);
       }
     }
+  } else if constexpr (QKP) {
+    // 64x192 wavefront tiles: one A and one B fragment set, each fragment refilled for the next
+    // substep right after its last MFMA of this one (A fragment fm after its row of FN MFMAs, B
+    // fragment fn after the last row's), so every refill has at least FN MFMAs before its use.
+    static_assert(!PRE && EPI != EPI_CE_PREFIX, "fully rolled loop has no split K step");
+    bf16x8 fa[FM], fb[FN];
+    auto mmroll2 = [&](const bf16* An, const bf16* Bn, int kn) {
+      const int co = co_of(kn);
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fm], fb[fn], acc[fm][fn], 0, 0, 0);
+          if (fm == FM - 1) {
+            fb[fn] = *(const bf16x8*)(Bn + ob[fn] + co);
+            PIN;
+          }
+        }
+        fa[fm] = *(const bf16x8*)(An + oa[fm] + co);
+        PIN;
+      }
+    };
+    rda(As, 0, fa); rdb(Bs, 0, fb);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      const bf16* Ab = As + buf * BM * BK;
+      const bf16* Bb = Bs + buf * BN * BK;
+      PIN; mmroll2(Ab, Bb, 1); mmroll2(Ab, Bb, 2); mmroll2(Ab, Bb, 3);
+      __builtin_amdgcn_s_waitcnt(vmcnt_le(0));  // own loads of tile kt+1 have landed
+      __syncthreads();                          // everyone's too; buffer `buf` fully read
+      PIN;
+      if (kt + 2 < nk) GEMM_ISSUE(buf, (kt + 2) * BK);
+      else if (SS_OK && stage_ss && kt + 2 == nk) SS_ISSUE(buf);
+      PIN; mmroll2(As + (buf ^ 1) * BM * BK, Bs + (buf ^ 1) * BN * BK, 0);
+      __builtin_amdgcn_s_waitcnt(lgkmcnt_0);
+    }
   } else {
     bf16x8 fa0[FM], fa1[FM], fb[FN];
     // MFMAs of one substep with fragments fa and fb; B fragment fn is then refilled from
@@ -492,13 +551,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
         // the slice sums staged in LDS by SS_ISSUE, summed in row_rinv2's row-sum order
         const float* ssl = (const float*)(As + ss_buf * BM * BK);
         for (int i = tid; i < BM; i += NT) {
-          float s4[4] = {0.f, 0.f, 0.f, 0.f};
+          float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;  // named: a run-time-indexed array would live in scratch
           const int n4 = g.rs_n & ~3;
-          for (int j = 0; j < g.rs_n; ++j) {
-            if (j < n4) s4[j & 3] += ssl[j * BM + i];
-            else s4[0] += ssl[j * BM + i];
+          for (int j = 0; j < n4; j += 4) {
+            s0 += ssl[j * BM + i];
+            s1 += ssl[(j + 1) * BM + i];
+            s2 += ssl[(j + 2) * BM + i];
+            s3 += ssl[(j + 3) * BM + i];
           }
-          rinv[i] = rsqrtf(((s4[0] + s4[1]) + (s4[2] + s4[3])) / g.rs_c + g.eps);
+          for (int j = n4; j < g.rs_n; ++j) s0 += ssl[j * BM + i];
+          rinv[i] = rsqrtf(((s0 + s1) + (s2 + s3)) / g.rs_c + g.eps);
         }
       } else if (kpre <= 0) for (int i = tid; i < BM; i += NT) {
         const int row = m0 + i;
@@ -702,10 +764,119 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
       }
       __builtin_amdgcn_wave_barrier();  // reads of this group precede the next group's writes
     }
-  } else if constexpr (EPI == EPI_QKV && TN == 96) {
-    // v-only launches (every column a v column, nqk == 0, no value embeddings): each 32-row group
-    // of the wavefront's tile is staged through wavefront-private LDS transposed ([col][t], bf16)
-    // and written as 16-byte runs of 8 positions of v^T [B][Hkv][D][T].
+  } else if constexpr (EPI == EPI_QKV && (TN == 96 || TN == 192)) {
+    if constexpr (QKP) {
+      if (perm) {
+        // Fused q|k tile (head_dim 128) in RoPE-pair column order (qk_pair_row): the lane holds
+        // both halves of each of its pairs, so RoPE is lane-local.  Heads 0 and 2 of the tile
+        // lie in wavefronts 0 and 1; head 1's pairs j < 32 (wavefront 0, fragments 4-5) and
+        // j >= 32 (wavefront 1, fragments 0-1) swap their squares through LDS.  Every head's sum
+        // of squares is then formed as in the 128-wide form: the lane's pair j plus its pair
+        // j + 32, then a 32-lane butterfly.  Output rows are staged 16 at a time through
+        // wavefront-private LDS and written as 16-byte runs of q/k rows.
+        bf16* qk = (bf16*)g.out;
+        constexpr int LQ = TN + 8;                   // staging pitch (bf16)
+        constexpr int STG = WM * WN * 16 * LQ * 2;   // staging bytes
+        static_assert(STG + WM * WN * FM * 16 * 64 * 4 + BM * 4 <= (int)sizeof(lds), "q|k staging exceeds LDS");
+        bf16* const stg = lds + wid * 16 * LQ;
+        float* const xch = (float*)((char*)lds + STG);  // [wavefront][fm][r][lane] squares of head 1
+        float* const xown = xch + wid * (FM * 16 * 64);
+        const float* const xoth = xch + (wid ^ 1) * (FM * 16 * 64);  // the other wavefront of the row band
+        const int qcol0 = n0 < g.nseg0 ? g.q_off + n0 : g.k_off + (n0 - g.nseg0);
+        // Both phases are written for a compile-time wavefront column W (wn): pair q of it has
+        // j = 32 * ((3 W + q) & 1) + rl; head 1 is its pair QM (fragments 4-5 for W = 0, 0-1 for
+        // W = 1).  acc is only read: each phase rotates what it needs from the table.
+        auto rope = [&](auto wc) {  // head 1's squares (after RoPE) to LDS
+          constexpr int W = decltype(wc)::value, QM = W == 0 ? 2 : 0, PM = (3 * W + QM) & 1;
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm) {
+            // the 32-row group is 32 consecutive positions of one sequence (T % 32 == 0)
+            const float2* const csr = g.cs + ((m0 + wm * TM + fm * 32) % g.T + 4 * hl) * 64 + rl + PM * 32;
+#pragma unroll
+            for (int hc = 0; hc < 2; ++hc) {  // rows in chunks of 8: 8 table loads in flight
+              float2 c[8];
+#pragma unroll
+              for (int q8 = 0; q8 < 8; ++q8) {
+                const int r = 8 * hc + q8;
+                c[q8] = csr[(8 * (r >> 2) + (r & 3)) * 64];
+              }
+#pragma unroll
+              for (int q8 = 0; q8 < 8; ++q8) {
+                const int r = 8 * hc + q8;
+                const float u1 = acc[fm][2 * QM][r], u2 = acc[fm][2 * QM + 1][r];
+                const float y1 = u1 * c[q8].x + u2 * c[q8].y, y2 = -u1 * c[q8].y + u2 * c[q8].x;
+                xown[(fm * 16 + r) * 64 + lane] = y1 * y1 + y2 * y2;
+              }
+            }
+          }
+        };
+        auto finish = [&](auto wc) {  // RoPE, norms, bf16 staging, 16-byte row stores
+          constexpr int W = decltype(wc)::value, QA = W == 0 ? 0 : 1;  // whole head: pairs QA, QA + 1
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm) {
+            const float2* const csr = g.cs + ((m0 + wm * TM + fm * 32) % g.T + 4 * hl) * 64 + rl;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {  // rows 16h .. 16h+15 of the 32-row group
+#pragma unroll
+              for (int hc = 0; hc < 2; ++hc) {  // rows in chunks of 4: 8 table loads in flight
+                float2 c[2][4];
+#pragma unroll
+                for (int q8 = 0; q8 < 4; ++q8) {
+                  const int r = 8 * h + 4 * hc + q8;
+#pragma unroll
+                  for (int p = 0; p < 2; ++p) c[p][q8] = csr[(8 * (r >> 2) + (r & 3)) * 64 + p * 32];
+                }
+#pragma unroll
+                for (int q8 = 0; q8 < 4; ++q8) {
+                  const int r = 8 * h + 4 * hc + q8;
+                  float y[6];
+#pragma unroll
+                  for (int q = 0; q < 3; ++q) {
+                    const float2 cc = c[(3 * W + q) & 1][q8];
+                    const float u1 = acc[fm][2 * q][r], u2 = acc[fm][2 * q + 1][r];
+                    y[2 * q] = u1 * cc.x + u2 * cc.y;
+                    y[2 * q + 1] = -u1 * cc.y + u2 * cc.x;
+                  }
+                  const float ea = y[2 * QA] * y[2 * QA] + y[2 * QA + 1] * y[2 * QA + 1];      // pairs j < 32
+                  const float eb = y[2 * QA + 2] * y[2 * QA + 2] + y[2 * QA + 3] * y[2 * QA + 3];  // j >= 32
+                  // head 1: wavefront 0 holds its pairs j < 32, wavefront 1 those j >= 32
+                  const float em = xown[(fm * 16 + r) * 64 + lane], eo = xoth[(fm * 16 + r) * 64 + lane];
+                  const float sw = rsqrtf(sum32(ea + eb) * (1.0f / 128.0f) + g.eps);
+                  const float sm = rsqrtf(sum32(em + eo) * (1.0f / 128.0f) + g.eps);
+                  bf16* const sr = stg + (8 * ((r >> 2) - 2 * h) + 4 * hl + (r & 3)) * LQ + rl;
+#pragma unroll
+                  for (int fn = 0; fn < FN; ++fn) {
+                    const bool mid = W == 0 ? fn >= 4 : fn < 2;
+                    sr[fn * 32] = (bf16)(y[fn] * (mid ? sm : sw));
+                  }
+                }
+              }
+              __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+              __builtin_amdgcn_wave_barrier();
+              __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+              const int row0 = m0 + wm * TM + fm * 32 + 16 * h;
+#pragma unroll
+              for (int k = 0; k < 16 * (TN / 8) / 64; ++k) {  // 16 rows x 24 runs of 8 columns
+                const int idx = lane + 64 * k, lr = idx / (TN / 8), ch = idx % (TN / 8);
+                const int fn = ch >> 2, p0 = 96 * W + 32 * (fn >> 1);
+                const int col = qcol0 + 128 * (p0 >> 6) + (p0 & 63) + 64 * (fn & 1) + 8 * (ch & 3);
+                if (row0 + lr < M)
+                  *(bf16x8*)(qk + (size_t)(row0 + lr) * g.ldo + col) = *(const bf16x8*)(stg + lr * LQ + 8 * ch);
+              }
+              __builtin_amdgcn_wave_barrier();  // reads of this group precede the next group's writes
+            }
+          }
+        };
+        __syncthreads();  // every wavefront is done with the operand tiles
+        if (wn == 0) rope(std::integral_constant<int, 0>{}); else rope(std::integral_constant<int, 1>{});
+        __syncthreads();  // head 1's squares of both wavefronts are in LDS
+        if (wn == 0) finish(std::integral_constant<int, 0>{}); else finish(std::integral_constant<int, 1>{});
+        return;
+      }
+    }
+    // v tiles (columns >= nqk, no value embeddings): each 32-row group of the wavefront's tile is
+    // staged through wavefront-private LDS transposed ([col][t], bf16) and written as 16-byte
+    // runs of 8 positions of v^T [B][Hkv][D][T].
     bf16* vt = (bf16*)g.vt;
     constexpr int LV = 32 + 8;  // staging pitch (bf16)
     static_assert(WM * WN * TN * LV * 2 <= (int)sizeof(lds), "v staging exceeds LDS");
@@ -733,7 +904,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
         const int idx = lane + 64 * k, cl = idx >> 2, ch = idx & 3;
         const int col = n0 + wn * TN + cl;
         if (col < N && row0 + ch * 8 < M) {
-          const int gg = g.v_head_off + col / g.D, d = col - (col / g.D) * g.D;
+          const int vc = col - g.nqk, gg = g.v_head_off + vc / g.D, d = vc - (vc / g.D) * g.D;
           *(bf16x8*)(vt + ((size_t)(bb * g.Hkv + gg) * g.D + d) * g.T + t0 + ch * 8) =
               *(const bf16x8*)(stg + cl * LV + ch * 8);
         }
@@ -1340,6 +1511,16 @@ hipError_t launch_gemm_bf16(Epi epi, const GemmArgs& a, hipStream_t s) {
     return a.logits != nullptr ? run_bf16<128, 384, 2, 4>(epi, a, s) : run_bf16<256, 384, 2, 4>(epi, a, s);
   }
   if (epi == EPI_QKV && a.cs != nullptr && a.D != 128 && a.D != 64) return hipErrorInvalidValue;
+  // Fused q/k/v with 128-wide heads whose q, k and v segments are multiples of 384 columns (three
+  // heads): one launch of 256x384 tiles, eight wavefronts of 64x192, q|k tiles in RoPE-pair column
+  // order (e.g. d24: 3 rounds of the CUs, against 3 of 256x256 q|k tiles plus 1 of v tiles).
+  if (epi == EPI_QKV && a.cs != nullptr && a.D == 128 && a.ve == nullptr && a.lda == a.ldb && a.T % 32 == 0 &&
+      a.nqk > 0 && a.nseg0 % 384 == 0 && a.nseg0 + a.nseg1 == a.nqk && a.nqk % 384 == 0 && a.N % 384 == 0 &&
+      a.ldo % 8 == 0 && a.q_off % 8 == 0 && a.k_off % 8 == 0) {
+    const int grid = ((a.M + 255) / 256) * (a.N / 384);
+    GPTK_LAUNCH((gemm_bf16_kernel<256, 384, 4, 2, EPI_QKV>), grid, 512, s, a);
+    return hipGetLastError();
+  }
   // Fused q/k/v: the q and k columns as one GEMM (256-wide tiles, whole heads per wavefront) and
   // the v columns as another on 256x384 tiles when that takes fewer rounds of the CUs than one
   // plan for all columns (e.g. d24: 3 rounds of q|k + 1 of v, against 4.5 for the whole).

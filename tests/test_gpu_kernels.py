@@ -161,13 +161,17 @@ def test_rope_table():
 
 @pytest.mark.parametrize("H,Hkv,D,B,T", [(2, 2, 128, 2, 192), (4, 2, 128, 2, 192), (2, 2, 64, 2, 192),
                                          (8, 4, 64, 2, 256), (3, 1, 128, 2, 192), (6, 6, 64, 2, 256),
-                                         (12, 4, 128, 8, 2048), (12, 12, 128, 8, 2048)])
+                                         (12, 4, 128, 8, 2048), (12, 12, 128, 8, 2048),
+                                         (3, 3, 128, 2, 192), (6, 3, 128, 3, 224)])
 def test_qkv_rope_norm_bf16(H, Hkv, D, B, T):
     """(2, 2, 64), (3, 1, 128) and (6, 6, 64) put a q/k or k/v boundary inside a 256-wide
     tile (at 128 or 384 columns, the nested model's 384-wide head blocks), which the tile loads
     from two weight matrices.  (12, 4, 128): the GQA projection over 16384 rows (2.5 rounds of
-    256x256 tiles: two rounds and a tail of 256x128 tiles).  Last case: the d24 projection
-    shape, q|k on 256x256 tiles and v on 256x384."""
+    256x256 tiles: two rounds and a tail of 256x128 tiles).  (12, 12, 128): the d24 projection
+    shape.  It and (3, 3, 128), (6, 3, 128) (q, k and v each a multiple of three 128-wide heads;
+    384 and 672 rows, so the last row block is partial) run the fused form as one launch of
+    256x384 tiles whose q|k tiles hold their columns in RoPE-pair order, with the middle head of
+    each tile split over two wavefronts."""
     torch = torch_mod()
     rng = np.random.default_rng(H * 10 + Hkv + D)
     C, eps = 256, 1e-6
