@@ -18,6 +18,7 @@ import argparse
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -188,8 +189,6 @@ def gemm_compare(gf, p, reps=20):
     gen = torch.Generator(device=dev).manual_seed(0)
 
     def timed(fn):
-        for _ in range(3):
-            fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
@@ -198,6 +197,17 @@ def gemm_compare(gf, p, reps=20):
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
+
+    def alternate(own, lib, rounds=5):
+        # both warmed up, then timed in alternation so that clock ramps and drift hit both alike
+        for _ in range(5):
+            own()
+            lib()
+        t_own, t_lib = [], []
+        for _ in range(rounds):
+            t_own.append(timed(own))
+            t_lib.append(timed(lib))
+        return statistics.median(t_own), statistics.median(t_lib)
 
     out = []
     for name, N, K in shapes:
@@ -209,8 +219,8 @@ def gemm_compare(gf, p, reps=20):
         ref = torch.nn.functional.linear(a, wt)
         torch.cuda.synchronize()
         rel = ((y.float() - ref.float()).abs().max() / ref.float().abs().max()).item()
-        t_own = timed(lambda: gf.gpt_op_linear(gf.GPT_BF16, 0, a, wt, M, N, K, y))
-        t_lib = timed(lambda: torch.nn.functional.linear(a, wt))
+        t_own, t_lib = alternate(lambda: gf.gpt_op_linear(gf.GPT_BF16, 0, a, wt, M, N, K, y),
+                                 lambda: torch.nn.functional.linear(a, wt))
         fl = 2.0 * M * N * K
         print(f"[bench] gemm {name} {M}x{N}x{K}: own {t_own * 1e3:.1f} us ({fl / t_own / 1e9:.0f} TF/s), "
               f"library {t_lib * 1e3:.1f} us ({fl / t_lib / 1e9:.0f} TF/s), max rel diff {rel:.1e}",
