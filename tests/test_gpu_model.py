@@ -100,6 +100,20 @@ def test_ragged_bf16_gqa_with_ignores_and_logits():
     _check_logits_bf16(got["logits"], ref["logits"])
 
 
+def test_qkv_384_tiles_bf16_ragged():
+    """q, k and v each a multiple of three 128-wide heads (6 query heads, 3 KV heads): the q/k/v
+    projection runs as one launch of 256x384 tiles in RoPE-pair column order, here with the
+    input row scale of layers >= 1 and B*T = 576 rows (the last row block partial)."""
+    p = _ragged_preset(d_model=512, n_head=6, n_kv_head=3, mlp_dim=1024, seq_len=192, batch=3,
+                       seed=19)
+    w, tok, tgt = gptdata.make_inputs(p, ignore_frac=0.05)
+    windows = [100, 64, 192]
+    _, got = _run(p, w, tok, tgt, want_logits=True, windows=windows)
+    ref = oracle.forward(p, params_of(w), tok, tgt, want_logits=True, windows=windows)
+    _check_bf16(got, ref)
+    _check_logits_bf16(got["logits"], ref["logits"])
+
+
 def test_head_dim_64_bf16():
     p = _ragged_preset(n_head=4, n_kv_head=2, head_dim=64, seq_len=256, vocab=777, seed=9)
     w, tok, tgt = gptdata.make_inputs(p)
