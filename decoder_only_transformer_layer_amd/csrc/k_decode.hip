@@ -49,20 +49,30 @@ __device__ __forceinline__ void gv_apply(const GvEpi& e, int b, int n, float v) 
 
 // bf16 weights and activations: y[b][n] = sum_k act[b][k] W[n][k] for b < B <= 32.  A block
 // owns 32 weight rows (three row segments W0 | W1 | W2 with boundaries on multiples of 32) and
-// one of KS contiguous ranges of 64-column K steps; its NW wavefronts (GV_WAVES at launch) take the range's steps in
+// one of KS contiguous ranges of 64-column K steps; its NW wavefronts take the range's steps in
 // turn.  In a step, lane l (row l % 32, half g = l / 32) holds W[row][kb + 32g + 8m .. +8] for
 // MFMA m = 0..3 and the batch operand holds act[b = l % 32][the same columns], so each MFMA sums
-// 16 columns and the four cover the step.  The wavefronts' tiles are summed through LDS in a
-// fixed order.  With KS > 1 the block stores its tile as partial[ks][b][n] and the consumer of
-// the product sums the KS tiles in split order (no block waits on another); with KS = 1 the
-// epilogue is applied here.
-template <int NW>
+// 16 columns and the four cover the step.  The weight tiles (32 rows x 64 columns, 4 KB) do not
+// go to registers directly: loaded that way, each 16-byte-per-lane load touches 32 rows, i.e. 32
+// cache lines with 32 bytes used of each.  Instead each wavefront copies its steps' tiles into
+// its own LDS slots by DMA (buffer_load ... lds), 8 rows x 128 bytes per instruction with the
+// 16-byte chunks of row r at slot c ^ swz8(r), issues up to DEPTH steps' copies (and the batch
+// operand's loads) at once, waits for them, and reads the fragments from LDS.  The wavefronts'
+// tiles are summed through LDS in a fixed order.  With KS > 1 the block stores its tile as
+// partial[ks][b][n] and the consumer of the product sums the KS tiles in split order (no block
+// waits on another); with KS = 1 the epilogue is applied here.
+__device__ __forceinline__ int gv_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// s_waitcnt immediate for vmcnt = 0 (gfx9 encoding; expcnt and lgkmcnt at their maxima)
+constexpr int GV_VMCNT0 = 0x0F70;
+typedef __attribute__((address_space(3))) void* gv_lds_t;
+template <int NW, int DEPTH>
 __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(
     const bf16* __restrict__ act, int lda, int B, const bf16* __restrict__ W0,
     const bf16* __restrict__ W1, const bf16* __restrict__ W2, int nseg0, int nseg1, int N, int K,
     int KS, float* __restrict__ partial, GvEpi e) {
-  __shared__ float red[NW][64 * 16];
+  __shared__ __attribute__((aligned(16))) bf16 wl[NW][DEPTH][GV_ROWS * GV_KB];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wids = __builtin_amdgcn_readfirstlane(wid);
   const int rb = blockIdx.x / KS, ks = blockIdx.x % KS;
   const int n0 = rb * GV_ROWS;
   const bf16* W;
@@ -71,41 +81,58 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(
   else if (n0 < nseg0 + nseg1) { W = W1; r0 = n0 - nseg0; }
   else { W = W2; r0 = n0 - nseg0 - nseg1; }
   const int row = lane & 31, g = lane >> 5;
-  const bool row_ok = n0 + row < N, b_ok = row < B;  // the batch operand's lane row is b
-  const bf16* wp = W + (size_t)(r0 + row) * K + 32 * g;
+  const bool b_ok = row < B;  // the batch operand's lane row is b
   const bf16* ap = act + (size_t)row * lda + 32 * g;
   const int nks = K / GV_KB, s0 = (int)((long)ks * nks / KS), s1 = (int)((long)(ks + 1) * nks / KS);
+  // The block's rows as a buffer resource: rows past N (last block) read as zero.  DMA lane L of
+  // instruction i fetches row 8i + L/8, chunk (L % 8) ^ swz(row); the K offset rides in soffset.
+  const int nrow = N - n0 < GV_ROWS ? N - n0 : GV_ROWS;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(W + (size_t)r0 * K), (short)0, nrow * K * 2, 0x00020000);
+  int voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rr = (lane >> 3) + 8 * i;
+    voff[i] = rr * K * 2 + (((lane & 7) ^ gv_swz(rr)) << 4);
+  }
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
   const bf16x8 zero = {};
-  // This wavefront's K steps s0 + wid, s0 + wid + NW, ...: double-buffered, the loads of
-  // the next step issued before the MFMAs of the current one (two named register sets, loop
-  // unrolled by two).
-  bf16x8 wa0[4], xb0[4], wa1[4], xb1[4];
-  auto load = [&](int st, bf16x8 (&wa)[4], bf16x8 (&xb)[4]) {
-    const int kb = st * GV_KB;
+  const int sw = gv_swz(row);
+  // this wavefront's K steps s0 + wid, s0 + wid + NW, ... in batches of DEPTH
+  for (int st0 = s0 + wids; st0 < s1; st0 += DEPTH * NW) {
+    bf16x8 xb[DEPTH][4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      wa[m] = row_ok ? *(const bf16x8*)(wp + kb + 8 * m) : zero;
-      xb[m] = b_ok ? *(const bf16x8*)(ap + kb + 8 * m) : zero;
+    for (int d = 0; d < DEPTH; ++d) {
+      const int st = st0 + d * NW;
+      if (st < s1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (gv_lds_t)(&wl[wids][d][i * 512]), 16, voff[i],
+                                                   st * GV_KB * 2, 0, 0);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) xb[d][m] = b_ok ? *(const bf16x8*)(ap + st * GV_KB + 8 * m) : zero;
+      }
     }
-  };
-  auto mma = [&](const bf16x8 (&wa)[4], const bf16x8 (&xb)[4]) {
+    __builtin_amdgcn_s_waitcnt(GV_VMCNT0);  // this wavefront's tiles are in LDS
 #pragma unroll
-    for (int m = 0; m < 4; ++m) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[m], xb[m], acc, 0, 0, 0);
-  };
-  int st = s0 + wid;
-  if (st < s1) load(st, wa0, xb0);
-  for (; st < s1; st += 2 * NW) {
-    if (st + NW < s1) load(st + NW, wa1, xb1);
-    mma(wa0, xb0);
-    if (st + NW >= s1) break;
-    if (st + 2 * NW < s1) load(st + 2 * NW, wa0, xb0);
-    mma(wa1, xb1);
+    for (int d = 0; d < DEPTH; ++d) {
+      if (st0 + d * NW < s1) {
+        const bf16* base = &wl[wid][d][row * GV_KB];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const bf16x8 wa = *(const bf16x8*)(base + (((4 * g + m) ^ sw) << 3));
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, xb[d][m], acc, 0, 0, 0);
+        }
+      }
+    }
   }
+  // each wavefront's tile through its own LDS slots (read only by itself until here)
+  float* const red = (float*)&wl[0][0][0];
+  constexpr int RS = DEPTH * GV_ROWS * GV_KB / 2;  // floats per wavefront's slots (>= 64 * 16)
 #pragma unroll
-  for (int r = 0; r < 16; ++r) red[wid][lane * 16 + r] = acc[r];
+  for (int r = 0; r < 16; ++r) red[wid * RS + lane * 16 + r] = acc[r];
   __syncthreads();
   float v[64 * 16 / (NW * 64)];
 #pragma unroll
@@ -113,7 +140,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(
     const int idx = threadIdx.x + i * NW * 64;
     float t = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) t += red[w][idx];
+    for (int w = 0; w < NW; ++w) t += red[w * RS + idx];
     v[i] = t;
   }
   auto coords = [&](int idx, int& b, int& n) {
@@ -595,9 +622,17 @@ hipError_t launch_gemv(bool bf, int kind, const void* act, int lda, int B, const
   if (bf) {
     if (KS > 1 && !partial) return hipErrorInvalidValue;
     const int grid = (N + GV_ROWS - 1) / GV_ROWS * KS;
-    gemv_bf16_kernel<GV_WAVES><<<grid, GV_WAVES * 64, 0, s>>>(
-        (const bf16*)act, lda, B, (const bf16*)W0, (const bf16*)W1, (const bf16*)W2, nseg0, nseg1,
-        N, K, KS, partial, e);
+    // K steps per wavefront (the largest split): up to 2 staged together in 8 or 16 KB of LDS
+    // per block, else up to 6 (96 KB: one block per CU, all its loads in flight at once).
+    const int per_wave = ((K / GV_KB + KS - 1) / KS + GV_WAVES - 1) / GV_WAVES;
+#define GPTK_GV(DEPTH)                                                                              \
+  gemv_bf16_kernel<GV_WAVES, DEPTH><<<grid, GV_WAVES * 64, 0, s>>>(                                 \
+      (const bf16*)act, lda, B, (const bf16*)W0, (const bf16*)W1, (const bf16*)W2, nseg0, nseg1, N, \
+      K, KS, partial, e)
+    if (per_wave <= 1) GPTK_GV(1);
+    else if (per_wave <= 2) GPTK_GV(2);
+    else GPTK_GV(6);
+#undef GPTK_GV
   } else {
     if (KS != 1) return hipErrorInvalidValue;
     gemv_f32_kernel<<<(N + 3) / 4, 256, 0, s>>>((const float*)act, lda, B, (const float*)W0,
