@@ -17,7 +17,7 @@ namespace gptk {
 namespace {
 
 constexpr int GV_ROWS = 32;   // weight rows per block (one 32x32 MFMA output tile, batch in N)
-constexpr int GV_WAVES = 4;   // wavefronts per block
+constexpr int GV_WAVES = 4;   // wavefronts per block (8 for the unsplit products with long K ranges)
 constexpr int GV_KB = 64;     // K per wavefront step: four 32x32x16 MFMAs
 constexpr int GV_TARGET_BLOCKS = 2048;  // K splits aim at this many blocks (2048: 0.6 % faster d24 step than 1024)
 
@@ -604,6 +604,8 @@ __global__ __launch_bounds__(SMP_THREADS) void sample_kernel(const float* __rest
 }  // namespace
 
 // K splits of a product: enough blocks to keep every CU busy, each wavefront with >= 1 step.
+// (Half the splits, two steps per wavefront loaded together, made the single products 2-10 %
+// faster at the d24 shapes but the whole d24 decode step 0.7 % slower.)
 int gemv_splits(int N, int K) {
   const int nrb = (N + GV_ROWS - 1) / GV_ROWS, nks = K / GV_KB;
   int ks = (GV_TARGET_BLOCKS + nrb - 1) / nrb;
@@ -622,16 +624,19 @@ hipError_t launch_gemv(bool bf, int kind, const void* act, int lda, int B, const
   if (bf) {
     if (KS > 1 && !partial) return hipErrorInvalidValue;
     const int grid = (N + GV_ROWS - 1) / GV_ROWS * KS;
-    // K steps per wavefront (the largest split): up to 2 staged together in 8 or 16 KB of LDS
-    // per block, else up to 6 (96 KB: one block per CU, all its loads in flight at once).
-    const int per_wave = ((K / GV_KB + KS - 1) / KS + GV_WAVES - 1) / GV_WAVES;
-#define GPTK_GV(DEPTH)                                                                              \
-  gemv_bf16_kernel<GV_WAVES, DEPTH><<<grid, GV_WAVES * 64, 0, s>>>(                                 \
+    // K steps of the largest split: up to two per wavefront staged together (8 or 16 KB of LDS
+    // per block); longer ranges (the unsplit MLP-up and lm_head products) on 8 wavefronts with
+    // up to three steps each in flight (96 KB: one block per CU).  Measured at the d24 shapes
+    // with the weights cold: 8 x 3 against 4 x 6 took MLP up 6.9 -> 6.4 us, lm_head 25.3 -> 23.2
+    // us; the whole d24 decode step 1.487 -> 1.477 ms.
+    const int steps = (K / GV_KB + KS - 1) / KS;
+#define GPTK_GV(NW, DEPTH)                                                                          \
+  gemv_bf16_kernel<NW, DEPTH><<<grid, NW * 64, 0, s>>>(                                             \
       (const bf16*)act, lda, B, (const bf16*)W0, (const bf16*)W1, (const bf16*)W2, nseg0, nseg1, N, \
       K, KS, partial, e)
-    if (per_wave <= 1) GPTK_GV(1);
-    else if (per_wave <= 2) GPTK_GV(2);
-    else GPTK_GV(6);
+    if (steps <= GV_WAVES) GPTK_GV(GV_WAVES, 1);
+    else if (steps <= 2 * GV_WAVES) GPTK_GV(GV_WAVES, 2);
+    else GPTK_GV(8, 3);
 #undef GPTK_GV
   } else {
     if (KS != 1) return hipErrorInvalidValue;
