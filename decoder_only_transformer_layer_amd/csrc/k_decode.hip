@@ -311,19 +311,23 @@ __global__ __launch_bounds__(DA_THREADS) void decode_attn_chunk_kernel(
     }
     return;
   }
-  // This thread's key half-row (score pass) and value rows (output pass) are requested first,
+  // This thread's key chunks (score pass) and value rows (output pass) are requested first,
   // together, then the queries: one memory round trip instead of three.  Keys past the chunk's
-  // end read the chunk's first key instead (their probability is 0).
-  constexpr int OCT = D / 8, PARTS = DA_THREADS / OCT;  // output pass: D=128: 16 x 16; D=64: 8 x 32
-  constexpr int VR = DA_CHUNK / PARTS;                  // value rows per thread
-  const int j = tid >> 1, hf = tid & 1;
+  // end read the chunk's first key instead (their probability is 0).  Both passes load 16-byte
+  // chunks (8 elements) with consecutive threads on consecutive chunks of a row, so that each
+  // load instruction covers whole rows.
+  constexpr int OCT = D / 8, PARTS = DA_THREADS / OCT;  // chunks per row; rows per instruction
+  constexpr int VR = DA_CHUNK / PARTS;                  // key / value rows per thread
   const int oc = tid % OCT, pt = tid / OCT;
-  Raw8<AT> kraw[D / 16], vraw[VR];
+  Raw8<AT> kraw[VR], vraw[VR];
   {
-    const AT* kr = kc + (((size_t)b * Hkv + g) * T + (j0 + (j < nk ? j : 0))) * D + hf * (D / 2);
-#pragma unroll
-    for (int u = 0; u < D / 16; ++u) ld_raw(kr + 8 * u, kraw[u]);
+    const AT* kb = kc + (((size_t)b * Hkv + g) * T + j0) * D + oc * 8;
     const AT* vb = vc + (((size_t)b * Hkv + g) * T + j0) * D + oc * 8;
+#pragma unroll
+    for (int k = 0; k < VR; ++k) {
+      const int jv = pt + k * PARTS;
+      ld_raw(kb + (size_t)(jv < nk ? jv : 0) * D, kraw[k]);
+    }
 #pragma unroll
     for (int k = 0; k < VR; ++k) {
       const int jv = pt + k * PARTS;
@@ -333,15 +337,24 @@ __global__ __launch_bounds__(DA_THREADS) void decode_attn_chunk_kernel(
   for (int i = tid; i < G * D; i += DA_THREADS)
     qs[i / D][i % D] = to_f32(q[(size_t)b * H * D + (size_t)(g * G + i / D) * D + i % D]);
   __syncthreads();
-  // scores: thread (key j = tid / 2, half = tid % 2) over D/2 dimensions, halves joined by a shuffle
+  // scores: thread (chunk oc, rows pt + k * PARTS) forms 8-element partial dot products, summed
+  // over the OCT threads of a row by DPP butterflies within 16-lane rows
   for (int gi = 0; gi < G; ++gi) {
-    float s = 0.f;
+    float qv[8];
 #pragma unroll
-    for (int u = 0; u < D / 16; ++u)
+    for (int i = 0; i < 8; ++i) qv[i] = qs[gi][oc * 8 + i];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) s = fmaf(qs[gi][hf * (D / 2) + 8 * u + i], raw_at(kraw[u], i), s);
-    s += __shfl_xor(s, 1);
-    if (hf == 0 && j < DA_CHUNK) sc[gi][j] = j < nk ? s * scale : -INFINITY;
+    for (int k = 0; k < VR; ++k) {
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s = fmaf(qv[i], raw_at(kraw[k], i), s);
+      s += dpp<0xB1>(s);   // quad_perm [1,0,3,2]
+      s += dpp<0x4E>(s);   // quad_perm [2,3,0,1]
+      s += dpp<0x141>(s);  // row_half_mirror: 8-lane sums
+      if constexpr (OCT == 16) s += dpp<0x140>(s);  // row_mirror: 16-lane sums
+      const int jv = pt + k * PARTS;
+      if (oc == 0) sc[gi][jv] = jv < nk ? s * scale : -INFINITY;
+    }
   }
   __syncthreads();
   // per head: chunk max and sum (one wavefront per head, two keys per lane)
