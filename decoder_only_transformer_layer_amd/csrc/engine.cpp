@@ -613,10 +613,12 @@ struct DecodeSplits {
   int qkv, out, down;
 };
 
+// bf16: the out-projection does not split K -- it adds into x itself, and the MLP-up product
+// normalises x on the fly (launch_gemv's xnorm), so no norm kernel runs between the two.
 static DecodeSplits decode_splits(const gpt_cfg* c) {
   if (c->dtype != GPT_BF16) return {1, 1, 1};
   const int C = c->d_model, H = c->n_head, Hkv = c->n_kv_head, D = c->head_dim, F = c->mlp_dim;
-  return {gemv_splits((H + 2 * Hkv) * D, C), gemv_splits(C, H * D), gemv_splits(C, F)};
+  return {gemv_splits((H + 2 * Hkv) * D, C), 1, gemv_splits(C, F)};
 }
 
 struct DecodeLayout {
@@ -710,12 +712,18 @@ gpt_status gpt_decode_step(const gpt_cfg* c, const gpt_weights* w, const int32_t
                           flags, s));
     CK(launch_decode_attn(bf, q, kc, vc, pos, B, T, H, Hkv, D, win, c->attn_scale, o,
                           (float*)(ws + L.part), s));
-    // x += o W_O^T (partials summed by the norm kernel), xn = RMSNorm(x)
+    // x += o W_O^T, then h = relu(RMSNorm(x) W_1^T)^2: bf16 -- the norm inside the MLP-up
+    // product; fp32 -- xn = RMSNorm(x) by the norm kernel first
     CK(launch_gemv(bf, DEC_RESID, o, H * D, B, w->wo[l], w->wo[l], w->wo[l], C, 0, C, H * D, x, C, s,
                    ks.out, gpart));
-    CK(launch_mix_norm(x, x0, w->resid_lambda, w->x0_lambda, l, false, xn, bf, B, C, eps, s, 0,
-                       ks.out > 1 ? gpart : nullptr, ks.out));
-    CK(launch_gemv(bf, DEC_RELU2, xn, C, B, w->w1[l], w->w1[l], w->w1[l], F, 0, F, C, hb, F, s));
+    if (bf) {
+      CK(launch_gemv(bf, DEC_RELU2, x, C, B, w->w1[l], w->w1[l], w->w1[l], F, 0, F, C, hb, F, s, 1,
+                     nullptr, 0.f, nullptr, nullptr, 0, 0, true, eps));
+    } else {
+      CK(launch_mix_norm(x, x0, w->resid_lambda, w->x0_lambda, l, false, xn, bf, B, C, eps, s, 0,
+                         ks.out > 1 ? gpart : nullptr, ks.out));
+      CK(launch_gemv(bf, DEC_RELU2, xn, C, B, w->w1[l], w->w1[l], w->w1[l], F, 0, F, C, hb, F, s));
+    }
     // x += h W_2^T, then the next layer's x0 mix and norm (or the final norm)
     CK(launch_gemv(bf, DEC_RESID, hb, F, B, w->w2[l], w->w2[l], w->w2[l], C, 0, C, F, x, C, s,
                    ks.down, gpart));

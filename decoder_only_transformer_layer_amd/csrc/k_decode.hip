@@ -61,16 +61,22 @@ __device__ __forceinline__ void gv_apply(const GvEpi& e, int b, int n, float v) 
 // tiles are summed through LDS in a fixed order.  With KS > 1 the block stores its tile as
 // partial[ks][b][n] and the consumer of the product sums the KS tiles in split order (no block
 // waits on another); with KS = 1 the epilogue is applied here.
+// XN (KS = 1 only): the batch operand is the fp32 residual stream x [B][lda] itself, RMS-
+// normalised in the product: it is rounded to bf16 as loaded, each row's sum of squares of the
+// fp32 values is formed on the way (per lane in step order, then over the lanes and wavefronts
+// of the row in a fixed order), and the outputs of row b are scaled by 1/rms_b = (sum/K + eps)^-1/2
+// before the epilogue -- the row scale the forward's GEMMs apply to an un-normalised input.
 __device__ __forceinline__ int gv_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 // s_waitcnt immediate for vmcnt = 0 (gfx9 encoding; expcnt and lgkmcnt at their maxima)
 constexpr int GV_VMCNT0 = 0x0F70;
 typedef __attribute__((address_space(3))) void* gv_lds_t;
-template <int NW, int DEPTH>
+template <int NW, int DEPTH, bool XN>
 __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(
-    const bf16* __restrict__ act, int lda, int B, const bf16* __restrict__ W0,
+    const void* __restrict__ act_, int lda, int B, const bf16* __restrict__ W0,
     const bf16* __restrict__ W1, const bf16* __restrict__ W2, int nseg0, int nseg1, int N, int K,
-    int KS, float* __restrict__ partial, GvEpi e) {
+    int KS, float* __restrict__ partial, GvEpi e, float eps) {
   __shared__ __attribute__((aligned(16))) bf16 wl[NW][DEPTH][GV_ROWS * GV_KB];
+  __shared__ float ssl[XN ? NW : 1][64];  // XN: per-lane sums of squares
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wids = __builtin_amdgcn_readfirstlane(wid);
   const int rb = blockIdx.x / KS, ks = blockIdx.x % KS;
@@ -82,7 +88,9 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(
   else { W = W2; r0 = n0 - nseg0 - nseg1; }
   const int row = lane & 31, g = lane >> 5;
   const bool b_ok = row < B;  // the batch operand's lane row is b
-  const bf16* ap = act + (size_t)row * lda + 32 * g;
+  const bf16* ap = (const bf16*)act_ + (size_t)row * lda + 32 * g;
+  const float* axp = (const float*)act_ + (size_t)row * lda + 32 * g;
+  float ssq = 0.f;
   const int nks = K / GV_KB, s0 = (int)((long)ks * nks / KS), s1 = (int)((long)(ks + 1) * nks / KS);
   // The block's rows as a buffer resource: rows past N (last block) read as zero.  DMA lane L of
   // instruction i fetches row 8i + L/8, chunk (L % 8) ^ swz(row); the K offset rides in soffset.
@@ -103,6 +111,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(
   // this wavefront's K steps s0 + wid, s0 + wid + NW, ... in batches of DEPTH
   for (int st0 = s0 + wids; st0 < s1; st0 += DEPTH * NW) {
     bf16x8 xb[DEPTH][4];
+    f32x4 xf[XN ? DEPTH : 1][4][2];
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       const int st = st0 + d * NW;
@@ -112,7 +121,14 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (gv_lds_t)(&wl[wids][d][i * 512]), 16, voff[i],
                                                    st * GV_KB * 2, 0, 0);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) xb[d][m] = b_ok ? *(const bf16x8*)(ap + st * GV_KB + 8 * m) : zero;
+        for (int m = 0; m < 4; ++m) {
+          if constexpr (XN) {
+            xf[d][m][0] = b_ok ? *(const f32x4*)(axp + st * GV_KB + 8 * m) : f32x4{};
+            xf[d][m][1] = b_ok ? *(const f32x4*)(axp + st * GV_KB + 8 * m + 4) : f32x4{};
+          } else {
+            xb[d][m] = b_ok ? *(const bf16x8*)(ap + st * GV_KB + 8 * m) : zero;
+          }
+        }
       }
     }
     __builtin_amdgcn_s_waitcnt(GV_VMCNT0);  // this wavefront's tiles are in LDS
@@ -120,6 +136,16 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(
     for (int d = 0; d < DEPTH; ++d) {
       if (st0 + d * NW < s1) {
         const bf16* base = &wl[wid][d][row * GV_KB];
+        if constexpr (XN) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const float v = xf[d][m][i >> 2][i & 3];
+              ssq = fmaf(v, v, ssq);
+              xb[d][m][i] = (bf16)v;
+            }
+        }
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const bf16x8 wa = *(const bf16x8*)(base + (((4 * g + m) ^ sw) << 3));
@@ -133,6 +159,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(
   constexpr int RS = DEPTH * GV_ROWS * GV_KB / 2;  // floats per wavefront's slots (>= 64 * 16)
 #pragma unroll
   for (int r = 0; r < 16; ++r) red[wid * RS + lane * 16 + r] = acc[r];
+  if constexpr (XN) ssl[wid][lane] = ssq;
   __syncthreads();
   float v[64 * 16 / (NW * 64)];
 #pragma unroll
@@ -161,6 +188,12 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(
   for (int i = 0; i < 64 * 16 / (NW * 64); ++i) {
     int b, n;
     coords(threadIdx.x + i * NW * 64, b, n);
+    if constexpr (XN) {
+      float ss = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) ss += ssl[w][b] + ssl[w][b + 32];
+      v[i] *= rsqrtf(ss / (float)K + eps);
+    }
     if (b < B && n < N) gv_apply<bf16>(e, b, n, v[i]);
   }
 }
@@ -629,8 +662,9 @@ int gemv_splits(int N, int K) {
 hipError_t launch_gemv(bool bf, int kind, const void* act, int lda, int B, const void* W0,
                        const void* W1, const void* W2, int nseg0, int nseg1, int N, int K,
                        void* out, int ldo, hipStream_t s, int KS, float* partial, float cap,
-                       const int32_t* pos, const int32_t* tokens, int T, int V) {
+                       const int32_t* pos, const int32_t* tokens, int T, int V, bool xnorm, float eps) {
   if (B < 1 || B > 32 || N < 1 || K < 1 || K % GV_KB || KS < 1) return hipErrorInvalidValue;
+  if (xnorm && (!bf || KS != 1 || lda % 4)) return hipErrorInvalidValue;
   if ((nseg0 < N && nseg0 % GV_ROWS) || (nseg0 + nseg1 < N && (nseg0 + nseg1) % GV_ROWS))
     return hipErrorInvalidValue;  // interior segment boundaries on block boundaries
   GvEpi e{kind, out, ldo, cap, pos, tokens, T, V};
@@ -643,13 +677,19 @@ hipError_t launch_gemv(bool bf, int kind, const void* act, int lda, int B, const
     // with the weights cold: 8 x 3 against 4 x 6 took MLP up 6.9 -> 6.4 us, lm_head 25.3 -> 23.2
     // us; the whole d24 decode step 1.487 -> 1.477 ms.
     const int steps = (K / GV_KB + KS - 1) / KS;
-#define GPTK_GV(NW, DEPTH)                                                                          \
-  gemv_bf16_kernel<NW, DEPTH><<<grid, NW * 64, 0, s>>>(                                             \
-      (const bf16*)act, lda, B, (const bf16*)W0, (const bf16*)W1, (const bf16*)W2, nseg0, nseg1, N, \
-      K, KS, partial, e)
-    if (steps <= GV_WAVES) GPTK_GV(GV_WAVES, 1);
-    else if (steps <= 2 * GV_WAVES) GPTK_GV(GV_WAVES, 2);
-    else GPTK_GV(8, 3);
+#define GPTK_GV(NW, DEPTH, XN)                                                                      \
+  gemv_bf16_kernel<NW, DEPTH, XN><<<grid, NW * 64, 0, s>>>(                                         \
+      act, lda, B, (const bf16*)W0, (const bf16*)W1, (const bf16*)W2, nseg0, nseg1, N, K, KS,       \
+      partial, e, eps)
+    if (xnorm) {
+      if (steps <= GV_WAVES) GPTK_GV(GV_WAVES, 1, true);
+      else if (steps <= 2 * GV_WAVES) GPTK_GV(GV_WAVES, 2, true);
+      else GPTK_GV(8, 3, true);
+    } else {
+      if (steps <= GV_WAVES) GPTK_GV(GV_WAVES, 1, false);
+      else if (steps <= 2 * GV_WAVES) GPTK_GV(GV_WAVES, 2, false);
+      else GPTK_GV(8, 3, false);
+    }
 #undef GPTK_GV
   } else {
     if (KS != 1) return hipErrorInvalidValue;

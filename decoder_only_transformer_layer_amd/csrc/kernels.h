@@ -74,12 +74,15 @@ hipError_t launch_qk_rope_norm(void* qk, bool bf16, int ld, const float2* cs, in
 enum DecEpi { DEC_STORE = 0, DEC_RELU2 = 1, DEC_RESID = 2, DEC_LOGITS = 3 };
 // KS > 1 (bf16 only) splits K over KS blocks per row block: the product then only stores its
 // KS partial tiles in partial[KS][B][N] (no epilogue) and the consumer sums them in order.
+// xnorm (bf16, KS = 1): act is the fp32 residual stream [B][lda], RMS-normalised in the product
+// (rounded to bf16 as loaded, outputs of row b scaled by (sum_k x[b][k]^2 / K + eps)^-1/2).
 int gemv_splits(int N, int K);
 hipError_t launch_gemv(bool bf16, int kind, const void* act, int lda, int B, const void* W0,
                        const void* W1, const void* W2, int nseg0, int nseg1, int N, int K,
                        void* out, int ldo, hipStream_t s, int KS = 1, float* partial = nullptr,
                        float cap = 0.f, const int32_t* pos = nullptr,
-                       const int32_t* tokens = nullptr, int T = 0, int V = 0);
+                       const int32_t* tokens = nullptr, int T = 0, int V = 0,
+                       bool xnorm = false, float eps = 0.f);
 // RoPE at pos[b] + per-head RMSNorm of the q and k heads of y [KS][B][ldy] (fp32 K-split
 // partials summed in order; heads q | k | v), q_hat to qout [B, H*D], k_hat and v to the caches
 // [B, Hkv, T, D] at position pos[b]; a row with pos outside [0, T) writes nothing and raises
