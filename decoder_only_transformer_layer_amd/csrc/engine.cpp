@@ -600,8 +600,8 @@ static gpt_status validate_decode(const gpt_cfg* c) {
   const gpt_status st = validate(c);
   if (st != GPT_OK) return st;
   if (c->batch > 32 || c->seq_len > 8192 || c->n_head / c->n_kv_head > 8) return GPT_E_UNSUPPORTED;
-  // bf16 products split K and the residual-norm kernel sums their partials, up to this width
-  if (c->dtype == GPT_BF16 && c->d_model > mix_norm_add_max_cols()) return GPT_E_UNSUPPORTED;
+  // the widest bf16 model the decode tests cover
+  if (c->dtype == GPT_BF16 && c->d_model > 4096) return GPT_E_UNSUPPORTED;
   if (any_ve(c) || c->looped || c->nested_c1) return GPT_E_UNSUPPORTED;
   return GPT_OK;
 }
@@ -613,8 +613,8 @@ struct DecodeSplits {
   int qkv, out, down;
 };
 
-// bf16: the out-projection does not split K -- it adds into x itself, and the MLP-up product
-// normalises x on the fly (launch_gemv's xnorm), so no norm kernel runs between the two.
+// bf16: the out-projection does not split K -- it adds into x itself and leaves bf16(x) and
+// per-block sums of squares, from which the MLP-up product applies the norm as a row scale.
 static DecodeSplits decode_splits(const gpt_cfg* c) {
   if (c->dtype != GPT_BF16) return {1, 1, 1};
   const int C = c->d_model, H = c->n_head, Hkv = c->n_kv_head, D = c->head_dim, F = c->mlp_dim;
@@ -622,7 +622,7 @@ static DecodeSplits decode_splits(const gpt_cfg* c) {
 }
 
 struct DecodeLayout {
-  size_t flags, x, x0, xn, y, q, o, h, part, gpart, total;
+  size_t flags, x, x0, xn, y, q, o, h, part, gpart, ss_o, ss_m, total;
 };
 
 static DecodeLayout decode_plan(const gpt_cfg* c) {
@@ -642,6 +642,8 @@ static DecodeLayout decode_plan(const gpt_cfg* c) {
   L.h = off; off += up(B * F * es);
   L.part = off; off += up(B * H * (size_t)decode_attn_chunks(c->seq_len) * (D + 2) * 4);
   L.gpart = off; off += up(ro * 4);
+  L.ss_o = off; off += up(B * ((C + 31) / 32) * 4);               // bf16: out-projection row sums
+  L.ss_m = off; off += up(B * (size_t)add_mix_rows_blocks(C) * 4);  // bf16: MLP-down row sums
   L.total = off;
   return L;
 }
@@ -701,38 +703,52 @@ gpt_status gpt_decode_step(const gpt_cfg* c, const gpt_weights* w, const int32_t
   CK(launch_clear_u32(flags, 16, s));
   CK(launch_embed_norm(tokens, w->wte, bf, w->resid_lambda, w->x0_lambda, x0, x, xn, B, C, V, eps,
                        flags, s));
+  // bf16: xn holds bf16(x) of the un-normalised stream after layer 0's q/k/v (embed_norm's xn is
+  // normalised), and the products that read it apply 1/rms from per-block row sums (ss_o, ss_m).
+  float* ss_o = (float*)(ws + L.ss_o);
+  float* ss_m = (float*)(ws + L.ss_m);
+  const int no = (C + 31) / 32, nm = add_mix_rows_blocks(C);
   for (int l = 0; l < c->n_layer; ++l) {
     char* kc = (char*)kv_cache + (size_t)l * 2 * cache_half;
     char* vc = kc + cache_half;
     const int win = c->window[l] < T ? c->window[l] : T;
     // q/k/v (K-split partials in y), then RoPE + QK-norm and the cache append
     CK(launch_gemv(bf, DEC_STORE, xn, C, B, w->wq[l], w->wk[l], w->wv[l], H * D, Hkv * D, nqkv, C,
-                   y, nqkv, s, ks.qkv, y));
+                   y, nqkv, s, ks.qkv, y, 0.f, nullptr, nullptr, 0, 0, bf && l > 0 ? ss_m : nullptr, nm,
+                   eps));
     CK(launch_rope_append(bf, y, nqkv, ks.qkv, pos, B, T, H, Hkv, D, eps, c->rope_base, q, kc, vc,
                           flags, s));
     CK(launch_decode_attn(bf, q, kc, vc, pos, B, T, H, Hkv, D, win, c->attn_scale, o,
                           (float*)(ws + L.part), s));
-    // x += o W_O^T, then h = relu(RMSNorm(x) W_1^T)^2: bf16 -- the norm inside the MLP-up
-    // product; fp32 -- xn = RMSNorm(x) by the norm kernel first
-    CK(launch_gemv(bf, DEC_RESID, o, H * D, B, w->wo[l], w->wo[l], w->wo[l], C, 0, C, H * D, x, C, s,
-                   ks.out, gpart));
+    // x += o W_O^T, then h = relu(RMSNorm(x) W_1^T)^2 (bf16: the norm as the MLP-up product's row
+    // scale; fp32: xn = RMSNorm(x) by the norm kernel first)
     if (bf) {
-      CK(launch_gemv(bf, DEC_RELU2, x, C, B, w->w1[l], w->w1[l], w->w1[l], F, 0, F, C, hb, F, s, 1,
-                     nullptr, 0.f, nullptr, nullptr, 0, 0, true, eps));
+      CK(launch_gemv(bf, DEC_RESID_RS, o, H * D, B, w->wo[l], w->wo[l], w->wo[l], C, 0, C, H * D, x, C,
+                     s, 1, nullptr, 0.f, nullptr, nullptr, 0, 0, nullptr, 0, 0.f, xn, ss_o));
+      CK(launch_gemv(bf, DEC_RELU2, xn, C, B, w->w1[l], w->w1[l], w->w1[l], F, 0, F, C, hb, F, s, 1,
+                     nullptr, 0.f, nullptr, nullptr, 0, 0, ss_o, no, eps));
     } else {
-      CK(launch_mix_norm(x, x0, w->resid_lambda, w->x0_lambda, l, false, xn, bf, B, C, eps, s, 0,
-                         ks.out > 1 ? gpart : nullptr, ks.out));
+      CK(launch_gemv(bf, DEC_RESID, o, H * D, B, w->wo[l], w->wo[l], w->wo[l], C, 0, C, H * D, x, C, s));
+      CK(launch_mix_norm(x, x0, w->resid_lambda, w->x0_lambda, l, false, xn, bf, B, C, eps, s));
       CK(launch_gemv(bf, DEC_RELU2, xn, C, B, w->w1[l], w->w1[l], w->w1[l], F, 0, F, C, hb, F, s));
     }
-    // x += h W_2^T, then the next layer's x0 mix and norm (or the final norm)
-    CK(launch_gemv(bf, DEC_RESID, hb, F, B, w->w2[l], w->w2[l], w->w2[l], C, 0, C, F, x, C, s,
-                   ks.down, gpart));
+    // x += h W_2^T, then the next layer's x0 mix (bf16: bf16(x) and row sums for the next
+    // product; fp32: the norm as well)
     const bool more = l + 1 < c->n_layer;
-    CK(launch_mix_norm(x, x0, w->resid_lambda, w->x0_lambda, l + 1, more, xn, bf, B, C, eps, s, 0,
-                       ks.down > 1 ? gpart : nullptr, ks.down));
+    if (bf) {
+      CK(launch_gemv(bf, DEC_RESID, hb, F, B, w->w2[l], w->w2[l], w->w2[l], C, 0, C, F, x, C, s,
+                     ks.down, gpart));
+      // (KS = 1: the product has added into x itself and there are no partials)
+      CK(launch_add_mix_rows(x, ks.down > 1 ? gpart : nullptr, ks.down > 1 ? ks.down : 0, x0,
+                             w->resid_lambda, w->x0_lambda, l + 1, more, xn, ss_m, B, C, s));
+    } else {
+      CK(launch_gemv(bf, DEC_RESID, hb, F, B, w->w2[l], w->w2[l], w->w2[l], C, 0, C, F, x, C, s));
+      CK(launch_mix_norm(x, x0, w->resid_lambda, w->x0_lambda, l + 1, more, xn, bf, B, C, eps, s));
+    }
   }
+  // logits of the final norm (bf16: as the product's row scale)
   CK(launch_gemv(bf, DEC_LOGITS, xn, C, B, w->lm_head, w->lm_head, w->lm_head, V, 0, V, C, logits,
-                 V, s, 1, nullptr, c->softcap, pos, tokens, T, V));
+                 V, s, 1, nullptr, c->softcap, pos, tokens, T, V, bf ? ss_m : nullptr, nm, eps));
   return GPT_OK;
 }
 

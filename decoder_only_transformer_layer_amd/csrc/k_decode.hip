@@ -24,9 +24,11 @@ constexpr int GV_TARGET_BLOCKS = 2048;  // K splits aim at this many blocks (204
 // Per-(row b, column n) epilogue of a decode-step product.
 struct GvEpi {
   int kind;           // DEC_* below
-  void* out; int ldo; // STORE: f32; RELU2: activation type; RESID: f32 (x += v); LOGITS: f32
+  void* out; int ldo; // STORE: f32; RELU2: activation type; RESID, RESID_RS: f32 (x += v); LOGITS: f32
   float cap;
   const int32_t* pos; const int32_t* tokens; int T; int V;  // LOGITS: rows with bad input -> NaN
+  const float* rs; int rs_n; float eps;  // row scale: 1/rms of row b from rs[b * rs_n + j], j < rs_n
+  bf16* xb; float* ss;                   // RESID_RS: bf16(x) [B][ldo] and ss[b * gridDim.x + block]
 };
 
 template <typename AT>
@@ -61,22 +63,24 @@ __device__ __forceinline__ void gv_apply(const GvEpi& e, int b, int n, float v) 
 // tiles are summed through LDS in a fixed order.  With KS > 1 the block stores its tile as
 // partial[ks][b][n] and the consumer of the product sums the KS tiles in split order (no block
 // waits on another); with KS = 1 the epilogue is applied here.
-// XN (KS = 1 only): the batch operand is the fp32 residual stream x [B][lda] itself, RMS-
-// normalised in the product: it is rounded to bf16 as loaded, each row's sum of squares of the
-// fp32 values is formed on the way (per lane in step order, then over the lanes and wavefronts
-// of the row in a fixed order), and the outputs of row b are scaled by 1/rms_b = (sum/K + eps)^-1/2
-// before the epilogue -- the row scale the forward's GEMMs apply to an un-normalised input.
+// Row scale (e.rs given): the batch operand is bf16(x) of an un-normalised residual stream x and
+// the outputs of row b (partial tiles included) are scaled by 1/rms_b = (sum / K + eps)^-1/2,
+// sum = the producer's per-block sums of squares of row b's fp32 values, added in block order:
+// the row scale the forward's GEMMs apply to an un-normalised input.
+// DEC_RESID_RS (KS = 1): x += y, and the block also writes bf16(x) for the next product and the
+// sum of squares of its 32 columns of each row of x (columns in order), ss[b * nblocks + block].
 __device__ __forceinline__ int gv_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 // s_waitcnt immediate for vmcnt = 0 (gfx9 encoding; expcnt and lgkmcnt at their maxima)
 constexpr int GV_VMCNT0 = 0x0F70;
 typedef __attribute__((address_space(3))) void* gv_lds_t;
-template <int NW, int DEPTH, bool XN>
+template <int NW, int DEPTH>
 __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(
-    const void* __restrict__ act_, int lda, int B, const bf16* __restrict__ W0,
+    const bf16* __restrict__ act, int lda, int B, const bf16* __restrict__ W0,
     const bf16* __restrict__ W1, const bf16* __restrict__ W2, int nseg0, int nseg1, int N, int K,
-    int KS, float* __restrict__ partial, GvEpi e, float eps) {
+    int KS, float* __restrict__ partial, GvEpi e) {
   __shared__ __attribute__((aligned(16))) bf16 wl[NW][DEPTH][GV_ROWS * GV_KB];
-  __shared__ float ssl[XN ? NW : 1][64];  // XN: per-lane sums of squares
+  __shared__ float rsc[32];                 // row scales (e.rs)
+  __shared__ float sq[32][GV_ROWS + 1];     // DEC_RESID_RS: squares of the updated x
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wids = __builtin_amdgcn_readfirstlane(wid);
   const int rb = blockIdx.x / KS, ks = blockIdx.x % KS;
@@ -88,9 +92,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(
   else { W = W2; r0 = n0 - nseg0 - nseg1; }
   const int row = lane & 31, g = lane >> 5;
   const bool b_ok = row < B;  // the batch operand's lane row is b
-  const bf16* ap = (const bf16*)act_ + (size_t)row * lda + 32 * g;
-  const float* axp = (const float*)act_ + (size_t)row * lda + 32 * g;
-  float ssq = 0.f;
+  const bf16* ap = act + (size_t)row * lda + 32 * g;
   const int nks = K / GV_KB, s0 = (int)((long)ks * nks / KS), s1 = (int)((long)(ks + 1) * nks / KS);
   // The block's rows as a buffer resource: rows past N (last block) read as zero.  DMA lane L of
   // instruction i fetches row 8i + L/8, chunk (L % 8) ^ swz(row); the K offset rides in soffset.
@@ -108,10 +110,24 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
   const bf16x8 zero = {};
   const int sw = gv_swz(row);
+  // Row scales: wavefront w sums the per-block sums of squares of rows w, w + NW, ... (lane j
+  // holding blocks j and j + 64, rs_n <= 128); requested here, with the first weight loads.
+  constexpr int RB = 32 / NW;  // rows per wavefront (B <= 32)
+  float rsv[RB][2];
+  if (e.rs != nullptr) {
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const int b = wids + r * NW;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int j = lane + 64 * h;
+        rsv[r][h] = (b < B && j < e.rs_n) ? e.rs[b * e.rs_n + j] : 0.f;
+      }
+    }
+  }
   // this wavefront's K steps s0 + wid, s0 + wid + NW, ... in batches of DEPTH
   for (int st0 = s0 + wids; st0 < s1; st0 += DEPTH * NW) {
     bf16x8 xb[DEPTH][4];
-    f32x4 xf[XN ? DEPTH : 1][4][2];
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       const int st = st0 + d * NW;
@@ -121,14 +137,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (gv_lds_t)(&wl[wids][d][i * 512]), 16, voff[i],
                                                    st * GV_KB * 2, 0, 0);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          if constexpr (XN) {
-            xf[d][m][0] = b_ok ? *(const f32x4*)(axp + st * GV_KB + 8 * m) : f32x4{};
-            xf[d][m][1] = b_ok ? *(const f32x4*)(axp + st * GV_KB + 8 * m + 4) : f32x4{};
-          } else {
-            xb[d][m] = b_ok ? *(const bf16x8*)(ap + st * GV_KB + 8 * m) : zero;
-          }
-        }
+        for (int m = 0; m < 4; ++m) xb[d][m] = b_ok ? *(const bf16x8*)(ap + st * GV_KB + 8 * m) : zero;
       }
     }
     __builtin_amdgcn_s_waitcnt(GV_VMCNT0);  // this wavefront's tiles are in LDS
@@ -136,16 +145,6 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(
     for (int d = 0; d < DEPTH; ++d) {
       if (st0 + d * NW < s1) {
         const bf16* base = &wl[wid][d][row * GV_KB];
-        if constexpr (XN) {
-#pragma unroll
-          for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const float v = xf[d][m][i >> 2][i & 3];
-              ssq = fmaf(v, v, ssq);
-              xb[d][m][i] = (bf16)v;
-            }
-        }
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const bf16x8 wa = *(const bf16x8*)(base + (((4 * g + m) ^ sw) << 3));
@@ -159,7 +158,16 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(
   constexpr int RS = DEPTH * GV_ROWS * GV_KB / 2;  // floats per wavefront's slots (>= 64 * 16)
 #pragma unroll
   for (int r = 0; r < 16; ++r) red[wid * RS + lane * 16 + r] = acc[r];
-  if constexpr (XN) ssl[wid][lane] = ssq;
+  if (e.rs != nullptr) {
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const int b = wids + r * NW;
+      if (b < B) {
+        const float ss = wave_sum(rsv[r][0] + rsv[r][1]);
+        if (lane == 0) rsc[b] = rsqrtf(ss / (float)K + e.eps);
+      }
+    }
+  }
   __syncthreads();
   float v[64 * 16 / (NW * 64)];
 #pragma unroll
@@ -175,6 +183,14 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(
     n = n0 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
     b = l & 31;
   };
+  if (e.rs != nullptr) {
+#pragma unroll
+    for (int i = 0; i < 64 * 16 / (NW * 64); ++i) {
+      int b, n;
+      coords(threadIdx.x + i * NW * 64, b, n);
+      if (b < B) v[i] *= rsc[b];
+    }
+  }
   if (KS > 1) {
 #pragma unroll
     for (int i = 0; i < 64 * 16 / (NW * 64); ++i) {
@@ -184,16 +200,32 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(
     }
     return;
   }
+  if (e.kind == DEC_RESID_RS) {
+#pragma unroll
+    for (int i = 0; i < 64 * 16 / (NW * 64); ++i) {
+      int b, n;
+      coords(threadIdx.x + i * NW * 64, b, n);
+      float w = 0.f;
+      if (b < B && n < N) {
+        const size_t o = (size_t)b * e.ldo + n;
+        w = ((float*)e.out)[o] + v[i];
+        ((float*)e.out)[o] = w;
+        e.xb[o] = (bf16)w;
+      }
+      sq[b][n - n0] = w * w;
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < B) {
+      float ss = 0.f;
+      for (int j = 0; j < GV_ROWS; ++j) ss += sq[threadIdx.x][j];
+      e.ss[threadIdx.x * gridDim.x + blockIdx.x] = ss;
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 64 * 16 / (NW * 64); ++i) {
     int b, n;
     coords(threadIdx.x + i * NW * 64, b, n);
-    if constexpr (XN) {
-      float ss = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) ss += ssl[w][b] + ssl[w][b + 32];
-      v[i] *= rsqrtf(ss / (float)K + eps);
-    }
     if (b < B && n < N) gv_apply<bf16>(e, b, n, v[i]);
   }
 }
@@ -673,12 +705,15 @@ int gemv_splits(int N, int K) {
 hipError_t launch_gemv(bool bf, int kind, const void* act, int lda, int B, const void* W0,
                        const void* W1, const void* W2, int nseg0, int nseg1, int N, int K,
                        void* out, int ldo, hipStream_t s, int KS, float* partial, float cap,
-                       const int32_t* pos, const int32_t* tokens, int T, int V, bool xnorm, float eps) {
+                       const int32_t* pos, const int32_t* tokens, int T, int V, const float* rs,
+                       int rs_n, float eps, void* xb, float* ss) {
   if (B < 1 || B > 32 || N < 1 || K < 1 || K % GV_KB || KS < 1) return hipErrorInvalidValue;
-  if (xnorm && (!bf || KS != 1 || lda % 4)) return hipErrorInvalidValue;
+  if ((rs != nullptr || kind == DEC_RESID_RS) && !bf) return hipErrorInvalidValue;
+  if (rs != nullptr && (rs_n < 1 || rs_n > 128)) return hipErrorInvalidValue;
+  if (kind == DEC_RESID_RS && (KS != 1 || xb == nullptr || ss == nullptr)) return hipErrorInvalidValue;
   if ((nseg0 < N && nseg0 % GV_ROWS) || (nseg0 + nseg1 < N && (nseg0 + nseg1) % GV_ROWS))
     return hipErrorInvalidValue;  // interior segment boundaries on block boundaries
-  GvEpi e{kind, out, ldo, cap, pos, tokens, T, V};
+  GvEpi e{kind, out, ldo, cap, pos, tokens, T, V, rs, rs_n, eps, (bf16*)xb, ss};
   if (bf) {
     if (KS > 1 && !partial) return hipErrorInvalidValue;
     const int grid = (N + GV_ROWS - 1) / GV_ROWS * KS;
@@ -688,19 +723,13 @@ hipError_t launch_gemv(bool bf, int kind, const void* act, int lda, int B, const
     // with the weights cold: 8 x 3 against 4 x 6 took MLP up 6.9 -> 6.4 us, lm_head 25.3 -> 23.2
     // us; the whole d24 decode step 1.487 -> 1.477 ms.
     const int steps = (K / GV_KB + KS - 1) / KS;
-#define GPTK_GV(NW, DEPTH, XN)                                                                      \
-  gemv_bf16_kernel<NW, DEPTH, XN><<<grid, NW * 64, 0, s>>>(                                         \
-      act, lda, B, (const bf16*)W0, (const bf16*)W1, (const bf16*)W2, nseg0, nseg1, N, K, KS,       \
-      partial, e, eps)
-    if (xnorm) {
-      if (steps <= GV_WAVES) GPTK_GV(GV_WAVES, 1, true);
-      else if (steps <= 2 * GV_WAVES) GPTK_GV(GV_WAVES, 2, true);
-      else GPTK_GV(8, 3, true);
-    } else {
-      if (steps <= GV_WAVES) GPTK_GV(GV_WAVES, 1, false);
-      else if (steps <= 2 * GV_WAVES) GPTK_GV(GV_WAVES, 2, false);
-      else GPTK_GV(8, 3, false);
-    }
+#define GPTK_GV(NW, DEPTH)                                                                          \
+  gemv_bf16_kernel<NW, DEPTH><<<grid, NW * 64, 0, s>>>(                                             \
+      (const bf16*)act, lda, B, (const bf16*)W0, (const bf16*)W1, (const bf16*)W2, nseg0, nseg1, N, \
+      K, KS, partial, e)
+    if (steps <= GV_WAVES) GPTK_GV(GV_WAVES, 1);
+    else if (steps <= 2 * GV_WAVES) GPTK_GV(GV_WAVES, 2);
+    else GPTK_GV(8, 3);
 #undef GPTK_GV
   } else {
     if (KS != 1) return hipErrorInvalidValue;

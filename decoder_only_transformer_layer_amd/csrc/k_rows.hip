@@ -153,65 +153,50 @@ __global__ __launch_bounds__(256) void mix_norm_kernel(
   }
 }
 
-// One block per row (few rows, long partial sums): x += sum_k add[k] (K-split partial
-// products, summed in a fixed order), then the optional x0 mix, then xn = RMSNorm(x).  Each
-// thread owns up to AMN_NP 4-element chunks (one when C <= 4 * blockDim).  A chunk's partial
-// products are loaded AMN_KB at a time, all before any is added, so their round trips overlap;
-// the sum runs over four interleaved accumulators (split k into k mod 4, combined pairwise), and
-// the updated chunks stay in registers through the block's sum of squares.
-constexpr int AMN_KB = 32, AMN_NP = 2, AMN_NTH = 512;
-template <typename AT>
-__global__ __launch_bounds__(AMN_NTH) void add_mix_norm_kernel(float* __restrict__ x,
-                                                            const float* __restrict__ add, int ks,
-                                                            const float* __restrict__ x0,
-                                                            const float* __restrict__ lam,
-                                                            const float* __restrict__ mu, int layer,
-                                                            bool mix, AT* __restrict__ xn, int M,
-                                                            int C, float eps) {
-  __shared__ float red[AMN_NTH / 64];
-  const int row = blockIdx.x, tid = threadIdx.x, nth = blockDim.x;
-  float* xr = x + (size_t)row * C;
-  const float a = mix ? lam[layer] : 1.f, b = mix ? mu[layer] : 0.f;
-  f32x4 v[AMN_NP];
-  float ss = 0.f;
+// Rows of x after a K-split product, each row spread over blocks of AMR_COLS columns (few rows,
+// long partial sums): x += sum_k add[k] (the partials of a chunk all loaded, AMN_KB at a time,
+// before any is added, then summed over four interleaved accumulators -- k into k mod 4,
+// combined pairwise), then the optional x0 mix x = lam[layer] x + mu[layer] x0.  Writes x,
+// xb = bf16(x) and the block's sum of squares of its columns of x, ss[row * nblk + blk] (per
+// thread its 4 columns in order, then a wavefront butterfly); the consuming product applies the
+// row scale 1/rms from those sums.
+constexpr int AMN_KB = 32, AMR_COLS = 256;
+__global__ __launch_bounds__(64) void add_mix_rows_kernel(float* __restrict__ x,
+                                                          const float* __restrict__ add, int ks,
+                                                          const float* __restrict__ x0,
+                                                          const float* __restrict__ lam,
+                                                          const float* __restrict__ mu, int layer,
+                                                          bool mix, bf16* __restrict__ xb,
+                                                          float* __restrict__ ss, int M, int C) {
+  const int blk = blockIdx.x, row = blockIdx.y;
+  const int i = blk * AMR_COLS + 4 * threadIdx.x;
+  float q = 0.f;
+  if (i < C) {
+    float* const xr = x + (size_t)row * C + i;
+    const f32x4 xv = *(const f32x4*)xr;
+    const f32x4 x0v = mix ? *(const f32x4*)(x0 + (size_t)row * C + i) : f32x4{};
+    f32x4 y4[4] = {};
+    for (int k0 = 0; k0 < ks; k0 += AMN_KB) {
+      f32x4 t[AMN_KB];
 #pragma unroll
-  for (int p = 0; p < AMN_NP; ++p) {
-    const int i = 4 * (tid + p * nth);
-    if (i < C) {
-      const f32x4 xv = *(const f32x4*)(xr + i);
-      const f32x4 x0v = mix ? *(const f32x4*)(x0 + (size_t)row * C + i) : f32x4{};
-      f32x4 y4[4] = {};
-      for (int k0 = 0; k0 < ks; k0 += AMN_KB) {
-        f32x4 t[AMN_KB];
+      for (int k = 0; k < AMN_KB; ++k)
+        if (k0 + k < ks) t[k] = *(const f32x4*)(add + ((size_t)(k0 + k) * M + row) * C + i);
 #pragma unroll
-        for (int k = 0; k < AMN_KB; ++k)
-          if (k0 + k < ks) t[k] = *(const f32x4*)(add + ((size_t)(k0 + k) * M + row) * C + i);
-#pragma unroll
-        for (int k = 0; k < AMN_KB; ++k)
-          if (k0 + k < ks) y4[k & 3] += t[k];  // AMN_KB is a multiple of 4: (k0 + k) & 3 == k & 3
-      }
-      const f32x4 y = (y4[0] + y4[1]) + (y4[2] + y4[3]);
-      f32x4 w = xv + y;
-      if (mix) w = a * w + b * x0v;
-      *(f32x4*)(xr + i) = w;
-      ss += w[0] * w[0] + w[1] * w[1] + w[2] * w[2] + w[3] * w[3];
-      v[p] = w;
+      for (int k = 0; k < AMN_KB; ++k)
+        if (k0 + k < ks) y4[k & 3] += t[k];  // AMN_KB is a multiple of 4: (k0 + k) & 3 == k & 3
     }
-  }
-  ss = wave_sum(ss);
-  if ((tid & 63) == 0) red[tid >> 6] = ss;
-  __syncthreads();
-  float tot = 0.f;
-  for (int j = 0; j < (nth >> 6); ++j) tot += red[j];
-  const float r = rsqrtf(tot / (float)C + eps);
+    const f32x4 y = (y4[0] + y4[1]) + (y4[2] + y4[3]);
+    f32x4 w = xv + y;
+    if (mix) w = lam[layer] * w + mu[layer] * x0v;
+    *(f32x4*)xr = w;
+    bf16x4 wb;
 #pragma unroll
-  for (int p = 0; p < AMN_NP; ++p) {
-    const int i = 4 * (tid + p * nth);
-    if (i < C) {
-      float e[4] = {v[p][0] * r, v[p][1] * r, v[p][2] * r, v[p][3] * r};
-      store4(xn + (size_t)row * C + i, e);
-    }
+    for (int k = 0; k < 4; ++k) wb[k] = (bf16)w[k];
+    *(bf16x4*)(xb + (size_t)row * C + i) = wb;
+    q = w[0] * w[0] + w[1] * w[1] + w[2] * w[2] + w[3] * w[3];
   }
+  q = wave_sum(q);
+  if (threadIdx.x == 0) ss[(size_t)row * gridDim.x + blk] = q;
 }
 
 __global__ void rope_table_kernel(float2* __restrict__ cs, int T, int half, double base) {
@@ -312,20 +297,20 @@ hipError_t launch_embed_norm(const int32_t* tokens, const void* wte, bool wbf16,
   });
 }
 
-int mix_norm_add_max_cols() { return 4 * AMN_NTH * AMN_NP; }
+int add_mix_rows_blocks(int C) { return (C + AMR_COLS - 1) / AMR_COLS; }
+
+hipError_t launch_add_mix_rows(float* x, const float* add, int ks, const float* x0, const float* lam,
+                               const float* mu, int layer, bool mix, void* xb, float* ss, int M,
+                               int C, hipStream_t s) {
+  if (C % 4 || ks < 0 || (ks > 0 && add == nullptr) || M < 1) return hipErrorInvalidValue;
+  add_mix_rows_kernel<<<dim3(add_mix_rows_blocks(C), M), 64, 0, s>>>(x, add, ks, x0, lam, mu, layer, mix,
+                                                                    (bf16*)xb, ss, M, C);
+  return hipGetLastError();
+}
 
 hipError_t launch_mix_norm(float* x, const float* x0, const float* lam, const float* mu, int layer,
                            bool mix, void* xn, bool xbf16, int M, int C, float eps, hipStream_t s,
-                           int c1, const float* add, int add_ks) {
-  if (add != nullptr) {  // x += the K-split partial products (summed in split order), fused
-    if (C % 4 || add_ks < 1 || (c1 > 0 && c1 != C) || C > 4 * AMN_NTH * AMN_NP) return hipErrorInvalidValue;
-    const int chunks = C / 4, nth = chunks <= AMN_NTH ? (chunks + 63) / 64 * 64 : AMN_NTH;
-    if (xbf16)
-      add_mix_norm_kernel<bf16><<<M, nth, 0, s>>>(x, add, add_ks, x0, lam, mu, layer, mix, (bf16*)xn, M, C, eps);
-    else
-      add_mix_norm_kernel<float><<<M, nth, 0, s>>>(x, add, add_ks, x0, lam, mu, layer, mix, (float*)xn, M, C, eps);
-    return hipGetLastError();
-  }
+                           int c1) {
   if (c1 <= 0) c1 = C;
   if (C % 4 || c1 % 4 || c1 > C) return hipErrorInvalidValue;
   const int grid = (M + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;

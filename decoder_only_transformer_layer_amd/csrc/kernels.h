@@ -46,13 +46,17 @@ hipError_t launch_embed_norm(const int32_t* tokens, const void* wte, bool wbf16,
                              float eps, unsigned* flags, hipStream_t s, const void* pe = nullptr,
                              int c1 = 0);
 
-// x += sum_k add[k] (add: optional [add_ks][M][C] partials, summed in order), then if mix:
-// x = lam[layer] x + mu[layer] x0 (in place).  Then xn = RMSNorm(x).
+// If mix: x = lam[layer] x + mu[layer] x0 (in place).  Then xn = RMSNorm(x).
 hipError_t launch_mix_norm(float* x, const float* x0, const float* lam, const float* mu, int layer,
                            bool mix, void* xn, bool xbf16, int M, int C, float eps, hipStream_t s,
-                           int c1 = 0, const float* add = nullptr, int add_ks = 0);
-// Widest row (C) launch_mix_norm takes with partials to add (add != NULL).
-int mix_norm_add_max_cols();
+                           int c1 = 0);
+// x += sum_k add[k] (add: [ks][M][C] partials, summed in order; ks = 0: none), then if mix: x = lam[layer] x +
+// mu[layer] x0 (in place); xb = bf16(x) and ss [M][add_mix_rows_blocks(C)] = per-block sums of
+// squares of each row of x (its row scale is applied by the consuming product).
+int add_mix_rows_blocks(int C);
+hipError_t launch_add_mix_rows(float* x, const float* add, int ks, const float* x0, const float* lam,
+                               const float* mu, int layer, bool mix, void* xb, float* ss, int M,
+                               int C, hipStream_t s);
 
 // fp32 path value embedding, in place on the v columns of qkv [M][ld] (v head h at column
 // voff + h*D): v += 3 sigmoid(xn[m][0:12] . gate[h]) * ve[tokens[m]][h*D : (h+1)*D].
@@ -71,18 +75,22 @@ hipError_t launch_qk_rope_norm(void* qk, bool bf16, int ld, const float2* cs, in
 // K a multiple of 64), then per element: DEC_STORE out_f32 = y; DEC_RELU2 out_act =
 // relu(y)^2; DEC_RESID out_f32 += y; DEC_LOGITS out_f32 = cap tanh(y / cap), NaN for rows whose
 // pos is outside [0, T) or whose token is outside [0, V).
-enum DecEpi { DEC_STORE = 0, DEC_RELU2 = 1, DEC_RESID = 2, DEC_LOGITS = 3 };
+// DEC_RESID_RS (bf16, KS = 1): x += y, also xb = bf16(x) [B][ldo] and ss [B][N / 32] = per-block
+// sums of squares of each row of x, for a consumer's row scale.
+enum DecEpi { DEC_STORE = 0, DEC_RELU2 = 1, DEC_RESID = 2, DEC_LOGITS = 3, DEC_RESID_RS = 4 };
 // KS > 1 (bf16 only) splits K over KS blocks per row block: the product then only stores its
 // KS partial tiles in partial[KS][B][N] (no epilogue) and the consumer sums them in order.
-// xnorm (bf16, KS = 1): act is the fp32 residual stream [B][lda], RMS-normalised in the product
-// (rounded to bf16 as loaded, outputs of row b scaled by (sum_k x[b][k]^2 / K + eps)^-1/2).
+// rs (bf16): act is bf16(x) of an un-normalised x and the outputs of row b (partials included)
+// are scaled by (sum_{j < rs_n} rs[b * rs_n + j] / K + eps)^-1/2, rs holding per-block sums of
+// squares of row b of x (from DEC_RESID_RS or launch_add_mix_rows), rs_n <= 128.
 int gemv_splits(int N, int K);
 hipError_t launch_gemv(bool bf16, int kind, const void* act, int lda, int B, const void* W0,
                        const void* W1, const void* W2, int nseg0, int nseg1, int N, int K,
                        void* out, int ldo, hipStream_t s, int KS = 1, float* partial = nullptr,
                        float cap = 0.f, const int32_t* pos = nullptr,
                        const int32_t* tokens = nullptr, int T = 0, int V = 0,
-                       bool xnorm = false, float eps = 0.f);
+                       const float* rs = nullptr, int rs_n = 0, float eps = 0.f, void* xb = nullptr,
+                       float* ss = nullptr);
 // RoPE at pos[b] + per-head RMSNorm of the q and k heads of y [KS][B][ldy] (fp32 K-split
 // partials summed in order; heads q | k | v), q_hat to qout [B, H*D], k_hat and v to the caches
 // [B, Hkv, T, D] at position pos[b]; a row with pos outside [0, T) writes nothing and raises
