@@ -214,8 +214,8 @@ def test_decode_validation_and_argument_errors(lib):
     c = gf.make_cfg(p)
     assert gf.gpt_kv_cache_bytes(c) == 24 * 2 * 8 * 12 * 2048 * 128 * 2
     assert gf.gpt_decode_workspace_bytes(c) > 0
-    # bf16 d_model beyond the residual-norm kernel's 4096 columns: refused before any launch (the
-    # forward itself takes it)
+    # bf16 d_model beyond 4096 (the widest the decode products' row scales and the decode tests
+    # cover): refused before any launch (the forward itself takes it)
     wide = p.with_(d_model=8192, n_head=64, n_kv_head=64, mlp_dim=4 * 8192, n_layer=2)
     assert gf.gpt_validate(gf.make_cfg(wide)) == gf.GPT_OK
     for bad in (p.with_(batch=33), p.with_(seq_len=16384), gptdata.preset("d24gve"),

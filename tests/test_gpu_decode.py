@@ -108,6 +108,19 @@ def test_decode_group8_multichunk_bf16():
     _check_bf16_logits(got, ref)
 
 
+def test_decode_widest_bf16():
+    """bf16 at the widest model decoding takes (d_model 4096: the out-projection leaves 128
+    per-block row sums, the most a product's row scale takes), one layer, 2 rows over 64
+    positions, row 1 one position behind row 0."""
+    p = gptdata.Preset(name="decwide", n_layer=1, d_model=4096, n_head=32, n_kv_head=32, head_dim=128,
+                       mlp_dim=4096, vocab=512, seq_len=64, batch=2, dtype="bf16", short_window=64,
+                       lambda_range=(0.9, 1.1), mu_range=(0.0, 0.2), seed=59)
+    w, tok, _ = gptdata.make_inputs(p)
+    got = _decode_all(p, w, tok, lag=[0, 1])
+    ref = oracle.forward(p, params_of(w), tok, want_logits=True)["logits"]
+    _check_bf16_logits(got, ref)
+
+
 def test_decode_d24_positions():
     """d24 weights, 2 rows, the whole 2048-token cache: logits at positions 0, 511, 1023, 1024,
     1500 and 2047 of row 0 against one oracle forward of that row."""
