@@ -718,10 +718,10 @@ hipError_t launch_gemv(bool bf, int kind, const void* act, int lda, int B, const
     if (KS > 1 && !partial) return hipErrorInvalidValue;
     const int grid = (N + GV_ROWS - 1) / GV_ROWS * KS;
     // K steps of the largest split: up to two per wavefront staged together (8 or 16 KB of LDS
-    // per block); longer ranges (the unsplit MLP-up and lm_head products) on 8 wavefronts with
-    // up to three steps each in flight (96 KB: one block per CU).  Measured at the d24 shapes
-    // with the weights cold: 8 x 3 against 4 x 6 took MLP up 6.9 -> 6.4 us, lm_head 25.3 -> 23.2
-    // us; the whole d24 decode step 1.487 -> 1.477 ms.
+    // per block); longer ranges (the unsplit out-projection, MLP-up and lm_head products) on 8
+    // wavefronts with two steps each in flight per batch (64 KB: two blocks per CU).  Measured
+    // at the d24 shapes with the weights cold (MLP up / lm_head): 4 x 6 steps 6.9 / 25.3 us,
+    // 8 x 3 6.4 / 23.5 us, 8 x 2 6.4 / 19.2 us, 16 x 2 6.3 / 22.7 us.
     const int steps = (K / GV_KB + KS - 1) / KS;
 #define GPTK_GV(NW, DEPTH)                                                                          \
   gemv_bf16_kernel<NW, DEPTH><<<grid, NW * 64, 0, s>>>(                                             \
@@ -729,7 +729,7 @@ hipError_t launch_gemv(bool bf, int kind, const void* act, int lda, int B, const
       K, KS, partial, e)
     if (steps <= GV_WAVES) GPTK_GV(GV_WAVES, 1);
     else if (steps <= 2 * GV_WAVES) GPTK_GV(GV_WAVES, 2);
-    else GPTK_GV(8, 3);
+    else GPTK_GV(8, 2);
 #undef GPTK_GV
   } else {
     if (KS != 1) return hipErrorInvalidValue;
