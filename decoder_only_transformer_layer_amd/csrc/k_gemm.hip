@@ -874,10 +874,54 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int pid) {
         return;
       }
     }
-    // v tiles (columns >= nqk, no value embeddings): each 32-row group of the wavefront's tile is
-    // staged through wavefront-private LDS transposed ([col][t], bf16) and written as 16-byte
-    // runs of 8 positions of v^T [B][Hkv][D][T].
+    // v tiles (columns >= nqk, no value embeddings): the wavefront's tile is staged through
+    // wavefront-private LDS transposed ([col][t], bf16) and written as 16-byte runs of 8
+    // positions of v^T [B][Hkv][D][T].  64-row wavefront tiles stage both 32-row groups
+    // together (in column groups of FG fragments, as LDS allows), so that each column's 64
+    // positions go out as one 128-byte run (two where the rows cross into the next sequence);
+    // 32-row wavefront tiles stage each group on its own.
     bf16* vt = (bf16*)g.vt;
+    if constexpr (FM == 2) {
+      constexpr int LV2 = 64 + 8;  // staging pitch (bf16)
+      constexpr int FG = (WM * WN * FN * 32 * LV2 * 2 <= (int)sizeof(lds)) ? FN : FN / 2;
+      static_assert(FN % FG == 0 && WM * WN * FG * 32 * LV2 * 2 <= (int)sizeof(lds), "v staging exceeds LDS");
+      bf16* const stg = lds + wid * FG * 32 * LV2;
+      __syncthreads();  // every wavefront is done with the operand tiles
+      // the 64 rows are consecutive positions of one sequence, or of two (T % 32 == 0)
+      const int row0 = m0 + wm * TM;
+      const int bb0 = row0 / g.T, t00 = row0 - bb0 * g.T;
+#pragma unroll
+      for (int f0 = 0; f0 < FN; f0 += FG) {
+#pragma unroll
+        for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+          for (int f = 0; f < FG; ++f)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {  // rows 32 fm + 8j + 4hl + (0..3): four consecutive t
+              bf16x4 v4;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) v4[i] = (bf16)acc[fm][f0 + f][4 * j + i];
+              *(bf16x4*)(stg + (f * 32 + rl) * LV2 + 32 * fm + 8 * j + 4 * hl) = v4;
+            }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int k = 0; k < FG * 32 * 8 / 64; ++k) {  // FG*32 columns x 8 runs of 8 positions
+          const int idx = lane + 64 * k, cl = idx >> 3, ch = idx & 7;
+          const int col = n0 + wn * TN + f0 * 32 + cl;
+          if (col < N && row0 + ch * 8 < M) {
+            const int vc = col - g.nqk, gg = g.v_head_off + vc / g.D, d = vc - (vc / g.D) * g.D;
+            const bool nxt = t00 + ch * 8 >= g.T;  // these 8 rows begin the next sequence
+            const int bb = bb0 + nxt, t = t00 + ch * 8 - (nxt ? g.T : 0);
+            *(bf16x8*)(vt + ((size_t)(bb * g.Hkv + gg) * g.D + d) * g.T + t) =
+                *(const bf16x8*)(stg + cl * LV2 + ch * 8);
+          }
+        }
+        __builtin_amdgcn_wave_barrier();  // reads of this group precede the next group's writes
+      }
+      return;
+    }
     constexpr int LV = 32 + 8;  // staging pitch (bf16)
     static_assert(WM * WN * TN * LV * 2 <= (int)sizeof(lds), "v staging exceeds LDS");
     bf16* const stg = lds + wid * TN * LV;
