@@ -600,7 +600,8 @@ static gpt_status validate_decode(const gpt_cfg* c) {
   const gpt_status st = validate(c);
   if (st != GPT_OK) return st;
   if (c->batch > 32 || c->seq_len > 8192 || c->n_head / c->n_kv_head > 8) return GPT_E_UNSUPPORTED;
-  // the widest bf16 model the decode tests cover
+  // bf16: a product's row scale takes up to 128 per-block row sums (the out-projection leaves
+  // d_model / 32 of them); 4096 is also the widest model the decode tests cover
   if (c->dtype == GPT_BF16 && c->d_model > 4096) return GPT_E_UNSUPPORTED;
   if (any_ve(c) || c->looped || c->nested_c1) return GPT_E_UNSUPPORTED;
   return GPT_OK;
