@@ -108,6 +108,19 @@ def test_decode_group8_multichunk_bf16():
     _check_bf16_logits(got, ref)
 
 
+def test_decode_32_rows_bf16():
+    """bf16 with the most rows a decode step takes (32: every lane of the products' batch operand
+    live, the row scales of rows 8-31 summed by the later wavefronts), GQA 2:1, rows staggered
+    by up to three positions."""
+    p = gptdata.Preset(name="dec32r", n_layer=2, d_model=256, n_head=4, n_kv_head=2, head_dim=64,
+                       mlp_dim=1024, vocab=600, seq_len=64, batch=32, dtype="bf16", short_window=24,
+                       lambda_range=(0.9, 1.1), mu_range=(0.0, 0.2), seed=63)
+    w, tok, _ = gptdata.make_inputs(p)
+    got = _decode_all(p, w, tok, lag=np.arange(32) % 4)
+    ref = oracle.forward(p, params_of(w), tok, want_logits=True)["logits"]
+    _check_bf16_logits(got, ref)
+
+
 def test_decode_widest_bf16():
     """bf16 at the widest model decoding takes (d_model 4096: the out-projection leaves 128
     per-block row sums, the most a product's row scale takes), one layer, 2 rows over 64
