@@ -17,7 +17,7 @@ namespace gptk {
 namespace {
 
 constexpr int GV_ROWS = 32;   // weight rows per block (one 32x32 MFMA output tile, batch in N)
-constexpr int GV_WAVES = 4;   // wavefronts per block (8 for the unsplit products with long K ranges)
+constexpr int GV_WAVES = 4;   // wavefronts per block for short K ranges (8 for longer ones)
 constexpr int GV_KB = 64;     // K per wavefront step: four 32x32x16 MFMAs
 constexpr int GV_TARGET_BLOCKS = 2048;  // K splits aim at this many blocks (2048: 0.6 % faster d24 step than 1024)
 
@@ -696,13 +696,14 @@ __global__ __launch_bounds__(SMP_THREADS) void sample_kernel(const float* __rest
 
 }  // namespace
 
-// K splits of a product: enough blocks to keep every CU busy, each wavefront with >= 1 step.
-// (Half the splits, two steps per wavefront loaded together, made the single products 2-10 %
-// faster at the d24 shapes but the whole d24 decode step 0.7 % slower.)
+// K splits of a product: enough blocks to keep every CU busy, each split with >= 8 K steps (one
+// per wavefront of an 8-wavefront block).  At d24 (q/k/v 3 splits, MLP down 12), against 4-
+// wavefront blocks and twice the splits: decode step 1.368 -> 1.353 ms, alternated on one box;
+// the same halved splits on 4 wavefronts with two steps each were 0.7 % slower.
 int gemv_splits(int N, int K) {
   const int nrb = (N + GV_ROWS - 1) / GV_ROWS, nks = K / GV_KB;
   int ks = (GV_TARGET_BLOCKS + nrb - 1) / nrb;
-  ks = ks < nks / GV_WAVES ? ks : nks / GV_WAVES;
+  ks = ks < nks / (2 * GV_WAVES) ? ks : nks / (2 * GV_WAVES);
   return ks > 1 ? ks : 1;
 }
 
@@ -721,8 +722,8 @@ hipError_t launch_gemv(bool bf, int kind, const void* act, int lda, int B, const
   if (bf) {
     if (KS > 1 && !partial) return hipErrorInvalidValue;
     const int grid = (N + GV_ROWS - 1) / GV_ROWS * KS;
-    // K steps of the largest split: up to two per wavefront staged together (8 or 16 KB of LDS
-    // per block); longer ranges (the unsplit out-projection, MLP-up and lm_head products) on 8
+    // K steps of the largest split: up to 4 on 4 wavefronts, up to 8 on 8 (one step each, 32 KB
+    // of LDS); longer ranges (the unsplit out-projection, MLP-up and lm_head products) on 8
     // wavefronts with two steps each in flight per batch (64 KB: two blocks per CU).  Measured
     // at the d24 shapes with the weights cold (MLP up / lm_head): 4 x 6 steps 6.9 / 25.3 us,
     // 8 x 3 6.4 / 23.5 us, 8 x 2 6.4 / 19.2 us, 16 x 2 6.3 / 22.7 us.
@@ -732,7 +733,7 @@ hipError_t launch_gemv(bool bf, int kind, const void* act, int lda, int B, const
       (const bf16*)act, lda, B, (const bf16*)W0, (const bf16*)W1, (const bf16*)W2, nseg0, nseg1, N, \
       K, KS, partial, e)
     if (steps <= GV_WAVES) GPTK_GV(GV_WAVES, 1);
-    else if (steps <= 2 * GV_WAVES) GPTK_GV(GV_WAVES, 2);
+    else if (steps <= 8) GPTK_GV(8, 1);
     else GPTK_GV(8, 2);
 #undef GPTK_GV
   } else {
