@@ -334,7 +334,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(
 // kernel merges the chunks: o = sum_c e^(m_c - m) O_c / sum_c e^(m_c - m) l_c.  Query head h
 // reads KV head h*Hkv/H, i.e. the group of head h is h / G.
 constexpr int DA_THREADS = 512;   // per chunk block (d24 decode step: 256 1.374 ms, 512 1.365, 1024 1.533)
-constexpr int DA_CHUNK = 128;       // keys per block (64: level at d24 decode, 1.410 vs 1.406 ms; 256: 1.48 ms)
+constexpr int DA_CHUNK = 128;       // keys per block (d24 decode step with 512-thread blocks: 64 1.451 ms, 128 1.352, 256 1.373)
 constexpr int DA_MAX_GROUP = 8;     // query heads per KV head
 
 
