@@ -278,17 +278,45 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(const bf16* __res
   }
 
   const float l = l_run + __shfl_xor(l_run, 32, 64);
-  // The wavefront's 32 output rows go out through LDS (the K/V ring, free once every wavefront
-  // is past its last tile) as whole rows: 16 bytes per lane, consecutive lanes on consecutive
-  // chunks of a row, instead of 8-byte pieces of 32 rows per store.
-  constexpr int OP = D + 8;                                 // staging pitch (bf16), 16-byte rows
-  constexpr int WB = 32 * OP;                               // staging elements per wavefront
-  constexpr int KW = (int)(sizeof(Ks) / sizeof(bf16)) / WB; // wavefronts staged in Ks, the rest in Vs
-  static_assert(KW + (int)(sizeof(Vs) / sizeof(bf16)) / WB >= NW, "output staging exceeds the K/V ring");
-  __syncthreads();  // every wavefront is done with the ring
-  bf16* const stg = wid < KW ? &Ks[0][0] + wid * WB : &Vs[0][0] + (wid - KW) * WB;
-  {
-    const float inv = 1.0f / l;  // rows past T (inf here) are not stored
+  // head_dim 128 without the prior: the wavefront's 32 output rows go out through LDS (the K/V
+  // ring, free once every wavefront is past its last tile) as whole rows, 16 bytes per lane with
+  // consecutive lanes on consecutive chunks of a row, instead of 8-byte pieces of 32 rows per
+  // store (d24: 117.2 -> 114.2 us per launch).  The head_dim-64 and prior forms store directly
+  // (staged, they measured level and 2 % slower).
+  constexpr bool STAGE_O = D == 128 && !PRIOR;
+  if constexpr (STAGE_O) {
+    constexpr int OP = D + 8;                                 // staging pitch (bf16), 16-byte rows
+    constexpr int WB = 32 * OP;                               // staging elements per wavefront
+    constexpr int KW = (int)(sizeof(Ks) / sizeof(bf16)) / WB; // wavefronts staged in Ks, the rest in Vs
+    static_assert(KW + (int)(sizeof(Vs) / sizeof(bf16)) / WB >= NW, "output staging exceeds the K/V ring");
+    __syncthreads();  // every wavefront is done with the ring
+    bf16* const stg = wid < KW ? &Ks[0][0] + wid * WB : &Vs[0][0] + (wid - KW) * WB;
+    {
+      const float inv = 1.0f / l;  // rows past T (inf here) are not stored
+#pragma unroll
+      for (int d = 0; d < DT; ++d)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          bf16x4 v4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v4[i] = (bf16)(ot[d][4 * j + i] * inv);
+          *(bf16x4*)(stg + rl * OP + d * 32 + 8 * j + 4 * hl) = v4;
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    constexpr int OCH = D / 8;  // 16-byte chunks per output row
+#pragma unroll
+    for (int k = 0; k < 32 * OCH / 64; ++k) {
+      const int idx = lane + 64 * k, r = idx / OCH, ch = idx % OCH;
+      const int q = qw + r;
+      if (q < T)
+        *(bf16x8*)(o + (size_t)(b * T + q) * (H * D) + h * D + 8 * ch) = *(const bf16x8*)(stg + r * OP + 8 * ch);
+    }
+  } else if (myq < T) {
+    const float inv = 1.0f / l;
+    bf16* op = o + (size_t)(b * T + myq) * (H * D) + h * D;
 #pragma unroll
     for (int d = 0; d < DT; ++d)
 #pragma unroll
@@ -296,19 +324,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(const bf16* __res
         bf16x4 v4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) v4[i] = (bf16)(ot[d][4 * j + i] * inv);
-        *(bf16x4*)(stg + rl * OP + d * 32 + 8 * j + 4 * hl) = v4;
+        *(bf16x4*)(op + d * 32 + 8 * j + 4 * hl) = v4;
       }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  constexpr int OCH = D / 8;  // 16-byte chunks per output row
-#pragma unroll
-  for (int k = 0; k < 32 * OCH / 64; ++k) {
-    const int idx = lane + 64 * k, r = idx / OCH, ch = idx % OCH;
-    const int q = qw + r;
-    if (q < T)
-      *(bf16x8*)(o + (size_t)(b * T + q) * (H * D) + h * D + 8 * ch) = *(const bf16x8*)(stg + r * OP + 8 * ch);
   }
 #endif
 }
