@@ -283,8 +283,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="d24")
     ap.add_argument("--cpu-rows", type=int, default=8,
-                    help="whole rows of the batch the CPU oracle evaluates (default: all of d24's 8)")
-    ap.add_argument("--cpu-budget-s", type=float, default=240.0,
+                    help="at most this many whole rows of the batch for the CPU oracle")
+    ap.add_argument("--cpu-budget-s", type=float, default=25.0,
                     help="stop the CPU oracle after the row that passes this many seconds")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-steps", type=int, default=3,
