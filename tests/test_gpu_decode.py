@@ -121,6 +121,21 @@ def test_decode_32_rows_bf16():
     _check_bf16_logits(got, ref)
 
 
+def test_decode_single_row_bf16():
+    """bf16 with one row (one live lane of the products' batch operand), d_model 640 (ten K steps
+    of 64: the products' two-deep tile loop with a ragged last round), a query group of 5 (10
+    heads of 64 on 2 KV heads), MLP down left unsplit, a 333-entry vocabulary (a ragged last
+    lm_head row block), windows 40 / full over 64 positions."""
+    p = gptdata.Preset(name="dec1r", n_layer=2, d_model=640, n_head=10, n_kv_head=2, head_dim=64,
+                       mlp_dim=1280, vocab=333, seq_len=64, batch=1, dtype="bf16", short_window=40,
+                       lambda_range=(0.9, 1.1), mu_range=(0.0, 0.2), seed=65)
+    w, tok, _ = gptdata.make_inputs(p)
+    windows = [40, 64]
+    got = _decode_all(p, w, tok, windows=windows)
+    ref = oracle.forward(p, params_of(w), tok, want_logits=True, windows=windows)["logits"]
+    _check_bf16_logits(got, ref)
+
+
 def test_decode_widest_bf16():
     """bf16 at the widest model decoding takes (d_model 4096: the out-projection leaves 128
     per-block row sums, the most a product's row scale takes), one layer, 2 rows over 64
