@@ -368,3 +368,21 @@ def test_prefill_then_decode_bf16():
     got = np.concatenate([first[None]] + [steps[s][None] for s in range(20)])
     want = np.stack([np.stack([ref[b, lens[b] - 1 + s] for b in range(3)]) for s in range(21)])
     _check_bf16_logits(got, want)
+
+
+def test_prefill_then_decode_single_row_bf16():
+    """bf16, one row (a 64-row forward for the prefill), GQA 2:1 at head_dim 64, a 333-entry
+    vocabulary: a prompt of 37 tokens padded to 64, then 32 decode steps (positions 37 to 68: the
+    first 27 overwrite the cache slots the prefill filled past the prompt, the last 5 go past the
+    padded length)."""
+    p = gptdata.Preset(name="pre1r", n_layer=2, d_model=256, n_head=4, n_kv_head=2, head_dim=64,
+                       mlp_dim=1024, vocab=333, seq_len=128, batch=1, dtype="bf16", short_window=48,
+                       lambda_range=(0.9, 1.1), mu_range=(0.0, 0.2), seed=67)
+    w, tok, _ = gptdata.make_inputs(p)
+    windows = [48, 128]
+    lens = [37]
+    first, steps = _prefill_then_decode(p, w, tok, 64, lens, 32, windows=windows)
+    ref = oracle.forward(p, params_of(w), tok, want_logits=True, windows=windows)["logits"]
+    got = np.concatenate([first[None]] + [steps[s][None] for s in range(32)])
+    want = np.stack([ref[0, lens[0] - 1 + s][None] for s in range(33)])
+    _check_bf16_logits(got, want)
