@@ -61,6 +61,20 @@ def test_decode_matches_forward_fp32():
     assert err <= 1e-3
 
 
+def test_decode_single_row_fp32():
+    """fp32 with one row, d_model 192 (three K steps of 64), a query group of 3 (3 heads of 64 on
+    one KV head), a 333-entry vocabulary, 40 positions (not a multiple of 64), window 16 / full."""
+    p = gptdata.Preset(name="dec1f", n_layer=2, d_model=192, n_head=3, n_kv_head=1, head_dim=64,
+                       mlp_dim=768, vocab=333, seq_len=40, batch=1, dtype="f32", short_window=16,
+                       lambda_range=(0.9, 1.1), mu_range=(0.0, 0.2), seed=69)
+    w, tok, _ = gptdata.make_inputs(p)
+    got = _decode_all(p, w, tok)
+    ref = oracle.forward(p, params_of(w), tok, want_logits=True)["logits"]
+    err = np.max(np.abs(got - ref)) / np.max(np.abs(ref))
+    print(f"  decode fp32: logits err/max {err:.2e}")
+    assert err <= 1e-3
+
+
 def _check_bf16_logits(got, ref):
     d = got - ref
     rms, mx = float(np.sqrt(np.mean(d * d))), float(np.max(np.abs(d)))
