@@ -121,6 +121,21 @@ def test_head_dim_64_bf16():
     _check_bf16(got, oracle.forward(p, params_of(w), tok, tgt))
 
 
+def test_single_row_bf16():
+    """One row of 64 tokens (the shortest bf16 sequence): B*T = 64 rows, a quarter of one
+    256-row GEMM tile and a single query tile; V = 333; windows 24 / full; 10% ignored targets;
+    the logits as well."""
+    p = _ragged_preset(n_layer=2, seq_len=64, batch=1, vocab=333, seed=13)
+    w, tok, tgt = gptdata.make_inputs(p, ignore_frac=0.1)
+    windows = [24, 64]
+    _, got = _run(p, w, tok, tgt, want_logits=True, windows=windows)
+    ref = oracle.forward(p, params_of(w), tok, tgt, want_logits=True, windows=windows)
+    assert got["status"] == gf.GPT_OK
+    _check_bf16(got, ref)
+    assert np.all(got["losses"][tgt == -1] == 0.0)
+    _check_logits_bf16(got["logits"], ref["logits"])
+
+
 def test_edge_cases_bf16():
     """Window 1 everywhere; an out-of-range token; all targets ignored; minimal T."""
     p = _ragged_preset(n_layer=2, seq_len=64, batch=3, vocab=300, seed=11)
